@@ -1,0 +1,221 @@
+"""Seeded generators and format encoders for the layer's inputs.
+
+Every tensor is drawn with its own ``torch.Generator`` whose seed mixes
+(workload id, seed, layer, tensor id, ...), so any one tensor can be regenerated alone.
+The stream depends on the device kind the generator runs on (CPU and GPU generators
+differ); a test draws its inputs once and hands the same bytes to both sides.
+
+Recipe (fixed by the workload descriptions; the pages give no weight statistics):
+  expert weights  fp32 N(0, 0.02), then quantised per group of 32 along the input dim
+  router          fp32 N(0, 0.02) [E][d]; int8 variant quantised per row
+  activations     fp32 N(0, 1) rounded to bf16 (round to nearest even)
+  Zipf bias       b_e = -s * ln(rank_e), rank = 1 + a seeded permutation of 0..E-1
+
+Encodings (the layer's input formats; decoding them is the layer's job, not this file's):
+  int4_g32  s = fp16(max|w_group| / 7); q = clamp(round_half_even(w / s), -8, 7);
+            byte = (q[2i] + 8) | (q[2i+1] + 8) << 4
+  int6_g32  s = fp16(max|w_group| / 31); q in [-32, 31]; code u = q + 32; the 32 codes of
+            a group form a 24-byte little-endian bit string, code i at bits [6i, 6i+6)
+  int8_row  s = fp16(max|w_row| / 127); q = clamp(round_half_even(w / s), -127, 127)
+An all-zero group gets s = 0 and every code q = 0.
+"""
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+FMT_FP32, FMT_INT8_ROW, FMT_INT4_G32, FMT_INT6_G32 = 0, 1, 2, 3
+FMT_BY_NAME = {"fp32": FMT_FP32, "int8_row": FMT_INT8_ROW, "int4_g32": FMT_INT4_G32,
+               "int6_g32": FMT_INT6_G32}
+
+# tensor ids inside one layer's seed
+_T_ROUTER, _T_BIAS, _T_GATE, _T_UP, _T_DOWN, _T_SGATE, _T_SUP, _T_SDOWN, _T_X = range(9)
+_MASK = (1 << 63) - 1
+
+
+def _seed(*parts):
+    h = 0x243F6A8885A308D3
+    for p in parts:
+        h = (h * 0x100000001B3 + int(p) + 0x9E3779B97F4A7C15) & _MASK
+        h ^= h >> 29
+    return h & _MASK
+
+
+def _gen(device, *parts):
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(*parts))
+    return g
+
+
+# ---------------------------------------------------------------- encoders
+
+def pack_int4(q):
+    """q int codes in [-8, 7], [..., K] -> uint8 [..., K/2]."""
+    u = (q + 8).to(torch.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).contiguous()
+
+
+def pack_int6(q):
+    """q int codes in [-32, 31], [..., K] (K % 32 == 0) -> uint8 [..., K*3/4]."""
+    u = (q + 32).to(torch.int32)
+    lead = u.shape[:-1]
+    u4 = u.reshape(*lead, -1, 4)              # 4 codes = 24 bits = 3 bytes
+    v = u4[..., 0] | (u4[..., 1] << 6) | (u4[..., 2] << 12) | (u4[..., 3] << 18)
+    b = torch.stack([v & 255, (v >> 8) & 255, (v >> 16) & 255], dim=-1)
+    return b.reshape(*lead, -1).to(torch.uint8).contiguous()
+
+
+def _group_quant(w, qmax, qmin):
+    *lead, N, K = w.shape
+    g = w.reshape(*lead, N, K // 32, 32)
+    s16 = (g.abs().amax(dim=-1) / float(qmax)).to(torch.float16)
+    s = s16.to(torch.float32)[..., None]
+    q = torch.where(s > 0, torch.round(g / torch.where(s > 0, s, torch.ones_like(s))),
+                    torch.zeros_like(g))
+    q = q.clamp(qmin, qmax).to(torch.int32).reshape(*lead, N, K)
+    return q, s16.contiguous()
+
+
+def quantize_int4_g32(w):
+    """fp32 [..., N, K] -> (packed uint8 [..., N, K/2], fp16 scales [..., N, K/32])."""
+    q, s = _group_quant(w, 7, -8)
+    return pack_int4(q), s
+
+
+def quantize_int6_g32(w):
+    """fp32 [..., N, K] -> (packed uint8 [..., N, K*3/4], fp16 scales [..., N, K/32])."""
+    q, s = _group_quant(w, 31, -32)
+    return pack_int6(q), s
+
+
+def quantize_int8_row(w):
+    """fp32 [E, d] -> (int8 [E, d], fp16 scales [E])."""
+    s16 = (w.abs().amax(dim=-1) / 127.0).to(torch.float16)
+    s = s16.to(torch.float32)[:, None]
+    q = torch.where(s > 0, torch.round(w / torch.where(s > 0, s, torch.ones_like(s))),
+                    torch.zeros_like(w))
+    return q.clamp(-127, 127).to(torch.int8).contiguous(), s16.contiguous()
+
+
+_QUANT = {"int4_g32": quantize_int4_g32, "int6_g32": quantize_int6_g32}
+
+
+def zipf_bias(E, s, gen, device):
+    """Router bias making expert popularity heavy-headed: b_e = -s * ln(rank_e)."""
+    rank = torch.randperm(E, generator=gen, device=device).to(torch.float64) + 1.0
+    return (-s * torch.log(rank)).to(torch.float32).contiguous()
+
+
+def bits16(t):
+    """bf16 / fp16 tensor -> numpy uint16 bit patterns (host copy)."""
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- a layer's tensors
+
+@dataclass
+class ExpertSet:
+    fmt: str
+    E: int
+    d: int
+    F: int
+    w_gate: torch.Tensor   # uint8 [E][F][d packed]
+    w_up: torch.Tensor     # uint8 [E][F][d packed]
+    w_down: torch.Tensor   # uint8 [E][d][F packed]
+    s_gate: torch.Tensor   # fp16 [E][F][d/32]
+    s_up: torch.Tensor     # fp16 [E][F][d/32]
+    s_down: torch.Tensor   # fp16 [E][d][F/32]
+
+    def host(self):
+        return {"fmt": FMT_BY_NAME[self.fmt], "E": self.E, "d": self.d, "F": self.F,
+                "w_gate": self.w_gate.cpu().numpy(), "w_up": self.w_up.cpu().numpy(),
+                "w_down": self.w_down.cpu().numpy(), "s_gate": bits16(self.s_gate),
+                "s_up": bits16(self.s_up), "s_down": bits16(self.s_down)}
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in
+                   (self.w_gate, self.w_up, self.w_down, self.s_gate, self.s_up, self.s_down))
+
+
+@dataclass
+class Router:
+    fmt: str
+    E: int
+    d: int
+    w: torch.Tensor                 # fp32 [E][d] or int8 [E][d]
+    scale: Optional[torch.Tensor]   # fp16 [E] (int8 only)
+    bias: Optional[torch.Tensor]    # fp32 [E] or None
+
+    def host(self):
+        return {"fmt": FMT_BY_NAME[self.fmt], "E": self.E, "d": self.d,
+                "w": self.w.cpu().numpy(),
+                "scale": None if self.scale is None else bits16(self.scale),
+                "bias": None if self.bias is None else self.bias.cpu().numpy()}
+
+
+@dataclass
+class Layer:
+    router: Router
+    routed: ExpertSet
+    shared: Optional[ExpertSet]
+
+
+def _experts(fmt, E, d, F, device, gens):
+    gg, gu, gd = gens
+    wg = torch.randn((E, F, d), generator=gg, device=device, dtype=torch.float32) * 0.02
+    pg, sg = _QUANT[fmt](wg)
+    del wg
+    wu = torch.randn((E, F, d), generator=gu, device=device, dtype=torch.float32) * 0.02
+    pu, su = _QUANT[fmt](wu)
+    del wu
+    wd = torch.randn((E, d, F), generator=gd, device=device, dtype=torch.float32) * 0.02
+    pd, sd = _QUANT[fmt](wd)
+    del wd
+    return ExpertSet(fmt, E, d, F, pg, pu, pd, sg, su, sd)
+
+
+def make_layer(w, seed=0, layer=0, device="cpu", bias=None, with_shared=True,
+               expert_chunk=64):
+    """All weights of one layer of workload ``w``.
+
+    bias: None -> the workload's own choice ("none" | "zipf"); or "none" / "zipf".
+    Routed experts are drawn in chunks of ``expert_chunk`` experts (each chunk its own
+    generator) to bound the fp32 staging memory.
+    """
+    bias = w.bias if bias is None else bias
+    dev = torch.device(device)
+    g = _gen(dev, w.wid, seed, layer, _T_ROUTER)
+    rw = torch.randn((w.E, w.d), generator=g, device=dev, dtype=torch.float32) * 0.02
+    if w.router_fmt == "int8_row":
+        rq, rs = quantize_int8_row(rw)
+        router_w, router_s = rq, rs
+    else:
+        router_w, router_s = rw.contiguous(), None
+    b = zipf_bias(w.E, 1.1, _gen(dev, w.wid, seed, layer, _T_BIAS), dev) if bias == "zipf" \
+        else None
+    router = Router(w.router_fmt, w.E, w.d, router_w, router_s, b)
+
+    parts = []
+    for e0 in range(0, w.E, expert_chunk):
+        n = min(expert_chunk, w.E - e0)
+        gens = [_gen(dev, w.wid, seed, layer, tid, e0) for tid in (_T_GATE, _T_UP, _T_DOWN)]
+        parts.append(_experts(w.routed_fmt, n, w.d, w.F, dev, gens))
+    routed = ExpertSet(w.routed_fmt, w.E, w.d, w.F,
+                       *[torch.cat([getattr(p, a) for p in parts]).contiguous() for a in
+                         ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")])
+    del parts
+    shared = None
+    if with_shared:
+        gens = [_gen(dev, w.wid, seed, layer, tid, 1 << 20) for tid in (_T_SGATE, _T_SUP,
+                                                                         _T_SDOWN)]
+        shared = _experts(w.shared_fmt, 1, w.d, w.F, dev, gens)
+    return Layer(router, routed, shared)
+
+
+def make_tokens(w, T=None, seed=0, layer=0, device="cpu", stream=0):
+    """bf16 [T][d] activations, N(0, 1) rounded to bf16."""
+    T = w.T if T is None else T
+    g = _gen(torch.device(device), w.wid, seed, layer, _T_X, stream, T)
+    x = torch.randn((T, w.d), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16).contiguous()
