@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) quantized routed-expert MoE layer.
+ *
+ * The layer, as the pages describe it: each layer owns 512 routed experts, every token
+ * is sent to 10 of them and to one shared expert that is always on
+ * [Strata 与 Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会]; a router that
+ * lives on the GPU makes the choice [本地部署Qwen3.8-Flash-Next模型的两条路线
+ * (blog.cycleuser.org), section 硬件形态决定了各自的走法]; expert weights are 4-bit,
+ * some mixed layers 6-bit and a dense projection 8-bit [same page, section 精度和内存占用];
+ * prefill batches many tokens per expert while decode is latency bound [telli.sh page,
+ * section GPU、RAM 和 SSD 各司其职].  One layer is the composition
+ *
+ *     moe_route -> moe_permute -> moe_expert_ffn (routed; and shared, dense) -> moe_combine
+ *
+ * Conventions for every entry point
+ *   - Pointers to tensors are DEVICE pointers (hipMalloc'd or torch-owned memory); the
+ *     descriptor structs themselves are read on the host during the call.  The caller
+ *     owns all memory; the library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *     entry point only enqueues work on that stream and returns; nothing synchronises
+ *     except moe_check_device_error.
+ *   - bf16 and fp16 values travel as uint16_t bit patterns.
+ *   - Validation happens on the host before any launch.  A failing call launches
+ *     nothing and returns a negative status; moe_last_error() has the detail (per
+ *     thread).  T = 0 is a valid no-op.
+ *   - Results are deterministic: the same inputs give the same bits on every run.
+ *
+ * Weight formats (groups of 32 consecutive elements along a row's input dimension):
+ *   MOE_FMT_INT4_G32  row of K codes = K/2 bytes; byte i: element 2i in the low nibble,
+ *                     2i+1 in the high nibble; value = s * (nibble - 8); one fp16 scale
+ *                     s per group, scales [rows][K/32].
+ *   MOE_FMT_INT6_G32  row = K*3/4 bytes; each group of 32 codes is a 24-byte
+ *                     little-endian bit string, code i at bits [6i, 6i+6);
+ *                     value = s * (code - 32).
+ *   MOE_FMT_INT8_ROW  router only: int8 [E][d] with one fp16 scale per row.
+ *   MOE_FMT_FP32      router only: fp32 [E][d].
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, bad format */
+    MOE_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for */
+    MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than moe_workspace_size */
+    MOE_ERR_HIP = -4,           /* a HIP runtime call failed (launch, sync, copy) */
+    MOE_ERR_DEVICE = -5         /* a kernel reported bad data (expert id out of range) */
+};
+
+enum { MOE_FMT_FP32 = 0, MOE_FMT_INT8_ROW = 1, MOE_FMT_INT4_G32 = 2, MOE_FMT_INT6_G32 = 3 };
+
+/* Operation ids for moe_workspace_size. */
+enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_EXPERT_FFN = 2 };
+
+/* Router: logits = W x (+ bias).  fmt FP32: w = fp32 [E][d], scale unused.
+ * fmt INT8_ROW: w = int8 [E][d], scale = fp16 [E].  bias = fp32 [E] or NULL.
+ * Needs d % 256 == 0 (FP32) or d % 1024 == 0 (INT8_ROW); 1 <= E <= 1024. */
+typedef struct moe_router {
+    int32_t fmt;
+    int32_t n_experts;
+    int32_t d_model;
+    int32_t reserved;        /* must be 0 */
+    const void* w;
+    const uint16_t* scale;
+    const float* bias;
+} moe_router;
+
+/* A set of E experts of one format (INT4_G32 or INT6_G32).  Expert e:
+ *   gate, up : [d_ff][d_model] -> w_gate/w_up bytes [E][d_ff][row bytes(d_model)],
+ *              s_gate/s_up fp16 [E][d_ff][d_model/32]
+ *   down     : [d_model][d_ff] -> w_down bytes [E][d_model][row bytes(d_ff)],
+ *              s_down fp16 [E][d_model][d_ff/32]
+ * The shared expert is a set with E = 1.  d_model and d_ff must each be a power of two
+ * in [32, 2048] or a multiple of 2048; weight pointers must be 16-byte aligned. */
+typedef struct moe_experts {
+    int32_t fmt;
+    int32_t n_experts;
+    int32_t d_model;
+    int32_t d_ff;
+    const uint8_t* w_gate;
+    const uint8_t* w_up;
+    const uint8_t* w_down;
+    const uint16_t* s_gate;
+    const uint16_t* s_up;
+    const uint16_t* s_down;
+} moe_experts;
+
+/*
+ * moe_route -- router logits, top-k selection and gate weights for T tokens.
+ *   x       bf16 [T][d] (16-byte aligned)
+ *   ids     int32 [T][k]: out; the k experts with the largest fp32 logits, slot 0 the
+ *           largest; equal logits (+0 == -0) -> lower expert id first
+ *   weights fp32 [T][k]: out; softmax over the k selected logits (the full softmax
+ *           renormalised over the selected experts); sums to 1 up to rounding
+ *   logits  fp32 [T][E]: optional out (NULL: kept in the workspace)
+ *   ws      workspace of moe_workspace_size(MOE_OP_ROUTE, T, k, E, d, 0) bytes
+ *           (0 when logits != NULL)
+ * Logits are computed in one fixed fp32 order, the same for every T: the row is cut
+ * into 16-byte vectors dealt round-robin to 64 lanes, each lane runs one
+ * fused-multiply-add chain over its vectors in ascending order, and the 64 lane sums
+ * are combined by a butterfly with offsets 1, 2, 4, ..., 32; then + bias (FP32), or
+ * fl(fl(sum * scale) + bias) (INT8_ROW).  Requires 1 <= k <= min(E, 64).
+ */
+moe_status moe_route(const moe_router* r, const uint16_t* x, int32_t T, int32_t k,
+                     int32_t* ids, float* weights, float* logits, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * moe_permute -- group the P = T*k (token, slot) pairs by expert, stably.
+ *   ids           int32 [T][k] expert ids from moe_route
+ *   offsets       int32 [E+1]: out; expert e's pairs are sorted_pairs[offsets[e] ..
+ *                 offsets[e+1]); offsets[E] = number of valid pairs
+ *   sorted_pairs  int32 [P]: out; pair indices p = t*k + j, by expert then by p
+ *   pair_pos      int32 [P]: out; position of pair p in sorted_pairs (-1 if its id is
+ *                 outside [0, E): such pairs are dropped and the device error flag read
+ *                 by moe_check_device_error is raised)
+ *   ws            moe_workspace_size(MOE_OP_PERMUTE, T, k, E, 0, 0) bytes
+ * Integer-exact; no order-dependent atomics.
+ */
+moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                       int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- y = Wd (silu(Wg x) * (Wu x)) for every (token, expert) pair.
+ * Grouped mode (routed experts): ids, offsets, sorted_pairs from moe_route/moe_permute;
+ *   y is bf16 [T*k][d] in sorted order: row i belongs to pair sorted_pairs[i] and its
+ *   token sorted_pairs[i] / k.  Rows past offsets[E] are left untouched.
+ * Dense mode (shared expert): ids, offsets and sorted_pairs all NULL, ex->n_experts == 1,
+ *   k ignored; y is bf16 [T][d], row t for token t.
+ * Arithmetic: fp32 accumulation of bf16 activations times dequantised weights; the
+ * hidden activation h = silu(g) * u is rounded to bf16 before the down projection.
+ * Small calls (rows <= 64) run a weight-streaming GEMV path; larger ones a grouped MFMA
+ * GEMM path.  ws: moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, d_ff) bytes
+ * (pass k = 1, E = 1 for dense mode).
+ */
+moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, int32_t k,
+                          const int32_t* ids, const int32_t* offsets,
+                          const int32_t* sorted_pairs, uint16_t* y, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- out[t] = bf16( sum_{j<k} w[t][j] * y_pairs[pair_pos[t*k+j]]  + y_shared[t] )
+ * with the sum taken in fp32 over slots j = 0..k-1 in order, then the shared row added,
+ * then one rounding to bf16.  y_shared may be NULL.  Pairs with pair_pos < 0 contribute
+ * nothing.  If residual (bf16 [T][d]) is not NULL the stored value is instead
+ * bf16(residual + bf16(that sum)), the next layer's input in a stacked sweep.
+ * out may alias residual.  Needs d % 8 == 0 and 16-byte aligned rows.
+ */
+moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const float* weights,
+                       const uint16_t* y_shared, const uint16_t* residual, int32_t T,
+                       int32_t k, int32_t d, uint16_t* out, void* stream);
+
+/* Workspace bytes an operation needs for these sizes (0 = none).  Pure host function. */
+size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d,
+                          int32_t d_ff);
+
+/* Synchronises `stream`, then reports and clears the current device's error flag:
+ * MOE_ERR_DEVICE if a kernel saw an expert id outside [0, E) since the last check. */
+moe_status moe_check_device_error(void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

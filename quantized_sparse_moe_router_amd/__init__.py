@@ -1,0 +1,92 @@
+"""MI355X-native quantized routed-expert MoE layer.
+
+The compute path is the C ABI of ``libmoe_mi355x.so`` (include/moe.h): moe_route,
+moe_permute, moe_expert_ffn and moe_combine, all HIP kernels for gfx950.  This package
+is its Python binding (``_lib``) plus ``MoeLayer``, which owns the buffers of one layer
+call and enqueues the four calls on the current stream.  Torch only provides device
+memory and streams.
+"""
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32,
+    MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MoeError,
+    moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_workspace_size,
+    moe_check_device_error, moe_status_string, moe_last_error, moe_version,
+    router_desc, experts_desc,
+)
+
+_FMT = {"fp32": MOE_FMT_FP32, "int8_row": MOE_FMT_INT8_ROW, "int4_g32": MOE_FMT_INT4_G32,
+        "int6_g32": MOE_FMT_INT6_G32}
+
+
+def _fmt(f):
+    return _FMT[f] if isinstance(f, str) else int(f)
+
+
+def router_desc_of(r):
+    """Descriptor of an object with fmt, w, scale, bias attributes (tensors on the GPU)."""
+    return router_desc(_fmt(r.fmt), r.w, r.scale, r.bias)
+
+
+def experts_desc_of(ex):
+    """Descriptor of an object with fmt, d, F, w_gate.. s_down attributes."""
+    return experts_desc(_fmt(ex.fmt), ex.d, ex.F, ex.w_gate, ex.w_up, ex.w_down, ex.s_gate,
+                        ex.s_up, ex.s_down)
+
+
+class MoeLayer:
+    """Buffers and calls of one MoE layer for up to ``T_max`` tokens.
+
+    forward(x) enqueues, on the current stream:
+      moe_route -> moe_expert_ffn(shared, dense) -> moe_permute -> moe_expert_ffn(routed)
+      -> moe_combine
+    and returns ``out`` (bf16 [T][d]).  Intermediate results stay readable as attributes
+    (logits, ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared).
+    """
+
+    def __init__(self, router, routed, shared, k, T_max, device="cuda"):
+        self.router = router_desc_of(router)
+        self.routed = experts_desc_of(routed)
+        self.shared = experts_desc_of(shared) if shared is not None else None
+        self.E, self.d, self.F, self.k = routed.E, routed.d, routed.F, k
+        self.T_max = T_max
+        dev = torch.device(device)
+        T, E, d, F = T_max, self.E, self.d, self.F
+        P = T * k
+        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        self.logits = torch.empty((T, E), dtype=f32, device=dev)
+        self.ids = torch.empty((T, k), dtype=i32, device=dev)
+        self.weights = torch.empty((T, k), dtype=f32, device=dev)
+        self.offsets = torch.empty((E + 1,), dtype=i32, device=dev)
+        self.sorted_pairs = torch.empty((P,), dtype=i32, device=dev)
+        self.pair_pos = torch.empty((P,), dtype=i32, device=dev)
+        self.y_pairs = torch.empty((P, d), dtype=bf, device=dev)
+        self.y_shared = torch.empty((T, d), dtype=bf, device=dev) if shared is not None \
+            else None
+        self.out = torch.empty((T, d), dtype=bf, device=dev)
+        ws_perm = moe_workspace_size(MOE_OP_PERMUTE, T, k, E, d, F)
+        ws_ffn = max(moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, F),
+                     moe_workspace_size(MOE_OP_EXPERT_FFN, T, 1, 1, d, F))
+        self.ws_perm = torch.empty((max(ws_perm, 256),), dtype=torch.uint8, device=dev)
+        self.ws_ffn = torch.empty((max(ws_ffn, 256),), dtype=torch.uint8, device=dev)
+
+    def forward(self, x, residual=None, out=None):
+        T = x.shape[0]
+        if T > self.T_max:
+            raise ValueError("T = %d exceeds T_max = %d" % (T, self.T_max))
+        k, E, d = self.k, self.E, self.d
+        out = self.out[:T] if out is None else out
+        moe_route(self.router, x, T, k, self.ids, self.weights, self.logits)
+        if self.shared is not None:
+            moe_expert_ffn(self.shared, x, T, 1, None, None, None, self.y_shared, self.ws_ffn)
+        moe_permute(self.ids, T, k, E, self.offsets, self.sorted_pairs, self.pair_pos,
+                    self.ws_perm)
+        moe_expert_ffn(self.routed, x, T, k, self.ids, self.offsets, self.sorted_pairs,
+                       self.y_pairs, self.ws_ffn)
+        moe_combine(self.y_pairs, self.pair_pos, self.weights,
+                    self.y_shared if self.shared is not None else None, residual, T, k, d, out)
+        return out
+
+    __call__ = forward

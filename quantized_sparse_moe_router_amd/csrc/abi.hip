@@ -1,0 +1,224 @@
+// abi.hip -- the library's C entry points: argument validation, workspace sizing and
+// shape-based dispatch to the gfx950 kernels.  See include/moe.h for the contract.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "moe_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+moe_status ok() {
+    g_last_error.clear();
+    return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool supported_ffn_dim(int n) {
+    return n == 128 || n == 256 || n == 512 || n == 1024 || n == 2048 || n == 4096;
+}
+
+bool supported_router_dim(int fmt, int d) {
+    if (fmt == MOE_FMT_FP32) return d == 256 || d == 512 || d == 1024 || d == 2048 || d == 4096;
+    return d == 1024 || d == 2048 || d == 4096;
+}
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxK = 64;
+constexpr int64_t kGemvMaxRows = 64;   // pair rows up to which the GEMV path runs
+
+size_t route_ws(int64_t T, int E) { return round_up((size_t)T * (size_t)E * sizeof(float)); }
+
+size_t ffn_ws(int64_t rows, int E, int F) {
+    const size_t gemv = round_up((size_t)rows * (size_t)F * 2);
+    const size_t mfma = moe::ffn_mfma_ws_bytes(rows, E, F);
+    return gemv > mfma ? gemv : mfma;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_DEVICE: return "device reported bad data";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d,
+                          int32_t d_ff) {
+    (void)d;
+    if (T <= 0 || k <= 0 || E <= 0) return 0;
+    switch (op) {
+        case MOE_OP_ROUTE: return route_ws(T, E);
+        case MOE_OP_PERMUTE: return moe::permute_ws_bytes((int64_t)T * k, E);
+        case MOE_OP_EXPERT_FFN: return d_ff > 0 ? ffn_ws((int64_t)T * k, E, d_ff) : 0;
+        default: return 0;
+    }
+}
+
+moe_status moe_route(const moe_router* r, const uint16_t* x, int32_t T, int32_t k,
+                     int32_t* ids, float* weights, float* logits, void* ws, size_t ws_bytes,
+                     void* stream) {
+    if (!r) return fail(MOE_ERR_INVALID_ARG, "moe_route: router descriptor is NULL");
+    if (r->fmt != MOE_FMT_FP32 && r->fmt != MOE_FMT_INT8_ROW)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: router format %d is not FP32 or INT8_ROW",
+                    r->fmt);
+    if (r->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "moe_route: reserved field not 0");
+    const int E = r->n_experts, d = r->d_model;
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: n_experts %d outside [1, %d]", E,
+                    kMaxExperts);
+    if (!supported_router_dim(r->fmt, d))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_route: d_model %d unsupported (FP32: 256..4096 powers of two; "
+                    "INT8_ROW: 1024, 2048, 4096)", d);
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_route: T = %d < 0", T);
+    if (k < 1 || k > E || k > kMaxK)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: k = %d outside [1, min(E, %d)]", k, kMaxK);
+    if (!r->w || !aligned16(r->w))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: router weights NULL or not 16-byte aligned");
+    if (r->fmt == MOE_FMT_INT8_ROW && !r->scale)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: INT8_ROW router needs scales");
+    if (T == 0) return ok();
+    if (!x || !aligned16(x))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route: x NULL or not 16-byte aligned");
+    if (!ids || !weights) return fail(MOE_ERR_INVALID_ARG, "moe_route: ids/weights NULL");
+    float* lg = logits;
+    if (!lg) {
+        if (!ws || ws_bytes < route_ws(T, E) || !aligned16(ws))
+            return fail(MOE_ERR_WORKSPACE,
+                        "moe_route: logits == NULL needs a 16-byte aligned workspace of %zu "
+                        "bytes (got %zu)", route_ws(T, E), ws_bytes);
+        lg = static_cast<float*>(ws);
+    }
+    return hip_status(moe::launch_route(*r, x, T, k, ids, weights, lg,
+                                        static_cast<hipStream_t>(stream)),
+                      "moe_route");
+}
+
+moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E, int32_t* offsets,
+                       int32_t* sorted_pairs, int32_t* pair_pos, void* ws, size_t ws_bytes,
+                       void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_permute: T = %d < 0", T);
+    if (k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "moe_permute: k = %d", k);
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "moe_permute: E = %d outside [1, %d]", E, kMaxExperts);
+    if ((int64_t)T * k > INT32_MAX)
+        return fail(MOE_ERR_INVALID_ARG, "moe_permute: T*k overflows int32");
+    if (!offsets) return fail(MOE_ERR_INVALID_ARG, "moe_permute: offsets NULL");
+    if (T > 0 && (!ids || !sorted_pairs || !pair_pos))
+        return fail(MOE_ERR_INVALID_ARG, "moe_permute: ids/sorted_pairs/pair_pos NULL");
+    const size_t need = moe::permute_ws_bytes((int64_t)T * k, E);
+    if (need && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(MOE_ERR_WORKSPACE, "moe_permute: needs %zu workspace bytes (got %zu)", need,
+                    ws_bytes);
+    return hip_status(moe::launch_permute(ids, T, k, E, offsets, sorted_pairs, pair_pos, ws,
+                                          static_cast<hipStream_t>(stream)),
+                      "moe_permute");
+}
+
+moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, int32_t k,
+                          const int32_t* ids, const int32_t* offsets,
+                          const int32_t* sorted_pairs, uint16_t* y, void* ws,
+                          size_t ws_bytes, void* stream) {
+    if (!ex) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: expert descriptor is NULL");
+    if (ex->fmt != MOE_FMT_INT4_G32 && ex->fmt != MOE_FMT_INT6_G32)
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: format %d is not INT4_G32/INT6_G32",
+                    ex->fmt);
+    const int E = ex->n_experts, d = ex->d_model, F = ex->d_ff;
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_experts %d", E);
+    if (!supported_ffn_dim(d) || !supported_ffn_dim(F))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_expert_ffn: d_model %d / d_ff %d must be 128..4096 powers of two", d, F);
+    if (!ex->w_gate || !ex->w_up || !ex->w_down || !ex->s_gate || !ex->s_up || !ex->s_down)
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: a weight or scale pointer is NULL");
+    if (!aligned16(ex->w_gate) || !aligned16(ex->w_up) || !aligned16(ex->w_down))
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: weights not 16-byte aligned");
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: T = %d < 0", T);
+    const bool grouped = ids || offsets || sorted_pairs;
+    if (grouped && (!ids || !offsets || !sorted_pairs))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_expert_ffn: ids, offsets and sorted_pairs must be all set or all NULL");
+    if (!grouped && E != 1)
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: dense mode needs n_experts == 1");
+    if (grouped && (k < 1 || k > kMaxK))
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: k = %d", k);
+    if (T == 0) return ok();
+    if (!x || !aligned16(x) || !y || !aligned16(y))
+        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: x/y NULL or not 16-byte aligned");
+    const int64_t rows = grouped ? (int64_t)T * k : (int64_t)T;
+    if (rows > INT32_MAX) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: too many rows");
+    const size_t need = ffn_ws(rows, grouped ? E : 1, F);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: needs %zu workspace bytes (got %zu)",
+                    need, ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (rows <= kGemvMaxRows)
+        e = moe::launch_ffn_gemv(*ex, x, T, grouped ? k : 1, ids, offsets, sorted_pairs, y,
+                                 static_cast<uint16_t*>(ws), s);
+    else
+        e = moe::launch_ffn_mfma(*ex, x, T, grouped ? k : 1, offsets, sorted_pairs, y, ws, s);
+    return hip_status(e, "moe_expert_ffn");
+}
+
+moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const float* weights,
+                       const uint16_t* y_shared, const uint16_t* residual, int32_t T, int32_t k,
+                       int32_t d, uint16_t* out, void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_combine: T = %d < 0", T);
+    if (k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "moe_combine: k = %d", k);
+    if (d < 8 || d % 8 != 0) return fail(MOE_ERR_INVALID_ARG, "moe_combine: d = %d", d);
+    if (T == 0) return ok();
+    if (!y_pairs || !pair_pos || !weights || !out)
+        return fail(MOE_ERR_INVALID_ARG, "moe_combine: y_pairs/pair_pos/weights/out NULL");
+    if (!aligned16(y_pairs) || !aligned16(out) || (y_shared && !aligned16(y_shared)) ||
+        (residual && !aligned16(residual)))
+        return fail(MOE_ERR_INVALID_ARG, "moe_combine: bf16 rows must be 16-byte aligned");
+    return hip_status(moe::launch_combine(y_pairs, pair_pos, weights, y_shared, residual, T, k,
+                                          d, out, static_cast<hipStream_t>(stream)),
+                      "moe_combine");
+}
+
+moe_status moe_check_device_error(void* stream) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e, "moe_check_device_error: sync");
+    int flag = 0;
+    e = moe::read_and_clear_device_error(&flag);
+    if (e != hipSuccess) return hip_status(e, "moe_check_device_error: read flag");
+    if (flag) return fail(MOE_ERR_DEVICE, "an expert id outside [0, E) reached moe_permute");
+    return ok();
+}
+
+}  // extern "C"

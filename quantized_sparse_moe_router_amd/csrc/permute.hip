@@ -1,0 +1,207 @@
+// permute.hip -- stable grouping of (token, slot) pairs by expert on gfx950.
+//
+// Prefill runs many tokens per expert in one batch [Strata 与 Qwen3.8-Flash-Next
+// (telli.sh), section GPU、RAM 和 SSD 各司其职]; the grouped GEMM needs each expert's
+// pairs contiguous.  The order inside an expert's segment is by pair index p = t*k + j
+// (a stable counting sort), so the result is a function of the ids alone.
+//
+// Work is cut into chunks of kChunk consecutive pairs:
+//   1. per-chunk histograms (LDS integer atomics: the counts do not depend on order);
+//   2. one block scans the histograms per expert over chunks and over experts;
+//   3. each chunk ranks its pairs in pair order, one wave, 64 pairs per round, and
+//      scatters them.
+// A call with at most kChunk pairs runs all three steps in one block.
+#include "moe_common.h"
+
+namespace moe {
+
+// Raised (set to 1) by any kernel that meets an expert id outside [0, E).
+static __device__ int g_bad_id_flag;
+
+namespace {
+
+constexpr int kChunk = 1024;     // pairs per chunk
+constexpr int kMaxE = 1024;
+
+// rank of this lane's id among lower lanes of the wave holding the same id, and the
+// number of lanes in the wave holding it (valid lanes only)
+__device__ __forceinline__ void wave_rank(int id, bool valid, int lane, int& rank, int& cnt) {
+    rank = 0;
+    cnt = 0;
+    const int vflag = valid ? 1 : 0;
+    for (int src = 0; src < 64; ++src) {
+        const int oid = __builtin_amdgcn_readlane(id, src);
+        const int ov = __builtin_amdgcn_readlane(vflag, src);
+        const bool same = valid && ov && oid == id;
+        cnt += same ? 1 : 0;
+        rank += (same && src < lane) ? 1 : 0;
+    }
+}
+
+// Scatter one chunk's pairs [p0, p1) in pair order, given per-expert bases in LDS.
+// Must be run by exactly one wave (threads 0..63 of the block).
+__device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t p0, int64_t p1, int E,
+                              int* base, int32_t* __restrict__ sorted_pairs,
+                              int32_t* __restrict__ pair_pos) {
+    const int lane = threadIdx.x;
+    for (int64_t q = p0; q < p1; q += 64) {
+        const int64_t p = q + lane;
+        const bool inrange = p < p1;
+        int id = inrange ? ids[p] : -1;
+        const bool valid = inrange && id >= 0 && id < E;
+        if (inrange && !valid) {
+            pair_pos[p] = -1;
+            atomicOr(&g_bad_id_flag, 1);
+        }
+        int rank, cnt;
+        wave_rank(id, valid, lane, rank, cnt);
+        int pos = 0;
+        if (valid) pos = base[id] + rank;
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            sorted_pairs[pos] = (int32_t)p;
+            pair_pos[p] = pos;
+            if (rank == cnt - 1) base[id] += cnt;     // last lane of this id updates
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Exclusive scan of cnt[0..E) into out[0..E], out[E] = total; blockDim.x = 1024.
+__device__ void block_exclusive_scan(const int* cnt, int* out, int E) {
+    __shared__ int part[1024 / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int v = (tid < E) ? cnt[tid] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) part[wv] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < 1024 / 64; ++i) {
+            const int pv = part[i];
+            part[i] = run;
+            run += pv;
+        }
+    }
+    __syncthreads();
+    const int excl = incl - v + part[wv];
+    if (tid < E) out[tid] = excl;
+    if (tid == E - 1) out[E] = excl + v;
+    __syncthreads();
+}
+
+// All three steps in one block (P <= kChunk).  blockDim.x = 1024.
+__global__ void __launch_bounds__(1024) permute_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
+    __shared__ int hist[kMaxE];
+    __shared__ int base[kMaxE + 1];
+    const int tid = threadIdx.x;
+    if (tid < E) hist[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) {
+        const int id = ids[p];
+        if (id >= 0 && id < E) atomicAdd(&hist[id], 1);
+    }
+    __syncthreads();
+    block_exclusive_scan(hist, base, E);
+    for (int e = tid; e <= E; e += blockDim.x) offsets[e] = base[e];
+    __syncthreads();
+    if (tid < 64) scatter_chunk(ids, 0, P, E, base, sorted_pairs, pair_pos);
+}
+
+// Step 1: chunk histograms -> hist[chunk][E].
+__global__ void __launch_bounds__(256) chunk_hist_kernel(const int32_t* __restrict__ ids,
+                                                         int64_t P, int E,
+                                                         int* __restrict__ hist) {
+    __shared__ int h[kMaxE];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) h[e] = 0;
+    __syncthreads();
+    const int64_t p0 = (int64_t)blockIdx.x * kChunk;
+    const int64_t p1 = min(P, p0 + kChunk);
+    for (int64_t p = p0 + tid; p < p1; p += 256) {
+        const int id = ids[p];
+        if (id >= 0 && id < E) atomicAdd(&h[id], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+// Step 2: per expert, exclusive scan over chunks; then over experts -> offsets; the
+// chunk table becomes each chunk's starting position per expert.  One block of 1024.
+__global__ void __launch_bounds__(1024) chunk_scan_kernel(int* __restrict__ hist, int nchunk,
+                                                          int E,
+                                                          int32_t* __restrict__ offsets) {
+    __shared__ int tot[kMaxE];
+    __shared__ int off[kMaxE + 1];
+    const int e = threadIdx.x;
+    if (e < E) {
+        int run = 0;
+        for (int c = 0; c < nchunk; ++c) {
+            const int v = hist[(size_t)c * E + e];
+            hist[(size_t)c * E + e] = run;
+            run += v;
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    block_exclusive_scan(tot, off, E);
+    for (int i = e; i <= E; i += blockDim.x) offsets[i] = off[i];
+    if (e < E)
+        for (int c = 0; c < nchunk; ++c) hist[(size_t)c * E + e] += off[e];
+}
+
+// Step 3: scatter each chunk.  blockDim.x = 64.
+__global__ void __launch_bounds__(64) chunk_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int E, const int* __restrict__ start,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
+    __shared__ int base[kMaxE];
+    for (int e = threadIdx.x; e < E; e += 64) base[e] = start[(size_t)blockIdx.x * E + e];
+    __syncthreads();
+    const int64_t p0 = (int64_t)blockIdx.x * kChunk;
+    const int64_t p1 = min(P, p0 + kChunk);
+    scatter_chunk(ids, p0, p1, E, base, sorted_pairs, pair_pos);
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int64_t P, int E) {
+    if (P <= kChunk) return 0;
+    const int64_t nchunk = (P + kChunk - 1) / kChunk;
+    return (size_t)nchunk * (size_t)E * sizeof(int);
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* pair_pos, void* ws, hipStream_t s) {
+    const int64_t P = (int64_t)T * k;
+    if (P <= kChunk) {
+        permute_small_kernel<<<1, 1024, 0, s>>>(ids, (int)P, E, offsets, sorted_pairs,
+                                                pair_pos);
+        return hipGetLastError();
+    }
+    const int nchunk = (int)((P + kChunk - 1) / kChunk);
+    int* hist = static_cast<int*>(ws);
+    chunk_hist_kernel<<<nchunk, 256, 0, s>>>(ids, P, E, hist);
+    chunk_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunk, E, offsets);
+    chunk_scatter_kernel<<<nchunk, 64, 0, s>>>(ids, P, E, hist, sorted_pairs, pair_pos);
+    return hipGetLastError();
+}
+
+hipError_t read_and_clear_device_error(int* flag) {
+    int zero = 0;
+    hipError_t e = hipMemcpyFromSymbol(flag, HIP_SYMBOL(g_bad_id_flag), sizeof(int), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_bad_id_flag), &zero, sizeof(int), 0,
+                             hipMemcpyHostToDevice);
+}
+
+}  // namespace moe

@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point declared in
+include/moe.h, sizes workspaces, and rejects bad arguments before launching anything.
+No call here reaches a kernel, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from quantized_sparse_moe_router_amd import _lib
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from quantized_sparse_moe_router_amd import _lib
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert b"gfx950" in L.moe_version()
+    assert L.moe_status_string(0) == b"ok"
+    assert L.moe_status_string(-3) == b"workspace too small"
+
+
+def test_workspace_sizes(L):
+    from quantized_sparse_moe_router_amd import _lib
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 1, 10, 512, 2048, 512) == 2048
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 0, 10, 512, 2048, 512) == 0
+    # small permutes run in one block without workspace
+    assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 1, 10, 512, 2048, 512) == 0
+    assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 8192, 10, 512, 2048, 512) >= 80 * 512 * 4
+    assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 1, 10, 512, 2048, 512) >= 10 * 512 * 2
+
+
+def _router(fmt=0, E=512, d=2048, w=16, scale=None, reserved=0):
+    from quantized_sparse_moe_router_amd import _lib
+    return _lib.moe_router(fmt, E, d, reserved, w, scale, None)
+
+
+def _experts(fmt=2, E=512, d=2048, F=512, p=16):
+    from quantized_sparse_moe_router_amd import _lib
+    return _lib.moe_experts(fmt, E, d, F, p, p, p, p, p, p)
+
+
+def _err(L):
+    return L.moe_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,T,k,expect", [
+    (dict(fmt=3), 1, 10, "format"),
+    (dict(E=0), 1, 10, "n_experts"),
+    (dict(E=2000), 1, 10, "n_experts"),
+    (dict(d=300), 1, 10, "d_model"),
+    (dict(fmt=1, d=256), 1, 10, "d_model"),
+    (dict(), -1, 10, "T"),
+    (dict(), 1, 0, "k"),
+    (dict(E=8), 1, 9, "k"),
+    (dict(), 1, 65, "k"),
+    (dict(w=None), 1, 10, "router weights"),
+    (dict(w=8), 1, 10, "aligned"),
+    (dict(fmt=1), 1, 10, "scales"),
+    (dict(reserved=1), 1, 10, "reserved"),
+])
+def test_route_rejects(L, kw, T, k, expect):
+    r = _router(**kw)
+    st = L.moe_route(ctypes.byref(r), 16, T, k, 16, 16, None, None, 0, None)
+    assert st == -1 and expect in _err(L)
+
+
+def test_route_null_descriptor_and_workspace(L):
+    assert L.moe_route(None, 16, 1, 10, 16, 16, None, None, 0, None) == -1
+    r = _router()
+    st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, None, None, 0, None)
+    assert st == -3 and "workspace" in _err(L)
+    st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, None, 16, 100, None)
+    assert st == -3
+    st = L.moe_route(ctypes.byref(r), 8, 1, 10, 16, 16, 16, None, 0, None)
+    assert st == -1 and "x" in _err(L)
+
+
+def test_route_zero_tokens_is_noop(L):
+    r = _router()
+    assert L.moe_route(ctypes.byref(r), None, 0, 10, None, None, None, None, 0, None) == 0
+
+
+def test_permute_rejects(L):
+    assert L.moe_permute(16, -1, 10, 512, 16, 16, 16, None, 0, None) == -1
+    assert L.moe_permute(16, 1, 0, 512, 16, 16, 16, None, 0, None) == -1
+    assert L.moe_permute(16, 1, 10, 0, 16, 16, 16, None, 0, None) == -1
+    assert L.moe_permute(16, 1, 10, 512, None, 16, 16, None, 0, None) == -1
+    assert L.moe_permute(None, 1, 10, 512, 16, 16, 16, None, 0, None) == -1
+    assert L.moe_permute(16, 8192, 10, 512, 16, 16, 16, None, 0, None) == -3
+    assert L.moe_permute(16, 2 ** 30, 10, 512, 16, 16, 16, None, 0, None) == -1
+
+
+def test_expert_ffn_rejects(L):
+    def call(ex, x=16, T=1, k=10, ids=16, off=16, sp=16, y=16, ws=16, wsb=1 << 30):
+        return L.moe_expert_ffn(ctypes.byref(ex) if ex is not None else None, x, T, k, ids,
+                                off, sp, y, ws, wsb, None)
+    assert call(None) == -1
+    assert call(_experts(fmt=0)) == -1
+    assert call(_experts(d=300)) == -1
+    assert call(_experts(F=96)) == -1
+    assert call(_experts(p=None)) == -1
+    assert call(_experts(p=8)) == -1
+    assert call(_experts(), ids=None) == -1                     # partly grouped
+    assert call(_experts(), ids=None, off=None, sp=None) == -1  # dense needs E == 1
+    assert call(_experts(), x=8) == -1
+    assert call(_experts(), ws=None) == -3
+    assert call(_experts(), wsb=10) == -3
+    assert call(_experts(), T=-1) == -1
+    assert call(_experts(), T=0) == 0
+
+
+def test_combine_rejects(L):
+    assert L.moe_combine(16, 16, 16, None, None, 1, 10, 2047, 16, None) == -1
+    assert L.moe_combine(16, 16, 16, None, None, 1, 0, 2048, 16, None) == -1
+    assert L.moe_combine(None, 16, 16, None, None, 1, 10, 2048, 16, None) == -1
+    assert L.moe_combine(8, 16, 16, None, None, 1, 10, 2048, 16, None) == -1
+    assert L.moe_combine(16, 16, 16, 8, None, 1, 10, 2048, 16, None) == -1
+    assert L.moe_combine(None, None, None, None, None, 0, 10, 2048, None, None) == 0
