@@ -1,0 +1,49 @@
+"""The layer's calls captured in a HIP graph: every replay must reproduce the eager
+result bit for bit (the kernels are deterministic), with eager work and host
+synchronisation between replays."""
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_sparse_moe_router_amd as moe
+    w = synth.WORKLOADS["decode_d2048_e512_top10_t1"]
+    lay = synth.make_layer(w, seed=3, device="cuda", bias="zipf")
+    xs = synth.make_tokens(w, T=4, seed=3, device="cuda")
+    layer = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, 4)
+    print("case graph decode T=1..4", flush=True)
+    eager = []
+    for T in (1, 4):
+        eager.append(layer.forward(xs[:T]).clone())
+    torch.cuda.synchronize()
+
+    x_in = torch.empty_like(xs)
+    x_in.copy_(xs)
+    outs = [torch.empty((1, w.d), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((4, w.d), dtype=torch.bfloat16, device="cuda")]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x_in[:1], out=outs[0])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x_in[:1], out=outs[0])
+        layer.forward(x_in[:4], out=outs[1])
+    for rep in range(4):
+        outs[0].zero_()
+        outs[1].zero_()
+        _ = torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], eager[0]), rep
+        assert torch.equal(outs[1], eager[1]), rep
+    moe.moe_check_device_error()
