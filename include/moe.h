@@ -24,6 +24,10 @@
  *     nothing and returns a negative status; moe_last_error() has the detail (per
  *     thread).  T = 0 is a valid no-op.
  *   - Results are deterministic: the same inputs give the same bits on every run.
+ *   - Workspaces: size them with moe_workspace_size and ZERO-FILL them once before their
+ *     first use.  The first bytes of the route workspace hold an arrival counter that
+ *     the kernel counts up and resets before it finishes, so every call leaves it zero
+ *     again.  Two calls that run at the same time need two workspaces.
  *
  * Weight formats (groups of 32 consecutive elements along a row's input dimension):
  *   MOE_FMT_INT4_G32  row of K codes = K/2 bytes; byte i: element 2i in the low nibble,
@@ -52,7 +56,8 @@ enum {
     MOE_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for */
     MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than moe_workspace_size */
     MOE_ERR_HIP = -4,           /* a HIP runtime call failed (launch, sync, copy) */
-    MOE_ERR_DEVICE = -5         /* a kernel reported bad data (expert id out of range) */
+    MOE_ERR_DEVICE = -5         /* a kernel reported bad data (expert id out of range) or a
+                                   bounded wait that timed out */
 };
 
 enum { MOE_FMT_FP32 = 0, MOE_FMT_INT8_ROW = 1, MOE_FMT_INT4_G32 = 2, MOE_FMT_INT6_G32 = 3 };
@@ -78,8 +83,8 @@ typedef struct moe_router {
  *              s_gate/s_up fp16 [E][d_ff][d_model/32]
  *   down     : [d_model][d_ff] -> w_down bytes [E][d_model][row bytes(d_ff)],
  *              s_down fp16 [E][d_model][d_ff/32]
- * The shared expert is a set with E = 1.  d_model and d_ff must each be a power of two
- * in [32, 2048] or a multiple of 2048; weight pointers must be 16-byte aligned. */
+ * The shared expert is a set with E = 1.  d_model and d_ff must each be one of 128, 256,
+ * 512, 1024, 2048, 4096; weight pointers must be 16-byte aligned. */
 typedef struct moe_experts {
     int32_t fmt;
     int32_t n_experts;
@@ -101,8 +106,10 @@ typedef struct moe_experts {
  *   weights fp32 [T][k]: out; softmax over the k selected logits (the full softmax
  *           renormalised over the selected experts); sums to 1 up to rounding
  *   logits  fp32 [T][E]: optional out (NULL: kept in the workspace)
- *   ws      workspace of moe_workspace_size(MOE_OP_ROUTE, T, k, E, d, 0) bytes
- *           (0 when logits != NULL)
+ *   ws      zero-initialised workspace of moe_workspace_size(MOE_OP_ROUTE, T, k, E, d, 0)
+ *           bytes (256 bytes are enough when logits != NULL)
+ * With T <= 16 the logits and the selection run in one launch (the last block to finish
+ * its rows selects); larger T runs an LDS-tiled GEMM and a selection kernel.
  * Logits are computed in one fixed fp32 order, the same for every T: the row is cut
  * into 16-byte vectors dealt round-robin to 64 lanes, each lane runs one
  * fused-multiply-add chain over its vectors in ascending order, and the 64 lane sums
@@ -138,9 +145,14 @@ moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  *   k ignored; y is bf16 [T][d], row t for token t.
  * Arithmetic: fp32 accumulation of bf16 activations times dequantised weights; the
  * hidden activation h = silu(g) * u is rounded to bf16 before the down projection.
- * Small calls (rows <= 64) run a weight-streaming GEMV path; larger ones a grouped MFMA
- * GEMM path.  ws: moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, d_ff) bytes
- * (pass k = 1, E = 1 for dense mode).
+ * Small calls (at most 64 rows, and a (d_model, d_ff) pair with a GEMV kernel: (2048, 512),
+ * (2048, 1024), (2048, 2048), (4096, 1024), (1024, 512), (256, 128)) stream each selected
+ * expert's weights once (two launches: gate/up + SwiGLU, then down); they derive each
+ * pair's row from ids alone and do not read offsets or sorted_pairs, so moe_permute may
+ * run concurrently with them.  Larger calls run a grouped MFMA GEMM that reads offsets
+ * and sorted_pairs.
+ * ws: moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, d_ff) bytes (pass k = 1, E = 1
+ * for dense mode).
  */
 moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, int32_t k,
                           const int32_t* ids, const int32_t* offsets,
@@ -164,7 +176,8 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
                           int32_t d_ff);
 
 /* Synchronises `stream`, then reports and clears the current device's error flag:
- * MOE_ERR_DEVICE if a kernel saw an expert id outside [0, E) since the last check. */
+ * MOE_ERR_DEVICE if, since the last check, a kernel saw an expert id outside [0, E) or a
+ * kernel's bounded wait for another block's results timed out. */
 moe_status moe_check_device_error(void* stream);
 
 /* Static text for a status code. */

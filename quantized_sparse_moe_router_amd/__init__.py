@@ -39,10 +39,11 @@ def experts_desc_of(ex):
 class MoeLayer:
     """Buffers and calls of one MoE layer for up to ``T_max`` tokens.
 
-    forward(x) enqueues, on the current stream:
-      moe_route -> moe_expert_ffn(shared, dense) -> moe_permute -> moe_expert_ffn(routed)
-      -> moe_combine
-    and returns ``out`` (bf16 [T][d]).  Intermediate results stay readable as attributes
+    forward(x) enqueues moe_route -> moe_permute -> moe_expert_ffn(routed) on the current
+    stream and moe_expert_ffn(shared, dense) on a side stream forked from it, joins, then
+    moe_combine; it returns ``out`` (bf16 [T][d]).  For small calls (T*k <= 64) the routed
+    experts do not read the grouping, so moe_permute runs on a second side stream beside
+    them.  Graph capture records the forks and joins.  Intermediate results stay readable as attributes
     (logits, ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared).
     """
 
@@ -66,11 +67,18 @@ class MoeLayer:
         self.y_shared = torch.empty((T, d), dtype=bf, device=dev) if shared is not None \
             else None
         self.out = torch.empty((T, d), dtype=bf, device=dev)
+        ws_route = moe_workspace_size(MOE_OP_ROUTE, T, k, E, d, F)
         ws_perm = moe_workspace_size(MOE_OP_PERMUTE, T, k, E, d, F)
-        ws_ffn = max(moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, F),
-                     moe_workspace_size(MOE_OP_EXPERT_FFN, T, 1, 1, d, F))
-        self.ws_perm = torch.empty((max(ws_perm, 256),), dtype=torch.uint8, device=dev)
-        self.ws_ffn = torch.empty((max(ws_ffn, 256),), dtype=torch.uint8, device=dev)
+        ws_ffn = moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, F)
+        ws_sh = moe_workspace_size(MOE_OP_EXPERT_FFN, T, 1, 1, d, F)
+        # workspaces start zeroed: their counter areas must be zero before first use
+        u8 = torch.uint8
+        self.ws_route = torch.zeros((max(ws_route, 256),), dtype=u8, device=dev)
+        self.ws_perm = torch.zeros((max(ws_perm, 256),), dtype=u8, device=dev)
+        self.ws_ffn = torch.zeros((max(ws_ffn, 1024),), dtype=u8, device=dev)
+        self.ws_shared = torch.zeros((max(ws_sh, 1024),), dtype=u8, device=dev)
+        self.side = torch.cuda.Stream(device=dev)     # default priority
+        self.side2 = torch.cuda.Stream(device=dev)
 
     def forward(self, x, residual=None, out=None):
         T = x.shape[0]
@@ -78,13 +86,29 @@ class MoeLayer:
             raise ValueError("T = %d exceeds T_max = %d" % (T, self.T_max))
         k, E, d = self.k, self.E, self.d
         out = self.out[:T] if out is None else out
-        moe_route(self.router, x, T, k, self.ids, self.weights, self.logits)
+        main = torch.cuda.current_stream()
         if self.shared is not None:
-            moe_expert_ffn(self.shared, x, T, 1, None, None, None, self.y_shared, self.ws_ffn)
-        moe_permute(self.ids, T, k, E, self.offsets, self.sorted_pairs, self.pair_pos,
-                    self.ws_perm)
+            # the shared expert does not depend on routing: run it on a side stream
+            self.side.wait_stream(main)
+            moe_expert_ffn(self.shared, x, T, 1, None, None, None, self.y_shared,
+                           self.ws_shared, stream=self.side)
+        moe_route(self.router, x, T, k, self.ids, self.weights, self.logits, self.ws_route)
+        small = T * k <= 64
+        if small:
+            # small calls of moe_expert_ffn read only ids, so the grouping (needed by the
+            # combine) can run beside the routed experts
+            self.side2.wait_stream(main)
+            moe_permute(self.ids, T, k, E, self.offsets, self.sorted_pairs, self.pair_pos,
+                        self.ws_perm, stream=self.side2)
+        else:
+            moe_permute(self.ids, T, k, E, self.offsets, self.sorted_pairs, self.pair_pos,
+                        self.ws_perm)
         moe_expert_ffn(self.routed, x, T, k, self.ids, self.offsets, self.sorted_pairs,
                        self.y_pairs, self.ws_ffn)
+        if small:
+            main.wait_stream(self.side2)
+        if self.shared is not None:
+            main.wait_stream(self.side)
         moe_combine(self.y_pairs, self.pair_pos, self.weights,
                     self.y_shared if self.shared is not None else None, residual, T, k, d, out)
         return out

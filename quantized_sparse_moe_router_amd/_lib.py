@@ -119,6 +119,7 @@ def moe_workspace_size(op, T, k, E, d, d_ff):
 
 
 def moe_route(router, x, T, k, ids, weights, logits=None, ws=None, stream=None):
+    """ws: a zero-initialised workspace of moe_workspace_size(MOE_OP_ROUTE, ...) bytes."""
     st = lib().moe_route(ctypes.byref(router), _ptr(x), T, k, _ptr(ids), _ptr(weights),
                          _ptr(logits), _ptr(ws), 0 if ws is None else ws.numel() *
                          ws.element_size(), _stream(stream))

@@ -47,8 +47,13 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = 64;
 constexpr int64_t kGemvMaxRows = 64;   // pair rows up to which the GEMV path runs
 
-size_t route_ws(int64_t T, int E) { return round_up((size_t)T * (size_t)E * sizeof(float)); }
+// route workspace: [counter][logits when the caller passes none]
+size_t route_ws(int64_t T, int E, bool need_logits) {
+    return moe::kRouteCounterBytes +
+           (need_logits ? round_up((size_t)T * (size_t)E * sizeof(float)) : 0);
+}
 
+// expert FFN workspace: [counters][h][tile list]
 size_t ffn_ws(int64_t rows, int E, int F) {
     const size_t gemv = round_up((size_t)rows * (size_t)F * 2);
     const size_t mfma = moe::ffn_mfma_ws_bytes(rows, E, F);
@@ -80,7 +85,7 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
     (void)d;
     if (T <= 0 || k <= 0 || E <= 0) return 0;
     switch (op) {
-        case MOE_OP_ROUTE: return route_ws(T, E);
+        case MOE_OP_ROUTE: return route_ws(T, E, true);
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes((int64_t)T * k, E);
         case MOE_OP_EXPERT_FFN: return d_ff > 0 ? ffn_ws((int64_t)T * k, E, d_ff) : 0;
         default: return 0;
@@ -114,15 +119,16 @@ moe_status moe_route(const moe_router* r, const uint16_t* x, int32_t T, int32_t 
     if (!x || !aligned16(x))
         return fail(MOE_ERR_INVALID_ARG, "moe_route: x NULL or not 16-byte aligned");
     if (!ids || !weights) return fail(MOE_ERR_INVALID_ARG, "moe_route: ids/weights NULL");
-    float* lg = logits;
-    if (!lg) {
-        if (!ws || ws_bytes < route_ws(T, E) || !aligned16(ws))
-            return fail(MOE_ERR_WORKSPACE,
-                        "moe_route: logits == NULL needs a 16-byte aligned workspace of %zu "
-                        "bytes (got %zu)", route_ws(T, E), ws_bytes);
-        lg = static_cast<float*>(ws);
-    }
-    return hip_status(moe::launch_route(*r, x, T, k, ids, weights, lg,
+    const size_t need = route_ws(T, E, logits == nullptr);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(MOE_ERR_WORKSPACE,
+                    "moe_route: needs a 16-byte aligned workspace of %zu bytes (got %zu)", need,
+                    ws_bytes);
+    unsigned* counter = static_cast<unsigned*>(ws);
+    float* lg = logits ? logits
+                       : reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                                  moe::kRouteCounterBytes);
+    return hip_status(moe::launch_route(*r, x, T, k, ids, weights, lg, counter,
                                         static_cast<hipStream_t>(stream)),
                       "moe_route");
 }
@@ -186,9 +192,8 @@ moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, i
                     need, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (rows <= kGemvMaxRows)
-        e = moe::launch_ffn_gemv(*ex, x, T, grouped ? k : 1, ids, offsets, sorted_pairs, y,
-                                 static_cast<uint16_t*>(ws), s);
+    if (rows <= kGemvMaxRows && moe::ffn_gemv_has_shape(d, F))
+        e = moe::launch_ffn_gemv(*ex, x, T, grouped ? k : 1, ids, y, ws, s);
     else
         e = moe::launch_ffn_mfma(*ex, x, T, grouped ? k : 1, offsets, sorted_pairs, y, ws, s);
     return hip_status(e, "moe_expert_ffn");
@@ -217,7 +222,8 @@ moe_status moe_check_device_error(void* stream) {
     int flag = 0;
     e = moe::read_and_clear_device_error(&flag);
     if (e != hipSuccess) return hip_status(e, "moe_check_device_error: read flag");
-    if (flag) return fail(MOE_ERR_DEVICE, "an expert id outside [0, E) reached moe_permute");
+    if (flag & 1) return fail(MOE_ERR_DEVICE, "an expert id outside [0, E) was seen");
+    if (flag) return fail(MOE_ERR_DEVICE, "a kernel's bounded wait timed out");
     return ok();
 }
 

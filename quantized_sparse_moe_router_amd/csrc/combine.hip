@@ -6,6 +6,8 @@
 // so the result does not depend on scheduling; it is bound by reading the pair outputs.
 #include "moe_common.h"
 
+#pragma clang fp contract(off)
+
 namespace moe {
 namespace {
 
@@ -22,16 +24,35 @@ __global__ void __launch_bounds__(256) combine_kernel(
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const int q = pair_pos[(size_t)t * k + j];
-        if (q < 0) continue;
-        const float wj = w[(size_t)t * k + j];
-        const uint4 v = *reinterpret_cast<const uint4*>(y_pairs + (size_t)q * d + 8 * c8);
-        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+    // slots in chunks of 8: all index/weight loads, then all row loads, then the sums in
+    // slot order, so a chunk's loads are in flight together.  Padding slots and dropped
+    // pairs (bad ids) read row 0 and add it with weight 0.
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int q[8];
+        float wj[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = __builtin_fmaf(wj, bf16lo(vv[i]), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(wj, bf16hi(vv[i]), acc[2 * i + 1]);
+        for (int j = 0; j < 8; ++j) {
+            const int jj = min(j0 + j, k - 1);
+            q[j] = pair_pos[(size_t)t * k + jj];
+            wj[j] = w[(size_t)t * k + jj];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j0 + j >= k || q[j] < 0) wj[j] = 0.0f;
+            q[j] = max(q[j], 0);
+        }
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            v[j] = *reinterpret_cast<const uint4*>(y_pairs + (size_t)q[j] * d + 8 * c8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t vv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = __builtin_fmaf(wj[j], bf16lo(vv[i]), acc[2 * i]);
+                acc[2 * i + 1] = __builtin_fmaf(wj[j], bf16hi(vv[i]), acc[2 * i + 1]);
+            }
         }
     }
     if (y_shared) {

@@ -13,16 +13,24 @@
 // v_dot2_f32_bf16, and the offset (128 + zero point) times the group's activation sum is
 // removed afterwards; the fp16 group scale is applied once per group.
 //
-// Grouped mode: block x = a position in the expert-sorted pair list; only the first
-// position of each expert's segment does work (the others return at once), looping over
-// the segment's pairs MT at a time so each weight row is read once per MT tokens.
-// Dense mode (shared expert): block x = a chunk of MT tokens.
+// Two launches: gate/up + SwiGLU -> h (bf16), then down -> y.  In each, a block owns one
+// slot and a block of rows and issues all its weight loads before it reads activations.
+//
+// Grouped mode (at most 64 pairs): a slot is a pair p.  A block reads the whole ids vector
+// with one load, so the expert e = ids[p] is known after one memory round trip and the
+// weight loads start at once; the pairs routed to e form a ballot mask, every MT-th of
+// them leads a chunk of MT pairs and the others return.  A pair's row is its
+// expert-sorted position (valid pairs with a smaller id, plus earlier pairs with the same
+// id), the same position moe_permute assigns.
+// Dense mode (shared expert): a slot is a chunk of MT tokens.
 #include "moe_common.h"
+
+// Every fused multiply-add below is written out, so a token's arithmetic is the same
+// whatever the number of tokens that share a pass (batch invariance).
+#pragma clang fp contract(off)
 
 namespace moe {
 namespace {
-
-constexpr int kMT = 4;   // tokens per pass over the weights
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -99,30 +107,87 @@ struct Fmt<MOE_FMT_INT6_G32> {
     static constexpr float kBias = 160.0f;    // 128 + 32
 };
 
+enum { kModeGateUp = 0, kModeDown = 1 };
+
 template <int FMT>
-__device__ __forceinline__ float group_dot(const uint8_t* gptr, const uint32_t* xp) {
+struct GroupBits {
+    uint4 a;
+    uint2 b;   // int6: bytes 16..23 of the group
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_bits(const uint8_t* p, GroupBits<FMT>& g) {
     if constexpr (FMT == MOE_FMT_INT4_G32) {
-        return group_dot_int4(*reinterpret_cast<const uint4*>(gptr), xp);
+        g.a = *reinterpret_cast<const uint4*>(p);
     } else {
-        const uint2* p = reinterpret_cast<const uint2*>(gptr);
-        const uint2 a = p[0], b = p[1], c = p[2];
-        const uint32_t w6[6] = {a.x, a.y, b.x, b.y, c.x, c.y};
+        const uint2* q = reinterpret_cast<const uint2*>(p);
+        const uint2 x0 = q[0], x1 = q[1], x2 = q[2];
+        g.a = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        g.b = x2;
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ float dot_bits(const GroupBits<FMT>& g, const uint32_t* xp) {
+    if constexpr (FMT == MOE_FMT_INT4_G32) {
+        return group_dot_int4(g.a, xp);
+    } else {
+        const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
         return group_dot_int6(w6, xp);
     }
 }
 
-enum { kModeGateUp = 0, kModeDown = 1 };
+struct Slot {
+    int e;              // expert (grouped) or 0 (dense)
+    uint64_t members;   // grouped: pairs routed to e, bit q = pair q
+    int seg0;           // grouped: sorted position of e's first pair
+    int first;          // grouped: rank (among e's pairs) of this chunk's first pair
+    int dense0, dense_n;
+};
 
-// One projection pass.  K = input length; rows = output rows of the projection.
+// Resolve slot s; returns false if this block has nothing to do.
+template <int MT>
+__device__ __forceinline__ bool resolve_slot(int s, int T, int k, const int32_t* ids, int E,
+                                             Slot& sl) {
+    const int lane = threadIdx.x & 63;
+    if (ids) {
+        const int P = T * k;
+        const int my = (lane < P) ? ids[lane] : -1;
+        const int e = __builtin_amdgcn_readlane(my, s);
+        if (e < 0 || e >= E) return false;
+        const bool valid = lane < P && my >= 0 && my < E;
+        sl.members = __ballot(valid && my == e);
+        // rank of pair s among e's pairs; the pairs of rank 0, MT, 2MT, ... each lead a
+        // chunk of MT pairs, the others return
+        const int rank = __popcll(sl.members & ((1ull << s) - 1ull));
+        if (rank % MT != 0) return false;
+        sl.first = rank;
+        sl.seg0 = __popcll(__ballot(valid && my < e));
+        sl.e = e;
+        sl.dense0 = sl.dense_n = 0;
+    } else {
+        sl.e = 0;
+        sl.members = 0;
+        sl.seg0 = 0;
+        sl.first = 0;
+        sl.dense0 = s * MT;
+        if (sl.dense0 >= T) return false;
+        sl.dense_n = min(MT, T - sl.dense0);
+    }
+    return true;
+}
+
+// One projection over a block of rows.  K = input length; rows = output rows.
 //   GateUp: rows = d_ff, inputs = x rows of the tokens, output h (bf16) per pair row.
 //   Down  : rows = d_model, inputs = h rows of the pairs, output y (bf16) per pair row.
-template <int FMT, int MODE, int LPR, int GPL, int ITERS>
-__global__ void __launch_bounds__(256) ffn_gemv_kernel(
-    const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
-    const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
-    const uint16_t* __restrict__ act, int T, int k, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs, int E,
-    int rows, uint16_t* __restrict__ out) {
+// MT = tokens per pass over the weights (a slot's pairs are taken MT at a time).
+template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT>
+__device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
+                                          const uint16_t* __restrict__ sa,
+                                          const uint8_t* __restrict__ wb,
+                                          const uint16_t* __restrict__ sb,
+                                          const uint16_t* __restrict__ act, int k, int rows,
+                                          int rb, const Slot& sl, uint16_t* __restrict__ out) {
     constexpr int K = LPR * GPL * 32;
     constexpr int RPW = 64 / LPR;                  // rows per load instruction
     constexpr int ROWS_PER_BLOCK = 4 * ITERS * RPW;
@@ -134,92 +199,112 @@ __global__ void __launch_bounds__(256) ffn_gemv_kernel(
     const int wave = threadIdx.x >> 6;
     const int gp = lane % LPR;                      // group slot in the row
     const int rsub = lane / LPR;                    // row inside a load instruction
+    const bool grouped = sl.members != 0;
 
-    // ---- which expert and which activation rows
-    int e, seg_begin, seg_end;
-    const bool grouped = offsets != nullptr;
+    // ---- activation rows of this block's chunk (at most MT pairs / tokens); requested
+    // before the weights so both are in flight together
+    int arow[MT], orow[MT];
+    int mcount = 0;
+    uint32_t xv[MT][GPL][16];
     if (grouped) {
-        const int pos = blockIdx.x;
-        const int nvalid = offsets[E];
-        if (pos >= nvalid) return;
-        e = ids[sorted_pairs[pos]];
-        seg_begin = offsets[e];
-        if (pos != seg_begin) return;
-        seg_end = offsets[e + 1];
+        uint64_t rest = sl.members;
+        for (int skip = 0; skip < sl.first; ++skip) rest &= rest - 1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            arow[m] = 0;
+            orow[m] = 0;
+            if (rest) {
+                const int q = (int)__builtin_ctzll(rest);
+                rest &= rest - 1;
+                const int srow = sl.seg0 + sl.first + m;        // expert-sorted position
+                arow[m] = (MODE == kModeGateUp) ? q / k : srow;
+                orow[m] = srow;
+                ++mcount;
+            }
+        }
     } else {
-        e = 0;
-        seg_begin = blockIdx.x * kMT;
-        if (seg_begin >= T) return;
-        seg_end = min(T, seg_begin + kMT);
+        mcount = sl.dense_n;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            arow[m] = sl.dense0 + min(m, mcount - 1);
+            orow[m] = arow[m];
+        }
     }
-
-    const int row_base = blockIdx.y * ROWS_PER_BLOCK + wave * ITERS * RPW + rsub;
-    const size_t mat_row0 = (size_t)e * rows;
-
-    for (int c0 = seg_begin; c0 < seg_end; c0 += kMT) {
-        const int mcount = min(kMT, seg_end - c0);
-        // activations: for each token slot and group, 16 packed bf16 pairs
-        uint32_t xv[kMT][GPL][16];
-        float sx[kMT][GPL];
 #pragma unroll
-        for (int m = 0; m < kMT; ++m) {
-            if (m < mcount) {
-                const int r = c0 + m;
-                size_t arow;
-                if (MODE == kModeGateUp)
-                    arow = grouped ? (size_t)(sorted_pairs[r] / k) : (size_t)r;
-                else
-                    arow = (size_t)r;
-                const uint16_t* ap = act + arow * K;
+    for (int m = 0; m < MT; ++m) {
+        if (m < mcount) {
+            const uint16_t* ap = act + (size_t)arow[m] * K;
 #pragma unroll
-                for (int i = 0; i < GPL; ++i) {
-                    const uint4* src = reinterpret_cast<const uint4*>(ap + 32 * (gp + LPR * i));
+            for (int i = 0; i < GPL; ++i) {
+                const uint4* src = reinterpret_cast<const uint4*>(ap + 32 * (gp + LPR * i));
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const uint4 q = src[v];
-                        xv[m][i][4 * v + 0] = q.x;
-                        xv[m][i][4 * v + 1] = q.y;
-                        xv[m][i][4 * v + 2] = q.z;
-                        xv[m][i][4 * v + 3] = q.w;
-                    }
-                    sx[m][i] = group_sum_x(xv[m][i]);
+                for (int v = 0; v < 4; ++v) {
+                    const uint4 q = src[v];
+                    xv[m][i][4 * v + 0] = q.x;
+                    xv[m][i][4 * v + 1] = q.y;
+                    xv[m][i][4 * v + 2] = q.z;
+                    xv[m][i][4 * v + 3] = q.w;
                 }
             }
         }
+    }
+
+    // ---- every weight load of this wave
+    const int row_base = rb * ROWS_PER_BLOCK + wave * ITERS * RPW + rsub;
+    const size_t mat_row0 = (size_t)sl.e * rows;
+    GroupBits<FMT> wbits[ITERS][NMAT][GPL];
+    uint16_t sbits[ITERS][NMAT][GPL];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int row = row_base + it * RPW;
+        const size_t mrow = mat_row0 + (row < rows ? row : 0);
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+            const uint8_t* wbase = (mt == 0 ? wa : wb) + mrow * ROW_BYTES;
+            const uint16_t* sbase = (mt == 0 ? sa : sb) + mrow * (K / 32);
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) {
+                const int g = gp + LPR * i;
+                load_bits<FMT>(wbase + (size_t)g * GB, wbits[it][mt][i]);
+                sbits[it][mt][i] = sbase[g];
+            }
+        }
+    }
+
+    // ---- compute
+    {
+        float sx[MT][GPL];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < mcount)
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) sx[m][i] = group_sum_x(xv[m][i]);
 
 #pragma unroll
         for (int it = 0; it < ITERS; ++it) {
             const int row = row_base + it * RPW;
-            const bool rv = row < rows;
-            const size_t mrow = mat_row0 + (rv ? row : 0);
-            float acc[NMAT][kMT];
+            float acc[NMAT][MT];
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-                for (int m = 0; m < kMT; ++m) acc[mt][m] = 0.0f;
+                for (int m = 0; m < MT; ++m) acc[mt][m] = 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) {
-                const uint8_t* wbase = (mt == 0 ? wa : wb) + mrow * ROW_BYTES;
-                const uint16_t* sbase = (mt == 0 ? sa : sb) + mrow * (K / 32);
+            for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) {
-                    const int g = gp + LPR * i;
-                    const float s = f16_to_f32(sbase[g]);
-                    const uint8_t* gptr = wbase + (size_t)g * GB;
+                    const float s = f16_to_f32(sbits[it][mt][i]);
 #pragma unroll
-                    for (int m = 0; m < kMT; ++m) {
+                    for (int m = 0; m < MT; ++m)
                         if (m < mcount) {
-                            const float raw = group_dot<FMT>(gptr, xv[m][i]);
-                            acc[mt][m] = __builtin_fmaf(
-                                s, raw - Fmt<FMT>::kBias * sx[m][i], acc[mt][m]);
+                            const float raw = dot_bits<FMT>(wbits[it][mt][i], xv[m][i]);
+                            const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx[m][i], raw);
+                            acc[mt][m] = __builtin_fmaf(s, part, acc[mt][m]);
                         }
-                    }
                 }
-            }
 #pragma unroll
-            for (int m = 0; m < kMT; ++m) {
+            for (int m = 0; m < MT; ++m) {
                 if (m < mcount) {
-                    float v0 = group_sum<LPR>(acc[0][m]);
+                    const float v0 = group_sum<LPR>(acc[0][m]);
                     float res;
                     if constexpr (MODE == kModeGateUp) {
                         const float u = group_sum<LPR>(acc[NMAT - 1][m]);
@@ -227,65 +312,101 @@ __global__ void __launch_bounds__(256) ffn_gemv_kernel(
                     } else {
                         res = v0;
                     }
-                    if (rv && gp == 0)
-                        out[(size_t)(c0 + m) * rows + row] = (uint16_t)f32_to_bf16(res);
+                    if (row < rows && gp == 0)
+                        out[(size_t)orow[m] * rows + row] = (uint16_t)f32_to_bf16(res);
                 }
             }
         }
     }
 }
 
-template <int FMT, int MODE>
-hipError_t launch_pass(const uint8_t* wa, const uint16_t* sa, const uint8_t* wb,
-                       const uint16_t* sb, const uint16_t* act, int K, int T, int k,
-                       const int32_t* ids, const int32_t* offsets, const int32_t* sorted_pairs,
-                       int E, int rows, uint16_t* out, int nslots, hipStream_t s) {
-#define MOE_GEMV_CASE(KV, LPRV, GPLV, ITV)                                                  \
-    case KV: {                                                                              \
-        constexpr int RPB = 4 * ITV * (64 / LPRV);                                          \
-        dim3 grid(nslots, (rows + RPB - 1) / RPB);                                          \
-        ffn_gemv_kernel<FMT, MODE, LPRV, GPLV, ITV><<<grid, 256, 0, s>>>(                   \
-            wa, sa, wb, sb, act, T, k, ids, offsets, sorted_pairs, E, rows, out);           \
-        break;                                                                              \
-    }
-    switch (K) {
-        MOE_GEMV_CASE(128, 4, 1, 1)
-        MOE_GEMV_CASE(256, 8, 1, 1)
-        MOE_GEMV_CASE(512, 16, 1, 2)
-        MOE_GEMV_CASE(1024, 32, 1, 2)
-        MOE_GEMV_CASE(2048, 64, 1, 4)
-        MOE_GEMV_CASE(4096, 64, 2, 2)
-        default:
-            return hipErrorInvalidValue;
-    }
-#undef MOE_GEMV_CASE
+template <int K>
+struct Shape {
+    static constexpr int LPR = K >= 2048 ? 64 : K / 32;
+    static constexpr int GPL = K >= 2048 ? K / 2048 : 1;
+    static constexpr int ITERS = K >= 4096 ? 2 : 1;
+    static constexpr int RPB = 4 * ITERS * (64 / LPR);
+};
+
+// grid.x = slots, grid.y = row blocks
+template <int FMT, int D, int F, int MT>
+__global__ void __launch_bounds__(256) ffn_gateup_kernel(
+    const uint8_t* __restrict__ wg, const uint16_t* __restrict__ sg,
+    const uint8_t* __restrict__ wu, const uint16_t* __restrict__ su,
+    const uint16_t* __restrict__ x, int T, int k, const int32_t* __restrict__ ids, int E,
+    uint16_t* __restrict__ h) {
+    using GU = Shape<D>;   // gate/up rows have K = d_model
+    Slot sl;
+    if (!resolve_slot<MT>(blockIdx.x, T, k, ids, E, sl)) return;
+    gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, MT>(wg, sg, wu, su, x, k, F,
+                                                                blockIdx.y, sl, h);
+}
+
+template <int FMT, int D, int F, int MT>
+__global__ void __launch_bounds__(256) ffn_down_kernel(
+    const uint8_t* __restrict__ wd, const uint16_t* __restrict__ sd,
+    const uint16_t* __restrict__ h, int T, int k, const int32_t* __restrict__ ids, int E,
+    uint16_t* __restrict__ y) {
+    using DN = Shape<F>;   // down rows have K = d_ff
+    Slot sl;
+    if (!resolve_slot<MT>(blockIdx.x, T, k, ids, E, sl)) return;
+    gemv_rows<FMT, kModeDown, DN::LPR, DN::GPL, DN::ITERS, MT>(wd, sd, nullptr, nullptr, h, k,
+                                                              D, blockIdx.y, sl, y);
+}
+
+template <int FMT, int D, int F, int MT>
+hipError_t launch_mt(const moe_experts& ex, const uint16_t* x, int T, int k, const int32_t* ids,
+                     uint16_t* y, uint16_t* h, hipStream_t s) {
+    const int nslots = ids ? T * k : (T + MT - 1) / MT;
+    constexpr int n_gu = (F + Shape<D>::RPB - 1) / Shape<D>::RPB;
+    constexpr int n_dn = (D + Shape<F>::RPB - 1) / Shape<F>::RPB;
+    ffn_gateup_kernel<FMT, D, F, MT><<<dim3(nslots, n_gu), 256, 0, s>>>(
+        ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, T, k, ids, ex.n_experts, h);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    ffn_down_kernel<FMT, D, F, MT><<<dim3(nslots, n_dn), 256, 0, s>>>(
+        ex.w_down, ex.s_down, h, T, k, ids, ex.n_experts, y);
     return hipGetLastError();
 }
 
+// MT: a slot never holds more pairs than tokens (a token picks an expert at most once)
+template <int FMT, int D, int F>
+hipError_t launch_shape(const moe_experts& ex, const uint16_t* x, int T, int k,
+                        const int32_t* ids, uint16_t* y, void* ws, hipStream_t s) {
+    uint16_t* h = static_cast<uint16_t*>(ws);
+    if (T == 1) return launch_mt<FMT, D, F, 1>(ex, x, T, k, ids, y, h, s);
+    if (T == 2) return launch_mt<FMT, D, F, 2>(ex, x, T, k, ids, y, h, s);
+    return launch_mt<FMT, D, F, 4>(ex, x, T, k, ids, y, h, s);
+}
+
 template <int FMT>
-hipError_t launch_ffn(const moe_experts& ex, const uint16_t* x, int T, int k,
-                      const int32_t* ids, const int32_t* offsets, const int32_t* sorted_pairs,
-                      uint16_t* y, uint16_t* h_ws, hipStream_t s) {
-    const int d = ex.d_model, F = ex.d_ff, E = ex.n_experts;
-    const bool grouped = offsets != nullptr;
-    const int nslots = grouped ? T * k : (T + kMT - 1) / kMT;
-    hipError_t err = launch_pass<FMT, kModeGateUp>(ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x,
-                                                   d, T, k, ids, offsets, sorted_pairs, E, F,
-                                                   h_ws, nslots, s);
-    if (err != hipSuccess) return err;
-    return launch_pass<FMT, kModeDown>(ex.w_down, ex.s_down, nullptr, nullptr, h_ws, F, T, k,
-                                       ids, offsets, sorted_pairs, E, d, y, nslots, s);
+hipError_t launch_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
+                      const int32_t* ids, uint16_t* y, void* ws, hipStream_t s) {
+#define MOE_DEC(DV, FV)                                                                  \
+    if (ex.d_model == DV && ex.d_ff == FV)                                               \
+        return launch_shape<FMT, DV, FV>(ex, x, T, k, ids, y, ws, s);
+    MOE_DEC(2048, 512)
+    MOE_DEC(256, 128)
+    MOE_DEC(2048, 1024)
+    MOE_DEC(4096, 1024)
+    MOE_DEC(1024, 512)
+    MOE_DEC(2048, 2048)
+#undef MOE_DEC
+    return hipErrorNotSupported;
 }
 
 }  // namespace
 
+bool ffn_gemv_has_shape(int d, int F) {
+    return (d == 2048 && (F == 512 || F == 1024 || F == 2048)) || (d == 256 && F == 128) ||
+           (d == 4096 && F == 1024) || (d == 1024 && F == 512);
+}
+
 hipError_t launch_ffn_gemv(const moe_experts& ex, const uint16_t* x, int T, int k,
-                           const int32_t* ids, const int32_t* offsets,
-                           const int32_t* sorted_pairs, uint16_t* y, uint16_t* h_ws,
-                           hipStream_t s) {
+                           const int32_t* ids, uint16_t* y, void* ws, hipStream_t s) {
     if (ex.fmt == MOE_FMT_INT4_G32)
-        return launch_ffn<MOE_FMT_INT4_G32>(ex, x, T, k, ids, offsets, sorted_pairs, y, h_ws, s);
-    return launch_ffn<MOE_FMT_INT6_G32>(ex, x, T, k, ids, offsets, sorted_pairs, y, h_ws, s);
+        return launch_fmt<MOE_FMT_INT4_G32>(ex, x, T, k, ids, y, ws, s);
+    return launch_fmt<MOE_FMT_INT6_G32>(ex, x, T, k, ids, y, ws, s);
 }
 
 }  // namespace moe

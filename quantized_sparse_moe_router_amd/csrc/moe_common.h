@@ -40,12 +40,36 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 __device__ __forceinline__ int shfl_xor(int v, int m) { return __shfl_xor(v, m, kWave); }
 
+// DPP lane permutations (gfx9 encodings): quad_perm [1,0,3,2] and [2,3,0,1] pair lanes
+// whose index differs in bit 0 / bit 1; row_half_mirror pairs lane i with 7-i inside each
+// 8-lane group; row_mirror pairs lane i with 15-i inside each 16-lane row.  Applied in that
+// order to values that are already equal across the smaller aligned block, each step adds
+// the two halves of the next aligned block, i.e. the same tree as xor offsets 1, 2, 4, 8.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf,
+                                                      false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 64); every lane of the group
-// ends with the group's sum.
+// ends with the group's sum, combined as the butterfly tree over xor offsets 1..G/2.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) v += shfl_xor(v, m);
+    if constexpr (G >= 2) v = v + dpp<kDppXor1>(v);
+    if constexpr (G >= 4) v = v + dpp<kDppXor2>(v);
+    if constexpr (G >= 8) v = v + dpp<kDppHalfMirror>(v);
+    if constexpr (G >= 16) v = v + dpp<kDppMirror>(v);
+    if constexpr (G >= 32) v = v + shfl_xor(v, 16);
+    if constexpr (G >= 64) v = v + shfl_xor(v, 32);
     return v;
 }
 
@@ -56,19 +80,28 @@ __device__ __forceinline__ float group_sum(float v) {
 // validated by the C entry points.
 namespace moe {
 
+// Workspace area that holds an arrival counter.  It must be zero before a workspace's
+// first use; every call leaves it zero.
+constexpr size_t kRouteCounterBytes = 256;
+
+// Device error word (per device): bit 0 = expert id out of range, bit 1 = a bounded wait
+// timed out.  Returns its device address for the current device.
+int* device_error_flag();
+hipError_t read_and_clear_device_error(int* flag);
+
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
-                        float* weights, float* logits, hipStream_t s);
+                        float* weights, float* logits, unsigned* counter, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted_pairs, int32_t* pair_pos, void* ws, hipStream_t s);
 size_t permute_ws_bytes(int64_t P, int E);
-hipError_t read_and_clear_device_error(int* flag);
 
-// Grouped (ids/offsets/sorted_pairs non-null) or dense (all null) expert FFN.
+// Small calls: weight-streaming GEMV, gate/up then down; positions come from ids
+// (grouped) or the token index (dense, ids == nullptr).  ws = [h].
+bool ffn_gemv_has_shape(int d_model, int d_ff);
 hipError_t launch_ffn_gemv(const moe_experts& ex, const uint16_t* x, int T, int k,
-                           const int32_t* ids, const int32_t* offsets,
-                           const int32_t* sorted_pairs, uint16_t* y, uint16_t* h_ws,
-                           hipStream_t s);
+                           const int32_t* ids, uint16_t* y, void* ws, hipStream_t s);
+// Large calls: grouped MFMA GEMM.  ws = [h][tile list].
 hipError_t launch_ffn_mfma(const moe_experts& ex, const uint16_t* x, int T, int k,
                            const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
                            void* ws, hipStream_t s);

@@ -15,7 +15,8 @@
 
 namespace moe {
 
-// Raised (set to 1) by any kernel that meets an expert id outside [0, E).
+// Device error word: bit 0 is raised by any kernel that meets an expert id outside
+// [0, E), bit 1 by a bounded wait that timed out.
 static __device__ int g_bad_id_flag;
 
 namespace {
@@ -95,6 +96,62 @@ __device__ void block_exclusive_scan(const int* cnt, int* out, int E) {
     if (tid < E) out[tid] = excl;
     if (tid == E - 1) out[E] = excl + v;
     __syncthreads();
+}
+
+// Decode-sized calls (P <= 64): one wave.  Histogram in LDS, a wave-wide exclusive scan
+// gives offsets; a pair's sorted position is offsets[id] plus the number of earlier pairs
+// with the same id.
+__global__ void __launch_bounds__(64) permute_wave_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
+    __shared__ int hist[kMaxE];
+    const int lane = threadIdx.x;
+    const int id = (lane < P) ? ids[lane] : -1;
+    const bool valid = lane < P && id >= 0 && id < E;
+    for (int e = lane; e < E; e += 64) hist[e] = 0;
+    __syncthreads();
+    if (lane < P && !valid) {
+        pair_pos[lane] = -1;
+        atomicOr(&g_bad_id_flag, 1);
+    }
+    if (valid) atomicAdd(&hist[id], 1);
+    __syncthreads();
+    // lane owns entries [lane*C, lane*C + C)
+    const int C = (E + 63) / 64;
+    int local = 0;
+    for (int j = 0; j < C; ++j) {
+        const int e = lane * C + j;
+        if (e < E) local += hist[e];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    int run = incl - local;
+    __syncthreads();
+    for (int j = 0; j < C; ++j) {
+        const int e = lane * C + j;
+        if (e < E) {
+            const int c = hist[e];
+            hist[e] = run;                 // now the exclusive prefix (start of e)
+            offsets[e] = run;
+            run += c;
+        }
+    }
+    if (lane == 63) offsets[E] = incl;     // total of valid pairs
+    __syncthreads();
+    int rank = 0;
+    for (int q = 0; q < P; ++q) {          // uniform loop: readlane needs a uniform lane
+        const int oid = __builtin_amdgcn_readlane(id, q);
+        rank += (q < lane && oid == id) ? 1 : 0;
+    }
+    if (valid) {
+        const int pos = hist[id] + rank;
+        sorted_pairs[pos] = lane;
+        pair_pos[lane] = pos;
+    }
 }
 
 // All three steps in one block (P <= kChunk).  blockDim.x = 1024.
@@ -182,6 +239,10 @@ size_t permute_ws_bytes(int64_t P, int E) {
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted_pairs, int32_t* pair_pos, void* ws, hipStream_t s) {
     const int64_t P = (int64_t)T * k;
+    if (P <= 64) {
+        permute_wave_kernel<<<1, 64, 0, s>>>(ids, (int)P, E, offsets, sorted_pairs, pair_pos);
+        return hipGetLastError();
+    }
     if (P <= kChunk) {
         permute_small_kernel<<<1, 1024, 0, s>>>(ids, (int)P, E, offsets, sorted_pairs,
                                                 pair_pos);
@@ -193,6 +254,18 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
     chunk_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunk, E, offsets);
     chunk_scatter_kernel<<<nchunk, 64, 0, s>>>(ids, P, E, hist, sorted_pairs, pair_pos);
     return hipGetLastError();
+}
+
+int* device_error_flag() {
+    static int* addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_bad_id_flag)) == hipSuccess)
+            addr[dev] = static_cast<int*>(p);
+    }
+    return addr[dev];
 }
 
 hipError_t read_and_clear_device_error(int* flag) {

@@ -19,11 +19,11 @@ namespace {
 // One wave per expert row.  Lane l holds its vectors v = l + 64 j of the row in
 // registers and walks them for every token; the butterfly is a shuffle-xor tree.
 // PV = elements per 16-byte vector (4 fp32 or 16 int8); NV = vectors per lane.
-template <int FMT, int NV>
-__global__ void __launch_bounds__(256) router_gemv_kernel(
+template <int FMT, int NV, bool DEVICE_SCOPE_STORE>
+__device__ __forceinline__ void router_gemv_rows(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
-    float* __restrict__ logits) {
+    float* logits) {
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -76,13 +76,16 @@ __global__ void __launch_bounds__(256) router_gemv_kernel(
                 }
             }
         }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) acc = acc + shfl_xor(acc, off);
+        acc = group_sum<64>(acc);     // butterfly over xor offsets 1..32
         if (lane == 0) {
             float l = acc;
             if constexpr (FMT == MOE_FMT_INT8_ROW) l = l * se;
             if (bias) l = l + b;
-            logits[(size_t)t * E + e] = l;
+            if constexpr (DEVICE_SCOPE_STORE)
+                __hip_atomic_store(logits + (size_t)t * E + e, l, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else
+                logits[(size_t)t * E + e] = l;
         }
     }
 }
@@ -244,115 +247,201 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(
 }
 
 // ------------------------------------------------------------------ top-k + weights
-// One wave per token.  Lane l holds logits of experts l, l+64, ...; k rounds of "best
-// remaining" (larger logit first, equal logits -> lower id), then softmax over the k
-// selected logits in fp32, shifted by the largest.
-__device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb) {
-    return va > vb || (va == vb && ea < eb);
+// One wave per token.  Each (logit, expert) becomes a 64-bit key whose unsigned order is
+// the selection order: the logit's bits mapped to an order-preserving unsigned integer
+// (-0 first turned into +0 so the two compare equal) in the high word, and 0xffffffff - e
+// in the low word so that equal logits favour the lower expert id.  k rounds of a wave
+// max over the lanes' best untaken keys pick the experts in slot order; then the weights
+// are the softmax over the k selected logits in fp32, shifted by the largest.
+__device__ __forceinline__ uint32_t order_bits(float v) {
+    uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Selection and weights of one token by one wave.  Keys are 64-bit: the logit's bits mapped
+// to an order-preserving unsigned integer in the high word, 0xffffffff - e in the low word,
+// so "larger key" is "larger logit, then lower id".  Each lane sorts its NPL keys once;
+// each of the k rounds takes the wave maximum of the lanes' heads (DPP inside 16-lane rows,
+// then the four row maxima on the scalar unit) and the owning lane advances its head.
+template <int NPL, bool DEVICE_SCOPE_LOAD>
+__device__ __forceinline__ void topk_token(const float* lt, int E, int k, int32_t* ids_t,
+                                           float* w_t) {
+    const int lane = threadIdx.x & 63;
+    uint64_t key[NPL];
+    float v[NPL];
+    // all loads first, unconditionally (clamped index), so they are in flight together
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+        if constexpr (DEVICE_SCOPE_LOAD)
+            v[i] = __hip_atomic_load(const_cast<float*>(lt) + e, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        else
+            v[i] = lt[e];
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? (((uint64_t)order_bits(v[i]) << 32) | (0xffffffffu - (uint32_t)e))
+                         : 0ull;                       // padding keys lose to every id
+    }
+    // descending sort of the lane's keys (odd-even transposition network)
+#pragma unroll
+    for (int r = 0; r < NPL; ++r)
+#pragma unroll
+        for (int i = r & 1; i + 1 < NPL; i += 2) {
+            const uint64_t a = key[i], b = key[i + 1];
+            key[i] = a > b ? a : b;
+            key[i + 1] = a > b ? b : a;
+        }
+    uint64_t mine = 0ull;
+    int head = 0;                                      // index of the lane's next key
+    for (int j = 0; j < k; ++j) {
+        uint64_t b = 0ull;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) b = (head == i) ? key[i] : b;
+        const uint64_t cand = b;
+        uint64_t o;
+        o = dpp64<kDppXor1>(b);       b = o > b ? o : b;
+        o = dpp64<kDppXor2>(b);       b = o > b ? o : b;
+        o = dpp64<kDppHalfMirror>(b); b = o > b ? o : b;
+        o = dpp64<kDppMirror>(b);     b = o > b ? o : b;
+        uint64_t win = readlane64(b, 0);
+#pragma unroll
+        for (int r = 16; r < 64; r += 16) {
+            const uint64_t c = readlane64(b, r);
+            win = c > win ? c : win;
+        }
+        // keys are unique (the low word holds the id): exactly one lane owns the winner
+        head += (cand == win) ? 1 : 0;
+        if (lane == j) mine = win;
+    }
+    const uint32_t my_hi = (uint32_t)(mine >> 32), my_lo = (uint32_t)mine;
+    const int my_e = (int)(0xffffffffu - my_lo);
+    const uint32_t vbits = (my_hi & 0x80000000u) ? (my_hi & 0x7fffffffu) : ~my_hi;
+    const float my_v = (lane < k) ? __uint_as_float(vbits) : 0.0f;
+    const float vmax = __shfl(my_v, 0, 64);
+    const float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
+    const float sum = group_sum<64>(ex);
+    if (lane < k) {
+        ids_t[lane] = my_e;
+        w_t[lane] = ex / sum;
+    }
 }
 
 template <int NPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T,
                                                    int E, int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ weights) {
-    const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float* lt = logits + (size_t)t * E;
-    float v[NPL];
-    uint32_t taken = 0u;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = (e < E) ? lt[e] : 0.0f;
-        if (e >= E) taken |= 1u << i;
+    topk_token<NPL, false>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
+                           weights + (size_t)t * k);
+}
+
+// Few tokens: logits and selection in one launch.  Every block computes its rows' logits
+// for all tokens, writes them with device-scope stores, waits for those stores, then
+// counts itself in; the last block to arrive reads every logit with device-scope loads,
+// runs the selection for all tokens and resets the counter, leaving the workspace as it
+// found it.  No cache-wide flush or invalidation is involved.
+template <int FMT, int NV, int NPL>
+__global__ void __launch_bounds__(256) router_gemv_topk_kernel(
+    const void* __restrict__ W, const uint16_t* __restrict__ scale,
+    const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d, int k,
+    float* logits, int32_t* __restrict__ ids, float* __restrict__ weights, unsigned* counter) {
+    router_gemv_rows<FMT, NV, true>(W, scale, bias, x, T, E, d, logits);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this block's stores done
+    __syncthreads();
+    __shared__ int is_last;
+    if (threadIdx.x == 0) is_last = (atomicAdd(counter, 1u) == gridDim.x - 1) ? 1 : 0;
+    __syncthreads();
+    if (!is_last) return;
+    for (int t = threadIdx.x >> 6; t < T; t += 4)
+        topk_token<NPL, true>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
+                              weights + (size_t)t * k);
+    if (threadIdx.x == 0) atomicExch(counter, 0u);
+}
+
+template <int FMT, int NV>
+hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
+                     float* weights, float* logits, unsigned* counter, hipStream_t s) {
+    const int E = r.n_experts, d = r.d_model;
+    const int npl = (E + 63) / 64;
+    if (T <= 16) {   // few tokens: one wave per expert row, selection by the last block
+        const dim3 grid((E + 3) / 4), block(256);
+#define MOE_GT(N)                                                                         \
+    router_gemv_topk_kernel<FMT, NV, N><<<grid, block, 0, s>>>(r.w, r.scale, r.bias, x, T, \
+                                                               E, d, k, logits, ids, weights, \
+                                                               counter)
+        if (npl <= 1) MOE_GT(1);
+        else if (npl <= 2) MOE_GT(2);
+        else if (npl <= 4) MOE_GT(4);
+        else if (npl <= 8) MOE_GT(8);
+        else MOE_GT(16);
+#undef MOE_GT
+        return hipGetLastError();
     }
-    float my_v = 0.0f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -__builtin_inff();
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const int e = lane + 64 * i;
-            if (!((taken >> i) & 1u) && ranks_before(v[i], e, bv, be)) { bv = v[i]; be = e; }
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float ov = shfl_xor(bv, off);
-            const int oe = shfl_xor(be, off);
-            if (ranks_before(ov, oe, bv, be)) { bv = ov; be = oe; }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) { my_v = bv; my_e = be; }
-    }
-    const float vmax = __shfl(my_v, 0, 64);
-    float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) sum += shfl_xor(sum, off);
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        weights[(size_t)t * k + lane] = ex / sum;
-    }
+    router_gemm_kernel<FMT, NV>
+        <<<dim3((T + RT_TM - 1) / RT_TM, (E + RT_TE - 1) / RT_TE), dim3(256), 0, s>>>(
+            r.w, r.scale, r.bias, x, T, E, d, logits);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid((T + 3) / 4), block(256);
+    if (npl <= 1)
+        topk_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
+    else if (npl <= 2)
+        topk_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
+    else if (npl <= 4)
+        topk_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
+    else if (npl <= 8)
+        topk_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
+    else
+        topk_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, ids, weights);
+    return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
-                         hipStream_t s) {
-    const int E = r.n_experts, d = r.d_model;
+hipError_t launch_fmt(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
+                      float* weights, float* logits, unsigned* counter, hipStream_t s) {
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
-    const int nv = d / (64 * PV);
-    // small T: one wave per expert row; large T: LDS-tiled GEMM (same summation order)
-    const bool gemv = T <= 16;
-#define MOE_ROUTE_CASE(NVC)                                                              \
-    case NVC:                                                                            \
-        if constexpr (RT_KC % (NVC * PV) == 0) {                                         \
-            if (gemv)                                                                    \
-                router_gemv_kernel<FMT, NVC><<<dim3((E + 3) / 4), dim3(256), 0, s>>>(    \
-                    r.w, r.scale, r.bias, x, T, E, d, logits);                           \
-            else                                                                         \
-                router_gemm_kernel<FMT, NVC>                                             \
-                    <<<dim3((T + RT_TM - 1) / RT_TM, (E + RT_TE - 1) / RT_TE), dim3(256), \
-                       0, s>>>(r.w, r.scale, r.bias, x, T, E, d, logits);                \
-            break;                                                                       \
-        } else {                                                                         \
-            return hipErrorInvalidValue;                                                 \
-        }
-    switch (nv) {
-        MOE_ROUTE_CASE(1)
-        MOE_ROUTE_CASE(2)
-        MOE_ROUTE_CASE(4)
-        MOE_ROUTE_CASE(8)
-        MOE_ROUTE_CASE(16)
-        default:
-            return hipErrorInvalidValue;
+    const int nv = r.d_model / (64 * PV);
+    // chain length per lane must divide the GEMM kernel's 64-element chunk
+#define MOE_NV(N)                                                                         \
+    if (nv == N) {                                                                        \
+        if constexpr (RT_KC % (N * PV) == 0)                                              \
+            return launch_nv<FMT, N>(r, x, T, k, ids, weights, logits, counter, s);       \
+        else                                                                              \
+            return hipErrorInvalidValue;                                                  \
     }
-#undef MOE_ROUTE_CASE
-    return hipGetLastError();
+    MOE_NV(1)
+    MOE_NV(2)
+    MOE_NV(4)
+    MOE_NV(8)
+    MOE_NV(16)
+#undef MOE_NV
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
-                        float* weights, float* logits, hipStream_t s) {
-    hipError_t err = (r.fmt == MOE_FMT_INT8_ROW)
-                         ? launch_logits<MOE_FMT_INT8_ROW>(r, x, T, logits, s)
-                         : launch_logits<MOE_FMT_FP32>(r, x, T, logits, s);
-    if (err != hipSuccess) return err;
-    const int npl = (r.n_experts + 63) / 64;
-    const dim3 grid((T + 3) / 4), block(256);
-    if (npl <= 1)
-        topk_kernel<1><<<grid, block, 0, s>>>(logits, T, r.n_experts, k, ids, weights);
-    else if (npl <= 2)
-        topk_kernel<2><<<grid, block, 0, s>>>(logits, T, r.n_experts, k, ids, weights);
-    else if (npl <= 4)
-        topk_kernel<4><<<grid, block, 0, s>>>(logits, T, r.n_experts, k, ids, weights);
-    else if (npl <= 8)
-        topk_kernel<8><<<grid, block, 0, s>>>(logits, T, r.n_experts, k, ids, weights);
-    else
-        topk_kernel<16><<<grid, block, 0, s>>>(logits, T, r.n_experts, k, ids, weights);
-    return hipGetLastError();
+                        float* weights, float* logits, unsigned* counter, hipStream_t s) {
+    if (r.fmt == MOE_FMT_INT8_ROW)
+        return launch_fmt<MOE_FMT_INT8_ROW>(r, x, T, k, ids, weights, logits, counter, s);
+    return launch_fmt<MOE_FMT_FP32>(r, x, T, k, ids, weights, logits, counter, s);
 }
 
 }  // namespace moe

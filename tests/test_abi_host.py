@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
 
 def test_workspace_sizes(L):
     from quantized_sparse_moe_router_amd import _lib
-    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 1, 10, 512, 2048, 512) == 2048
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 1, 10, 512, 2048, 512) == 256 + 2048
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 0, 10, 512, 2048, 512) == 0
     # small permutes run in one block without workspace
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 1, 10, 512, 2048, 512) == 0
@@ -94,6 +94,9 @@ def test_route_null_descriptor_and_workspace(L):
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, None, None, 0, None)
     assert st == -3 and "workspace" in _err(L)
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, None, 16, 100, None)
+    assert st == -3
+    # with a logits output the workspace still holds the arrival counter
+    st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, 16, None, 0, None)
     assert st == -3
     st = L.moe_route(ctypes.byref(r), 8, 1, 10, 16, 16, 16, None, 0, None)
     assert st == -1 and "x" in _err(L)
