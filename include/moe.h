@@ -83,8 +83,9 @@ typedef struct moe_router {
  *              s_gate/s_up fp16 [E][d_ff][d_model/32]
  *   down     : [d_model][d_ff] -> w_down bytes [E][d_model][row bytes(d_ff)],
  *              s_down fp16 [E][d_model][d_ff/32]
- * The shared expert is a set with E = 1.  d_model and d_ff must each be one of 128, 256,
- * 512, 1024, 2048, 4096; weight pointers must be 16-byte aligned. */
+ * The shared expert is a set with E = 1.  d_model must be one of 256, 512, 1024, 2048,
+ * 4096 and d_ff one of 128, 256, ..., 4096; weight and scale pointers must be 16-byte
+ * aligned. */
 typedef struct moe_experts {
     int32_t fmt;
     int32_t n_experts;

@@ -165,13 +165,16 @@ moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, i
     const int E = ex->n_experts, d = ex->d_model, F = ex->d_ff;
     if (E < 1 || E > kMaxExperts)
         return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_experts %d", E);
-    if (!supported_ffn_dim(d) || !supported_ffn_dim(F))
+    if (!supported_ffn_dim(d) || d < 256 || !supported_ffn_dim(F))
         return fail(MOE_ERR_INVALID_ARG,
-                    "moe_expert_ffn: d_model %d / d_ff %d must be 128..4096 powers of two", d, F);
+                    "moe_expert_ffn: d_model %d must be 256..4096 and d_ff %d 128..4096, "
+                    "powers of two", d, F);
     if (!ex->w_gate || !ex->w_up || !ex->w_down || !ex->s_gate || !ex->s_up || !ex->s_down)
         return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: a weight or scale pointer is NULL");
-    if (!aligned16(ex->w_gate) || !aligned16(ex->w_up) || !aligned16(ex->w_down))
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: weights not 16-byte aligned");
+    if (!aligned16(ex->w_gate) || !aligned16(ex->w_up) || !aligned16(ex->w_down) ||
+        !aligned16(ex->s_gate) || !aligned16(ex->s_up) || !aligned16(ex->s_down))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_expert_ffn: weights or scales not 16-byte aligned");
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: T = %d < 0", T);
     const bool grouped = ids || offsets || sorted_pairs;
     if (grouped && (!ids || !offsets || !sorted_pairs))

@@ -4,31 +4,55 @@
 // Qwen3.8-Flash-Next (telli.sh), section GPU、RAM 和 SSD 各司其职], so per expert the FFN
 // is a dense contraction: [M_e x d] x [d x 2F] (gate and up), SwiGLU, then
 // [M_e x F] x [F x d] (down).  That is the one place the layer maps onto the matrix
-// cores.  Weight tiles are dequantised to bf16 once per block and k-step into LDS;
-// activation rows are gathered by the sorted pair list into LDS; both feed
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+// cores: v_mfma_f32_32x32x16_bf16, fp32 accumulation.
 //
-// Work list: one entry per (expert, 128-row tile of that expert's pairs), built on the
+// Work list: one entry per (expert, BM-row tile of that expert's pairs), built on the
 // device from the offsets (no host round trip).  The grid covers the largest possible
 // list; blocks past its end return at once.
+//
+// Block = 4 waves, one per SIMD, tile BM = 256 rows x BN = 256 output columns; wave w owns
+// columns [64 w, 64 w + 64) for all 256 rows (8 x 2 MFMA blocks of 32 x 32, 256 fp32
+// accumulators in AGPRs).  All waves share the tile's rows, so a partial tile (an
+// expert's last rows) shrinks every wave's MFMA work alike.
+//
+// Data movement per k-step of 64:
+//   - activations: global -> LDS directly (global_load_lds_dwordx4, no register round
+//     trip), 256 rows x 128 bytes, XOR-swizzled 16-byte chunks so the MFMA operand reads
+//     are free of bank conflicts;
+//   - weight codes and fp16 scales: global -> LDS directly, into a region private to the
+//     wave that uses them; each lane later reads back exactly the 16 (int4) or 24 (int6)
+//     bytes of the one 32-code group it dequantises;
+//   - dequantisation happens in registers straight into the MFMA B operand (no LDS
+//     round trip for bf16 weights);
+//   - the bf16 output tile is staged through LDS so global stores are full rows.  The MFMA k order inside a step is permuted so that
+//     lane half h of every operand covers the 32-code group h: codes and scales of one
+//     group serve four MFMA sub-steps.
+// Three LDS stages: loads for step ks + 2 are issued at the start of step ks, so each
+// has about two k-steps to land.  Loads are counted by hand (s_waitcnt vmcnt) because the
+// compiler does not track LDS written by these loads.
 #include "moe_common.h"
+
+#include <type_traits>
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128;          // rows (pairs) per tile
-constexpr int BN = 128;          // output columns per tile (gate/up: 64 f x 2)
+constexpr int BM = 256;          // rows (pairs) per tile
+constexpr int BN = 256;          // output columns per tile (gate/up: 128 f x 2)
+constexpr int NW = 4;            // waves per block
+constexpr int NT = 64 * NW;      // threads per block
+constexpr int TN = BN / NW;      // columns per wave
+constexpr int NI = TN / 32;      // 32-column MFMA blocks per wave (2)
+constexpr int MI = BM / 32;      // 32-row MFMA blocks per tile (8)
 constexpr int BK = 64;           // reduction step
-constexpr int LDP = BK + 8;      // LDS row pitch in bf16 (padding against bank conflicts)
+constexpr int kStages = 3;       // LDS pipeline stages
+constexpr int kXcds = 8;         // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-struct TileList {
-    int4* tiles;     // {expert, row begin, row end (segment end), 0}
-    int* count;
-};
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // plain vector: stays in VGPRs
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 size_t tile_capacity(int64_t rows, int E) { return (size_t)((rows + BM - 1) / BM + E); }
 
@@ -67,251 +91,408 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
 }
 
 // -------------------------------------------------------------- dequantisation
-// 32 codes of one group (one row, one scale) -> 32 bf16 (16 packed pairs).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     bf16x2_t p = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, p);
 }
 
-__device__ __forceinline__ void dequant_int4(const uint4 w, float s, uint32_t* out) {
-    const float c = -8.0f * s;
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        uint32_t lo = wd[q] & 0x0f0f0f0fu, hi = (wd[q] >> 4) & 0x0f0f0f0fu;
-        // keep the nibbles byte-aligned so each converts with one byte-to-float op
-        asm volatile("" : "+v"(lo), "+v"(hi));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const float e0 = (float)((lo >> (8 * b)) & 0xffu);
-            const float e1 = (float)((hi >> (8 * b)) & 0xffu);
-            out[4 * q + b] = pack_bf16(__builtin_fmaf(e0, s, c), __builtin_fmaf(e1, s, c));
-        }
-    }
-}
-
-__device__ __forceinline__ void dequant_int6(const uint32_t* w6, float s, uint32_t* out) {
-    const float c = -32.0f * s;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        const uint64_t lo64 = (uint64_t)w6[3 * half] | ((uint64_t)w6[3 * half + 1] << 32);
-        const uint64_t hi32 = w6[3 * half + 2];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            float v[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int bit = 6 * (2 * p + t);
-                uint32_t u;
-                if (bit + 6 <= 64)
-                    u = (uint32_t)(lo64 >> bit);
-                else if (bit >= 64)
-                    u = (uint32_t)(hi32 >> (bit - 64));
-                else
-                    u = (uint32_t)(lo64 >> bit) | (uint32_t)(hi32 << (64 - bit));
-                v[t] = __builtin_fmaf((float)(u & 63u), s, c);
-            }
-            out[8 * half + p] = pack_bf16(v[0], v[1]);
-        }
-    }
-}
-
+// The codes of one 32-code group: int4 = 16 bytes (a), int6 = 24 bytes (a, then b).
 template <int FMT>
-struct GroupLoad {
-    uint4 a;
-    uint2 b;   // int6 tail
+struct GroupCodes {
+    u32x4_t a;
+    u32x2_t b;
 };
 
+// Chunk c (codes 8c..8c+7) of a group, split into byte-aligned code fields: lo holds
+// codes 8c, 8c+2, 8c+4, 8c+6 in bytes 0..3, hi codes 8c+1, 8c+3, 8c+5, 8c+7.
 template <int FMT>
-__device__ __forceinline__ void load_group(const uint8_t* p, GroupLoad<FMT>& g) {
+__device__ __forceinline__ void chunk_codes(const GroupCodes<FMT>& g, int c, uint32_t& lo,
+                                            uint32_t& hi) {
     if constexpr (FMT == MOE_FMT_INT4_G32) {
-        g.a = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w = g.a[c];      // byte i: code 8c+2i (low nibble), 8c+2i+1 (high)
+        lo = w & 0x0f0f0f0fu;
+        hi = (w >> 4) & 0x0f0f0f0fu;
     } else {
-        const uint2* q = reinterpret_cast<const uint2*>(p);
-        const uint2 x0 = q[0], x1 = q[1], x2 = q[2];
-        g.a = make_uint4(x0.x, x0.y, x1.x, x1.y);
-        g.b = x2;
+        // 8 six-bit codes = bits [48c, 48c + 48) of the 24-byte group
+        const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
+        const int bit = 48 * c, wi = bit / 32, sh = bit % 32;
+        const uint64_t v = ((uint64_t)w6[wi] | ((uint64_t)w6[wi + 1] << 32)) >> sh;
+        uint32_t l = 0, h = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            l |= (uint32_t)((v >> (12 * p)) & 63u) << (8 * p);
+            h |= (uint32_t)((v >> (12 * p + 6)) & 63u) << (8 * p);
+        }
+        lo = l;
+        hi = h;
     }
+    asm volatile("" : "+v"(lo), "+v"(hi));   // keep the byte fields for byte-to-float ops
 }
 
+// Codes 8c+2b and 8c+2b+1 -> packed bf16 pair s * (code - zero point).
 template <int FMT>
-__device__ __forceinline__ void dequant_group(const GroupLoad<FMT>& g, float s, uint32_t* out) {
-    if constexpr (FMT == MOE_FMT_INT4_G32) {
-        dequant_int4(g.a, s, out);
-    } else {
-        const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
-        dequant_int6(w6, s, out);
-    }
+__device__ __forceinline__ uint32_t chunk_pair(uint32_t lo, uint32_t hi, int b, float s) {
+    const float zc = (FMT == MOE_FMT_INT4_G32) ? -8.0f * s : -32.0f * s;
+    const float e0 = (float)((lo >> (8 * b)) & 0xffu);
+    const float e1 = (float)((hi >> (8 * b)) & 0xffu);
+    return pack_bf16(__builtin_fmaf(e0, s, zc), __builtin_fmaf(e1, s, zc));
 }
+
+// -------------------------------------------------------------- global -> LDS loads
+// lds is the wave-uniform byte address of the destination, set in M0 (the instruction
+// needs one wait state after M0 is written).  Lane l's data lands at lds + 16 l for
+// dwordx4 and dwordx3 (12 bytes used), and at lds + 4 l for ushort (zero-extended to 32
+// bits).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma12(const void* g, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+// wait until at most n of this wave's global loads are outstanding (n <= 63) and, with
+// the _LDS form, until its LDS reads are done too (before a barrier after which other
+// waves' loads overwrite what was read)
+#define MOE_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define MOE_WAIT_VMCNT_LDS(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
 
 enum { kGateUp = 0, kDown = 1 };
 
+// LDS bytes of one pipeline stage
+template <int FMT>
+struct StageLayout {
+    static constexpr int GB = (FMT == MOE_FMT_INT4_G32) ? 16 : 24;   // bytes per group
+    static constexpr int DMA_B = (FMT == MOE_FMT_INT4_G32) ? 1 : 2;   // loads per group
+    static constexpr int A = BM * BK * 2;                             // activations
+    static constexpr int B_WJ = DMA_B * 64 * 16;                      // codes of (wave, j)
+    static constexpr int B = NW * NI * B_WJ;
+    static constexpr int S_WJ = 64 * 4;                               // scales of (wave, j)
+    static constexpr int S = NW * NI * S_WJ;
+    static constexpr int BYTES = A + B + S;
+};
+template <int FMT>
+constexpr int kGemmLds = kStages * StageLayout<FMT>::BYTES;
+static_assert(kStages * StageLayout<MOE_FMT_INT6_G32>::BYTES <= 160 * 1024, "LDS");
+
 // -------------------------------------------------------------- grouped GEMM
-// 256 threads = 4 waves in a 2 x 2 layout, each wave a 64 x 64 sub-tile made of 4 x 4
-// MFMA 16x16x32 blocks.
-//   kGateUp: K = d, B rows = 64 gate rows and the 64 up rows of the same f; the LDS B
-//            tile is ordered [gate f0..+31 | up f0..+31 | gate f0+32..+63 | up f0+32..+63]
-//            so each lane holds the gate and up outputs of the same (row, f); epilogue
-//            h = silu(g) * u -> bf16 [rows][F].
-//   kDown  : K = F, B rows = 128 rows of W_down; epilogue y -> bf16 [rows][d].
+//   kGateUp: K = d; block column tile ny covers f in [128 ny, 128 ny + 128); wave w's
+//            MFMA block j = 0 holds the gate rows, j = 1 the up rows of the same 32 f's,
+//            so a lane holds g and u of the same (row, f); epilogue h = silu(g) * u ->
+//            bf16 [rows][F].
+//   kDown  : K = F; wave w's blocks hold W_down rows 256 ny + 64 w + 32 j + (0..31);
+//            epilogue y -> bf16 [rows][d].
 // dense (sorted_pairs == nullptr): one expert, rows are tokens 0..T-1.
+// MB = 32-row MFMA blocks of the tile that hold rows (1..8); rows past the tile's end
+// repeat its last row (loads stay in bounds) and are never stored.
+struct GemmArgs {
+    const uint8_t* wa;
+    const uint16_t* sa;
+    const uint8_t* wb;
+    const uint16_t* sb;
+    const uint16_t* act;
+    int K, n_out, topk;
+    const int32_t* sorted_pairs;
+    uint16_t* out;
+};
+
+template <int FMT, int MODE, int MB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int m1, int ny,
+                                          uint8_t* smem) {
+    using L = StageLayout<FMT>;
+    constexpr int GB = L::GB;
+    constexpr int NG = MB + NI * L::DMA_B + NI;   // global loads per wave per k-step
+    static_assert(NG <= 16, "one load per slot of sub-step 0");
+    const int K = g.K;
+    const int nk = K / BK;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;                  // lane half: 32-code group h of the k-step
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // ---- activation rows this lane loads: row r = 32 i + 8 wave + lane / 8 of the tile
+    // into LDS chunk position lane % 8 of that row.  Position p of row r holds logical
+    // 16-byte chunk p ^ ((r / 2) % 8): the 16 rows an MFMA operand read touches per LDS
+    // cycle then cover all 64 banks.
+    const uint16_t* a_src[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int r = 32 * i + 8 * wave + (lane >> 3);
+        const int pos = min(m0 + r, m1 - 1);
+        size_t arow;
+        if (MODE == kGateUp && g.sorted_pairs)
+            arow = (size_t)(g.sorted_pairs[pos] / g.topk);
+        else
+            arow = (size_t)pos;
+        a_src[i] = g.act + arow * K + 8 * ((lane & 7) ^ ((r >> 1) & 7));
+    }
+    // ---- weight rows of this lane's two MFMA columns (column lane % 32 of block j)
+    const uint8_t* b_src[NI];
+    const uint16_t* s_src[NI];
+    {
+        const size_t row_bytes = (size_t)K / 32 * GB;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            size_t grow;
+            const uint8_t* wm;
+            const uint16_t* sm;
+            if (MODE == kGateUp) {
+                grow = (size_t)e * g.n_out + ny * (BN / 2) + 32 * wave + (lane & 31);
+                wm = j == 0 ? g.wa : g.wb;
+                sm = j == 0 ? g.sa : g.sb;
+            } else {
+                grow = (size_t)e * g.n_out + ny * BN + TN * wave + 32 * j + (lane & 31);
+                wm = g.wa;
+                sm = g.sa;
+            }
+            b_src[j] = wm + grow * row_bytes + h * GB;
+            s_src[j] = sm + grow * (K / 32) + h;
+        }
+    }
+
+    f32x16_t acc[MB][NI];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // stage byte offsets (relative to smem / absolute LDS addresses)
+    const uint32_t a_rd = (uint32_t)(lane & 31) * 128;   // + 4096 i + swizzled chunk
+    const uint32_t own_b = (uint32_t)(wave * NI) * L::B_WJ + lane * 16;
+    const uint32_t own_s = (uint32_t)(wave * NI) * L::S_WJ + lane * 4;
+
+    // load number q (0..NG-1) of k-step `step` (clamped to the last step) into stage st
+    auto issue = [&](int q, int step, int st) __attribute__((always_inline)) {
+        const int kk = min(step, nk - 1);
+        const uint32_t base = lds0 + st * L::BYTES;
+        if (q < MB) {
+            dma16(a_src[q] + kk * BK, base + (32 * q + 8 * wave) * 128);
+        } else if (q < MB + NI * L::DMA_B) {
+            const int j = (q - MB) / L::DMA_B, part = (q - MB) % L::DMA_B;
+            const uint8_t* src = b_src[j] + (size_t)kk * 2 * GB;
+            const uint32_t dst = base + L::A + (wave * NI + j) * L::B_WJ;
+            if (L::DMA_B == 1)
+                dma16(src, dst);
+            else
+                dma12(src + 12 * part, dst + 1024 * part);
+        } else {
+            const int j = q - MB - NI * L::DMA_B;
+            dma2(s_src[j] + kk * 2, base + L::A + L::B + (wave * NI + j) * L::S_WJ);
+        }
+    };
+    // this lane's group codes and scale of MFMA column block j, from stage st
+    auto read_codes = [&](int st, int j, GroupCodes<FMT>& c, float& s)
+        __attribute__((always_inline)) {
+        const uint8_t* base = smem + st * L::BYTES;
+        const uint8_t* p = base + L::A + own_b + j * L::B_WJ;
+        if constexpr (FMT == MOE_FMT_INT4_G32) {
+            c.a = *reinterpret_cast<const u32x4_t*>(p);
+        } else {
+            const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(p);          // bytes 0..11
+            const u32x4_t q1 = *reinterpret_cast<const u32x4_t*>(p + 1024);   // bytes 12..23
+            c.a = u32x4_t{q0.x, q0.y, q0.z, q1.x};
+            c.b = u32x2_t{q1.y, q1.z};
+        }
+        s = f16_to_f32(*reinterpret_cast<const uint16_t*>(base + L::A + L::B + own_s +
+                                                          j * L::S_WJ));
+    };
+    // A operand of MFMA row block i, sub-step ss: logical chunk 4 h + ss of row 32 i +
+    // lane % 32 (k = 32 h + 8 ss .. + 7 of the step)
+    auto read_a = [&](int st, int i, int ss) __attribute__((always_inline)) {
+        const uint32_t chunk = (uint32_t)((4 * h + ss) ^ ((lane >> 1) & 7));
+        return *reinterpret_cast<const bf16x8_t*>(smem + st * L::BYTES + a_rd + 4096 * i +
+                                                  (chunk << 4));
+    };
+
+    // codes/scales of the current k-step (codes, zc = -zero_point * scale) and of the next
+    GroupCodes<FMT> codes[NI], codes_n[NI];
+    float scale[NI], scale_n[NI];
+    bf16x8_t fa[2][MB], fb[2][NI];
+    uint32_t lo = 0, hi = 0;
+    float e0 = 0.0f, e1 = 0.0f;
+    constexpr float kZero = (FMT == MOE_FMT_INT4_G32) ? 8.0f : 32.0f;
+
+    // Half H of B operand pair b (codes 8 ss + 2b, +1) of column block j for sub-step ss,
+    // into fb[F][j]: half 0 converts the two codes to float, half 1 scales and packs them.
+    auto dequant_half = [&](const GroupCodes<FMT>* cd, const float* sc, int F, int j, int ss,
+                            int b, int half) __attribute__((always_inline)) {
+        if (half == 0) {
+            if (b == 0) chunk_codes<FMT>(cd[j], ss, lo, hi);
+            e0 = (float)((lo >> (8 * b)) & 0xffu);
+            e1 = (float)((hi >> (8 * b)) & 0xffu);
+        } else {
+            const float s = sc[j], zc = -kZero * s;
+            u32x4_t v = __builtin_bit_cast(u32x4_t, fb[F][j]);
+            v[b] = pack_bf16(__builtin_fmaf(e0, s, zc), __builtin_fmaf(e1, s, zc));
+            fb[F][j] = __builtin_bit_cast(bf16x8_t, v);
+        }
+    };
+    // The product is formed transposed, D^T = B^T A^T (weights as the first operand): the
+    // two operand layouts are mirror images, and the transposed result leaves each lane
+    // one row of the tile with runs of 4 adjacent output columns.
+    auto mfma = [&](int F, int t) __attribute__((always_inline)) {
+        const int i = t / NI, j = t % NI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[F][j], fa[F][i], acc[i][j],
+                                                            0, 0, 0);
+    };
+
+    // ---- prologue: steps 0 and 1 in flight, step 0's operands of sub-step 0 ready
+#pragma unroll
+    for (int q = 0; q < NG; ++q) issue(q, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NG; ++q) issue(q, 1, 1);
+    MOE_WAIT_VMCNT(NG);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NI; ++j) read_codes(0, j, codes[j], scale[j]);
+#pragma unroll
+    for (int i = 0; i < MB; ++i) fa[0][i] = read_a(0, i, 0);
+#pragma unroll
+    for (int p = 0; p < 8 * NI; ++p) dequant_half(codes, scale, 0, p / 8, 0, (p / 2) % 4, p % 2);
+
+    // ---- main loop.  One k-step is an explicit issue order of 4 x 16 slots.  A slot holds
+    // at most one MFMA and after it about four issue cycles of other work: a global load of
+    // step ks + 2, an A operand read, or half of one packed bf16 B pair (2-3 VALU ops) for
+    // the next sub-step.  A 32x32x16 MFMA leaves its wave free to issue for about 16 of its
+    // 32 cycles, so this keeps the matrix pipe fed; sched_barrier keeps the compiler from
+    // regrouping the slots.
+    int st = 0;                                   // stage of step ks
+    for (int ks = 0; ks < nk; ++ks) {
+        const int st1 = st == kStages - 1 ? 0 : st + 1;
+        const int st2 = st1 == kStages - 1 ? 0 : st1 + 1;
+#pragma unroll
+        for (int u = 0; u < 48; ++u) {            // sub-steps 0..2
+            const int ss = u / 16, t = u % 16, F = ss & 1;
+            if (t < MB * NI) mfma(F, t);
+            if (ss == 0 && t < NG) issue(t, ks + 2, st2);
+            if (t % 2 == 0 && t / 2 < MB) fa[F ^ 1][t / 2] = read_a(st, t / 2, ss + 1);
+            dequant_half(codes, scale, F ^ 1, t / 8, ss + 1, (t / 2) % 4, t % 2);
+            // this wave's loads of step ks + 1 are done; its codes are private to the wave
+            if (ss == 2 && t == 0) MOE_WAIT_VMCNT(NG);
+            if (ss == 2 && (t == 1 || t == 3)) read_codes(st1, t / 2, codes_n[t / 2], scale_n[t / 2]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // every wave's loads of step ks + 1 have landed once all pass the barrier; stage st
+        // is not read after it
+        MOE_WAIT_VMCNT_LDS(NG);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {            // sub-step 3, and step ks + 1's sub-step 0
+            if (t < MB * NI) mfma(1, t);
+            if (t % 2 == 0 && t / 2 < MB) fa[0][t / 2] = read_a(st1, t / 2, 0);
+            dequant_half(codes_n, scale_n, 0, t / 8, 0, (t / 2) % 4, t % 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            codes[j] = codes_n[j];
+            scale[j] = scale_n[j];
+        }
+        st = st1;
+    }
+    // the last two steps' loads (re-reads of the last step) are still in flight; after the
+    // barrier no wave reads the stages and LDS holds the output tile
+    MOE_WAIT_VMCNT(0);
+    __syncthreads();
+
+    // ---- epilogue: accumulator r of lane l in block (i, j) is tile row 32 i + l % 32 and
+    // column 32 j + 8 (r / 4) + 4 (l / 32) + r % 4 of the wave's 64 columns.  The bf16
+    // tile goes through LDS (row pitch padded against bank conflicts) so that global
+    // stores are whole 16-byte chunks of contiguous rows.
+    constexpr int OCOLS = MODE == kGateUp ? BN / 2 : BN;   // output columns of the block
+    constexpr int OP = OCOLS * 2 + 16;                      // LDS row pitch in bytes
+    constexpr int RP = MODE == kGateUp ? BM : BM / 2;       // rows per pass
+    static_assert(RP * OP <= kStages * L::BYTES, "output tile fits in LDS");
+    const int col0 = ny * OCOLS;
+#pragma unroll
+    for (int pass = 0; pass < BM / RP; ++pass) {
+        if (32 * MB <= pass * RP) break;                    // no rows in this pass
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            if ((32 * i) / RP != pass) continue;
+            uint8_t* lrow = smem + (32 * i - pass * RP + (lane & 31)) * OP;
+            if constexpr (MODE == kGateUp) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    float hv[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const float gt = acc[i][0][4 * rb + c], u = acc[i][1][4 * rb + c];
+                        // silu(g) * u = g * u / (1 + 2^(-g log2 e))
+                        const float den =
+                            1.0f + __builtin_amdgcn_exp2f(-gt * 1.4426950408889634f);
+                        hv[c] = gt * u * __builtin_amdgcn_rcpf(den);
+                    }
+                    *reinterpret_cast<u32x2_t*>(lrow + 2 * (32 * wave + 8 * rb + 4 * h)) =
+                        u32x2_t{pack_bf16(hv[0], hv[1]), pack_bf16(hv[2], hv[3])};
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+                        *reinterpret_cast<u32x2_t*>(lrow +
+                                                    2 * (TN * wave + 32 * j + 8 * rb + 4 * h)) =
+                            u32x2_t{pack_bf16(acc[i][j][4 * rb], acc[i][j][4 * rb + 1]),
+                                    pack_bf16(acc[i][j][4 * rb + 2], acc[i][j][4 * rb + 3])};
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = OCOLS / 8;                      // 16-byte chunks per row
+#pragma unroll
+        for (int n = 0; n < RP * CPR / NT; ++n) {
+            const int qd = tid + NT * n, r = qd / CPR, c = qd % CPR;
+            const int grow = m0 + pass * RP + r;
+            if (r < 32 * MB - pass * RP && grow < m1)
+                *reinterpret_cast<u32x4_t*>(g.out + (size_t)grow * g.n_out + col0 + 8 * c) =
+                    *reinterpret_cast<const u32x4_t*>(smem + r * OP + 16 * c);
+        }
+        if (pass + 1 < BM / RP) __syncthreads();
+    }
+}
+
 template <int FMT, int MODE>
-__global__ void __launch_bounds__(256) grouped_gemm_kernel(
+__global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(
     const uint8_t* __restrict__ wa, const uint16_t* __restrict__ sa,
     const uint8_t* __restrict__ wb, const uint16_t* __restrict__ sb,
     const uint16_t* __restrict__ act, int K, int n_out, int topk,
     const int32_t* __restrict__ sorted_pairs, const int4* __restrict__ tiles,
-    const int* __restrict__ tile_count, int T_dense, uint16_t* __restrict__ out) {
-    constexpr int GB = (FMT == MOE_FMT_INT4_G32) ? 16 : 24;   // bytes per 32-code group
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDP];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDP];
-
-    // ---- which tile
+    const int* __restrict__ tile_count, int T_dense, int n_ny, uint16_t* __restrict__ out) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // XCD-aware order: workgroups go round-robin to the 8 XCDs, so XCD x runs blocks
+    // x, x + 8, x + 16, ...; give each XCD whole row tiles, all n_ny column blocks of a tile
+    // back to back, so the tile's activation rows are fetched into that XCD's L2 once.
+    const int xcd = blockIdx.x % kXcds, q = blockIdx.x / kXcds;
+    const int tile = (q / n_ny) * kXcds + xcd, ny = q % n_ny;
     int e, m0, m1;
     if (tiles) {
-        if ((int)blockIdx.x >= *tile_count) return;
-        const int4 t = tiles[blockIdx.x];
+        if (tile >= *tile_count) return;
+        const int4 t = tiles[tile];
         e = t.x; m0 = t.y; m1 = t.z;
     } else {
         e = 0;
-        m0 = blockIdx.x * BM;
+        m0 = tile * BM;
         if (m0 >= T_dense) return;
         m1 = T_dense;
     }
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // ---- A rows this thread stages: rows r = tid/8 + 32 i, 16-byte column tid%8
-    const int a_col = (tid & 7) * 8;
-    const uint16_t* a_src[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = (tid >> 3) + 32 * i;
-        const int pos = m0 + r;
-        if (pos < m1) {
-            size_t arow;
-            if (MODE == kGateUp && sorted_pairs)
-                arow = (size_t)(sorted_pairs[pos] / topk);
-            else
-                arow = (size_t)pos;
-            a_src[i] = act + arow * K + a_col;
-        } else {
-            a_src[i] = nullptr;
-        }
-    }
-    // ---- B row this thread dequantises: LDS row nn = tid/2, group half = tid%2
-    const int nn = tid >> 1, bhalf = tid & 1;
-    const uint8_t* b_w;
-    const uint16_t* b_s;
-    {
-        const size_t rows_per_expert = (MODE == kGateUp) ? (size_t)(n_out) : (size_t)n_out;
-        int mat = 0, r;
-        if (MODE == kGateUp) {
-            const int f0 = blockIdx.y * (BN / 2);
-            const int blk = nn >> 5;                  // 0..3
-            mat = blk & 1;                            // 0 gate, 1 up
-            r = f0 + 32 * (blk >> 1) + (nn & 31);
-        } else {
-            r = blockIdx.y * BN + nn;
-        }
-        const size_t grow = (size_t)e * rows_per_expert + r;
-        const size_t row_bytes = (size_t)K / 32 * GB;
-        b_w = ((mat == 0) ? wa : wb) + grow * row_bytes + (size_t)bhalf * GB;
-        b_s = ((mat == 0) ? sa : sb) + grow * (K / 32) + bhalf;
-    }
-
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    uint4 a_reg[4];
-    GroupLoad<FMT> b_reg;
-    float b_scale;
-
-    auto load_global = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a_reg[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0)
-                                : make_uint4(0u, 0u, 0u, 0u);
-        load_group<FMT>(b_w + (size_t)(k0 / 32) * GB, b_reg);
-        b_scale = f16_to_f32(b_s[k0 / 32]);
-    };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(&As[buf][(tid >> 3) + 32 * i][a_col]) = a_reg[i];
-        uint32_t deq[16];
-        dequant_group<FMT>(b_reg, b_scale, deq);
-        uint4* dst = reinterpret_cast<uint4*>(&Bs[buf][nn][32 * bhalf]);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            dst[v] = make_uint4(deq[4 * v], deq[4 * v + 1], deq[4 * v + 2], deq[4 * v + 3]);
-    };
-
-    const int nk = K / BK;
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nk) load_global((ks + 1) * BK);
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8_t a[4], b[4];
-            const int kc = kk + 8 * (lane >> 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8_t*>(
-                    &As[buf][wm * 64 + i * 16 + (lane & 15)][kc]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const bf16x8_t*>(
-                    &Bs[buf][wn * 64 + j * 16 + (lane & 15)][kc]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j],
-                                                                        0, 0, 0);
-        }
-        if (ks + 1 < nk) store_lds(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue
-    const int col = lane & 15, rq = 4 * (lane >> 4);
-    if constexpr (MODE == kGateUp) {
-        const int F = n_out;
-        const int fbase = blockIdx.y * (BN / 2) + wn * 32;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm * 64 + i * 16 + rq + r;
-                    if (row < m1) {
-                        const float g = acc[i][j][r], u = acc[i][j + 2][r];
-                        const float h = g / (1.0f + expf(-g)) * u;
-                        out[(size_t)row * F + fbase + j * 16 + col] = (uint16_t)f32_to_bf16(h);
-                    }
-                }
-    } else {
-        const int nbase = blockIdx.y * BN + wn * 64;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + wm * 64 + i * 16 + rq + r;
-                    if (row < m1)
-                        out[(size_t)row * n_out + nbase + j * 16 + col] =
-                            (uint16_t)f32_to_bf16(acc[i][j][r]);
-                }
+    const GemmArgs g{wa, sa, wb, sb, act, K, n_out, topk, sorted_pairs, out};
+    const int mb = min(MI, (m1 - m0 + 31) / 32);   // >= 1, block-uniform
+    static_assert(MI == 8, "row-block dispatch below assumes 8 blocks per tile");
+    switch (mb) {
+        case 8: gemm_tile<FMT, MODE, 8>(g, e, m0, m1, ny, smem); break;
+        case 7: gemm_tile<FMT, MODE, 7>(g, e, m0, m1, ny, smem); break;
+        case 6: gemm_tile<FMT, MODE, 6>(g, e, m0, m1, ny, smem); break;
+        case 5: gemm_tile<FMT, MODE, 5>(g, e, m0, m1, ny, smem); break;
+        case 4: gemm_tile<FMT, MODE, 4>(g, e, m0, m1, ny, smem); break;
+        case 3: gemm_tile<FMT, MODE, 3>(g, e, m0, m1, ny, smem); break;
+        case 2: gemm_tile<FMT, MODE, 2>(g, e, m0, m1, ny, smem); break;
+        default: gemm_tile<FMT, MODE, 1>(g, e, m0, m1, ny, smem); break;
     }
 }
 
@@ -337,10 +518,31 @@ hipError_t launch_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
     } else {
         gx = (T + BM - 1) / BM;
     }
-    grouped_gemm_kernel<FMT, kGateUp><<<dim3(gx, F / (BN / 2)), 256, 0, s>>>(
-        ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, d, F, k, sorted_pairs, tiles, count, T, h);
-    grouped_gemm_kernel<FMT, kDown><<<dim3(gx, d / BN), 256, 0, s>>>(
-        ex.w_down, ex.s_down, nullptr, nullptr, h, F, d, k, sorted_pairs, tiles, count, T, y);
+    // opt in to more than 64 KiB of LDS, once per device
+    constexpr int kMaxDev = 64;
+    static bool attr_set[kMaxDev] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev >= kMaxDev || !attr_set[dev]) {
+        err = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&grouped_gemm_kernel<FMT, kGateUp>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds<FMT>);
+        if (err != hipSuccess) return err;
+        err = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&grouped_gemm_kernel<FMT, kDown>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds<FMT>);
+        if (err != hipSuccess) return err;
+        if (dev < kMaxDev) attr_set[dev] = true;
+    }
+    const int gx8 = (gx + kXcds - 1) / kXcds * kXcds;   // whole tiles per XCD
+    const int ny_gu = F / (BN / 2), ny_dn = d / BN;
+    grouped_gemm_kernel<FMT, kGateUp><<<gx8 * ny_gu, NT, kGemmLds<FMT>, s>>>(
+        ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, d, F, k, sorted_pairs, tiles, count, T, ny_gu,
+        h);
+    grouped_gemm_kernel<FMT, kDown><<<gx8 * ny_dn, NT, kGemmLds<FMT>, s>>>(
+        ex.w_down, ex.s_down, nullptr, nullptr, h, F, d, k, sorted_pairs, tiles, count, T, ny_dn,
+        y);
     return hipGetLastError();
 }
 
