@@ -3,15 +3,17 @@
 Headline (one JSON line on stdout): decode tokens/s of one MoE layer at the pages'
 routing shape (d_model 2048, 512 routed experts, top-10 + 1 shared, expert FFN width
 512, int4 group-32 weights, one token per call).  A step is the whole hot path for one
-token: router + top-k, shared expert, grouping, routed experts, combine.  Inputs are
-resident in HBM before timing; the step sequence is captured in a HIP graph and replayed.
+token: router + top-k, shared expert, routed experts, combine -- moe_layer_decode, which
+is checked bit for bit against the four-call composition before timing (whose time per
+step is reported too).  Inputs are resident in HBM before timing; the step sequence is
+captured in a HIP graph and replayed.
 To keep the 256 MB Infinity Cache from serving the weights, steps rotate over
 ``--copies`` distinct copies of the layer (a different token per copy).
 
 Also reported in the same line:
-  roofline      the routed expert FFN call of a decode step (the HBM-bound hot spot):
-                algorithmic bytes (selected experts' packed weights + scales, activations
-                in, pair rows out) / its event-timed average duration vs 8 TB/s
+  roofline      the expert kernel of a decode step (moe_experts_decode, one launch):
+                algorithmic bytes (10 routed + 1 shared expert's packed weights and scales,
+                activations in and out) / its event-timed average duration vs 8 TB/s
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
   prefill       8192-token prefill through one layer (Zipf routing): tokens/s and the
                 grouped GEMM's MFMA utilisation (useful flops / time / 2.5 PFLOP/s)
@@ -112,55 +114,56 @@ def main():
 
     def step_all():
         for i in range(L):
+            layers[i].decode(xs[i])
+
+    def step_all_calls():
+        for i in range(L):
             layers[i].forward(xs[i])
 
-    # eager pass: fills every layer's buffers and checks for device errors
+    # eager passes: fill every layer's buffers, check for device errors, and check that the
+    # two-launch layer equals the four-call composition bit for bit
+    step_all_calls()
+    ref = [lay.out[:1].clone() for lay in layers]
     step_all()
     torch.cuda.synchronize()
     moe.moe_check_device_error()
+    for i in range(L):
+        if not torch.equal(layers[i].out[:1].view(torch.int16), ref[i].view(torch.int16)):
+            raise SystemExit("bench.py: moe_layer_decode differs from the four calls")
 
     reps = max(1, -(-args.steps // L))
     warm = max(1, -(-args.warmup // L))
     steps = reps * L
-    if args.eager:
-        for _ in range(warm):
-            step_all()
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(reps):
-            step_all()
-        t1.record()
-        torch.cuda.synchronize()
-        ms_replay = t0.elapsed_time(t1) / reps
-    else:
-        ms_replay, _ = time_graph(step_all, reps, warm)
-    ms_step = ms_replay / L
+
+    def timed(fn, n_reps):
+        if args.eager:
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(n_reps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / n_reps
+        return time_graph(fn, n_reps, warm)[0]
+
+    ms_step = timed(step_all, reps) / L
     tok_s = 1000.0 / ms_step
+    ms_step_calls = timed(step_all_calls, max(4, reps // 2)) / L
 
-    # ---- roofline: the routed expert FFN call (selected experts' weights streamed once)
+    # ---- roofline: the expert kernel of the decode step (moe_experts_decode: the routed
+    # experts and the shared one streamed once, SwiGLU, combine) -- one launch per call
     E_b = expert_bytes(base.routed)
-    alg_bytes_ffn = w.k * E_b + w.d * 2 + w.k * w.d * 2
+    alg_bytes_exp = (w.k + 1) * E_b + 2 * w.d * 2
 
-    def ffn_all():
+    def experts_all():
         for i in range(L):
-            lay = layers[i]
-            moe.moe_expert_ffn(lay.routed, xs[i], 1, w.k, lay.ids, lay.offsets,
-                               lay.sorted_pairs, lay.y_pairs, lay.ws_ffn)
+            layers[i].experts_decode(xs[i])
 
-    ffn_reps = max(4, reps // 2)
-    ms_ffn = time_graph(ffn_all, ffn_reps)[0] / L if not args.eager else None
-    if ms_ffn is None:
-        ffn_all()
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(ffn_reps):
-            ffn_all()
-        t1.record()
-        torch.cuda.synchronize()
-        ms_ffn = t0.elapsed_time(t1) / (ffn_reps * L)
-    achieved = alg_bytes_ffn / (ms_ffn * 1e-3) / 1e9
+    ms_exp = timed(experts_all, max(4, reps // 2)) / L
+    achieved = alg_bytes_exp / (ms_exp * 1e-3) / 1e9
     alg_bytes_step = (base.router.w.numel() * base.router.w.element_size()
                       + (w.k + 1) * E_b + 2 * w.d * 2)
 
@@ -180,13 +183,17 @@ def main():
         "config": {"workload": "decode_d2048_e512_top10_t1", "d_model": w.d, "experts": w.E,
                    "top_k": w.k, "shared_experts": 1, "d_ff": w.F, "tokens_per_step": 1,
                    "layer_copies_rotated": L, "graph": not args.eager,
+                   "entry_point": "moe_layer_decode",
                    "step_weight_stream_GBps": round(alg_bytes_step / (ms_step * 1e-3) / 1e9, 1),
-                   "alg_bytes_per_step": alg_bytes_step},
-        "roofline": {"bound": "hbm", "kernel": "routed expert FFN call (gate/up+SwiGLU, down)",
+                   "alg_bytes_per_step": alg_bytes_step,
+                   "ms_per_step_four_calls": round(ms_step_calls, 5)},
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_ffn_kernel (moe_experts_decode: 10 routed + 1 shared "
+                               "expert FFN and combine, one launch)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": alg_bytes_ffn,
-                     "avg_launch_us": round(ms_ffn * 1e3, 3)},
+                     "alg_bytes_per_launch": alg_bytes_exp,
+                     "avg_launch_us": round(ms_exp * 1e3, 3)},
     }
 
     # ---- prefill: 8192 tokens, Zipf routing, one layer

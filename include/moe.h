@@ -12,6 +12,8 @@
  *
  *     moe_route -> moe_permute -> moe_expert_ffn (routed; and shared, dense) -> moe_combine
  *
+ * and, for a few tokens, moe_layer_decode runs that composition in two launches.
+ *
  * Conventions for every entry point
  *   - Pointers to tensors are DEVICE pointers (hipMalloc'd or torch-owned memory); the
  *     descriptor structs themselves are read on the host during the call.  The caller
@@ -63,7 +65,13 @@ enum {
 enum { MOE_FMT_FP32 = 0, MOE_FMT_INT8_ROW = 1, MOE_FMT_INT4_G32 = 2, MOE_FMT_INT6_G32 = 3 };
 
 /* Operation ids for moe_workspace_size. */
-enum { MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_EXPERT_FFN = 2 };
+enum {
+    MOE_OP_ROUTE = 0,
+    MOE_OP_PERMUTE = 1,
+    MOE_OP_EXPERT_FFN = 2,
+    MOE_OP_LAYER_DECODE = 3,
+    MOE_OP_EXPERTS_DECODE = 4
+};
 
 /* Router: logits = W x (+ bias).  fmt FP32: w = fp32 [E][d], scale unused.
  * fmt INT8_ROW: w = int8 [E][d], scale = fp16 [E].  bias = fp32 [E] or NULL.
@@ -171,6 +179,43 @@ moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, i
 moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const float* weights,
                        const uint16_t* y_shared, const uint16_t* residual, int32_t T,
                        int32_t k, int32_t d, uint16_t* out, void* stream);
+
+/*
+ * moe_layer_decode -- the whole layer for a few tokens (decode, MTP verification): the same
+ * result, bit for bit, as
+ *     moe_route -> moe_permute -> moe_expert_ffn(routed) -> moe_expert_ffn(shared, dense)
+ *     -> moe_combine(residual)
+ * on the same inputs, in two launches: the route kernel, then one kernel that runs the
+ * routed and shared expert FFNs and the combine (blocks hand h and y rows to each other
+ * through the workspace; no host round trip).  Each token is sent to k experts and to the
+ * shared one, as the layer the pages describe [Strata 与 Qwen3.8-Flash-Next (telli.sh),
+ * section 稀疏架构创造了机会].
+ *   routed   the routed expert set; n_experts and d_model must match the router's
+ *   shared   the shared expert (n_experts 1, same format, d_model and d_ff) or NULL
+ *   x        bf16 [T][d]; ids int32 [T][k] and weights fp32 [T][k] are outputs as in
+ *            moe_route; residual bf16 [T][d] or NULL; out bf16 [T][d] (may alias residual)
+ *   ws       zero-initialised workspace of moe_workspace_size(MOE_OP_LAYER_DECODE, T, k,
+ *            E, d, d_ff) bytes; its counters are left zero by every call
+ * Needs T*k <= 64 and a (d_model, d_ff) pair with a GEMV kernel (see moe_expert_ffn);
+ * otherwise MOE_ERR_UNSUPPORTED and the caller uses the four calls.  A bounded wait that
+ * times out raises the device error flag (moe_check_device_error).
+ */
+moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
+                            int32_t* ids, float* weights, const uint16_t* residual,
+                            uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_experts_decode -- the second launch of moe_layer_decode on its own: given ids and
+ * weights from moe_route, the routed and shared expert FFNs and the combine in one kernel,
+ * bit for bit equal to moe_permute -> moe_expert_ffn x 2 -> moe_combine.  Arguments as in
+ * moe_layer_decode; ws: zero-initialised, moe_workspace_size(MOE_OP_EXPERTS_DECODE, T, k,
+ * E, d, d_ff) bytes.  ids must lie in [0, n_experts) (moe_route's always do).
+ */
+moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shared,
+                              const uint16_t* x, int32_t T, int32_t k, const int32_t* ids,
+                              const float* weights, const uint16_t* residual, uint16_t* out,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes an operation needs for these sizes (0 = none).  Pure host function. */
 size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d,

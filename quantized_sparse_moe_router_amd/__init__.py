@@ -1,18 +1,20 @@
 """MI355X-native quantized routed-expert MoE layer.
 
 The compute path is the C ABI of ``libmoe_mi355x.so`` (include/moe.h): moe_route,
-moe_permute, moe_expert_ffn and moe_combine, all HIP kernels for gfx950.  This package
-is its Python binding (``_lib``) plus ``MoeLayer``, which owns the buffers of one layer
-call and enqueues the four calls on the current stream.  Torch only provides device
-memory and streams.
+moe_permute, moe_expert_ffn and moe_combine, and moe_layer_decode (the same composition
+in two launches for a few tokens), all HIP kernels for gfx950.  This package is its
+Python binding (``_lib``) plus ``MoeLayer``, which owns the buffers of one layer call and
+enqueues the calls on the current stream.  Torch only provides device memory and streams.
 """
 import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
     MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32,
-    MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MoeError,
-    moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_workspace_size,
+    MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE,
+    MOE_OP_EXPERTS_DECODE, MoeError,
+    moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_layer_decode, moe_experts_decode,
+    moe_workspace_size,
     moe_check_device_error, moe_status_string, moe_last_error, moe_version,
     router_desc, experts_desc,
 )
@@ -43,8 +45,12 @@ class MoeLayer:
     stream and moe_expert_ffn(shared, dense) on a side stream forked from it, joins, then
     moe_combine; it returns ``out`` (bf16 [T][d]).  For small calls (T*k <= 64) the routed
     experts do not read the grouping, so moe_permute runs on a second side stream beside
-    them.  Graph capture records the forks and joins.  Intermediate results stay readable as attributes
-    (logits, ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared).
+    them.  Graph capture records the forks and joins.  Intermediate results stay readable
+    as attributes (logits, ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared).
+
+    decode(x) computes the same output bit for bit with moe_layer_decode (two launches, no
+    side streams) when T*k <= 64 and the shapes allow it (``can_decode``); it fills ids,
+    weights and out only.
     """
 
     def __init__(self, router, routed, shared, k, T_max, device="cuda"):
@@ -77,6 +83,15 @@ class MoeLayer:
         self.ws_perm = torch.zeros((max(ws_perm, 256),), dtype=u8, device=dev)
         self.ws_ffn = torch.zeros((max(ws_ffn, 1024),), dtype=u8, device=dev)
         self.ws_shared = torch.zeros((max(ws_sh, 1024),), dtype=u8, device=dev)
+        self.can_decode = (P <= 64 and (shared is None or (shared.fmt == routed.fmt and
+                                                          shared.F == F)))
+        ws_dec = moe_workspace_size(MOE_OP_LAYER_DECODE, T, k, E, d, F) if self.can_decode \
+            else 0
+        self.can_decode = self.can_decode and ws_dec > 0
+        self.ws_decode = torch.zeros((max(ws_dec, 256),), dtype=u8, device=dev)
+        ws_xd = moe_workspace_size(MOE_OP_EXPERTS_DECODE, T, k, E, d, F) if self.can_decode \
+            else 0
+        self.ws_experts_decode = torch.zeros((max(ws_xd, 256),), dtype=u8, device=dev)
         self.side = torch.cuda.Stream(device=dev)     # default priority
         self.side2 = torch.cuda.Stream(device=dev)
 
@@ -111,6 +126,23 @@ class MoeLayer:
             main.wait_stream(self.side)
         moe_combine(self.y_pairs, self.pair_pos, self.weights,
                     self.y_shared if self.shared is not None else None, residual, T, k, d, out)
+        return out
+
+    def decode(self, x, residual=None, out=None):
+        T = x.shape[0]
+        if T > self.T_max:
+            raise ValueError("T = %d exceeds T_max = %d" % (T, self.T_max))
+        out = self.out[:T] if out is None else out
+        moe_layer_decode(self.router, self.routed, self.shared, x, T, self.k, self.ids,
+                         self.weights, residual, out, self.ws_decode)
+        return out
+
+    def experts_decode(self, x, residual=None, out=None):
+        """The expert side of decode() on its own, from the current ids and weights."""
+        T = x.shape[0]
+        out = self.out[:T] if out is None else out
+        moe_experts_decode(self.routed, self.shared, x, T, self.k, self.ids, self.weights,
+                           residual, out, self.ws_experts_decode)
         return out
 
     __call__ = forward

@@ -17,10 +17,11 @@ MOE_OK = 0
 MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE = \
     -1, -2, -3, -4, -5
 MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32 = 0, 1, 2, 3
-MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN = 0, 1, 2
+MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE, MOE_OP_EXPERTS_DECODE = \
+    0, 1, 2, 3, 4
 
 EXPORTED = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-            "moe_workspace_size", "moe_check_device_error", "moe_status_string",
+            "moe_layer_decode", "moe_experts_decode", "moe_workspace_size", "moe_check_device_error", "moe_status_string",
             "moe_last_error", "moe_version")
 
 
@@ -61,6 +62,8 @@ def lib():
             "moe_permute": [P, I32, I32, I32, P, P, P, P, SZ, P],
             "moe_expert_ffn": [P, P, I32, I32, P, P, P, P, P, SZ, P],
             "moe_combine": [P, P, P, P, P, I32, I32, I32, P, P],
+            "moe_layer_decode": [P, P, P, P, I32, I32, P, P, P, P, P, SZ, P],
+            "moe_experts_decode": [P, P, P, I32, I32, P, P, P, P, P, SZ, P],
             "moe_workspace_size": [I32, I32, I32, I32, I32, I32],
             "moe_check_device_error": [P],
             "moe_status_string": [I32],
@@ -145,6 +148,27 @@ def moe_combine(y_pairs, pair_pos, weights, y_shared, residual, T, k, d, out, st
     st = lib().moe_combine(_ptr(y_pairs), _ptr(pair_pos), _ptr(weights), _ptr(y_shared),
                            _ptr(residual), T, k, d, _ptr(out), _stream(stream))
     _check(st, "moe_combine")
+
+
+def moe_layer_decode(router, routed, shared, x, T, k, ids, weights, residual, out, ws,
+                     stream=None):
+    """ws: a zero-initialised workspace of moe_workspace_size(MOE_OP_LAYER_DECODE, ...)."""
+    st = lib().moe_layer_decode(ctypes.byref(router), ctypes.byref(routed),
+                                ctypes.byref(shared) if shared is not None else None,
+                                _ptr(x), T, k, _ptr(ids), _ptr(weights), _ptr(residual),
+                                _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream))
+    _check(st, "moe_layer_decode")
+
+
+def moe_experts_decode(routed, shared, x, T, k, ids, weights, residual, out, ws, stream=None):
+    """ws: a zero-initialised workspace of moe_workspace_size(MOE_OP_EXPERTS_DECODE, ...)."""
+    st = lib().moe_experts_decode(ctypes.byref(routed),
+                                  ctypes.byref(shared) if shared is not None else None,
+                                  _ptr(x), T, k, _ptr(ids), _ptr(weights), _ptr(residual),
+                                  _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _check(st, "moe_experts_decode")
 
 
 def moe_check_device_error(stream=None):

@@ -46,6 +46,7 @@ bool supported_router_dim(int fmt, int d) {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxK = 64;
 constexpr int64_t kGemvMaxRows = 64;   // pair rows up to which the GEMV path runs
+constexpr int64_t kDecodeMaxPairs = 64; // pairs up to which moe_layer_decode runs
 
 // route workspace: [counter][logits when the caller passes none]
 size_t route_ws(int64_t T, int E, bool need_logits) {
@@ -58,6 +59,54 @@ size_t ffn_ws(int64_t rows, int E, int F) {
     const size_t gemv = round_up((size_t)rows * (size_t)F * 2);
     const size_t mfma = moe::ffn_mfma_ws_bytes(rows, E, F);
     return gemv > mfma ? gemv : mfma;
+}
+
+// one-launch decode workspace: [route workspace][decode rows and counters]
+size_t decode_ws(int T, int k, int E, int d, int F) {
+    return round_up(route_ws(T, E, true)) + moe::decode_ws_layout(T, k, d, F).bytes;
+}
+
+// Router descriptor checks shared by moe_route and moe_layer_decode.
+moe_status check_router(const moe_router* r, const char* who) {
+    if (!r) return fail(MOE_ERR_INVALID_ARG, "%s: router descriptor is NULL", who);
+    if (r->fmt != MOE_FMT_FP32 && r->fmt != MOE_FMT_INT8_ROW)
+        return fail(MOE_ERR_INVALID_ARG, "%s: router format %d is not FP32 or INT8_ROW", who,
+                    r->fmt);
+    if (r->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "%s: reserved field not 0", who);
+    const int E = r->n_experts, d = r->d_model;
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "%s: n_experts %d outside [1, %d]", who, E,
+                    kMaxExperts);
+    if (!supported_router_dim(r->fmt, d))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "%s: d_model %d unsupported (FP32: 256..4096 powers of two; "
+                    "INT8_ROW: 1024, 2048, 4096)", who, d);
+    if (!r->w || !aligned16(r->w))
+        return fail(MOE_ERR_INVALID_ARG, "%s: router weights NULL or not 16-byte aligned", who);
+    if (r->fmt == MOE_FMT_INT8_ROW && !r->scale)
+        return fail(MOE_ERR_INVALID_ARG, "%s: INT8_ROW router needs scales", who);
+    return MOE_OK;
+}
+
+// Expert-set descriptor checks shared by moe_expert_ffn and moe_layer_decode.
+moe_status check_experts(const moe_experts* ex, const char* who) {
+    if (!ex) return fail(MOE_ERR_INVALID_ARG, "%s: expert descriptor is NULL", who);
+    if (ex->fmt != MOE_FMT_INT4_G32 && ex->fmt != MOE_FMT_INT6_G32)
+        return fail(MOE_ERR_INVALID_ARG, "%s: format %d is not INT4_G32/INT6_G32", who,
+                    ex->fmt);
+    const int E = ex->n_experts, d = ex->d_model, F = ex->d_ff;
+    if (E < 1 || E > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "%s: n_experts %d", who, E);
+    if (!supported_ffn_dim(d) || d < 256 || !supported_ffn_dim(F))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "%s: d_model %d must be 256..4096 and d_ff %d 128..4096, "
+                    "powers of two", who, d, F);
+    if (!ex->w_gate || !ex->w_up || !ex->w_down || !ex->s_gate || !ex->s_up || !ex->s_down)
+        return fail(MOE_ERR_INVALID_ARG, "%s: a weight or scale pointer is NULL", who);
+    if (!aligned16(ex->w_gate) || !aligned16(ex->w_up) || !aligned16(ex->w_down) ||
+        !aligned16(ex->s_gate) || !aligned16(ex->s_up) || !aligned16(ex->s_down))
+        return fail(MOE_ERR_INVALID_ARG, "%s: weights or scales not 16-byte aligned", who);
+    return MOE_OK;
 }
 
 }  // namespace
@@ -88,6 +137,14 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
         case MOE_OP_ROUTE: return route_ws(T, E, true);
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes((int64_t)T * k, E);
         case MOE_OP_EXPERT_FFN: return d_ff > 0 ? ffn_ws((int64_t)T * k, E, d_ff) : 0;
+        case MOE_OP_LAYER_DECODE:
+            return (d > 0 && d_ff > 0 && moe::decode_fits(T, k, d_ff, false))
+                       ? decode_ws(T, k, E, d, d_ff)
+                       : 0;
+        case MOE_OP_EXPERTS_DECODE:
+            return (d > 0 && d_ff > 0 && moe::decode_fits(T, k, d_ff, false))
+                       ? moe::decode_ws_layout(T, k, d, d_ff).bytes
+                       : 0;
         default: return 0;
     }
 }
@@ -95,26 +152,12 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
 moe_status moe_route(const moe_router* r, const uint16_t* x, int32_t T, int32_t k,
                      int32_t* ids, float* weights, float* logits, void* ws, size_t ws_bytes,
                      void* stream) {
-    if (!r) return fail(MOE_ERR_INVALID_ARG, "moe_route: router descriptor is NULL");
-    if (r->fmt != MOE_FMT_FP32 && r->fmt != MOE_FMT_INT8_ROW)
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: router format %d is not FP32 or INT8_ROW",
-                    r->fmt);
-    if (r->reserved != 0) return fail(MOE_ERR_INVALID_ARG, "moe_route: reserved field not 0");
-    const int E = r->n_experts, d = r->d_model;
-    if (E < 1 || E > kMaxExperts)
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: n_experts %d outside [1, %d]", E,
-                    kMaxExperts);
-    if (!supported_router_dim(r->fmt, d))
-        return fail(MOE_ERR_INVALID_ARG,
-                    "moe_route: d_model %d unsupported (FP32: 256..4096 powers of two; "
-                    "INT8_ROW: 1024, 2048, 4096)", d);
+    const moe_status st = check_router(r, "moe_route");
+    if (st != MOE_OK) return st;
+    const int E = r->n_experts;
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_route: T = %d < 0", T);
     if (k < 1 || k > E || k > kMaxK)
         return fail(MOE_ERR_INVALID_ARG, "moe_route: k = %d outside [1, min(E, %d)]", k, kMaxK);
-    if (!r->w || !aligned16(r->w))
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: router weights NULL or not 16-byte aligned");
-    if (r->fmt == MOE_FMT_INT8_ROW && !r->scale)
-        return fail(MOE_ERR_INVALID_ARG, "moe_route: INT8_ROW router needs scales");
     if (T == 0) return ok();
     if (!x || !aligned16(x))
         return fail(MOE_ERR_INVALID_ARG, "moe_route: x NULL or not 16-byte aligned");
@@ -158,23 +201,9 @@ moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, i
                           const int32_t* ids, const int32_t* offsets,
                           const int32_t* sorted_pairs, uint16_t* y, void* ws,
                           size_t ws_bytes, void* stream) {
-    if (!ex) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: expert descriptor is NULL");
-    if (ex->fmt != MOE_FMT_INT4_G32 && ex->fmt != MOE_FMT_INT6_G32)
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: format %d is not INT4_G32/INT6_G32",
-                    ex->fmt);
+    const moe_status st = check_experts(ex, "moe_expert_ffn");
+    if (st != MOE_OK) return st;
     const int E = ex->n_experts, d = ex->d_model, F = ex->d_ff;
-    if (E < 1 || E > kMaxExperts)
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: n_experts %d", E);
-    if (!supported_ffn_dim(d) || d < 256 || !supported_ffn_dim(F))
-        return fail(MOE_ERR_INVALID_ARG,
-                    "moe_expert_ffn: d_model %d must be 256..4096 and d_ff %d 128..4096, "
-                    "powers of two", d, F);
-    if (!ex->w_gate || !ex->w_up || !ex->w_down || !ex->s_gate || !ex->s_up || !ex->s_down)
-        return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: a weight or scale pointer is NULL");
-    if (!aligned16(ex->w_gate) || !aligned16(ex->w_up) || !aligned16(ex->w_down) ||
-        !aligned16(ex->s_gate) || !aligned16(ex->s_up) || !aligned16(ex->s_down))
-        return fail(MOE_ERR_INVALID_ARG,
-                    "moe_expert_ffn: weights or scales not 16-byte aligned");
     if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_expert_ffn: T = %d < 0", T);
     const bool grouped = ids || offsets || sorted_pairs;
     if (grouped && (!ids || !offsets || !sorted_pairs))
@@ -217,6 +246,87 @@ moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const f
     return hip_status(moe::launch_combine(y_pairs, pair_pos, weights, y_shared, residual, T, k,
                                           d, out, static_cast<hipStream_t>(stream)),
                       "moe_combine");
+}
+
+// Checks shared by moe_experts_decode and moe_layer_decode (routed, shared, T, k, rows).
+moe_status check_decode(const moe_experts* routed, const moe_experts* shared, int T, int k,
+                        const uint16_t* x, const uint16_t* residual, const uint16_t* out,
+                        const char* who) {
+    moe_status st = check_experts(routed, who);
+    if (st != MOE_OK) return st;
+    const int E = routed->n_experts, d = routed->d_model, F = routed->d_ff;
+    if (shared) {
+        st = check_experts(shared, who);
+        if (st != MOE_OK) return st;
+        if (shared->n_experts != 1)
+            return fail(MOE_ERR_INVALID_ARG, "%s: shared set must have 1 expert", who);
+        if (shared->fmt != routed->fmt || shared->d_model != d || shared->d_ff != F)
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "%s: the shared expert must have the routed experts' format and shape",
+                        who);
+    }
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", who, T);
+    if (k < 1 || k > E || k > kMaxK)
+        return fail(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, min(E, %d)]", who, k, kMaxK);
+    if (T == 0) return MOE_OK;
+    if ((int64_t)T * k > kDecodeMaxPairs || !moe::ffn_gemv_has_shape(d, F) ||
+        !moe::decode_fits(T, k, F, shared != nullptr))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: T*k = %d (at most %d; h rows of all slots within %d KiB) or shape "
+                    "(%d, %d) not supported; use the four calls", who, T * k,
+                    (int)kDecodeMaxPairs, (int)(moe::kDecodeMaxLds / 1024), d, F);
+    if (!x || !aligned16(x) || !out || !aligned16(out) || (residual && !aligned16(residual)))
+        return fail(MOE_ERR_INVALID_ARG, "%s: x/out NULL or rows not 16-byte aligned", who);
+    return MOE_OK;
+}
+
+moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shared,
+                              const uint16_t* x, int32_t T, int32_t k, const int32_t* ids,
+                              const float* weights, const uint16_t* residual, uint16_t* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+    const moe_status st = check_decode(routed, shared, T, k, x, residual, out,
+                                       "moe_experts_decode");
+    if (st != MOE_OK) return st;
+    if (T == 0) return ok();
+    if (!ids || !weights)
+        return fail(MOE_ERR_INVALID_ARG, "moe_experts_decode: ids/weights NULL");
+    const size_t need = moe::decode_ws_layout(T, k, routed->d_model, routed->d_ff).bytes;
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(MOE_ERR_WORKSPACE, "moe_experts_decode: needs %zu workspace bytes (got %zu)",
+                    need, ws_bytes);
+    return hip_status(moe::launch_decode_ffn(*routed, shared, x, T, k, ids, weights, residual,
+                                             out, ws, static_cast<hipStream_t>(stream)),
+                      "moe_experts_decode");
+}
+
+moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
+                            int32_t* ids, float* weights, const uint16_t* residual,
+                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    moe_status st = check_router(r, "moe_layer_decode");
+    if (st != MOE_OK) return st;
+    st = check_decode(routed, shared, T, k, x, residual, out, "moe_layer_decode");
+    if (st != MOE_OK) return st;
+    const int E = r->n_experts, d = r->d_model, F = routed->d_ff;
+    if (routed->n_experts != E || routed->d_model != d)
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_layer_decode: router (E %d, d %d) and experts (E %d, d %d) differ", E,
+                    d, routed->n_experts, routed->d_model);
+    if (T == 0) return ok();
+    if (!ids || !weights) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: ids/weights NULL");
+    const size_t need = decode_ws(T, k, E, d, F);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(MOE_ERR_WORKSPACE, "moe_layer_decode: needs %zu workspace bytes (got %zu)",
+                    need, ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    unsigned* counter = reinterpret_cast<unsigned*>(base);
+    float* lg = reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
+    hipError_t e = moe::launch_route(*r, x, T, k, ids, weights, lg, counter, s);
+    if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
+    e = moe::launch_decode_ffn(*routed, shared, x, T, k, ids, weights, residual, out,
+                               base + round_up(route_ws(T, E, true)), s);
+    return hip_status(e, "moe_layer_decode");
 }
 
 moe_status moe_check_device_error(void* stream) {

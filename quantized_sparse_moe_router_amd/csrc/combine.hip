@@ -4,9 +4,8 @@
 // expert, which always contributes with weight one [Strata 与 Qwen3.8-Flash-Next
 // (telli.sh), section 稀疏架构创造了机会].  The sum is a gather in slot order (no atomics),
 // so the result does not depend on scheduling; it is bound by reading the pair outputs.
-#include "moe_common.h"
-
-#pragma clang fp contract(off)
+// The arithmetic is combine8 (combine_common.h).
+#include "combine_common.h"
 
 namespace moe {
 namespace {
@@ -21,65 +20,10 @@ __global__ void __launch_bounds__(256) combine_kernel(
     if (idx >= (int64_t)T * per_row) return;
     const int t = (int)(idx / per_row);
     const int c8 = (int)(idx % per_row);
-    float acc[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    // slots in chunks of 8: all index/weight loads, then all row loads, then the sums in
-    // slot order, so a chunk's loads are in flight together.  Padding slots and dropped
-    // pairs (bad ids) read row 0 and add it with weight 0.
-    for (int j0 = 0; j0 < k; j0 += 8) {
-        int q[8];
-        float wj[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int jj = min(j0 + j, k - 1);
-            q[j] = pair_pos[(size_t)t * k + jj];
-            wj[j] = w[(size_t)t * k + jj];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (j0 + j >= k || q[j] < 0) wj[j] = 0.0f;
-            q[j] = max(q[j], 0);
-        }
-        uint4 v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v[j] = *reinterpret_cast<const uint4*>(y_pairs + (size_t)q[j] * d + 8 * c8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t vv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = __builtin_fmaf(wj[j], bf16lo(vv[i]), acc[2 * i]);
-                acc[2 * i + 1] = __builtin_fmaf(wj[j], bf16hi(vv[i]), acc[2 * i + 1]);
-            }
-        }
-    }
-    if (y_shared) {
-        const uint4 v = *reinterpret_cast<const uint4*>(y_shared + (size_t)t * d + 8 * c8);
-        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += bf16lo(vv[i]);
-            acc[2 * i + 1] += bf16hi(vv[i]);
-        }
-    }
-    uint32_t o[4];
-    if (residual) {
-        const uint4 r = *reinterpret_cast<const uint4*>(residual + (size_t)t * d + 8 * c8);
-        const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = bf16lo(rr[i]) + bf16_to_f32(f32_to_bf16(acc[2 * i]));
-            const float hi = bf16hi(rr[i]) + bf16_to_f32(f32_to_bf16(acc[2 * i + 1]));
-            o[i] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            o[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
-    }
-    *reinterpret_cast<uint4*>(out + (size_t)t * d + 8 * c8) = make_uint4(o[0], o[1], o[2], o[3]);
+    const uint4 o = combine8<false>(y_pairs, pair_pos + (size_t)t * k, w + (size_t)t * k, k, d,
+                                    c8, y_shared ? y_shared + (size_t)t * d : nullptr,
+                                    residual ? residual + (size_t)t * d : nullptr);
+    *reinterpret_cast<uint4*>(out + (size_t)t * d + 8 * c8) = o;
 }
 
 }  // namespace

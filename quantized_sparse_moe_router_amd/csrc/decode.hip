@@ -1,0 +1,423 @@
+// decode.hip -- the expert side of a decode step in one launch: routed and shared expert
+// FFN (gate/up + SwiGLU, then down) and the weighted combine, for at most 64
+// (token, expert) pairs.
+//
+// Decode streams each selected expert's packed weights once per token and is bound by
+// memory bandwidth and latency, not arithmetic [Halogen Flash Server配置與實測 (lcz.me),
+// replies comparing decode with bandwidth].  Run as separate calls, the dependent steps
+// (gate/up, down, shared expert, combine) each pay a launch and a cold start; here they
+// share one grid of S = P + T_s slots (P routed pairs, then T_s shared-expert tokens):
+//   blocks [0, S * n_gu)   gate/up row blocks, one slot each: h rows of that slot,
+//                          stored device-coherent, then the block is counted;
+//   blocks [S * n_gu, + D / 4)
+//                          down row blocks, each owning 4 output rows for every slot:
+//                          they issue their weight loads at once, wait until every
+//                          gate/up block is counted, copy all h rows into LDS, compute
+//                          the 4 rows of y for every slot and combine them there into the
+//                          output rows -- no y round trip.
+// Gate/up blocks have the lower block ids and never wait, so they are dispatched first and
+// the wait ends; it is also bounded (device error bit 1 on timeout).  The last down block
+// to finish leaves the counters zero for the next call.  The per-row arithmetic is that of
+// gemv_rows (gemv_common.h) and the combine repeats combine8's operations (combine_common.h)
+// on each element, so the result equals the per-call path bit for bit.
+#include "combine_common.h"
+#include "gemv_common.h"
+
+namespace moe {
+namespace {
+
+struct DecodeArgs {
+    const uint8_t *rg, *ru, *rd;       // routed experts
+    const uint16_t *rsg, *rsu, *rsd;
+    int E;
+    const uint8_t *sg, *su, *sd;       // shared expert (sg == nullptr: none)
+    const uint16_t *ssg, *ssu, *ssd;
+    const uint16_t* x;
+    int T, k;
+    const int32_t* ids;
+    const float* weights;
+    const uint16_t* residual;
+    uint16_t* out;
+    uint16_t* h;                        // [S][F] bf16: pair rows, then shared-token rows
+    unsigned* ctr;                      // counters, layout DecodeCtr
+    int* err;
+};
+
+// gate/up: 16 rows per block (4 row loads per wave in flight)
+template <int K>
+struct GuShape {
+    static constexpr int LPR = Shape<K>::LPR;
+    static constexpr int GPL = Shape<K>::GPL;
+    static constexpr int ITERS = GPL >= 4 ? 1 : 4 / GPL;
+    static constexpr int RPB = 4 * ITERS * (64 / LPR);
+};
+
+constexpr int kSlotBatch = 12;  // slots whose down weights are in registers at once
+constexpr int NTHREADS = 256;
+
+// Counters (unsigned words in the workspace).  Many blocks hitting one word with device-
+// scope atomics or polls serialise at its coherence point, so counts are spread over
+// kLines words 128 bytes apart: gate/up blocks add to word (block % kLines) without waiting
+// for the result, and a down block's poll reads all kLines words in one wave load and sums
+// them.  Down blocks count themselves two-level (group word, then a top word) so that the
+// last one can leave every counter zero.
+constexpr int kLines = 16;
+struct DecodeCtr {
+    static constexpr int kGu = 0;                 // [kLines] gate/up blocks done, 32 apart
+    static constexpr int kDnSub = 32 * kLines;    // [kLines] down blocks done, 32 apart
+    static constexpr int kDnTop = 64 * kLines;    // down groups done
+    static constexpr int kWords = 64 * kLines + 32;
+};
+__device__ __forceinline__ unsigned ctr_add(unsigned* p) {
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctr_store(unsigned* p, unsigned v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- down: 4 output rows per block (one per wave) for every slot, then their combine.
+// A row's K = d_ff codes are read by LPR lanes exactly as in gemv_rows; the 64 / LPR lane
+// groups of a wave take different slots of the same row.
+template <int F>
+struct DnShape {
+    static constexpr int LPR = Shape<F>::LPR;
+    static constexpr int GPL = Shape<F>::GPL;
+    static constexpr int NG = 64 / LPR;          // slots per wave load
+    static constexpr int ROWS = NTHREADS / 64;   // rows per block
+    // wave loads in registers at once: enough for 12 slots (one token with 10 experts and
+    // the shared one) in one batch, or a larger batch for more slots
+    static constexpr int ITB_SMALL = (12 + NG - 1) / NG;
+    static constexpr int ITB_LARGE = NG >= 4 ? 6 : 8;
+};
+
+template <int FMT, int D, int F, int ITB>
+__device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, int S,
+                                                  unsigned gu_total, uint8_t* lds) {
+    using DS = DnShape<F>;
+    constexpr int LPR = DS::LPR, GPL = DS::GPL, NG = DS::NG;
+    constexpr int GB = Fmt<FMT>::kGroupBytes;
+    constexpr size_t ROW_BYTES = (size_t)F / 32 * GB;
+    constexpr int NGRP = F / 32;                 // groups per h row
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gp = lane % LPR, sub = lane / LPR;
+    const int row = r0 + wave;                   // < D: D is a multiple of DS::ROWS
+    const int P = a.T * a.k;
+    // LDS: h rows [S][F] bf16 | group sums of h [S][NGRP] | y [S][ROWS] | gate weights [64]
+    uint16_t* h_lds = reinterpret_cast<uint16_t*>(lds);
+    float* sx_lds = reinterpret_cast<float*>(lds + (size_t)S * F * 2);
+    float* y_lds = sx_lds + (size_t)S * NGRP;
+    float* w_lds = y_lds + (size_t)S * DS::ROWS;
+
+    // every slot's expert in one load: lane l holds the expert of pair l (an id outside
+    // [0, E), never produced by moe_route, reads expert 0)
+    int my_e = lane < P ? a.ids[lane] : 0;
+    my_e = (my_e >= 0 && my_e < a.E) ? my_e : 0;
+    if (threadIdx.x < P) w_lds[threadIdx.x] = a.weights[threadIdx.x];
+
+    GroupBits<FMT> wbits[ITB][GPL];
+    uint16_t sbits[ITB][GPL];
+    // wave loads it0 .. it0 + ITB - 1: slot it * NG + sub (slots past S - 1 repeat slot
+    // S - 1, so every load is unconditional and in bounds)
+    auto load_batch = [&](int it0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < ITB; ++q) {
+            const int s = min((it0 + q) * NG + sub, S - 1);
+            const int e = __shfl(my_e, s, 64);
+            const uint8_t* wb;
+            const uint16_t* sb;
+            if (s < P) {
+                const size_t mrow = (size_t)e * D + row;
+                wb = a.rd + mrow * ROW_BYTES;
+                sb = a.rsd + mrow * (F / 32);
+            } else {
+                wb = a.sd + (size_t)row * ROW_BYTES;
+                sb = a.ssd + (size_t)row * (F / 32);
+            }
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) {
+                const int g = gp + LPR * i;
+                load_bits<FMT>(wb + (size_t)g * GB, wbits[q][i]);
+                sbits[q][i] = sb[g];
+            }
+        }
+    };
+    // the ITB dot products are independent chains: all of them first (one basic block,
+    // so their latencies overlap), then the row sums and the stores
+    auto compute_batch = [&](int it0) __attribute__((always_inline)) {
+        float acc[ITB];
+#pragma unroll
+        for (int q = 0; q < ITB; ++q) {
+            const int s = min((it0 + q) * NG + sub, S - 1);
+            acc[q] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) {
+                const int g = gp + LPR * i;
+                uint32_t xv[16];
+                const uint4* src = reinterpret_cast<const uint4*>(h_lds + (size_t)s * F + 32 * g);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint4 t4 = src[v];
+                    xv[4 * v] = t4.x; xv[4 * v + 1] = t4.y;
+                    xv[4 * v + 2] = t4.z; xv[4 * v + 3] = t4.w;
+                }
+                const float sx = sx_lds[s * NGRP + g];
+                const float sc = f16_to_f32(sbits[q][i]);
+                const float raw = dot_bits<FMT>(wbits[q][i], xv);
+                const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx, raw);
+                acc[q] = __builtin_fmaf(sc, part, acc[q]);
+            }
+        }
+        float yv[ITB];
+#pragma unroll
+        for (int q = 0; q < ITB; ++q) yv[q] = bf16_to_f32(f32_to_bf16(group_sum<LPR>(acc[q])));
+#pragma unroll
+        for (int q = 0; q < ITB; ++q) {
+            const int s_raw = (it0 + q) * NG + sub;
+            if (gp == 0 && s_raw < S) y_lds[s_raw * DS::ROWS + wave] = yv[q];
+        }
+    };
+
+    const int n_it = (S + NG - 1) / NG;
+    load_batch(0);
+    // wait until every gate/up block has published its h rows: wave 0 sums the kLines
+    // counter words, one word per lane
+    __shared__ int timed_out;
+    if (wave == 0) {
+        unsigned spins = 0;
+        for (;;) {
+            unsigned v = lane < kLines
+                             ? __hip_atomic_load(a.ctr + DecodeCtr::kGu + 32 * lane,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : 0u;
+            // sum over the whole wave (lanes >= kLines hold 0), so every lane sees the
+            // same total and the loop exit is uniform
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+            if (v >= gu_total || spins >= kSpinLimit) break;
+            __builtin_amdgcn_s_sleep(2);
+            ++spins;
+        }
+        if (lane == 0) {
+            timed_out = spins >= kSpinLimit;
+            if (timed_out) atomicOr(a.err, 2);
+        }
+    }
+    __syncthreads();
+    // all h rows -> LDS with device-coherent loads, 8 per thread in flight at a time
+    {
+        const int n16 = S * F / 8;                    // 16-byte chunks
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)a.h, (short)0, S * F * 2, 0x00020000);
+        for (int c0 = 0; c0 < n16; c0 += 8 * NTHREADS) {
+            uint4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {    // past the end: the buffer bound returns zeros
+                const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (c0 + u * NTHREADS + (int)threadIdx.x) * 16, 0, kCpolSc1);
+                v[u] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = c0 + u * NTHREADS + threadIdx.x;
+                if (c < n16) reinterpret_cast<uint4*>(h_lds)[c] = v[u];
+            }
+        }
+    }
+    __syncthreads();
+    // group sums of h, once per (slot, group), in group_sum_x's order
+    for (int i = threadIdx.x; i < S * NGRP; i += NTHREADS)
+        sx_lds[i] = group_sum_x(reinterpret_cast<const uint32_t*>(h_lds + (size_t)i * 32));
+    __syncthreads();
+    for (int it0 = 0; it0 < n_it; it0 += ITB) {
+        if (it0 > 0) load_batch(it0);
+        compute_batch(it0);
+    }
+    __syncthreads();
+
+    // combine: lane 0 of each wave, for its row, in combine8's order of operations
+    if (lane != 0) return;
+    const float* y = y_lds + wave;
+    for (int t = 0; t < a.T; ++t) {
+        float acc = 0.0f;
+        for (int j0 = 0; j0 < a.k; j0 += 8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int jj = min(j0 + j, a.k - 1);
+                const float wj = (j0 + j < a.k) ? w_lds[t * a.k + jj] : 0.0f;
+                acc = __builtin_fmaf(wj, y[(t * a.k + jj) * DS::ROWS], acc);
+            }
+        }
+        if (a.sg) acc += y[(P + t) * DS::ROWS];
+        uint32_t o;
+        if (a.residual) {
+            const float r = bf16_to_f32(a.residual[(size_t)t * D + row]);
+            o = f32_to_bf16(r + bf16_to_f32(f32_to_bf16(acc)));
+        } else {
+            o = f32_to_bf16(acc);
+        }
+        a.out[(size_t)t * D + row] = (uint16_t)o;
+    }
+}
+
+template <int F>
+constexpr size_t dn_lds_bytes(int S) {
+    return (size_t)S * F * 2 + (size_t)S * (F / 32) * 4 + (size_t)S * DnShape<F>::ROWS * 4 +
+           64 * 4;
+}
+
+template <int FMT, int D, int F, int ITB>
+__global__ void __launch_bounds__(NTHREADS) decode_ffn_kernel(DecodeArgs a) {
+    using GU = GuShape<D>;   // gate/up rows: K = d_model
+    constexpr int n_gu = (F + GU::RPB - 1) / GU::RPB;
+    constexpr int n_dn = D / DnShape<F>::ROWS;
+    const int P = a.T * a.k;
+    const int S = P + (a.sg ? a.T : 0);
+    int b = blockIdx.x;
+    if (b < S * n_gu) {
+        // ---- gate/up + SwiGLU -> h row of slot s, then count this block
+        const int s = b / n_gu, rb = b % n_gu;
+        Slot sl;
+        sl.first = 0;
+        sl.dense_n = 0;
+        if (s < P) {
+            // one pair per slot: h row s, activation row s / k.  An id outside [0, E)
+            // (never produced by moe_route) reads expert 0 and raises device error bit 0.
+            const int e = a.ids[s];
+            sl.e = (e >= 0 && e < a.E) ? e : 0;
+            if (sl.e != e && threadIdx.x == 0 && rb == 0) atomicOr(a.err, 1);
+            sl.members = 1ull << s;
+            sl.seg0 = s;
+            sl.dense0 = 0;
+            gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1, true>(
+                a.rg, a.rsg, a.ru, a.rsu, a.x, a.k, F, rb, sl, a.h);
+        } else {
+            sl.e = 0;
+            sl.members = 0;
+            sl.seg0 = 0;
+            sl.dense0 = s - P;    // shared expert: token s - P, h row s
+            sl.dense_n = 1;
+            gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1, true>(
+                a.sg, a.ssg, a.su, a.ssu, a.x, a.k, F, rb, sl, a.h + (size_t)P * F);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's h stores are complete
+        __syncthreads();
+        if (threadIdx.x == 0) ctr_add(a.ctr + DecodeCtr::kGu + 32 * (blockIdx.x % kLines));
+        return;
+    }
+    b -= S * n_gu;
+    if (b >= n_dn) return;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    down_rows_combine<FMT, D, F, ITB>(a, b * DnShape<F>::ROWS, S, (unsigned)(S * n_gu), lds);
+    // the last down block leaves the counters zero for the next call (every other block
+    // of the launch has finished by then)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        constexpr int G = n_dn < kLines ? n_dn : kLines;   // down block groups
+        const int grp = b % G;
+        const unsigned n_grp = (unsigned)((n_dn - grp + G - 1) / G);
+        if (ctr_add(a.ctr + DecodeCtr::kDnSub + 32 * grp) == n_grp - 1 &&
+            ctr_add(a.ctr + DecodeCtr::kDnTop) == (unsigned)G - 1) {
+            for (int i = 0; i < kLines; ++i) {
+                ctr_store(a.ctr + DecodeCtr::kGu + 32 * i, 0u);
+                ctr_store(a.ctr + DecodeCtr::kDnSub + 32 * i, 0u);
+            }
+            ctr_store(a.ctr + DecodeCtr::kDnTop, 0u);
+        }
+    }
+}
+
+template <int FMT, int D, int F, int ITB>
+hipError_t launch_itb(const DecodeArgs& a, hipStream_t s) {
+    constexpr int n_gu = (F + GuShape<D>::RPB - 1) / GuShape<D>::RPB;
+    constexpr int n_dn = D / DnShape<F>::ROWS;
+    const int S = a.T * a.k + (a.sg ? a.T : 0);
+    const size_t lds = dn_lds_bytes<F>(S);
+    if (lds > 64 * 1024) {   // opt in to more than 64 KiB of LDS, once per device
+        constexpr int kMaxDev = 64;
+        static bool attr_set[kMaxDev] = {};
+        int dev = 0;
+        hipError_t err = hipGetDevice(&dev);
+        if (err != hipSuccess) return err;
+        if (dev >= kMaxDev || !attr_set[dev]) {
+            err = hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&decode_ffn_kernel<FMT, D, F, ITB>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeMaxLds);
+            if (err != hipSuccess) return err;
+            if (dev < kMaxDev) attr_set[dev] = true;
+        }
+    }
+    decode_ffn_kernel<FMT, D, F, ITB><<<S * n_gu + n_dn, NTHREADS, lds, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int FMT, int D, int F>
+hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
+    using DS = DnShape<F>;
+    const int S = a.T * a.k + (a.sg ? a.T : 0);
+    if (S <= DS::ITB_SMALL * DS::NG) return launch_itb<FMT, D, F, DS::ITB_SMALL>(a, s);
+    return launch_itb<FMT, D, F, DS::ITB_LARGE>(a, s);
+}
+
+template <int FMT>
+hipError_t launch_fmt(const DecodeArgs& a, int d, int F, hipStream_t s) {
+#define MOE_DEC(DV, FV) \
+    if (d == DV && F == FV) return launch_shape<FMT, DV, FV>(a, s);
+    MOE_DEC(2048, 512)
+    MOE_DEC(256, 128)
+    MOE_DEC(2048, 1024)
+    MOE_DEC(4096, 1024)
+    MOE_DEC(1024, 512)
+    MOE_DEC(2048, 2048)
+#undef MOE_DEC
+    return hipErrorNotSupported;
+}
+
+}  // namespace
+
+DecodeWs decode_ws_layout(int T, int k, int d, int F) {
+    (void)d;
+    auto al = [](size_t n) { return (n + 255) & ~size_t(255); };
+    const int S = T * k + T;   // room for the shared expert's rows
+    DecodeWs w;
+    size_t off = 0;
+    w.h = off; off += al((size_t)S * F * 2);
+    w.cnt = off; off += al((size_t)DecodeCtr::kWords * sizeof(unsigned));
+    w.bytes = off;
+    return w;
+}
+
+bool decode_fits(int T, int k, int F, bool shared) {
+    const int S = T * k + (shared ? T : 0);
+    // h rows and the y rows of one down block (at most 64 rows per block)
+    return T * k <= 64 && (size_t)S * F * 2 + (size_t)S * (F / 32) * 4 + (size_t)S * 16 +
+                              256 <= kDecodeMaxLds;
+}
+
+hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* shared,
+                             const uint16_t* x, int T, int k, const int32_t* ids,
+                             const float* weights, const uint16_t* residual, uint16_t* out,
+                             void* ws, hipStream_t s) {
+    const int d = routed.d_model, F = routed.d_ff;
+    const DecodeWs L = decode_ws_layout(T, k, d, F);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    DecodeArgs a;
+    a.rg = routed.w_gate; a.ru = routed.w_up; a.rd = routed.w_down;
+    a.rsg = routed.s_gate; a.rsu = routed.s_up; a.rsd = routed.s_down;
+    a.E = routed.n_experts;
+    a.sg = shared ? shared->w_gate : nullptr;
+    a.su = shared ? shared->w_up : nullptr;
+    a.sd = shared ? shared->w_down : nullptr;
+    a.ssg = shared ? shared->s_gate : nullptr;
+    a.ssu = shared ? shared->s_up : nullptr;
+    a.ssd = shared ? shared->s_down : nullptr;
+    a.x = x; a.T = T; a.k = k; a.ids = ids; a.weights = weights;
+    a.residual = residual; a.out = out;
+    a.h = reinterpret_cast<uint16_t*>(base + L.h);
+    unsigned* cnt = reinterpret_cast<unsigned*>(base + L.cnt);
+    a.ctr = cnt;
+    a.err = device_error_flag();
+    if (routed.fmt == MOE_FMT_INT4_G32) return launch_fmt<MOE_FMT_INT4_G32>(a, d, F, s);
+    return launch_fmt<MOE_FMT_INT6_G32>(a, d, F, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,392 @@
+// gemv_common.h -- building blocks of the weight-streaming GEMV for few tokens: group
+// dot products on packed int4 / int6 codes, slot resolution, and one projection over a
+// block of rows.  Shared by the per-call GEMV kernels and the one-launch decode layer, so
+// both compute every output with exactly the same operations in the same order.
+//
+// A row of K packed codes is read by LPR = min(64, K/32) lanes, one 32-code group (16
+// bytes int4, 24 bytes int6) per lane per step, so a wave covers 64/LPR rows per load
+// instruction with fully used 16-byte loads.  Codes become bf16 pairs (128 + u) with a
+// byte permute, are multiplied against bf16 activation pairs by v_dot2_f32_bf16, and the
+// offset (128 + zero point) times the group's activation sum is removed afterwards; the
+// fp16 group scale is applied once per group.
+//
+// Every fused multiply-add is written out and contraction is off, so a token's arithmetic
+// is the same whatever the number of tokens that share a pass (batch invariance).
+#pragma once
+#include "moe_common.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+namespace {
+
+// bounded waits: 2^20 polls (each a device-coherent load plus a short sleep, about a
+// microsecond), far beyond any real wait of a few microseconds
+constexpr unsigned kSpinLimit = 1u << 20;
+
+// cache policy of buffer loads that must see other blocks' device-coherent stores (sc1)
+constexpr int kCpolSc1 = 16;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// 16 bytes of int4 codes (32 elements) against 32 bf16 activations (16 pairs).
+// Returns sum_i (128 + u_i) * x_i.
+__device__ __forceinline__ float group_dot_int4(const uint4 w, const uint32_t* xp) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = wd[q] & 0x0f0f0f0fu;
+        const uint32_t hi = (wd[q] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t sel = 0x0c000c00u | (uint32_t)p | ((uint32_t)(4 + p) << 16);
+            const uint32_t pair = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+            acc = dot2(pair, xp[4 * q + p], acc);
+        }
+    }
+    return acc;
+}
+
+// 24 bytes of int6 codes (32 elements, little-endian bit string) against 32 bf16.
+__device__ __forceinline__ float group_dot_int6(const uint32_t* w6, const uint32_t* xp) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const uint64_t lo64 = (uint64_t)w6[3 * half] | ((uint64_t)w6[3 * half + 1] << 32);
+        const uint64_t hi32 = w6[3 * half + 2];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            uint32_t u[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int bit = 6 * (2 * p + s);          // bit inside these 96 bits
+                uint32_t v;
+                if (bit + 6 <= 64)
+                    v = (uint32_t)(lo64 >> bit);
+                else if (bit >= 64)
+                    v = (uint32_t)(hi32 >> (bit - 64));
+                else
+                    v = (uint32_t)(lo64 >> bit) | (uint32_t)(hi32 << (64 - bit));
+                u[s] = v & 63u;
+            }
+            const uint32_t pair = (u[0] | (u[1] << 16)) | 0x43004300u;
+            acc = dot2(pair, xp[8 * half + p], acc);
+        }
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float group_sum_x(const uint32_t* xp) {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += bf16lo(xp[i]) + bf16hi(xp[i]);
+    return s;
+}
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<MOE_FMT_INT4_G32> {
+    static constexpr int kGroupBytes = 16;
+    static constexpr float kBias = 136.0f;    // 128 (bf16 magic) + 8 (zero point)
+};
+template <>
+struct Fmt<MOE_FMT_INT6_G32> {
+    static constexpr int kGroupBytes = 24;
+    static constexpr float kBias = 160.0f;    // 128 + 32
+};
+
+enum { kModeGateUp = 0, kModeDown = 1 };
+
+template <int FMT>
+struct GroupBits {
+    uint4 a;
+    uint2 b;   // int6: bytes 16..23 of the group
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_bits(const uint8_t* p, GroupBits<FMT>& g) {
+    if constexpr (FMT == MOE_FMT_INT4_G32) {
+        g.a = *reinterpret_cast<const uint4*>(p);
+    } else {
+        const uint2* q = reinterpret_cast<const uint2*>(p);
+        const uint2 x0 = q[0], x1 = q[1], x2 = q[2];
+        g.a = make_uint4(x0.x, x0.y, x1.x, x1.y);
+        g.b = x2;
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ float dot_bits(const GroupBits<FMT>& g, const uint32_t* xp) {
+    if constexpr (FMT == MOE_FMT_INT4_G32) {
+        return group_dot_int4(g.a, xp);
+    } else {
+        const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
+        return group_dot_int6(w6, xp);
+    }
+}
+
+struct Slot {
+    int e;              // expert (grouped) or 0 (dense)
+    uint64_t members;   // grouped: pairs routed to e, bit q = pair q
+    int seg0;           // grouped: sorted position of e's first pair
+    int first;          // grouped: rank (among e's pairs) of this chunk's first pair
+    int dense0, dense_n;
+};
+
+// Resolve slot s; returns false if this block has nothing to do.
+template <int MT>
+__device__ __forceinline__ bool resolve_slot(int s, int T, int k, const int32_t* ids, int E,
+                                             Slot& sl) {
+    const int lane = threadIdx.x & 63;
+    if (ids) {
+        const int P = T * k;
+        const int my = (lane < P) ? ids[lane] : -1;
+        const int e = __builtin_amdgcn_readlane(my, s);
+        if (e < 0 || e >= E) return false;
+        const bool valid = lane < P && my >= 0 && my < E;
+        sl.members = __ballot(valid && my == e);
+        // rank of pair s among e's pairs; the pairs of rank 0, MT, 2MT, ... each lead a
+        // chunk of MT pairs, the others return
+        const int rank = __popcll(sl.members & ((1ull << s) - 1ull));
+        if (rank % MT != 0) return false;
+        sl.first = rank;
+        sl.seg0 = __popcll(__ballot(valid && my < e));
+        sl.e = e;
+        sl.dense0 = sl.dense_n = 0;
+    } else {
+        sl.e = 0;
+        sl.members = 0;
+        sl.seg0 = 0;
+        sl.first = 0;
+        sl.dense0 = s * MT;
+        if (sl.dense0 >= T) return false;
+        sl.dense_n = min(MT, T - sl.dense0);
+    }
+    return true;
+}
+
+// One projection over a block of rows.  K = input length; rows = output rows.
+//   GateUp: rows = d_ff, inputs = x rows of the tokens, output h (bf16) per pair row.
+//   Down  : rows = d_model, inputs = h rows of the pairs, output y (bf16) per pair row.
+// MT = tokens per pass over the weights (a slot's pairs are taken MT at a time).
+//
+// Cross-block mode (XB, the one-launch decode): outputs are read by other blocks of the
+// same launch, so they are stored device-coherent (the block's rows gathered in LDS, then
+// a few 8-byte stores).  For a down projection in this mode the activations (h) come from
+// other blocks: the block issues its weight loads first, waits until *ready reaches
+// `target` (a bounded spin by one thread; on timeout it raises bit 1 of *err and goes on),
+// and reads h with device-coherent loads.
+template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT, bool XB = false>
+__device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
+                                          const uint16_t* __restrict__ sa,
+                                          const uint8_t* __restrict__ wb,
+                                          const uint16_t* __restrict__ sb,
+                                          const uint16_t* act, int k, int rows,
+                                          int rb, const Slot& sl, uint16_t* out,
+                                          const unsigned* ready = nullptr,
+                                          unsigned target = 0, int* err = nullptr) {
+    constexpr int K = LPR * GPL * 32;
+    constexpr int RPW = 64 / LPR;                  // rows per load instruction
+    constexpr int ROWS_PER_BLOCK = 4 * ITERS * RPW;
+    constexpr int GB = Fmt<FMT>::kGroupBytes;
+    constexpr size_t ROW_BYTES = (size_t)K / 32 * GB;
+    constexpr int NMAT = (MODE == kModeGateUp) ? 2 : 1;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int gp = lane % LPR;                      // group slot in the row
+    const int rsub = lane / LPR;                    // row inside a load instruction
+    const bool grouped = sl.members != 0;
+
+    // ---- activation rows of this block's chunk (at most MT pairs / tokens); requested
+    // before the weights so both are in flight together
+    int arow[MT], orow[MT];
+    int mcount = 0;
+    uint32_t xv[MT][GPL][16];
+    if (grouped) {
+        uint64_t rest = sl.members;
+        for (int skip = 0; skip < sl.first; ++skip) rest &= rest - 1;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            arow[m] = 0;
+            orow[m] = 0;
+            if (rest) {
+                const int q = (int)__builtin_ctzll(rest);
+                rest &= rest - 1;
+                const int srow = sl.seg0 + sl.first + m;        // expert-sorted position
+                arow[m] = (MODE == kModeGateUp) ? q / k : srow;
+                orow[m] = srow;
+                ++mcount;
+            }
+        }
+    } else {
+        mcount = sl.dense_n;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            arow[m] = sl.dense0 + min(m, mcount - 1);
+            orow[m] = arow[m];
+        }
+    }
+    constexpr bool kWaitAct = XB && MODE == kModeDown;
+    // cross-block mode: one slot of one token per block (MT = 1), rows staged here
+    static_assert(!XB || MT == 1, "cross-block mode handles one token per block");
+    static_assert(!XB || ROWS_PER_BLOCK % 4 == 0, "rows are stored 4 at a time");
+    __shared__ uint16_t xb_rows[XB ? ROWS_PER_BLOCK : 1];
+    auto load_act = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            if (m < mcount) {
+                const uint16_t* ap = act + (size_t)arow[m] * K;
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) {
+                    const uint16_t* src = ap + 32 * (gp + LPR * i);
+                    if constexpr (kWaitAct) {
+                        const uint64_t* s64 = reinterpret_cast<const uint64_t*>(src);
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) {
+                            const uint64_t q = __hip_atomic_load(s64 + v, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT);
+                            xv[m][i][2 * v + 0] = (uint32_t)q;
+                            xv[m][i][2 * v + 1] = (uint32_t)(q >> 32);
+                        }
+                    } else {
+                        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const uint4 q = s4[v];
+                            xv[m][i][4 * v + 0] = q.x;
+                            xv[m][i][4 * v + 1] = q.y;
+                            xv[m][i][4 * v + 2] = q.z;
+                            xv[m][i][4 * v + 3] = q.w;
+                        }
+                    }
+                }
+            }
+        }
+    };
+    if constexpr (!kWaitAct) load_act();
+
+    // ---- every weight load of this wave
+    const int row_base = rb * ROWS_PER_BLOCK + wave * ITERS * RPW + rsub;
+    const size_t mat_row0 = (size_t)sl.e * rows;
+    GroupBits<FMT> wbits[ITERS][NMAT][GPL];
+    uint16_t sbits[ITERS][NMAT][GPL];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int row = row_base + it * RPW;
+        const size_t mrow = mat_row0 + (row < rows ? row : 0);
+#pragma unroll
+        for (int mt = 0; mt < NMAT; ++mt) {
+            const uint8_t* wbase = (mt == 0 ? wa : wb) + mrow * ROW_BYTES;
+            const uint16_t* sbase = (mt == 0 ? sa : sb) + mrow * (K / 32);
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) {
+                const int g = gp + LPR * i;
+                load_bits<FMT>(wbase + (size_t)g * GB, wbits[it][mt][i]);
+                sbits[it][mt][i] = sbase[g];
+            }
+        }
+    }
+
+    if constexpr (kWaitAct) {
+        // the weights are in flight; now wait for h
+        __shared__ int timed_out;
+        if (threadIdx.x == 0) {
+            unsigned spins = 0;
+            while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       target && spins < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(2);
+                ++spins;
+            }
+            timed_out = spins >= kSpinLimit;
+            if (timed_out) atomicOr(err, 2);
+        }
+        __syncthreads();
+        load_act();
+    }
+
+    // ---- compute
+    {
+        float sx[MT][GPL];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < mcount)
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) sx[m][i] = group_sum_x(xv[m][i]);
+
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int row = row_base + it * RPW;
+            float acc[NMAT][MT];
+#pragma unroll
+            for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[mt][m] = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < NMAT; ++mt)
+#pragma unroll
+                for (int i = 0; i < GPL; ++i) {
+                    const float s = f16_to_f32(sbits[it][mt][i]);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+                        if (m < mcount) {
+                            const float raw = dot_bits<FMT>(wbits[it][mt][i], xv[m][i]);
+                            const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx[m][i], raw);
+                            acc[mt][m] = __builtin_fmaf(s, part, acc[mt][m]);
+                        }
+                }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                if (m < mcount) {
+                    const float v0 = group_sum<LPR>(acc[0][m]);
+                    float res;
+                    if constexpr (MODE == kModeGateUp) {
+                        const float u = group_sum<LPR>(acc[NMAT - 1][m]);
+                        res = v0 / (1.0f + expf(-v0)) * u;
+                    } else {
+                        res = v0;
+                    }
+                    if (row < rows && gp == 0) {
+                        const uint16_t v = (uint16_t)f32_to_bf16(res);
+                        if constexpr (XB)
+                            xb_rows[row - rb * ROWS_PER_BLOCK] = v;
+                        else
+                            out[(size_t)orow[m] * rows + row] = v;
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (XB) {
+        // the block's rows are contiguous in its one output row: store them device-coherent
+        // 8 bytes at a time (a few wide stores rather than one narrow store per value)
+        __syncthreads();
+        const int r4 = threadIdx.x * 4;
+        if (r4 < ROWS_PER_BLOCK && rb * ROWS_PER_BLOCK + r4 < rows) {
+            const uint64_t v = (uint64_t)xb_rows[r4] | ((uint64_t)xb_rows[r4 + 1] << 16) |
+                               ((uint64_t)xb_rows[r4 + 2] << 32) |
+                               ((uint64_t)xb_rows[r4 + 3] << 48);
+            uint64_t* o = reinterpret_cast<uint64_t*>(out + (size_t)orow[0] * rows +
+                                                      rb * ROWS_PER_BLOCK + r4);
+            __hip_atomic_store(o, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int K>
+struct Shape {
+    static constexpr int LPR = K >= 2048 ? 64 : K / 32;
+    static constexpr int GPL = K >= 2048 ? K / 2048 : 1;
+    static constexpr int ITERS = K >= 4096 ? 2 : 1;
+    static constexpr int RPB = 4 * ITERS * (64 / LPR);
+};
+
+}  // namespace
+}  // namespace moe

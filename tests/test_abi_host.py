@@ -143,3 +143,36 @@ def test_combine_rejects(L):
     assert L.moe_combine(8, 16, 16, None, None, 1, 10, 2048, 16, None) == -1
     assert L.moe_combine(16, 16, 16, 8, None, 1, 10, 2048, 16, None) == -1
     assert L.moe_combine(None, None, None, None, None, 0, 10, 2048, None, None) == 0
+
+
+def test_layer_decode_rejects(L):
+    from quantized_sparse_moe_router_amd import _lib
+    r = _router()
+    ex = _experts()
+
+    def call(r=r, ex=ex, sh=None, T=1, k=10, x=16, ids=16, w=16, res=None, out=16, ws=16,
+             wsb=1 << 30):
+        return L.moe_layer_decode(ctypes.byref(r) if r is not None else None,
+                                  ctypes.byref(ex) if ex is not None else None,
+                                  ctypes.byref(sh) if sh is not None else None,
+                                  x, T, k, ids, w, res, out, ws, wsb, None)
+    assert call(r=None) == -1
+    assert call(ex=None) == -1
+    assert call(ex=_experts(E=256)) == -1 and "differ" in _err(L)
+    assert call(sh=_experts(E=2)) == -1
+    assert call(sh=_experts(E=1, F=1024)) == -2
+    assert call(sh=_experts(E=1, fmt=3)) == -2
+    assert call(T=7) == -2 and "four calls" in _err(L)          # 70 pairs
+    assert call(ex=_experts(F=4096)) == -2                       # no GEMV shape
+    assert call(k=0) == -1
+    assert call(T=-1) == -1
+    assert call(x=8) == -1
+    assert call(res=8) == -1
+    assert call(ids=None) == -1
+    assert call(ws=None) == -3
+    assert call(wsb=100) == -3
+    assert call(T=0, x=None, out=None, ids=None, w=None, ws=None, wsb=0) == 0
+    need = L.moe_workspace_size(_lib.MOE_OP_LAYER_DECODE, 1, 10, 512, 2048, 512)
+    assert need > 256 + 512 * 4
+    assert call(wsb=need - 1) == -3
+    assert L.moe_workspace_size(_lib.MOE_OP_LAYER_DECODE, 7, 10, 512, 2048, 512) == 0
