@@ -11,9 +11,10 @@ To keep the 256 MB Infinity Cache from serving the weights, steps rotate over
 ``--copies`` distinct copies of the layer (a different token per copy).
 
 Also reported in the same line:
-  roofline      the expert kernel of a decode step (moe_experts_decode, one launch):
-                algorithmic bytes (10 routed + 1 shared expert's packed weights and scales,
-                activations in and out) / its event-timed average duration vs 8 TB/s
+  roofline      the expert kernels of a decode step (moe_experts_decode: gate/up kernel then
+                down + combine kernel): algorithmic bytes (10 routed + 1 shared expert's
+                packed weights and scales, activations in and out) / their event-timed
+                average duration vs 8 TB/s
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
   prefill       8192-token prefill through one layer (Zipf routing): tokens/s and the
                 grouped GEMM's MFMA utilisation (useful flops / time / 2.5 PFLOP/s)
@@ -153,8 +154,8 @@ def main():
     tok_s = 1000.0 / ms_step
     ms_step_calls = timed(step_all_calls, max(4, reps // 2)) / L
 
-    # ---- roofline: the expert kernel of the decode step (moe_experts_decode: the routed
-    # experts and the shared one streamed once, SwiGLU, combine) -- one launch per call
+    # ---- roofline: the expert kernels of the decode step (moe_experts_decode: the routed
+    # experts and the shared one streamed once, SwiGLU, combine) -- two launches per call
     E_b = expert_bytes(base.routed)
     alg_bytes_exp = (w.k + 1) * E_b + 2 * w.d * 2
 
@@ -188,8 +189,8 @@ def main():
                    "alg_bytes_per_step": alg_bytes_step,
                    "ms_per_step_four_calls": round(ms_step_calls, 5)},
         "roofline": {"bound": "hbm",
-                     "kernel": "decode_ffn_kernel (moe_experts_decode: 10 routed + 1 shared "
-                               "expert FFN and combine, one launch)",
+                     "kernel": "decode_gateup_kernel + decode_down_kernel (moe_experts_decode:"
+                               " 10 routed + 1 shared expert FFN and combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "alg_bytes_per_launch": alg_bytes_exp,

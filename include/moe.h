@@ -12,7 +12,8 @@
  *
  *     moe_route -> moe_permute -> moe_expert_ffn (routed; and shared, dense) -> moe_combine
  *
- * and, for a few tokens, moe_layer_decode runs that composition in two launches.
+ * and, for a few tokens, moe_layer_decode runs that composition in three launches on one
+ * stream.
  *
  * Conventions for every entry point
  *   - Pointers to tensors are DEVICE pointers (hipMalloc'd or torch-owned memory); the
@@ -185,20 +186,21 @@ moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const f
  * result, bit for bit, as
  *     moe_route -> moe_permute -> moe_expert_ffn(routed) -> moe_expert_ffn(shared, dense)
  *     -> moe_combine(residual)
- * on the same inputs, in two launches: the route kernel, then one kernel that runs the
- * routed and shared expert FFNs and the combine (blocks hand h and y rows to each other
- * through the workspace; no host round trip).  Each token is sent to k experts and to the
- * shared one, as the layer the pages describe [Strata 与 Qwen3.8-Flash-Next (telli.sh),
- * section 稀疏架构创造了机会].
+ * on the same inputs, in three launches on `stream`: the route kernel, then a gate/up kernel
+ * for every (token, expert) pair and every token's shared expert (h rows in the
+ * workspace), then a down kernel that produces a few output rows of every pair per block
+ * and combines them in registers (y never goes to memory).  Each token is sent to k
+ * experts and to the shared one, as the layer the pages describe [Strata 与
+ * Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会].
  *   routed   the routed expert set; n_experts and d_model must match the router's
  *   shared   the shared expert (n_experts 1, same format, d_model and d_ff) or NULL
  *   x        bf16 [T][d]; ids int32 [T][k] and weights fp32 [T][k] are outputs as in
  *            moe_route; residual bf16 [T][d] or NULL; out bf16 [T][d] (may alias residual)
  *   ws       zero-initialised workspace of moe_workspace_size(MOE_OP_LAYER_DECODE, T, k,
- *            E, d, d_ff) bytes; its counters are left zero by every call
- * Needs T*k <= 64 and a (d_model, d_ff) pair with a GEMV kernel (see moe_expert_ffn);
- * otherwise MOE_ERR_UNSUPPORTED and the caller uses the four calls.  A bounded wait that
- * times out raises the device error flag (moe_check_device_error).
+ *            E, d, d_ff) bytes; the route kernel's counter is left zero by every call
+ * Needs T*k <= 64, the h rows of all T*k (+ T shared) slots within 128 KiB of LDS, and a
+ * (d_model, d_ff) pair with a GEMV kernel (see moe_expert_ffn); otherwise
+ * MOE_ERR_UNSUPPORTED and the caller uses the four calls.
  */
 moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
                             const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
@@ -206,11 +208,12 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_experts_decode -- the second launch of moe_layer_decode on its own: given ids and
- * weights from moe_route, the routed and shared expert FFNs and the combine in one kernel,
- * bit for bit equal to moe_permute -> moe_expert_ffn x 2 -> moe_combine.  Arguments as in
- * moe_layer_decode; ws: zero-initialised, moe_workspace_size(MOE_OP_EXPERTS_DECODE, T, k,
- * E, d, d_ff) bytes.  ids must lie in [0, n_experts) (moe_route's always do).
+ * moe_experts_decode -- the last two launches of moe_layer_decode on their own: given ids
+ * and weights from moe_route, the routed and shared expert FFNs and the combine, bit for
+ * bit equal to moe_permute -> moe_expert_ffn x 2 -> moe_combine.  Arguments as in
+ * moe_layer_decode; ws: moe_workspace_size(MOE_OP_EXPERTS_DECODE, T, k, E, d, d_ff) bytes
+ * (no zero-fill needed).  An id outside [0, n_experts) (moe_route never gives one) reads
+ * expert 0 and raises the device error flag (moe_check_device_error).
  */
 moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shared,
                               const uint16_t* x, int32_t T, int32_t k, const int32_t* ids,

@@ -2,7 +2,7 @@
 
 The compute path is the C ABI of ``libmoe_mi355x.so`` (include/moe.h): moe_route,
 moe_permute, moe_expert_ffn and moe_combine, and moe_layer_decode (the same composition
-in two launches for a few tokens), all HIP kernels for gfx950.  This package is its
+in three launches on one stream for a few tokens), all HIP kernels for gfx950.  This package is its
 Python binding (``_lib``) plus ``MoeLayer``, which owns the buffers of one layer call and
 enqueues the calls on the current stream.  Torch only provides device memory and streams.
 """
@@ -48,7 +48,7 @@ class MoeLayer:
     them.  Graph capture records the forks and joins.  Intermediate results stay readable
     as attributes (logits, ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared).
 
-    decode(x) computes the same output bit for bit with moe_layer_decode (two launches, no
+    decode(x) computes the same output bit for bit with moe_layer_decode (three launches, no
     side streams) when T*k <= 64 and the shapes allow it (``can_decode``); it fills ids,
     weights and out only.
     """

@@ -61,7 +61,7 @@ size_t ffn_ws(int64_t rows, int E, int F) {
     return gemv > mfma ? gemv : mfma;
 }
 
-// one-launch decode workspace: [route workspace][decode rows and counters]
+// decode layer workspace: [route workspace][h rows of every slot]
 size_t decode_ws(int T, int k, int E, int d, int F) {
     return round_up(route_ws(T, E, true)) + moe::decode_ws_layout(T, k, d, F).bytes;
 }

@@ -20,7 +20,7 @@ __global__ void __launch_bounds__(256) combine_kernel(
     if (idx >= (int64_t)T * per_row) return;
     const int t = (int)(idx / per_row);
     const int c8 = (int)(idx % per_row);
-    const uint4 o = combine8<false>(y_pairs, pair_pos + (size_t)t * k, w + (size_t)t * k, k, d,
+    const uint4 o = combine8(y_pairs, pair_pos + (size_t)t * k, w + (size_t)t * k, k, d,
                                     c8, y_shared ? y_shared + (size_t)t * d : nullptr,
                                     residual ? residual + (size_t)t * d : nullptr);
     *reinterpret_cast<uint4*>(out + (size_t)t * d + 8 * c8) = o;

@@ -1,6 +1,6 @@
 // combine_common.h -- the weighted combine of one token's expert outputs for 8 consecutive
-// output columns, shared by the per-call combine kernel and the one-launch decode layer so
-// that both round exactly alike.
+// output columns.  The decode layer's down kernel repeats these operations element by
+// element, so both round exactly alike.
 //
 // out = bf16( sum_{j<k} w_j * y[q_j]  + y_shared ), summed in fp32 in slot order; slots are
 // taken in chunks of 8 (all index/weight loads, then all row loads, then the fused
@@ -14,22 +14,8 @@
 namespace moe {
 namespace {
 
-// 16 bytes of bf16 row data; device-coherent when written by other blocks of the launch
-template <bool COHERENT>
-__device__ __forceinline__ uint4 load_row16(const uint16_t* p) {
-    if constexpr (COHERENT) {
-        const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-        const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
-    } else {
-        return *reinterpret_cast<const uint4*>(p);
-    }
-}
-
 // Columns 8 c8 .. 8 c8 + 7 of one token.  pos / w: the token's k sorted positions and gate
 // weights; y_shared_row / residual_row may be null.
-template <bool COHERENT>
 __device__ __forceinline__ uint4 combine8(const uint16_t* y_pairs, const int32_t* pos,
                                           const float* w, int k, int d, int c8,
                                           const uint16_t* y_shared_row,
@@ -53,7 +39,8 @@ __device__ __forceinline__ uint4 combine8(const uint16_t* y_pairs, const int32_t
         }
         uint4 v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = load_row16<COHERENT>(y_pairs + (size_t)q[j] * d + 8 * c8);
+        for (int j = 0; j < 8; ++j)
+            v[j] = *reinterpret_cast<const uint4*>(y_pairs + (size_t)q[j] * d + 8 * c8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t vv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
@@ -65,7 +52,7 @@ __device__ __forceinline__ uint4 combine8(const uint16_t* y_pairs, const int32_t
         }
     }
     if (y_shared_row) {
-        const uint4 v = load_row16<COHERENT>(y_shared_row + 8 * c8);
+        const uint4 v = *reinterpret_cast<const uint4*>(y_shared_row + 8 * c8);
         const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -1,25 +1,22 @@
-// decode.hip -- the expert side of a decode step in one launch: routed and shared expert
-// FFN (gate/up + SwiGLU, then down) and the weighted combine, for at most 64
+// decode.hip -- the expert side of a decode step in two launches: routed and shared
+// expert FFN (gate/up + SwiGLU, then down) and the weighted combine, for at most 64
 // (token, expert) pairs.
 //
 // Decode streams each selected expert's packed weights once per token and is bound by
 // memory bandwidth and latency, not arithmetic [Halogen Flash Server配置與實測 (lcz.me),
-// replies comparing decode with bandwidth].  Run as separate calls, the dependent steps
-// (gate/up, down, shared expert, combine) each pay a launch and a cold start; here they
-// share one grid of S = P + T_s slots (P routed pairs, then T_s shared-expert tokens):
-//   blocks [0, S * n_gu)   gate/up row blocks, one slot each: h rows of that slot,
-//                          stored device-coherent, then the block is counted;
-//   blocks [S * n_gu, + D / 4)
-//                          down row blocks, each owning 4 output rows for every slot:
-//                          they issue their weight loads at once, wait until every
-//                          gate/up block is counted, copy all h rows into LDS, compute
-//                          the 4 rows of y for every slot and combine them there into the
-//                          output rows -- no y round trip.
-// Gate/up blocks have the lower block ids and never wait, so they are dispatched first and
-// the wait ends; it is also bounded (device error bit 1 on timeout).  The last down block
-// to finish leaves the counters zero for the next call.  The per-row arithmetic is that of
-// gemv_rows (gemv_common.h) and the combine repeats combine8's operations (combine_common.h)
-// on each element, so the result equals the per-call path bit for bit.
+// replies comparing decode with bandwidth].  The per-call path runs gate/up, down and the
+// combine for the routed experts, and the shared expert beside them, as five launches on
+// two streams.  Here the S = P + T_s slots (P routed pairs, then T_s shared-expert tokens)
+// share two launches on one stream:
+//   decode_gateup_kernel  one block per (slot, 16-row block): h rows of every slot;
+//   decode_down_kernel    one block per 4 output rows: those rows of y for every slot
+//                         (h of all slots staged in LDS), combined in registers into the
+//                         output rows -- y never goes to memory.
+// Handing h over at a kernel boundary costs less than any wait between blocks of one
+// launch: blocks on different XCDs see each other's stores only through device-coherent
+// memory, a round trip of about a microsecond each way.  The per-row arithmetic is that
+// of gemv_rows (gemv_common.h) and the combine repeats combine8's operations
+// (combine_common.h) on each element, so the result equals the per-call path bit for bit.
 #include "combine_common.h"
 #include "gemv_common.h"
 
@@ -39,7 +36,6 @@ struct DecodeArgs {
     const uint16_t* residual;
     uint16_t* out;
     uint16_t* h;                        // [S][F] bf16: pair rows, then shared-token rows
-    unsigned* ctr;                      // counters, layout DecodeCtr
     int* err;
 };
 
@@ -52,28 +48,7 @@ struct GuShape {
     static constexpr int RPB = 4 * ITERS * (64 / LPR);
 };
 
-constexpr int kSlotBatch = 12;  // slots whose down weights are in registers at once
 constexpr int NTHREADS = 256;
-
-// Counters (unsigned words in the workspace).  Many blocks hitting one word with device-
-// scope atomics or polls serialise at its coherence point, so counts are spread over
-// kLines words 128 bytes apart: gate/up blocks add to word (block % kLines) without waiting
-// for the result, and a down block's poll reads all kLines words in one wave load and sums
-// them.  Down blocks count themselves two-level (group word, then a top word) so that the
-// last one can leave every counter zero.
-constexpr int kLines = 16;
-struct DecodeCtr {
-    static constexpr int kGu = 0;                 // [kLines] gate/up blocks done, 32 apart
-    static constexpr int kDnSub = 32 * kLines;    // [kLines] down blocks done, 32 apart
-    static constexpr int kDnTop = 64 * kLines;    // down groups done
-    static constexpr int kWords = 64 * kLines + 32;
-};
-__device__ __forceinline__ unsigned ctr_add(unsigned* p) {
-    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ctr_store(unsigned* p, unsigned v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // ---- down: 4 output rows per block (one per wave) for every slot, then their combine.
 // A row's K = d_ff codes are read by LPR lanes exactly as in gemv_rows; the 64 / LPR lane
@@ -92,7 +67,7 @@ struct DnShape {
 
 template <int FMT, int D, int F, int ITB>
 __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, int S,
-                                                  unsigned gu_total, uint8_t* lds) {
+                                                  uint8_t* lds) {
     using DS = DnShape<F>;
     constexpr int LPR = DS::LPR, GPL = DS::GPL, NG = DS::NG;
     constexpr int GB = Fmt<FMT>::kGroupBytes;
@@ -179,42 +154,16 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
 
     const int n_it = (S + NG - 1) / NG;
     load_batch(0);
-    // wait until every gate/up block has published its h rows: wave 0 sums the kLines
-    // counter words, one word per lane
-    __shared__ int timed_out;
-    if (wave == 0) {
-        unsigned spins = 0;
-        for (;;) {
-            unsigned v = lane < kLines
-                             ? __hip_atomic_load(a.ctr + DecodeCtr::kGu + 32 * lane,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                             : 0u;
-            // sum over the whole wave (lanes >= kLines hold 0), so every lane sees the
-            // same total and the loop exit is uniform
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-            if (v >= gu_total || spins >= kSpinLimit) break;
-            __builtin_amdgcn_s_sleep(2);
-            ++spins;
-        }
-        if (lane == 0) {
-            timed_out = spins >= kSpinLimit;
-            if (timed_out) atomicOr(a.err, 2);
-        }
-    }
-    __syncthreads();
-    // all h rows -> LDS with device-coherent loads, 8 per thread in flight at a time
+    // all h rows -> LDS, 8 loads per thread in flight at a time
     {
         const int n16 = S * F / 8;                    // 16-byte chunks
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)a.h, (short)0, S * F * 2, 0x00020000);
+        const uint4* src = reinterpret_cast<const uint4*>(a.h);
         for (int c0 = 0; c0 < n16; c0 += 8 * NTHREADS) {
             uint4 v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {    // past the end: the buffer bound returns zeros
-                const auto t4 = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, (c0 + u * NTHREADS + (int)threadIdx.x) * 16, 0, kCpolSc1);
-                v[u] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+            for (int u = 0; u < 8; ++u) {
+                const int c = min(c0 + u * NTHREADS + (int)threadIdx.x, n16 - 1);
+                v[u] = src[c];
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -265,65 +214,41 @@ constexpr size_t dn_lds_bytes(int S) {
            64 * 4;
 }
 
-template <int FMT, int D, int F, int ITB>
-__global__ void __launch_bounds__(NTHREADS) decode_ffn_kernel(DecodeArgs a) {
+template <int FMT, int D, int F>
+__global__ void __launch_bounds__(NTHREADS) decode_gateup_kernel(DecodeArgs a) {
     using GU = GuShape<D>;   // gate/up rows: K = d_model
     constexpr int n_gu = (F + GU::RPB - 1) / GU::RPB;
-    constexpr int n_dn = D / DnShape<F>::ROWS;
     const int P = a.T * a.k;
-    const int S = P + (a.sg ? a.T : 0);
-    int b = blockIdx.x;
-    if (b < S * n_gu) {
-        // ---- gate/up + SwiGLU -> h row of slot s, then count this block
-        const int s = b / n_gu, rb = b % n_gu;
-        Slot sl;
-        sl.first = 0;
-        sl.dense_n = 0;
-        if (s < P) {
-            // one pair per slot: h row s, activation row s / k.  An id outside [0, E)
-            // (never produced by moe_route) reads expert 0 and raises device error bit 0.
-            const int e = a.ids[s];
-            sl.e = (e >= 0 && e < a.E) ? e : 0;
-            if (sl.e != e && threadIdx.x == 0 && rb == 0) atomicOr(a.err, 1);
-            sl.members = 1ull << s;
-            sl.seg0 = s;
-            sl.dense0 = 0;
-            gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1, true>(
-                a.rg, a.rsg, a.ru, a.rsu, a.x, a.k, F, rb, sl, a.h);
-        } else {
-            sl.e = 0;
-            sl.members = 0;
-            sl.seg0 = 0;
-            sl.dense0 = s - P;    // shared expert: token s - P, h row s
-            sl.dense_n = 1;
-            gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1, true>(
-                a.sg, a.ssg, a.su, a.ssu, a.x, a.k, F, rb, sl, a.h + (size_t)P * F);
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's h stores are complete
-        __syncthreads();
-        if (threadIdx.x == 0) ctr_add(a.ctr + DecodeCtr::kGu + 32 * (blockIdx.x % kLines));
-        return;
+    const int s = blockIdx.x / n_gu, rb = blockIdx.x % n_gu;
+    Slot sl;
+    sl.first = 0;
+    if (s < P) {
+        // one pair per slot: h row s, activation row s / k.  An id outside [0, E) (never
+        // produced by moe_route) reads expert 0 and raises device error bit 0.
+        const int e = a.ids[s];
+        sl.e = (e >= 0 && e < a.E) ? e : 0;
+        if (sl.e != e && threadIdx.x == 0 && rb == 0) atomicOr(a.err, 1);
+        sl.members = 1ull << s;
+        sl.seg0 = s;
+        sl.dense0 = sl.dense_n = 0;
+        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1>(
+            a.rg, a.rsg, a.ru, a.rsu, a.x, a.k, F, rb, sl, a.h);
+    } else {
+        sl.e = 0;
+        sl.members = 0;
+        sl.seg0 = 0;
+        sl.dense0 = s - P;    // shared expert: token s - P, h row s
+        sl.dense_n = 1;
+        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1>(
+            a.sg, a.ssg, a.su, a.ssu, a.x, a.k, F, rb, sl, a.h + (size_t)P * F);
     }
-    b -= S * n_gu;
-    if (b >= n_dn) return;
+}
+
+template <int FMT, int D, int F, int ITB>
+__global__ void __launch_bounds__(NTHREADS) decode_down_kernel(DecodeArgs a) {
+    const int S = a.T * a.k + (a.sg ? a.T : 0);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    down_rows_combine<FMT, D, F, ITB>(a, b * DnShape<F>::ROWS, S, (unsigned)(S * n_gu), lds);
-    // the last down block leaves the counters zero for the next call (every other block
-    // of the launch has finished by then)
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        constexpr int G = n_dn < kLines ? n_dn : kLines;   // down block groups
-        const int grp = b % G;
-        const unsigned n_grp = (unsigned)((n_dn - grp + G - 1) / G);
-        if (ctr_add(a.ctr + DecodeCtr::kDnSub + 32 * grp) == n_grp - 1 &&
-            ctr_add(a.ctr + DecodeCtr::kDnTop) == (unsigned)G - 1) {
-            for (int i = 0; i < kLines; ++i) {
-                ctr_store(a.ctr + DecodeCtr::kGu + 32 * i, 0u);
-                ctr_store(a.ctr + DecodeCtr::kDnSub + 32 * i, 0u);
-            }
-            ctr_store(a.ctr + DecodeCtr::kDnTop, 0u);
-        }
-    }
+    down_rows_combine<FMT, D, F, ITB>(a, blockIdx.x * DnShape<F>::ROWS, S, lds);
 }
 
 template <int FMT, int D, int F, int ITB>
@@ -340,13 +265,16 @@ hipError_t launch_itb(const DecodeArgs& a, hipStream_t s) {
         if (err != hipSuccess) return err;
         if (dev >= kMaxDev || !attr_set[dev]) {
             err = hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&decode_ffn_kernel<FMT, D, F, ITB>),
+                reinterpret_cast<const void*>(&decode_down_kernel<FMT, D, F, ITB>),
                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeMaxLds);
             if (err != hipSuccess) return err;
             if (dev < kMaxDev) attr_set[dev] = true;
         }
     }
-    decode_ffn_kernel<FMT, D, F, ITB><<<S * n_gu + n_dn, NTHREADS, lds, s>>>(a);
+    decode_gateup_kernel<FMT, D, F><<<S * n_gu, NTHREADS, 0, s>>>(a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    decode_down_kernel<FMT, D, F, ITB><<<n_dn, NTHREADS, lds, s>>>(a);
     return hipGetLastError();
 }
 
@@ -381,7 +309,6 @@ DecodeWs decode_ws_layout(int T, int k, int d, int F) {
     DecodeWs w;
     size_t off = 0;
     w.h = off; off += al((size_t)S * F * 2);
-    w.cnt = off; off += al((size_t)DecodeCtr::kWords * sizeof(unsigned));
     w.bytes = off;
     return w;
 }
@@ -413,8 +340,6 @@ hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* share
     a.x = x; a.T = T; a.k = k; a.ids = ids; a.weights = weights;
     a.residual = residual; a.out = out;
     a.h = reinterpret_cast<uint16_t*>(base + L.h);
-    unsigned* cnt = reinterpret_cast<unsigned*>(base + L.cnt);
-    a.ctr = cnt;
     a.err = device_error_flag();
     if (routed.fmt == MOE_FMT_INT4_G32) return launch_fmt<MOE_FMT_INT4_G32>(a, d, F, s);
     return launch_fmt<MOE_FMT_INT6_G32>(a, d, F, s);

@@ -1,6 +1,6 @@
 // gemv_common.h -- building blocks of the weight-streaming GEMV for few tokens: group
 // dot products on packed int4 / int6 codes, slot resolution, and one projection over a
-// block of rows.  Shared by the per-call GEMV kernels and the one-launch decode layer, so
+// block of rows.  Shared by the per-call GEMV kernels and the decode layer kernels, so
 // both compute every output with exactly the same operations in the same order.
 //
 // A row of K packed codes is read by LPR = min(64, K/32) lanes, one 32-code group (16
@@ -19,13 +19,6 @@
 
 namespace moe {
 namespace {
-
-// bounded waits: 2^20 polls (each a device-coherent load plus a short sleep, about a
-// microsecond), far beyond any real wait of a few microseconds
-constexpr unsigned kSpinLimit = 1u << 20;
-
-// cache policy of buffer loads that must see other blocks' device-coherent stores (sc1)
-constexpr int kCpolSc1 = 16;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -176,22 +169,13 @@ __device__ __forceinline__ bool resolve_slot(int s, int T, int k, const int32_t*
 //   GateUp: rows = d_ff, inputs = x rows of the tokens, output h (bf16) per pair row.
 //   Down  : rows = d_model, inputs = h rows of the pairs, output y (bf16) per pair row.
 // MT = tokens per pass over the weights (a slot's pairs are taken MT at a time).
-//
-// Cross-block mode (XB, the one-launch decode): outputs are read by other blocks of the
-// same launch, so they are stored device-coherent (the block's rows gathered in LDS, then
-// a few 8-byte stores).  For a down projection in this mode the activations (h) come from
-// other blocks: the block issues its weight loads first, waits until *ready reaches
-// `target` (a bounded spin by one thread; on timeout it raises bit 1 of *err and goes on),
-// and reads h with device-coherent loads.
-template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT, bool XB = false>
+template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                                           const uint16_t* __restrict__ sa,
                                           const uint8_t* __restrict__ wb,
                                           const uint16_t* __restrict__ sb,
                                           const uint16_t* act, int k, int rows,
-                                          int rb, const Slot& sl, uint16_t* out,
-                                          const unsigned* ready = nullptr,
-                                          unsigned target = 0, int* err = nullptr) {
+                                          int rb, const Slot& sl, uint16_t* out) {
     constexpr int K = LPR * GPL * 32;
     constexpr int RPW = 64 / LPR;                  // rows per load instruction
     constexpr int ROWS_PER_BLOCK = 4 * ITERS * RPW;
@@ -234,11 +218,6 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
             orow[m] = arow[m];
         }
     }
-    constexpr bool kWaitAct = XB && MODE == kModeDown;
-    // cross-block mode: one slot of one token per block (MT = 1), rows staged here
-    static_assert(!XB || MT == 1, "cross-block mode handles one token per block");
-    static_assert(!XB || ROWS_PER_BLOCK % 4 == 0, "rows are stored 4 at a time");
-    __shared__ uint16_t xb_rows[XB ? ROWS_PER_BLOCK : 1];
     auto load_act = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -247,31 +226,20 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) {
                     const uint16_t* src = ap + 32 * (gp + LPR * i);
-                    if constexpr (kWaitAct) {
-                        const uint64_t* s64 = reinterpret_cast<const uint64_t*>(src);
+                    const uint4* s4 = reinterpret_cast<const uint4*>(src);
 #pragma unroll
-                        for (int v = 0; v < 8; ++v) {
-                            const uint64_t q = __hip_atomic_load(s64 + v, __ATOMIC_RELAXED,
-                                                                 __HIP_MEMORY_SCOPE_AGENT);
-                            xv[m][i][2 * v + 0] = (uint32_t)q;
-                            xv[m][i][2 * v + 1] = (uint32_t)(q >> 32);
-                        }
-                    } else {
-                        const uint4* s4 = reinterpret_cast<const uint4*>(src);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const uint4 q = s4[v];
-                            xv[m][i][4 * v + 0] = q.x;
-                            xv[m][i][4 * v + 1] = q.y;
-                            xv[m][i][4 * v + 2] = q.z;
-                            xv[m][i][4 * v + 3] = q.w;
-                        }
+                    for (int v = 0; v < 4; ++v) {
+                        const uint4 q = s4[v];
+                        xv[m][i][4 * v + 0] = q.x;
+                        xv[m][i][4 * v + 1] = q.y;
+                        xv[m][i][4 * v + 2] = q.z;
+                        xv[m][i][4 * v + 3] = q.w;
                     }
                 }
             }
         }
     };
-    if constexpr (!kWaitAct) load_act();
+    load_act();
 
     // ---- every weight load of this wave
     const int row_base = rb * ROWS_PER_BLOCK + wave * ITERS * RPW + rsub;
@@ -293,23 +261,6 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                 sbits[it][mt][i] = sbase[g];
             }
         }
-    }
-
-    if constexpr (kWaitAct) {
-        // the weights are in flight; now wait for h
-        __shared__ int timed_out;
-        if (threadIdx.x == 0) {
-            unsigned spins = 0;
-            while (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                       target && spins < kSpinLimit) {
-                __builtin_amdgcn_s_sleep(2);
-                ++spins;
-            }
-            timed_out = spins >= kSpinLimit;
-            if (timed_out) atomicOr(err, 2);
-        }
-        __syncthreads();
-        load_act();
     }
 
     // ---- compute
@@ -354,28 +305,10 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                         res = v0;
                     }
                     if (row < rows && gp == 0) {
-                        const uint16_t v = (uint16_t)f32_to_bf16(res);
-                        if constexpr (XB)
-                            xb_rows[row - rb * ROWS_PER_BLOCK] = v;
-                        else
-                            out[(size_t)orow[m] * rows + row] = v;
+                        out[(size_t)orow[m] * rows + row] = (uint16_t)f32_to_bf16(res);
                     }
                 }
             }
-        }
-    }
-    if constexpr (XB) {
-        // the block's rows are contiguous in its one output row: store them device-coherent
-        // 8 bytes at a time (a few wide stores rather than one narrow store per value)
-        __syncthreads();
-        const int r4 = threadIdx.x * 4;
-        if (r4 < ROWS_PER_BLOCK && rb * ROWS_PER_BLOCK + r4 < rows) {
-            const uint64_t v = (uint64_t)xb_rows[r4] | ((uint64_t)xb_rows[r4 + 1] << 16) |
-                               ((uint64_t)xb_rows[r4 + 2] << 32) |
-                               ((uint64_t)xb_rows[r4 + 3] << 48);
-            uint64_t* o = reinterpret_cast<uint64_t*>(out + (size_t)orow[0] * rows +
-                                                      rb * ROWS_PER_BLOCK + r4);
-            __hip_atomic_store(o, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -111,14 +111,12 @@ hipError_t launch_combine(const uint16_t* y_pairs, const int32_t* pair_pos, cons
                           const uint16_t* y_shared, const uint16_t* residual, int T, int k,
                           int d, uint16_t* out, hipStream_t s);
 
-// One-launch expert side of a decode step (routed + shared FFN and combine), at most 64
-// pairs and S = T*k (+ T shared) slots whose h rows fit in kDecodeMaxLds bytes of LDS.
-// Workspace: [h rows][counters], counters zero before the first use and left zero by
-// every call.
-constexpr int kDecodeMaxSlots = 128;
+// Expert side of a decode step (routed + shared FFN and combine) in two launches, at most
+// 64 pairs and S = T*k (+ T shared) slots whose h rows fit in kDecodeMaxLds bytes of LDS.
+// Workspace: [h rows].
 constexpr size_t kDecodeMaxLds = 128 * 1024;
 struct DecodeWs {
-    size_t h, cnt, bytes;
+    size_t h, bytes;
 };
 DecodeWs decode_ws_layout(int T, int k, int d_model, int d_ff);
 bool decode_fits(int T, int k, int d_ff, bool shared);
