@@ -43,7 +43,7 @@ bool supported_router_dim(int fmt, int d) {
     return d == 1024 || d == 2048 || d == 4096;
 }
 
-constexpr int kMaxExperts = 1024;
+constexpr int kMaxExperts = 1024;   // the decode layer's selection holds <= 16 keys per lane
 constexpr int kMaxK = 64;
 constexpr int64_t kGemvMaxRows = 64;   // pair rows up to which the GEMV path runs
 constexpr int64_t kDecodeMaxPairs = 64; // pairs up to which moe_layer_decode runs
@@ -61,9 +61,10 @@ size_t ffn_ws(int64_t rows, int E, int F) {
     return gemv > mfma ? gemv : mfma;
 }
 
-// decode layer workspace: [route workspace][h rows of every slot]
+// decode layer workspace: [router logits [T][E] fp32][h rows of every slot]
 size_t decode_ws(int T, int k, int E, int d, int F) {
-    return round_up(route_ws(T, E, true)) + moe::decode_ws_layout(T, k, d, F).bytes;
+    return round_up((size_t)T * (size_t)E * sizeof(float)) +
+           moe::decode_ws_layout(T, k, d, F).bytes;
 }
 
 // Router descriptor checks shared by moe_route and moe_layer_decode.
@@ -294,8 +295,11 @@ moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shar
     if (!ws || ws_bytes < need || !aligned16(ws))
         return fail(MOE_ERR_WORKSPACE, "moe_experts_decode: needs %zu workspace bytes (got %zu)",
                     need, ws_bytes);
-    return hip_status(moe::launch_decode_ffn(*routed, shared, x, T, k, ids, weights, residual,
-                                             out, ws, static_cast<hipStream_t>(stream)),
+    // no logits: the kernels only read ids and weights
+    return hip_status(moe::launch_decode_ffn(*routed, shared, x, T, k, nullptr,
+                                             const_cast<int32_t*>(ids),
+                                             const_cast<float*>(weights), residual, out, ws,
+                                             static_cast<hipStream_t>(stream)),
                       "moe_experts_decode");
 }
 
@@ -320,12 +324,11 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
                     need, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* base = static_cast<uint8_t*>(ws);
-    unsigned* counter = reinterpret_cast<unsigned*>(base);
-    float* lg = reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
-    hipError_t e = moe::launch_route(*r, x, T, k, ids, weights, lg, counter, s);
+    float* lg = reinterpret_cast<float*>(base);
+    hipError_t e = moe::launch_route_logits(*r, x, T, lg, s);
     if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
-    e = moe::launch_decode_ffn(*routed, shared, x, T, k, ids, weights, residual, out,
-                               base + round_up(route_ws(T, E, true)), s);
+    e = moe::launch_decode_ffn(*routed, shared, x, T, k, lg, ids, weights, residual, out,
+                               base + round_up((size_t)T * (size_t)E * sizeof(float)), s);
     return hip_status(e, "moe_layer_decode");
 }
 

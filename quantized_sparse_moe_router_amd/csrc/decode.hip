@@ -19,6 +19,7 @@
 // (combine_common.h) on each element, so the result equals the per-call path bit for bit.
 #include "combine_common.h"
 #include "gemv_common.h"
+#include "topk_common.h"
 
 namespace moe {
 namespace {
@@ -31,8 +32,9 @@ struct DecodeArgs {
     const uint16_t *ssg, *ssu, *ssd;
     const uint16_t* x;
     int T, k;
-    const int32_t* ids;
-    const float* weights;
+    const float* logits;                // [T][E] router logits, or null: ids / weights given
+    int32_t* ids;                       // [T][k]; written by the gate/up kernel when logits
+    float* weights;                     //   are given, read-only otherwise
     const uint16_t* residual;
     uint16_t* out;
     uint16_t* h;                        // [S][F] bf16: pair rows, then shared-token rows
@@ -83,11 +85,24 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     float* y_lds = sx_lds + (size_t)S * NGRP;
     float* w_lds = y_lds + (size_t)S * DS::ROWS;
 
-    // every slot's expert in one load: lane l holds the expert of pair l (an id outside
-    // [0, E), never produced by moe_route, reads expert 0)
-    int my_e = lane < P ? a.ids[lane] : 0;
-    my_e = (my_e >= 0 && my_e < a.E) ? my_e : 0;
-    if (threadIdx.x < P) w_lds[threadIdx.x] = a.weights[threadIdx.x];
+    // Loads that need nothing, all unconditional (clamped indexes) so that the compiler
+    // can count them: every slot's expert (lane l: pair l; an id outside [0, E), never
+    // produced by moe_route, reads expert 0), the gate weights, the residual of token
+    // `lane` (combined by this lane), and the first kHPass h chunks of this thread.
+    int my_e = a.ids[min(lane, P - 1)];
+    const float gate_w = a.weights[min((int)threadIdx.x, P - 1)];
+    const uint16_t* res_src = a.residual ? a.residual : a.x;   // x: same shape, unused
+    const uint16_t res_bits = res_src[(size_t)min(lane, a.T - 1) * D + row];
+    constexpr int kHPass = 4;
+    const int n16 = S * F / 8;                    // 16-byte chunks of h
+    // native 4-vectors: an array of HIP's uint4 struct is not kept in registers
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* hsrc = reinterpret_cast<const u32x4*>(a.h);
+    u32x4* hdst = reinterpret_cast<u32x4*>(h_lds);
+    u32x4 hv[kHPass];
+#pragma unroll
+    for (int u = 0; u < kHPass; ++u) hv[u] = hsrc[min(u * NTHREADS + (int)threadIdx.x, n16 - 1)];
+    my_e = (lane < P && my_e >= 0 && my_e < a.E) ? my_e : 0;
 
     GroupBits<FMT> wbits[ITB][GPL];
     uint16_t sbits[ITB][GPL];
@@ -154,23 +169,20 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
 
     const int n_it = (S + NG - 1) / NG;
     load_batch(0);
-    // all h rows -> LDS, 8 loads per thread in flight at a time
-    {
-        const int n16 = S * F / 8;                    // 16-byte chunks
-        const uint4* src = reinterpret_cast<const uint4*>(a.h);
-        for (int c0 = 0; c0 < n16; c0 += 8 * NTHREADS) {
-            uint4 v[8];
+    __builtin_amdgcn_sched_barrier(0);
+    if (threadIdx.x < P) w_lds[threadIdx.x] = gate_w;
+    // h rows -> LDS.  An index past the end is clamped to the last chunk, which then
+    // stores the same value twice: no branch, so no wait per chunk.
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = min(c0 + u * NTHREADS + (int)threadIdx.x, n16 - 1);
-                v[u] = src[c];
-            }
+    for (int u = 0; u < kHPass; ++u) hdst[min(u * NTHREADS + (int)threadIdx.x, n16 - 1)] = hv[u];
+    for (int c0 = kHPass * NTHREADS; c0 < n16; c0 += kHPass * NTHREADS) {
+        u32x4 hw[kHPass];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u * NTHREADS + threadIdx.x;
-                if (c < n16) reinterpret_cast<uint4*>(h_lds)[c] = v[u];
-            }
-        }
+        for (int u = 0; u < kHPass; ++u)
+            hw[u] = hsrc[min(c0 + u * NTHREADS + (int)threadIdx.x, n16 - 1)];
+#pragma unroll
+        for (int u = 0; u < kHPass; ++u)
+            hdst[min(c0 + u * NTHREADS + (int)threadIdx.x, n16 - 1)] = hw[u];
     }
     __syncthreads();
     // group sums of h, once per (slot, group), in group_sum_x's order
@@ -183,10 +195,10 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     }
     __syncthreads();
 
-    // combine: lane 0 of each wave, for its row, in combine8's order of operations
-    if (lane != 0) return;
+    // combine: lane t of each wave, token t of the wave's row, in combine8's order of
+    // operations
     const float* y = y_lds + wave;
-    for (int t = 0; t < a.T; ++t) {
+    for (int t = lane; t < a.T; t += 64) {
         float acc = 0.0f;
         for (int j0 = 0; j0 < a.k; j0 += 8) {
 #pragma unroll
@@ -199,7 +211,7 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
         if (a.sg) acc += y[(P + t) * DS::ROWS];
         uint32_t o;
         if (a.residual) {
-            const float r = bf16_to_f32(a.residual[(size_t)t * D + row]);
+            const float r = bf16_to_f32(t == lane ? res_bits : a.residual[(size_t)t * D + row]);
             o = f32_to_bf16(r + bf16_to_f32(f32_to_bf16(acc)));
         } else {
             o = f32_to_bf16(acc);
@@ -214,7 +226,10 @@ constexpr size_t dn_lds_bytes(int S) {
            64 * 4;
 }
 
-template <int FMT, int D, int F>
+// NPL > 0: every block selects its token's experts from the logits itself (topk_wave, each
+// wave redundantly, so no block waits for another) and the first row block of each
+// token's first pair writes that token's ids and weights.  NPL = 0: ids are given.
+template <int FMT, int D, int F, int NPL>
 __global__ void __launch_bounds__(NTHREADS) decode_gateup_kernel(DecodeArgs a) {
     using GU = GuShape<D>;   // gate/up rows: K = d_model
     constexpr int n_gu = (F + GU::RPB - 1) / GU::RPB;
@@ -224,8 +239,27 @@ __global__ void __launch_bounds__(NTHREADS) decode_gateup_kernel(DecodeArgs a) {
     sl.first = 0;
     if (s < P) {
         // one pair per slot: h row s, activation row s / k.  An id outside [0, E) (never
-        // produced by moe_route) reads expert 0 and raises device error bit 0.
-        const int e = a.ids[s];
+        // produced by the selection) reads expert 0 and raises device error bit 0.
+        int e;
+        if constexpr (NPL > 0) {
+            // wave 0 selects, the block reads its expert from LDS
+            const int t = s / a.k, j = s - t * a.k;
+            __shared__ int sel_lds;
+            if (threadIdx.x < 64) {
+                int sel_e;
+                float sel_w;
+                topk_wave<NPL, false>(a.logits + (size_t)t * a.E, a.E, a.k, sel_e, sel_w);
+                if (threadIdx.x == j) sel_lds = sel_e;
+                if (j == 0 && rb == 0 && threadIdx.x < a.k) {
+                    a.ids[(size_t)t * a.k + threadIdx.x] = sel_e;
+                    a.weights[(size_t)t * a.k + threadIdx.x] = sel_w;
+                }
+            }
+            __syncthreads();
+            e = sel_lds;
+        } else {
+            e = a.ids[s];
+        }
         sl.e = (e >= 0 && e < a.E) ? e : 0;
         if (sl.e != e && threadIdx.x == 0 && rb == 0) atomicOr(a.err, 1);
         sl.members = 1ull << s;
@@ -271,7 +305,12 @@ hipError_t launch_itb(const DecodeArgs& a, hipStream_t s) {
             if (dev < kMaxDev) attr_set[dev] = true;
         }
     }
-    decode_gateup_kernel<FMT, D, F><<<S * n_gu, NTHREADS, 0, s>>>(a);
+    if (!a.logits)
+        decode_gateup_kernel<FMT, D, F, 0><<<S * n_gu, NTHREADS, 0, s>>>(a);
+    else if (a.E <= 64 * 8)
+        decode_gateup_kernel<FMT, D, F, 8><<<S * n_gu, NTHREADS, 0, s>>>(a);
+    else
+        decode_gateup_kernel<FMT, D, F, 16><<<S * n_gu, NTHREADS, 0, s>>>(a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     decode_down_kernel<FMT, D, F, ITB><<<n_dn, NTHREADS, lds, s>>>(a);
@@ -321,9 +360,9 @@ bool decode_fits(int T, int k, int F, bool shared) {
 }
 
 hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* shared,
-                             const uint16_t* x, int T, int k, const int32_t* ids,
-                             const float* weights, const uint16_t* residual, uint16_t* out,
-                             void* ws, hipStream_t s) {
+                             const uint16_t* x, int T, int k, const float* logits,
+                             int32_t* ids, float* weights, const uint16_t* residual,
+                             uint16_t* out, void* ws, hipStream_t s) {
     const int d = routed.d_model, F = routed.d_ff;
     const DecodeWs L = decode_ws_layout(T, k, d, F);
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -337,7 +376,7 @@ hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* share
     a.ssg = shared ? shared->s_gate : nullptr;
     a.ssu = shared ? shared->s_up : nullptr;
     a.ssd = shared ? shared->s_down : nullptr;
-    a.x = x; a.T = T; a.k = k; a.ids = ids; a.weights = weights;
+    a.x = x; a.T = T; a.k = k; a.logits = logits; a.ids = ids; a.weights = weights;
     a.residual = residual; a.out = out;
     a.h = reinterpret_cast<uint16_t*>(base + L.h);
     a.err = device_error_flag();

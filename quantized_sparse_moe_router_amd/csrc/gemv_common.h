@@ -262,6 +262,10 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
             }
         }
     }
+    // every load above is issued before any arithmetic: left to itself the scheduler
+    // interleaves the dot products with the loads to save registers, which turns one
+    // memory round trip into several
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- compute
     {

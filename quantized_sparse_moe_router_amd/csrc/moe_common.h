@@ -91,6 +91,9 @@ hipError_t read_and_clear_device_error(int* flag);
 
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
                         float* weights, float* logits, unsigned* counter, hipStream_t s);
+// Router logits only (fp32 [T][E], the same values launch_route computes), for T <= 64.
+hipError_t launch_route_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
+                               hipStream_t s);
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted_pairs, int32_t* pair_pos, void* ws, hipStream_t s);
@@ -120,9 +123,11 @@ struct DecodeWs {
 };
 DecodeWs decode_ws_layout(int T, int k, int d_model, int d_ff);
 bool decode_fits(int T, int k, int d_ff, bool shared);
+// logits non-null: the selection runs inside (ids and weights are written); null: ids and
+// weights are inputs.
 hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* shared,
-                             const uint16_t* x, int T, int k, const int32_t* ids,
-                             const float* weights, const uint16_t* residual, uint16_t* out,
-                             void* ws, hipStream_t s);
+                             const uint16_t* x, int T, int k, const float* logits,
+                             int32_t* ids, float* weights, const uint16_t* residual,
+                             uint16_t* out, void* ws, hipStream_t s);
 
 }  // namespace moe

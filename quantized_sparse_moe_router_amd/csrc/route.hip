@@ -9,6 +9,7 @@
 // kernels below realise exactly that order, so decode (few tokens) and prefill (many
 // tokens) produce identical logits for the same token.
 #include "moe_common.h"
+#include "topk_common.h"
 
 #pragma clang fp contract(off)
 
@@ -247,109 +248,21 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(
 }
 
 // ------------------------------------------------------------------ top-k + weights
-// One wave per token.  Each (logit, expert) becomes a 64-bit key whose unsigned order is
-// the selection order: the logit's bits mapped to an order-preserving unsigned integer
-// (-0 first turned into +0 so the two compare equal) in the high word, and 0xffffffff - e
-// in the low word so that equal logits favour the lower expert id.  k rounds of a wave
-// max over the lanes' best untaken keys pick the experts in slot order; then the weights
-// are the softmax over the k selected logits in fp32, shifted by the largest.
-__device__ __forceinline__ uint32_t order_bits(float v) {
-    uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-    const uint32_t lo = (uint32_t)dpp<CTRL>((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)dpp<CTRL>((int)(uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// Selection and weights of one token by one wave.  Keys are 64-bit: the logit's bits mapped
-// to an order-preserving unsigned integer in the high word, 0xffffffff - e in the low word,
-// so "larger key" is "larger logit, then lower id".  Each lane sorts its NPL keys once;
-// each of the k rounds takes the wave maximum of the lanes' heads (DPP inside 16-lane rows,
-// then the four row maxima on the scalar unit) and the owning lane advances its head.
-template <int NPL, bool DEVICE_SCOPE_LOAD>
-__device__ __forceinline__ void topk_token(const float* lt, int E, int k, int32_t* ids_t,
-                                           float* w_t) {
-    const int lane = threadIdx.x & 63;
-    uint64_t key[NPL];
-    float v[NPL];
-    // all loads first, unconditionally (clamped index), so they are in flight together
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = min(lane + 64 * i, E - 1);
-        if constexpr (DEVICE_SCOPE_LOAD)
-            v[i] = __hip_atomic_load(const_cast<float*>(lt) + e, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        else
-            v[i] = lt[e];
-    }
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = (e < E) ? (((uint64_t)order_bits(v[i]) << 32) | (0xffffffffu - (uint32_t)e))
-                         : 0ull;                       // padding keys lose to every id
-    }
-    // descending sort of the lane's keys (odd-even transposition network)
-#pragma unroll
-    for (int r = 0; r < NPL; ++r)
-#pragma unroll
-        for (int i = r & 1; i + 1 < NPL; i += 2) {
-            const uint64_t a = key[i], b = key[i + 1];
-            key[i] = a > b ? a : b;
-            key[i + 1] = a > b ? b : a;
-        }
-    uint64_t mine = 0ull;
-    int head = 0;                                      // index of the lane's next key
-    for (int j = 0; j < k; ++j) {
-        uint64_t b = 0ull;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) b = (head == i) ? key[i] : b;
-        const uint64_t cand = b;
-        uint64_t o;
-        o = dpp64<kDppXor1>(b);       b = o > b ? o : b;
-        o = dpp64<kDppXor2>(b);       b = o > b ? o : b;
-        o = dpp64<kDppHalfMirror>(b); b = o > b ? o : b;
-        o = dpp64<kDppMirror>(b);     b = o > b ? o : b;
-        uint64_t win = readlane64(b, 0);
-#pragma unroll
-        for (int r = 16; r < 64; r += 16) {
-            const uint64_t c = readlane64(b, r);
-            win = c > win ? c : win;
-        }
-        // keys are unique (the low word holds the id): exactly one lane owns the winner
-        head += (cand == win) ? 1 : 0;
-        if (lane == j) mine = win;
-    }
-    const uint32_t my_hi = (uint32_t)(mine >> 32), my_lo = (uint32_t)mine;
-    const int my_e = (int)(0xffffffffu - my_lo);
-    const uint32_t vbits = (my_hi & 0x80000000u) ? (my_hi & 0x7fffffffu) : ~my_hi;
-    const float my_v = (lane < k) ? __uint_as_float(vbits) : 0.0f;
-    const float vmax = __shfl(my_v, 0, 64);
-    const float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
-    const float sum = group_sum<64>(ex);
-    if (lane < k) {
-        ids_t[lane] = my_e;
-        w_t[lane] = ex / sum;
-    }
-}
-
+// One wave per token: topk_wave (topk_common.h).
 template <int NPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T,
                                                    int E, int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ weights) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    topk_token<NPL, false>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
-                           weights + (size_t)t * k);
+    int e;
+    float w;
+    topk_wave<NPL, false>(logits + (size_t)t * E, E, k, e, w);
+    const int lane = threadIdx.x & 63;
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = e;
+        weights[(size_t)t * k + lane] = w;
+    }
 }
 
 // Few tokens: logits and selection in one launch.  Every block computes its rows' logits
@@ -369,10 +282,26 @@ __global__ void __launch_bounds__(256) router_gemv_topk_kernel(
     if (threadIdx.x == 0) is_last = (atomicAdd(counter, 1u) == gridDim.x - 1) ? 1 : 0;
     __syncthreads();
     if (!is_last) return;
-    for (int t = threadIdx.x >> 6; t < T; t += 4)
-        topk_token<NPL, true>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
-                              weights + (size_t)t * k);
+    const int lane = threadIdx.x & 63;
+    for (int t = threadIdx.x >> 6; t < T; t += 4) {
+        int e;
+        float w;
+        topk_wave<NPL, true>(logits + (size_t)t * E, E, k, e, w);
+        if (lane < k) {
+            ids[(size_t)t * k + lane] = e;
+            weights[(size_t)t * k + lane] = w;
+        }
+    }
     if (threadIdx.x == 0) atomicExch(counter, 0u);
+}
+
+// Logits only, for a consumer that runs the selection itself (the decode layer).
+template <int FMT, int NV>
+__global__ void __launch_bounds__(256) router_gemv_kernel(
+    const void* __restrict__ W, const uint16_t* __restrict__ scale,
+    const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
+    float* __restrict__ logits) {
+    router_gemv_rows<FMT, NV, false>(W, scale, bias, x, T, E, d, logits);
 }
 
 template <int FMT, int NV>
@@ -435,7 +364,34 @@ hipError_t launch_fmt(const moe_router& r, const uint16_t* x, int T, int k, int3
     return hipErrorInvalidValue;
 }
 
+template <int FMT>
+hipError_t launch_logits_fmt(const moe_router& r, const uint16_t* x, int T, float* logits,
+                             hipStream_t s) {
+    constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
+    const int nv = r.d_model / (64 * PV);
+    const dim3 grid((r.n_experts + 3) / 4), block(256);
+#define MOE_NV(N)                                                                         \
+    if (nv == N) {                                                                        \
+        router_gemv_kernel<FMT, N><<<grid, block, 0, s>>>(r.w, r.scale, r.bias, x, T,     \
+                                                          r.n_experts, r.d_model, logits);\
+        return hipGetLastError();                                                         \
+    }
+    MOE_NV(1)
+    MOE_NV(2)
+    MOE_NV(4)
+    MOE_NV(8)
+    MOE_NV(16)
+#undef MOE_NV
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_route_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
+                               hipStream_t s) {
+    if (r.fmt == MOE_FMT_INT8_ROW) return launch_logits_fmt<MOE_FMT_INT8_ROW>(r, x, T, logits, s);
+    return launch_logits_fmt<MOE_FMT_FP32>(r, x, T, logits, s);
+}
 
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
                         float* weights, float* logits, unsigned* counter, hipStream_t s) {

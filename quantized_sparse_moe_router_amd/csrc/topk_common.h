@@ -1,0 +1,142 @@
+// topk_common.h -- top-k expert selection and gate weights of one token by one wavefront.
+//
+// Every token goes to k of E routed experts [Strata 与 Qwen3.8-Flash-Next (telli.sh),
+// section 稀疏架构创造了机会]; the gate weights are the softmax over the k selected
+// logits, renormalised over the selection.  The result is exact (no approximation): the k
+// largest logits in descending order, equal logits taken lower expert id first.
+//
+// Keys: each (logit, expert) becomes a 64-bit key whose unsigned order is the selection
+// order -- the logit mapped to an order-preserving unsigned integer (-0 first turned into
+// +0, so the two compare equal) in the high word, 0xffffffff - e in the low word.  Lane l
+// holds experts l, l + 64, ... (NPL of them), sorts its keys once with a sorting network,
+// and each of the k rounds takes the wave maximum of the lanes' first keys on the high
+// words alone (32-bit lane maxima, then four row maxima on the scalar unit); only when
+// several lanes tie on the high word does a second round on the low words decide.  The
+// winning lane drops its first key.
+#pragma once
+#include "moe_common.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint32_t order_bits(float v) {
+    uint32_t u = (v == 0.0f) ? 0u : __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// DPP row broadcasts (gfx9): lane 15 of each row to the next row, lane 31 to rows 2 and 3
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// wave maximum of an unsigned 32-bit value, returned uniform: row maxima by DPP, then two
+// row broadcasts carry the maximum to lane 63
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    uint32_t o;
+    o = (uint32_t)dpp<kDppXor1>((int)v);       v = o > v ? o : v;
+    o = (uint32_t)dpp<kDppXor2>((int)v);       v = o > v ? o : v;
+    o = (uint32_t)dpp<kDppHalfMirror>((int)v); v = o > v ? o : v;
+    o = (uint32_t)dpp<kDppMirror>((int)v);     v = o > v ? o : v;
+    // rows 1 and 3 take the previous row's maximum; then rows 2 and 3 take lane 31's
+    o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast15, 0xa, 0xf, false);
+    v = o > v ? o : v;
+    o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kDppRowBcast31, 0xc, 0xf, false);
+    v = o > v ? o : v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Descending sort of N (a power of two) keys held by one lane: Batcher's odd-even merge
+// sort network (19 comparators for N = 8).
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&key)[N]) {
+#pragma unroll
+    for (int p = 1; p < N; p <<= 1)
+#pragma unroll
+        for (int kk = p; kk >= 1; kk >>= 1)
+#pragma unroll
+            for (int j = kk % p; j + kk < N; j += 2 * kk)
+#pragma unroll
+                for (int i = 0; i < kk; ++i)
+                    if (i + j + kk < N && (i + j) / (2 * p) == (i + j + kk) / (2 * p)) {
+                        const uint64_t x = key[i + j], y = key[i + j + kk];
+                        key[i + j] = x > y ? x : y;
+                        key[i + j + kk] = x > y ? y : x;
+                    }
+}
+
+// Selection and weights of one token's E logits (lt, fp32) by the calling wave; every lane
+// of the wave must call it.  Lane j < k returns the j-th selected expert and its weight.
+// Needs 1 <= k <= min(E, 64) and E <= 64 * NPL.  COHERENT: the logits were just stored by
+// other blocks of the same launch (device-scope stores), so they are read device-scope.
+template <int NPL, bool COHERENT>
+__device__ __forceinline__ void topk_wave(const float* lt, int E, int k, int& out_e,
+                                          float& out_w) {
+    const int lane = threadIdx.x & 63;
+    float v[NPL];
+    // all loads first, unconditionally (clamped index), so they are in flight together
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+        if constexpr (COHERENT)
+            v[i] = __hip_atomic_load(const_cast<float*>(lt) + e, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        else
+            v[i] = lt[e];
+    }
+    uint64_t key[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? (((uint64_t)order_bits(v[i]) << 32) | (0xffffffffu - (uint32_t)e))
+                         : 0ull;                       // padding keys lose to every id
+    }
+    sort_desc<NPL>(key);
+    uint32_t khi[NPL], klo[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        khi[i] = (uint32_t)(key[i] >> 32);
+        klo[i] = (uint32_t)key[i];
+    }
+    // round j: the lane whose first key is the wave maximum (exactly one: keys are unique)
+    // passes its key to lane j and drops it
+    uint32_t mine_hi = 0u, mine_lo = 0u;
+    for (int j = 0; j < k; ++j) {
+        const uint32_t m = wave_max_u32(khi[0]);
+        uint64_t wmask = __ballot(khi[0] == m);
+        if (__popcll(wmask) > 1) {
+            // equal high words: the larger low word (the lower id) wins; low words are
+            // unique among real keys, and a real key's low word beats padding's 0
+            const uint32_t lm = wave_max_u32(khi[0] == m ? klo[0] : 0u);
+            wmask = __ballot(khi[0] == m && klo[0] == lm);
+        }
+        const int wl = (int)__builtin_ctzll(wmask);
+        const uint32_t wl_lo = (uint32_t)__builtin_amdgcn_readlane((int)klo[0], wl);
+        if (lane == j) {
+            mine_hi = m;
+            mine_lo = wl_lo;
+        }
+        if (lane == wl) {
+#pragma unroll
+            for (int i = 0; i + 1 < NPL; ++i) {
+                khi[i] = khi[i + 1];
+                klo[i] = klo[i + 1];
+            }
+            khi[NPL - 1] = 0u;
+            klo[NPL - 1] = 0u;
+        }
+    }
+    const uint64_t mine = ((uint64_t)mine_hi << 32) | mine_lo;
+    // weights: softmax over the k selected logits in fp32, shifted by the largest
+    const uint32_t my_hi = (uint32_t)(mine >> 32), my_lo = (uint32_t)mine;
+    const uint32_t vbits = (my_hi & 0x80000000u) ? (my_hi & 0x7fffffffu) : ~my_hi;
+    const float my_v = (lane < k) ? __uint_as_float(vbits) : 0.0f;
+    const float vmax = __shfl(my_v, 0, 64);
+    const float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
+    const float sum = group_sum<64>(ex);
+    out_e = (int)(0xffffffffu - my_lo);
+    out_w = ex / sum;
+}
+
+}  // namespace
+}  // namespace moe
