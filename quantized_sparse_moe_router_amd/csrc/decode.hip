@@ -41,13 +41,14 @@ struct DecodeArgs {
     int* err;
 };
 
-// gate/up: 16 rows per block (4 row loads per wave in flight)
+// gate/up: 16 waves per block, each with one load instruction per matrix (short chains of
+// arithmetic per wave once the data is in; one selection per block of 16 waves)
+constexpr int GU_WAVES = 16;
 template <int K>
 struct GuShape {
     static constexpr int LPR = Shape<K>::LPR;
     static constexpr int GPL = Shape<K>::GPL;
-    static constexpr int ITERS = GPL >= 4 ? 1 : 4 / GPL;
-    static constexpr int RPB = 4 * ITERS * (64 / LPR);
+    static constexpr int RPB = GU_WAVES * (64 / LPR);   // rows per block
 };
 
 constexpr int NTHREADS = 256;
@@ -230,25 +231,42 @@ constexpr size_t dn_lds_bytes(int S) {
 // wave redundantly, so no block waits for another) and the first row block of each
 // token's first pair writes that token's ids and weights.  NPL = 0: ids are given.
 template <int FMT, int D, int F, int NPL>
-__global__ void __launch_bounds__(NTHREADS) decode_gateup_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(GU_WAVES * 64) decode_gateup_kernel(DecodeArgs a) {
     using GU = GuShape<D>;   // gate/up rows: K = d_model
     constexpr int n_gu = (F + GU::RPB - 1) / GU::RPB;
     const int P = a.T * a.k;
     const int s = blockIdx.x / n_gu, rb = blockIdx.x % n_gu;
+    const bool pair = s < P;
+    // the slot's activation row (token s / k, or s - P for the shared expert) goes to LDS
+    // once per block; requested first, so it is in flight during the selection
+    __shared__ __attribute__((aligned(16))) uint16_t x_lds[D];
+    {
+        const int t = pair ? s / a.k : s - P;
+        const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * D);
+        for (int i = threadIdx.x; i < D / 8; i += GU_WAVES * 64)
+            reinterpret_cast<uint4*>(x_lds)[i] = src[i];
+    }
+    // dense form of gemv_rows: one token, activation row 0 (x_lds), output row 0 of `out`
     Slot sl;
     sl.first = 0;
-    if (s < P) {
-        // one pair per slot: h row s, activation row s / k.  An id outside [0, E) (never
-        // produced by the selection) reads expert 0 and raises device error bit 0.
+    sl.members = 0;
+    sl.seg0 = 0;
+    sl.dense0 = 0;
+    sl.dense_n = 1;
+    if (pair) {
+        // h row s.  An id outside [0, E) (never produced by the selection) reads expert 0
+        // and raises device error bit 0.
         int e;
         if constexpr (NPL > 0) {
             // wave 0 selects, the block reads its expert from LDS
             const int t = s / a.k, j = s - t * a.k;
             __shared__ int sel_lds;
+            __shared__ uint64_t scratch[128];
             if (threadIdx.x < 64) {
                 int sel_e;
                 float sel_w;
-                topk_wave<NPL, false>(a.logits + (size_t)t * a.E, a.E, a.k, sel_e, sel_w);
+                topk_wave<NPL, false>(a.logits + (size_t)t * a.E, a.E, a.k, scratch, sel_e,
+                                      sel_w);
                 if (threadIdx.x == j) sel_lds = sel_e;
                 if (j == 0 && rb == 0 && threadIdx.x < a.k) {
                     a.ids[(size_t)t * a.k + threadIdx.x] = sel_e;
@@ -259,22 +277,17 @@ __global__ void __launch_bounds__(NTHREADS) decode_gateup_kernel(DecodeArgs a) {
             e = sel_lds;
         } else {
             e = a.ids[s];
+            __syncthreads();
         }
         sl.e = (e >= 0 && e < a.E) ? e : 0;
         if (sl.e != e && threadIdx.x == 0 && rb == 0) atomicOr(a.err, 1);
-        sl.members = 1ull << s;
-        sl.seg0 = s;
-        sl.dense0 = sl.dense_n = 0;
-        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1>(
-            a.rg, a.rsg, a.ru, a.rsu, a.x, a.k, F, rb, sl, a.h);
+        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, 1, 1, GU_WAVES>(
+            a.rg, a.rsg, a.ru, a.rsu, x_lds, a.k, F, rb, sl, a.h + (size_t)s * F);
     } else {
+        __syncthreads();
         sl.e = 0;
-        sl.members = 0;
-        sl.seg0 = 0;
-        sl.dense0 = s - P;    // shared expert: token s - P, h row s
-        sl.dense_n = 1;
-        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, 1>(
-            a.sg, a.ssg, a.su, a.ssu, a.x, a.k, F, rb, sl, a.h + (size_t)P * F);
+        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, 1, 1, GU_WAVES>(
+            a.sg, a.ssg, a.su, a.ssu, x_lds, a.k, F, rb, sl, a.h + (size_t)s * F);
     }
 }
 
@@ -306,11 +319,11 @@ hipError_t launch_itb(const DecodeArgs& a, hipStream_t s) {
         }
     }
     if (!a.logits)
-        decode_gateup_kernel<FMT, D, F, 0><<<S * n_gu, NTHREADS, 0, s>>>(a);
+        decode_gateup_kernel<FMT, D, F, 0><<<S * n_gu, GU_WAVES * 64, 0, s>>>(a);
     else if (a.E <= 64 * 8)
-        decode_gateup_kernel<FMT, D, F, 8><<<S * n_gu, NTHREADS, 0, s>>>(a);
+        decode_gateup_kernel<FMT, D, F, 8><<<S * n_gu, GU_WAVES * 64, 0, s>>>(a);
     else
-        decode_gateup_kernel<FMT, D, F, 16><<<S * n_gu, NTHREADS, 0, s>>>(a);
+        decode_gateup_kernel<FMT, D, F, 16><<<S * n_gu, GU_WAVES * 64, 0, s>>>(a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     decode_down_kernel<FMT, D, F, ITB><<<n_dn, NTHREADS, lds, s>>>(a);

@@ -169,7 +169,8 @@ __device__ __forceinline__ bool resolve_slot(int s, int T, int k, const int32_t*
 //   GateUp: rows = d_ff, inputs = x rows of the tokens, output h (bf16) per pair row.
 //   Down  : rows = d_model, inputs = h rows of the pairs, output y (bf16) per pair row.
 // MT = tokens per pass over the weights (a slot's pairs are taken MT at a time).
-template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT>
+// NW = waves per block; wave w owns ITERS consecutive groups of 64 / LPR rows.
+template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT, int NW = 4>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                                           const uint16_t* __restrict__ sa,
                                           const uint8_t* __restrict__ wb,
@@ -178,7 +179,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                                           int rb, const Slot& sl, uint16_t* out) {
     constexpr int K = LPR * GPL * 32;
     constexpr int RPW = 64 / LPR;                  // rows per load instruction
-    constexpr int ROWS_PER_BLOCK = 4 * ITERS * RPW;
+    constexpr int ROWS_PER_BLOCK = NW * ITERS * RPW;
     constexpr int GB = Fmt<FMT>::kGroupBytes;
     constexpr size_t ROW_BYTES = (size_t)K / 32 * GB;
     constexpr int NMAT = (MODE == kModeGateUp) ? 2 : 1;

@@ -253,11 +253,12 @@ template <int NPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int T,
                                                    int E, int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ weights) {
+    __shared__ uint64_t scratch[4][128];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     int e;
     float w;
-    topk_wave<NPL, false>(logits + (size_t)t * E, E, k, e, w);
+    topk_wave<NPL, false>(logits + (size_t)t * E, E, k, scratch[threadIdx.x >> 6], e, w);
     const int lane = threadIdx.x & 63;
     if (lane < k) {
         ids[(size_t)t * k + lane] = e;
@@ -279,6 +280,7 @@ __global__ void __launch_bounds__(256) router_gemv_topk_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this block's stores done
     __syncthreads();
     __shared__ int is_last;
+    __shared__ uint64_t scratch[4][128];
     if (threadIdx.x == 0) is_last = (atomicAdd(counter, 1u) == gridDim.x - 1) ? 1 : 0;
     __syncthreads();
     if (!is_last) return;
@@ -286,7 +288,7 @@ __global__ void __launch_bounds__(256) router_gemv_topk_kernel(
     for (int t = threadIdx.x >> 6; t < T; t += 4) {
         int e;
         float w;
-        topk_wave<NPL, true>(logits + (size_t)t * E, E, k, e, w);
+        topk_wave<NPL, true>(logits + (size_t)t * E, E, k, scratch[threadIdx.x >> 6], e, w);
         if (lane < k) {
             ids[(size_t)t * k + lane] = e;
             weights[(size_t)t * k + lane] = w;

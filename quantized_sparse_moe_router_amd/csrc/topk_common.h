@@ -8,11 +8,8 @@
 // Keys: each (logit, expert) becomes a 64-bit key whose unsigned order is the selection
 // order -- the logit mapped to an order-preserving unsigned integer (-0 first turned into
 // +0, so the two compare equal) in the high word, 0xffffffff - e in the low word.  Lane l
-// holds experts l, l + 64, ... (NPL of them), sorts its keys once with a sorting network,
-// and each of the k rounds takes the wave maximum of the lanes' first keys on the high
-// words alone (32-bit lane maxima, then four row maxima on the scalar unit); only when
-// several lanes tie on the high word does a second round on the low words decide.  The
-// winning lane drops its first key.
+// of the wave holds experts l, l + 64, ...; keys are unique, so the selection is the k
+// largest keys in descending order.
 #pragma once
 #include "moe_common.h"
 
@@ -65,32 +62,13 @@ __device__ __forceinline__ void sort_desc(uint64_t (&key)[N]) {
                     }
 }
 
-// Selection and weights of one token's E logits (lt, fp32) by the calling wave; every lane
-// of the wave must call it.  Lane j < k returns the j-th selected expert and its weight.
-// Needs 1 <= k <= min(E, 64) and E <= 64 * NPL.  COHERENT: the logits were just stored by
-// other blocks of the same launch (device-scope stores), so they are read device-scope.
-template <int NPL, bool COHERENT>
-__device__ __forceinline__ void topk_wave(const float* lt, int E, int k, int& out_e,
-                                          float& out_w) {
+// Lane j < k of the calling wave holds the j-th selected key (descending); the rest hold 0.
+// Serial form: each lane sorts its keys once; each of k rounds takes the wave maximum of
+// the lanes' first keys on the high words alone, and only when several lanes tie on the
+// high word a second round on the low words decides; the winning lane drops its key.
+template <int NPL>
+__device__ __forceinline__ uint64_t select_serial(uint64_t (&key)[NPL], int k) {
     const int lane = threadIdx.x & 63;
-    float v[NPL];
-    // all loads first, unconditionally (clamped index), so they are in flight together
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = min(lane + 64 * i, E - 1);
-        if constexpr (COHERENT)
-            v[i] = __hip_atomic_load(const_cast<float*>(lt) + e, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        else
-            v[i] = lt[e];
-    }
-    uint64_t key[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = (e < E) ? (((uint64_t)order_bits(v[i]) << 32) | (0xffffffffu - (uint32_t)e))
-                         : 0ull;                       // padding keys lose to every id
-    }
     sort_desc<NPL>(key);
     uint32_t khi[NPL], klo[NPL];
 #pragma unroll
@@ -98,8 +76,6 @@ __device__ __forceinline__ void topk_wave(const float* lt, int E, int k, int& ou
         khi[i] = (uint32_t)(key[i] >> 32);
         klo[i] = (uint32_t)key[i];
     }
-    // round j: the lane whose first key is the wave maximum (exactly one: keys are unique)
-    // passes its key to lane j and drops it
     uint32_t mine_hi = 0u, mine_lo = 0u;
     for (int j = 0; j < k; ++j) {
         const uint32_t m = wave_max_u32(khi[0]);
@@ -126,7 +102,82 @@ __device__ __forceinline__ void topk_wave(const float* lt, int E, int k, int& ou
             klo[NPL - 1] = 0u;
         }
     }
-    const uint64_t mine = ((uint64_t)mine_hi << 32) | mine_lo;
+    return ((uint64_t)mine_hi << 32) | mine_lo;
+}
+
+// Selection and weights of one token's E logits (lt, fp32) by the calling wave; every lane
+// of the wave must call it.  Lane j < k returns the j-th selected expert and its weight.
+// Needs 1 <= k <= min(E, 64) and E <= 64 * NPL; `scratch` is 128 keys of LDS owned by the
+// calling wave.  COHERENT: the logits were just stored by other blocks of the same launch
+// (device-scope stores), so they are read device-scope.
+//
+// Fast form (exact, for any input): let T be the k-th largest of the 64 lanes' largest high
+// words (a bitwise search, most significant bit first, on one value per lane).  At least k
+// keys have a high word >= T, so every selected key does; these candidates (usually a
+// few more than k) are compacted into LDS and each one's rank among them is counted.  When
+// there are more than 64 candidates (many equal logits) the serial form runs instead.
+template <int NPL, bool COHERENT>
+__device__ __forceinline__ void topk_wave(const float* lt, int E, int k, uint64_t* scratch,
+                                          int& out_e, float& out_w) {
+    const int lane = threadIdx.x & 63;
+    float v[NPL];
+    // all loads first, unconditionally (clamped index), so they are in flight together
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+        if constexpr (COHERENT)
+            v[i] = __hip_atomic_load(const_cast<float*>(lt) + e, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        else
+            v[i] = lt[e];
+    }
+    uint64_t key[NPL];
+    uint32_t lmax = 0u;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? (((uint64_t)order_bits(v[i]) << 32) | (0xffffffffu - (uint32_t)e))
+                         : 0ull;                       // padding keys lose to every id
+        const uint32_t h = (uint32_t)(key[i] >> 32);
+        lmax = h > lmax ? h : lmax;
+    }
+    // T: the largest value with at least k lane maxima >= T
+    uint32_t T = 0u;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = T | (1u << b);
+        if (__popcll(__ballot(lmax >= c)) >= k) T = c;
+    }
+    uint64_t bal[NPL];
+    int C = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        bal[i] = __ballot((uint32_t)(key[i] >> 32) >= T);
+        C += __popcll(bal[i]);
+    }
+    uint64_t mine;
+    if (C <= 64) {
+        // compaction in (i, lane) order
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            if ((bal[i] >> lane) & 1ull)
+                scratch[base + __popcll(bal[i] & ((1ull << lane) - 1ull))] = key[i];
+            base += __popcll(bal[i]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // rank of candidate `lane` among the C candidates (keys are unique)
+        const uint64_t ck = lane < C ? scratch[lane] : 0ull;
+        int rank = 0;
+        for (int c = 0; c < C; ++c) rank += scratch[c] > ck ? 1 : 0;
+        if (lane < C && rank < k) scratch[64 + rank] = ck;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        mine = lane < k ? scratch[64 + lane] : 0ull;
+    } else {
+        mine = select_serial<NPL>(key, k);
+    }
     // weights: softmax over the k selected logits in fp32, shifted by the largest
     const uint32_t my_hi = (uint32_t)(mine >> 32), my_lo = (uint32_t)mine;
     const uint32_t vbits = (my_hi & 0x80000000u) ? (my_hi & 0x7fffffffu) : ~my_hi;
