@@ -51,21 +51,23 @@ struct GuShape {
     static constexpr int RPB = GU_WAVES * (64 / LPR);   // rows per block
 };
 
-constexpr int NTHREADS = 256;
-
-// ---- down: 4 output rows per block (one per wave) for every slot, then their combine.
-// A row's K = d_ff codes are read by LPR lanes exactly as in gemv_rows; the 64 / LPR lane
-// groups of a wave take different slots of the same row.
+// ---- down: 4 output rows per block for every slot, then their combine.  16 waves: wave w
+// takes row w % 4 and every 4th wave load of that row (part w / 4).  A row's K = d_ff
+// codes are read by LPR lanes exactly as in gemv_rows; the 64 / LPR lane groups of a wave
+// take different slots of the same row.
+constexpr int DN_WAVES = 16;
+constexpr int DN_THREADS = DN_WAVES * 64;
 template <int F>
 struct DnShape {
     static constexpr int LPR = Shape<F>::LPR;
     static constexpr int GPL = Shape<F>::GPL;
     static constexpr int NG = 64 / LPR;          // slots per wave load
-    static constexpr int ROWS = NTHREADS / 64;   // rows per block
-    // wave loads in registers at once: enough for 12 slots (one token with 10 experts and
-    // the shared one) in one batch, or a larger batch for more slots
-    static constexpr int ITB_SMALL = (12 + NG - 1) / NG;
-    static constexpr int ITB_LARGE = NG >= 4 ? 6 : 8;
+    static constexpr int ROWS = 4;               // rows per block
+    static constexpr int SPLIT = DN_WAVES / ROWS;   // waves per row
+    // wave loads per wave in registers at once: one when every slot fits in one load per
+    // wave (a token with 10 experts and the shared one), else a batch of 4
+    static constexpr int ITB_SMALL = 1;
+    static constexpr int ITB_LARGE = 4;
 };
 
 template <int FMT, int D, int F, int ITB>
@@ -76,9 +78,11 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     constexpr int GB = Fmt<FMT>::kGroupBytes;
     constexpr size_t ROW_BYTES = (size_t)F / 32 * GB;
     constexpr int NGRP = F / 32;                 // groups per h row
+    constexpr int SPLIT = DS::SPLIT;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rw = wave % DS::ROWS, part = wave / DS::ROWS;
     const int gp = lane % LPR, sub = lane / LPR;
-    const int row = r0 + wave;                   // < D: D is a multiple of DS::ROWS
+    const int row = r0 + rw;                     // < D: D is a multiple of DS::ROWS
     const int P = a.T * a.k;
     // LDS: h rows [S][F] bf16 | group sums of h [S][NGRP] | y [S][ROWS] | gate weights [64]
     uint16_t* h_lds = reinterpret_cast<uint16_t*>(lds);
@@ -94,7 +98,7 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     const float gate_w = a.weights[min((int)threadIdx.x, P - 1)];
     const uint16_t* res_src = a.residual ? a.residual : a.x;   // x: same shape, unused
     const uint16_t res_bits = res_src[(size_t)min(lane, a.T - 1) * D + row];
-    constexpr int kHPass = 4;
+    constexpr int kHPass = 2;
     const int n16 = S * F / 8;                    // 16-byte chunks of h
     // native 4-vectors: an array of HIP's uint4 struct is not kept in registers
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -102,17 +106,19 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     u32x4* hdst = reinterpret_cast<u32x4*>(h_lds);
     u32x4 hv[kHPass];
 #pragma unroll
-    for (int u = 0; u < kHPass; ++u) hv[u] = hsrc[min(u * NTHREADS + (int)threadIdx.x, n16 - 1)];
+    for (int u = 0; u < kHPass; ++u)
+        hv[u] = hsrc[min(u * DN_THREADS + (int)threadIdx.x, n16 - 1)];
     my_e = (lane < P && my_e >= 0 && my_e < a.E) ? my_e : 0;
 
     GroupBits<FMT> wbits[ITB][GPL];
     uint16_t sbits[ITB][GPL];
-    // wave loads it0 .. it0 + ITB - 1: slot it * NG + sub (slots past S - 1 repeat slot
-    // S - 1, so every load is unconditional and in bounds)
-    auto load_batch = [&](int it0) __attribute__((always_inline)) {
+    // this wave's loads l0 .. l0 + ITB - 1: wave load part + SPLIT * l of the row, slot
+    // (part + SPLIT * l) * NG + sub (slots past S - 1 repeat slot S - 1, so every load is
+    // unconditional and in bounds)
+    auto load_batch = [&](int l0) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < ITB; ++q) {
-            const int s = min((it0 + q) * NG + sub, S - 1);
+            const int s = min((part + SPLIT * (l0 + q)) * NG + sub, S - 1);
             const int e = __shfl(my_e, s, 64);
             const uint8_t* wb;
             const uint16_t* sb;
@@ -134,11 +140,11 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     };
     // the ITB dot products are independent chains: all of them first (one basic block,
     // so their latencies overlap), then the row sums and the stores
-    auto compute_batch = [&](int it0) __attribute__((always_inline)) {
+    auto compute_batch = [&](int l0) __attribute__((always_inline)) {
         float acc[ITB];
 #pragma unroll
         for (int q = 0; q < ITB; ++q) {
-            const int s = min((it0 + q) * NG + sub, S - 1);
+            const int s = min((part + SPLIT * (l0 + q)) * NG + sub, S - 1);
             acc[q] = 0.0f;
 #pragma unroll
             for (int i = 0; i < GPL; ++i) {
@@ -163,42 +169,45 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
         for (int q = 0; q < ITB; ++q) yv[q] = bf16_to_f32(f32_to_bf16(group_sum<LPR>(acc[q])));
 #pragma unroll
         for (int q = 0; q < ITB; ++q) {
-            const int s_raw = (it0 + q) * NG + sub;
-            if (gp == 0 && s_raw < S) y_lds[s_raw * DS::ROWS + wave] = yv[q];
+            const int s_raw = (part + SPLIT * (l0 + q)) * NG + sub;
+            if (gp == 0 && s_raw < S) y_lds[s_raw * DS::ROWS + rw] = yv[q];
         }
     };
 
-    const int n_it = (S + NG - 1) / NG;
+    // wave loads of this wave: part, part + SPLIT, ... below ceil(S / NG)
+    const int n_l = ((S + NG - 1) / NG - part + SPLIT - 1) / SPLIT;
     load_batch(0);
     __builtin_amdgcn_sched_barrier(0);
     if (threadIdx.x < P) w_lds[threadIdx.x] = gate_w;
     // h rows -> LDS.  An index past the end is clamped to the last chunk, which then
     // stores the same value twice: no branch, so no wait per chunk.
 #pragma unroll
-    for (int u = 0; u < kHPass; ++u) hdst[min(u * NTHREADS + (int)threadIdx.x, n16 - 1)] = hv[u];
-    for (int c0 = kHPass * NTHREADS; c0 < n16; c0 += kHPass * NTHREADS) {
+    for (int u = 0; u < kHPass; ++u)
+        hdst[min(u * DN_THREADS + (int)threadIdx.x, n16 - 1)] = hv[u];
+    for (int c0 = kHPass * DN_THREADS; c0 < n16; c0 += kHPass * DN_THREADS) {
         u32x4 hw[kHPass];
 #pragma unroll
         for (int u = 0; u < kHPass; ++u)
-            hw[u] = hsrc[min(c0 + u * NTHREADS + (int)threadIdx.x, n16 - 1)];
+            hw[u] = hsrc[min(c0 + u * DN_THREADS + (int)threadIdx.x, n16 - 1)];
 #pragma unroll
         for (int u = 0; u < kHPass; ++u)
-            hdst[min(c0 + u * NTHREADS + (int)threadIdx.x, n16 - 1)] = hw[u];
+            hdst[min(c0 + u * DN_THREADS + (int)threadIdx.x, n16 - 1)] = hw[u];
     }
     __syncthreads();
     // group sums of h, once per (slot, group), in group_sum_x's order
-    for (int i = threadIdx.x; i < S * NGRP; i += NTHREADS)
+    for (int i = threadIdx.x; i < S * NGRP; i += DN_THREADS)
         sx_lds[i] = group_sum_x(reinterpret_cast<const uint32_t*>(h_lds + (size_t)i * 32));
     __syncthreads();
-    for (int it0 = 0; it0 < n_it; it0 += ITB) {
-        if (it0 > 0) load_batch(it0);
-        compute_batch(it0);
+    for (int l0 = 0; l0 < n_l; l0 += ITB) {
+        if (l0 > 0) load_batch(l0);
+        compute_batch(l0);
     }
     __syncthreads();
 
-    // combine: lane t of each wave, token t of the wave's row, in combine8's order of
+    // combine: lane t of the row's first wave, token t of the row, in combine8's order of
     // operations
-    const float* y = y_lds + wave;
+    if (part != 0) return;
+    const float* y = y_lds + rw;
     for (int t = lane; t < a.T; t += 64) {
         float acc = 0.0f;
         for (int j0 = 0; j0 < a.k; j0 += 8) {
@@ -292,7 +301,7 @@ __global__ void __launch_bounds__(GU_WAVES * 64) decode_gateup_kernel(DecodeArgs
 }
 
 template <int FMT, int D, int F, int ITB>
-__global__ void __launch_bounds__(NTHREADS) decode_down_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(DN_THREADS) decode_down_kernel(DecodeArgs a) {
     const int S = a.T * a.k + (a.sg ? a.T : 0);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     down_rows_combine<FMT, D, F, ITB>(a, blockIdx.x * DnShape<F>::ROWS, S, lds);
@@ -326,7 +335,7 @@ hipError_t launch_itb(const DecodeArgs& a, hipStream_t s) {
         decode_gateup_kernel<FMT, D, F, 16><<<S * n_gu, GU_WAVES * 64, 0, s>>>(a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    decode_down_kernel<FMT, D, F, ITB><<<n_dn, NTHREADS, lds, s>>>(a);
+    decode_down_kernel<FMT, D, F, ITB><<<n_dn, DN_THREADS, lds, s>>>(a);
     return hipGetLastError();
 }
 
@@ -334,7 +343,7 @@ template <int FMT, int D, int F>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
     using DS = DnShape<F>;
     const int S = a.T * a.k + (a.sg ? a.T : 0);
-    if (S <= DS::ITB_SMALL * DS::NG) return launch_itb<FMT, D, F, DS::ITB_SMALL>(a, s);
+    if (S <= DS::SPLIT * DS::NG) return launch_itb<FMT, D, F, DS::ITB_SMALL>(a, s);
     return launch_itb<FMT, D, F, DS::ITB_LARGE>(a, s);
 }
 
