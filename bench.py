@@ -42,6 +42,7 @@ def parse():
                    help="distinct layer copies rotated through (defeats the 256 MB MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="skip the 48-layer decode sweep")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="no graph capture (for profilers)")
     return p.parse_args()
@@ -197,9 +198,17 @@ def main():
                      "avg_launch_us": round(ms_exp * 1e3, 3)},
     }
 
-    # ---- prefill: 8192 tokens, Zipf routing, one layer
+    # ---- 48 chained layers, 1 and 4 tokens per step
+    if not args.no_sweep:
+        line["decode_sweep"] = decode_sweep(moe, synth, np, torch, args)
+        torch.cuda.empty_cache()
+
+    # ---- prefill: 8192 tokens Zipf; 32768 tokens mixed precision, Zipf and uniform
     if not args.no_prefill:
-        line["prefill"] = prefill_bench(moe, synth, np, torch)
+        line["prefill"] = prefill_bench(moe, synth, np, torch, "prefill_8192_zipf", None)
+        torch.cuda.empty_cache()
+        line["prefill_32k"] = [prefill_bench(moe, synth, np, torch, "prefill_32768_mixed", b)
+                               for b in ("zipf", "none")]
 
     # ---- CPU oracle on a bounded sample of the decode workload
     if not args.no_cpu_baseline:
@@ -208,9 +217,46 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def prefill_bench(moe, synth, np, torch):
-    w = synth.WORKLOADS["prefill_8192_zipf"]
-    lay = synth.make_layer(w, seed=0, device="cuda")
+def decode_sweep(moe, synth, np, torch, args):
+    """48 distinct layers chained through the residual, x_{l+1} = bf16(x_l + out_l), one
+    token and four tokens (one real + three drafts) per step; the whole 48-layer step is
+    one graph.  Weights: 48 x 0.91 GB resident, so no cache holds them between steps."""
+    w = synth.WORKLOADS["decode_sweep_48_layers"]
+    lays = [synth.make_layer(w, seed=0, layer=l, device="cuda") for l in range(w.layers)]
+    E_b = expert_bytes(lays[0].routed)
+    r_b = lays[0].router.w.numel() * lays[0].router.w.element_size()
+    out = {"workload": "decode_sweep_48_layers", "layers": w.layers, "router_bias": "zipf"}
+    for T in (1, 4):
+        mls = [moe.MoeLayer(L.router, L.routed, L.shared, w.k, T) for L in lays]
+        xs = [synth.make_tokens(w, T=T, seed=0, device="cuda")]
+        xs += [torch.empty_like(xs[0]) for _ in range(w.layers)]
+
+        def step():
+            for l in range(w.layers):
+                mls[l].decode(xs[l], residual=xs[l], out=xs[l + 1])
+
+        step()
+        torch.cuda.synchronize()
+        moe.moe_check_device_error()
+        # distinct routed experts per layer (the bytes a step must stream)
+        U = [int(np.unique(m.ids[:T].cpu().numpy()).size) for m in mls]
+        reps = max(4, args.steps // (8 * w.layers))
+        ms = time_graph(step, reps, 2)[0]
+        bytes_step = sum(r_b + (u + 1) * E_b + 2 * T * w.d * 2 for u in U)
+        out["T%d" % T] = {"tokens_per_s": round(T / (ms * 1e-3), 1),
+                          "ms_per_step": round(ms, 4),
+                          "us_per_layer": round(ms * 1e3 / w.layers, 3),
+                          "distinct_experts_per_layer_mean": round(float(np.mean(U)), 2),
+                          "alg_bytes_per_step": bytes_step,
+                          "weight_stream_GBps": round(bytes_step / (ms * 1e-3) / 1e9, 1)}
+        del mls, xs
+    del lays
+    return out
+
+
+def prefill_bench(moe, synth, np, torch, name, bias):
+    w = synth.WORKLOADS[name]
+    lay = synth.make_layer(w, seed=0, device="cuda", bias=bias)
     x = synth.make_tokens(w, seed=0, device="cuda")
     layer = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, w.T)
     layer.forward(x)
@@ -237,7 +283,8 @@ def prefill_bench(moe, synth, np, torch):
     ms_gemm = t0.elapsed_time(t1) / reps
     flops = 6.0 * P * w.d * w.F
     counts = np.diff(layer.offsets.cpu().numpy())
-    return {"workload": "prefill_8192_zipf", "tokens": w.T,
+    del layer, lay
+    return {"workload": name, "router_bias": bias or w.bias, "tokens": w.T,
             "tokens_per_s": round(w.T / (ms_layer * 1e-3), 1),
             "ms_layer": round(ms_layer, 4), "ms_routed_grouped_gemm": round(ms_gemm, 4),
             "routed_gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
