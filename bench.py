@@ -22,6 +22,7 @@ Also reported in the same line:
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +32,35 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+# Counter-measured memory traffic of moe_experts_decode, taken by two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE) and scaled by the same counters on a copy of known size; the
+# summary records a digest of the kernel sources it was measured on.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_experts_traffic.md")
+TRAFFIC_SOURCES = ["decode.hip", "gemv_common.h", "topk_common.h", "combine_common.h",
+                   "moe_common.h"]
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "quantized_sparse_moe_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per moe_experts_decode call from the committed counter summary, or None when
+    it is missing or was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(traffic_bytes_per_launch|source_digest): *(\S+)$", text, re.M))
+    if vals.get("source_digest") != kernel_source_digest():
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -45,6 +75,9 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the 48-layer decode sweep")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="no graph capture (for profilers)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only copy 256 MiB device to device 8 times (calibrates the memory "
+                        "traffic counters against a transfer of known size), then exit")
     return p.parse_args()
 
 
@@ -100,6 +133,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 8}), flush=True)
+        return
 
     import quantized_sparse_moe_router_amd as moe
     import synth
@@ -193,7 +236,7 @@ def main():
                      "kernel": "decode_gateup_kernel + decode_down_kernel (moe_experts_decode:"
                                " 10 routed + 1 shared expert FFN and combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "alg_bytes_per_launch": alg_bytes_exp,
                      "avg_launch_us": round(ms_exp * 1e3, 3)},
     }
