@@ -42,11 +42,16 @@ TRAFFIC_SOURCES = ["decode.hip", "gemv_common.h", "topk_common.h", "combine_comm
 
 
 def kernel_source_digest():
+    """Digest of the kernel sources with comments and whitespace removed, so that only a
+    change of the code itself marks the counter summary as stale."""
     import hashlib
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "quantized_sparse_moe_router_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_sparse_moe_router_amd", "csrc", f)) as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -59,8 +59,7 @@ enum {
     MOE_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for */
     MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than moe_workspace_size */
     MOE_ERR_HIP = -4,           /* a HIP runtime call failed (launch, sync, copy) */
-    MOE_ERR_DEVICE = -5         /* a kernel reported bad data (expert id out of range) or a
-                                   bounded wait that timed out */
+    MOE_ERR_DEVICE = -5         /* a kernel reported bad data (expert id out of range) */
 };
 
 enum { MOE_FMT_FP32 = 0, MOE_FMT_INT8_ROW = 1, MOE_FMT_INT4_G32 = 2, MOE_FMT_INT6_G32 = 3 };
@@ -225,8 +224,7 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
                           int32_t d_ff);
 
 /* Synchronises `stream`, then reports and clears the current device's error flag:
- * MOE_ERR_DEVICE if, since the last check, a kernel saw an expert id outside [0, E) or a
- * kernel's bounded wait for another block's results timed out. */
+ * MOE_ERR_DEVICE if, since the last check, a kernel saw an expert id outside [0, E). */
 moe_status moe_check_device_error(void* stream);
 
 /* Static text for a status code. */

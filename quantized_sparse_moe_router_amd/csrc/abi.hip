@@ -339,7 +339,7 @@ moe_status moe_check_device_error(void* stream) {
     e = moe::read_and_clear_device_error(&flag);
     if (e != hipSuccess) return hip_status(e, "moe_check_device_error: read flag");
     if (flag & 1) return fail(MOE_ERR_DEVICE, "an expert id outside [0, E) was seen");
-    if (flag) return fail(MOE_ERR_DEVICE, "a kernel's bounded wait timed out");
+    if (flag) return fail(MOE_ERR_DEVICE, "device error flag 0x%x", flag);
     return ok();
 }
 

@@ -84,8 +84,8 @@ namespace moe {
 // first use; every call leaves it zero.
 constexpr size_t kRouteCounterBytes = 256;
 
-// Device error word (per device): bit 0 = expert id out of range, bit 1 = a bounded wait
-// timed out.  Returns its device address for the current device.
+// Device error word (per device): bit 0 = expert id out of range.  Returns its device
+// address for the current device.
 int* device_error_flag();
 hipError_t read_and_clear_device_error(int* flag);
 

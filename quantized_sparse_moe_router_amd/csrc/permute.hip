@@ -16,7 +16,7 @@
 namespace moe {
 
 // Device error word: bit 0 is raised by any kernel that meets an expert id outside
-// [0, E), bit 1 by a bounded wait that timed out.
+// [0, E).
 static __device__ int g_bad_id_flag;
 
 namespace {
