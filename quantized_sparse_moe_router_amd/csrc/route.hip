@@ -92,158 +92,183 @@ __device__ __forceinline__ void router_gemv_rows(
 }
 
 // ------------------------------------------------------------------ many tokens: GEMM
-// A 64-token x 64-expert tile per block of 256 threads; each thread owns 4 tokens x 4
-// experts.  The reduction is walked lane by lane of the contract's 64 virtual lanes:
-// for virtual lane l the thread runs the fma chain over that lane's EL elements (in the
-// contract's order), then folds the lane sum into a 6-deep pairwise stack, which
-// reproduces the butterfly's tree ((a0+a1)+(a2+a3))+... exactly.
-// The chunk staged in LDS holds KC = 64 chain elements = LC virtual lanes.
-constexpr int RT_TM = 64, RT_TE = 64, RT_KC = 64;
+// The contract's reduction laid out across a wave: lane l runs virtual lane l's fma chain
+// (its vectors l + 64 j, elements in order) for every (token, expert) of the wave's tile,
+// so each chain is a plain register accumulator; at the end the 64 lane sums of each
+// output go through LDS and are added in the contract's tree (pairs of lanes, then pairs
+// of pairs, ...), which is the butterfly's tree.
+// Block = 8 waves, 4 along tokens x 2 along experts; wave tile TW tokens x EW experts.
+// Step j stages the 64 vectors of index j (a contiguous slice of the reduction dim) of
+// the block's token and expert rows in LDS, double-buffered; a step is taken in quarters
+// of 4 elements per lane (one quarter for fp32 vectors, four for int8 vectors).
+template <int FMT>
+struct RgShape {
+    static constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;   // elements per vector
+    static constexpr int NQ = PV / 4;                                // quarters per step
+    static constexpr int TW = (FMT == MOE_FMT_INT8_ROW) ? 4 : 8;     // tokens per wave
+    static constexpr int EW = (FMT == MOE_FMT_INT8_ROW) ? 16 : 12;   // experts per wave
+    static constexpr int BT = 4 * TW, BE = 2 * EW;                   // block tile
+    static constexpr int WB = (FMT == MOE_FMT_INT8_ROW) ? 1 : 4;     // bytes per weight
+    // one stage: x [BT][NQ][64][4] bf16, then W [BE][NQ][64][4]
+    static constexpr int XS = BT * 64 * PV * 2;
+    static constexpr int WS = BE * 64 * PV * WB;
+    static constexpr int STAGE = XS + WS;
+    static constexpr int RS = 68;          // reduction scratch row stride (floats)
+    static_assert(8 * 32 * RS * 4 <= 2 * STAGE, "reduction scratch fits in the stages");
+};
 
 template <int FMT, int NV>
-__global__ void __launch_bounds__(256) router_gemm_kernel(
+__global__ void __launch_bounds__(512) router_gemm_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
     float* __restrict__ logits) {
-    constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
-    constexpr int EL = NV * PV;          // chain elements per virtual lane
-    constexpr int LC = RT_KC / EL;       // virtual lanes per chunk
-    static_assert(RT_KC % EL == 0, "lane chain must divide the chunk");
+    using R = RgShape<FMT>;
+    constexpr int PV = R::PV, NQ = R::NQ, TW = R::TW, EW = R::EW, BT = R::BT, BE = R::BE;
+    constexpr int SL = 64 * PV;                       // slice elements per step
+    constexpr int XCH = BT * SL / 8 / 512;            // 16-byte x chunks per thread
+    constexpr int WCH = BE * SL * R::WB / 16 / 512;   // 16-byte W chunks per thread
+    static_assert(XCH >= 1 && WCH >= 1, "every thread stages whole chunks");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
+    const int tw0 = (wave >> 1) * TW, ew0 = (wave & 1) * EW;   // wave tile inside the block
 
-    __shared__ float xs[RT_KC][RT_TM];
-    __shared__ float ws[RT_KC][RT_TE];
+    // ---- staging: this thread's chunks of step j -> registers; registers -> LDS stage
+    // native 4-vectors: an array of HIP's uint4 struct is not kept in registers
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x4 xr[XCH], wr[WCH];
+    auto load_step = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < XCH; ++u) {
+            const int c = tid + 512 * u, row = c / (SL / 8), cc = c % (SL / 8);
+            const int t = min(t0 + row, T - 1);
+            xr[u] = *reinterpret_cast<const u32x4*>(x + (size_t)t * d + (size_t)SL * j + 8 * cc);
+        }
+#pragma unroll
+        for (int u = 0; u < WCH; ++u) {
+            constexpr int CPR = SL * R::WB / 16;      // chunks per W row
+            const int c = tid + 512 * u, row = c / CPR, cc = c % CPR;
+            const int e = min(e0 + row, E - 1);
+            wr[u] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(W) +
+                                                    ((size_t)e * d + (size_t)SL * j) * R::WB +
+                                                    16 * cc);
+        }
+    };
+    auto store_step = [&](int st) __attribute__((always_inline)) {
+        uint8_t* xs = smem + st * R::STAGE;
+        uint8_t* ws = xs + R::XS;
+#pragma unroll
+        for (int u = 0; u < XCH; ++u) {
+            const int c = tid + 512 * u, row = c / (SL / 8), cc = c % (SL / 8);
+            if constexpr (PV == 4) {
+                // elements 8 cc .. 8 cc + 7 = lanes 2 cc, 2 cc + 1, quarter 0
+                *reinterpret_cast<u32x4*>(xs + ((row * 64 + 2 * cc) * 4) * 2) = xr[u];
+            } else {
+                // lane cc / 2, quarters 2 (cc % 2) and 2 (cc % 2) + 1
+                const int l = cc >> 1, q0 = 2 * (cc & 1);
+                *reinterpret_cast<u32x2*>(xs + (((row * NQ + q0) * 64 + l) * 4) * 2) =
+                    u32x2{xr[u].x, xr[u].y};
+                *reinterpret_cast<u32x2*>(xs + (((row * NQ + q0 + 1) * 64 + l) * 4) * 2) =
+                    u32x2{xr[u].z, xr[u].w};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < WCH; ++u) {
+            constexpr int CPR = SL * R::WB / 16;
+            const int c = tid + 512 * u, row = c / CPR, cc = c % CPR;
+            if constexpr (PV == 4) {
+                // fp32: 4 elements = lane cc, quarter 0
+                *reinterpret_cast<u32x4*>(ws + ((row * 64 + cc) * 4) * 4) = wr[u];
+            } else {
+                // int8: 16 elements = lane cc, quarters 0..3, 4 bytes each
+                const uint32_t v[4] = {wr[u].x, wr[u].y, wr[u].z, wr[u].w};
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    *reinterpret_cast<uint32_t*>(ws + ((row * NQ + q) * 64 + cc) * 4) = v[q];
+            }
+        }
+    };
 
-    const int tid = threadIdx.x;
-    const int tx = tid & 15, ty = tid >> 4;
-    const int t0 = blockIdx.x * RT_TM, e0 = blockIdx.y * RT_TE;
+    float acc[TW][EW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int e = 0; e < EW; ++e) acc[t][e] = 0.0f;
 
-    float stk[6][4][4];
-    float acc[4][4];
-
-    // staging: (row, j) pieces of LC*PV contiguous elements
-    constexpr int PIECE = LC * PV;       // elements per piece
-    constexpr int PIECES = NV;           // pieces per row per chunk
-
-    for (int l0 = 0; l0 < 64; l0 += LC) {
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    for (int j = 0; j < NV; ++j) {
+        const int st = j & 1;
+        if (j + 1 < NV) load_step(j + 1);
+        const uint8_t* xs = smem + st * R::STAGE;
+        const uint8_t* ws = xs + R::XS;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            float xv[TW][4];
+#pragma unroll
+            for (int t = 0; t < TW; ++t) {
+                const uint2 p = *reinterpret_cast<const uint2*>(
+                    xs + ((((tw0 + t) * NQ + q) * 64 + lane) * 4) * 2);
+                xv[t][0] = bf16lo(p.x); xv[t][1] = bf16hi(p.x);
+                xv[t][2] = bf16lo(p.y); xv[t][3] = bf16hi(p.y);
+            }
+#pragma unroll
+            for (int e = 0; e < EW; ++e) {
+                float wv[4];
+                if constexpr (PV == 4) {
+                    const float4 f = *reinterpret_cast<const float4*>(
+                        ws + (((ew0 + e) * 64 + lane) * 4) * 4);
+                    wv[0] = f.x; wv[1] = f.y; wv[2] = f.z; wv[3] = f.w;
+                } else {
+                    const uint32_t b = *reinterpret_cast<const uint32_t*>(
+                        ws + (((ew0 + e) * NQ + q) * 64 + lane) * 4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) wv[r] = (float)(int8_t)((b >> (8 * r)) & 0xffu);
+                }
+#pragma unroll
+                for (int t = 0; t < TW; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[t][e] = __builtin_fmaf(xv[t][r], wv[r], acc[t][e]);
+            }
+        }
+        if (j + 1 < NV) store_step(st ^ 1);
         __syncthreads();
-        // x tile: RT_TM rows x PIECES pieces of PIECE bf16
-        for (int q = tid; q < RT_TM * PIECES * (PIECE / 4); q += 256) {
-            const int r = q / (PIECES * (PIECE / 4));
-            const int rem = q % (PIECES * (PIECE / 4));
-            const int j = rem / (PIECE / 4);
-            const int c4 = rem % (PIECE / 4);               // 4-element slot in the piece
-            const int t = t0 + r;
-            uint2 v = make_uint2(0u, 0u);
-            const int cbase = (l0 + 64 * j) * PV + 4 * c4;
-            if (t < T) v = *reinterpret_cast<const uint2*>(x + (size_t)t * d + cbase);
-            // element e_in_piece = 4*c4 + i belongs to virtual lane l0 + (4*c4+i)/PV at
-            // chain position j*PV + (4*c4+i)%PV
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ep = 4 * c4 + i;
-                const int kk = (ep / PV) * EL + j * PV + (ep % PV);
-                const uint32_t word = (i < 2) ? v.x : v.y;
-                xs[kk][r] = (i & 1) ? bf16hi(word) : bf16lo(word);
-            }
-        }
-        // w tile
-        if constexpr (FMT == MOE_FMT_INT8_ROW) {
-            for (int q = tid; q < RT_TE * PIECES * (PIECE / 4); q += 256) {
-                const int r = q / (PIECES * (PIECE / 4));
-                const int rem = q % (PIECES * (PIECE / 4));
-                const int j = rem / (PIECE / 4);
-                const int c4 = rem % (PIECE / 4);
-                const int e = e0 + r;
-                uint32_t v = 0u;
-                const int cbase = (l0 + 64 * j) * PV + 4 * c4;
-                if (e < E)
-                    v = *reinterpret_cast<const uint32_t*>(static_cast<const int8_t*>(W) +
-                                                           (size_t)e * d + cbase);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ep = 4 * c4 + i;
-                    const int kk = (ep / PV) * EL + j * PV + (ep % PV);
-                    ws[kk][r] = (float)(int8_t)((v >> (8 * i)) & 0xffu);
-                }
-            }
-        } else {
-            for (int q = tid; q < RT_TE * PIECES * (PIECE / 4); q += 256) {
-                const int r = q / (PIECES * (PIECE / 4));
-                const int rem = q % (PIECES * (PIECE / 4));
-                const int j = rem / (PIECE / 4);
-                const int c4 = rem % (PIECE / 4);
-                const int e = e0 + r;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                const int cbase = (l0 + 64 * j) * PV + 4 * c4;
-                if (e < E)
-                    v = *reinterpret_cast<const float4*>(static_cast<const float*>(W) +
-                                                         (size_t)e * d + cbase);
-                const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ep = 4 * c4 + i;
-                    const int kk = (ep / PV) * EL + j * PV + (ep % PV);
-                    ws[kk][r] = vv[i];
-                }
-            }
-        }
-        __syncthreads();
-
-#pragma unroll
-        for (int ll = 0; ll < LC; ++ll) {
-            const int l = l0 + ll;
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
-#pragma unroll 8
-            for (int kk = ll * EL; kk < (ll + 1) * EL; ++kk) {
-                const float4 xv = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
-                const float4 wv = *reinterpret_cast<const float4*>(&ws[kk][tx * 4]);
-                const float xa[4] = {xv.x, xv.y, xv.z, xv.w};
-                const float wa[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        acc[a][b] = __builtin_fmaf(xa[a], wa[b], acc[a][b]);
-            }
-            // fold lane l's sum into the pairwise stack
-            const int nlev = __builtin_ctz(~l);   // trailing one bits of l
-#pragma unroll
-            for (int lev = 0; lev < 6; ++lev) {
-                if (lev < nlev) {
-#pragma unroll
-                    for (int a = 0; a < 4; ++a)
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) acc[a][b] = stk[lev][a][b] + acc[a][b];
-                }
-            }
-#pragma unroll
-            for (int lev = 0; lev < 6; ++lev) {
-                if (lev == nlev) {
-#pragma unroll
-                    for (int a = 0; a < 4; ++a)
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) stk[lev][a][b] = acc[a][b];
-                }
-            }
-        }
     }
-    // after l = 63 the full tree sum is in acc (nlev = 6 -> not stored)
+
+    // ---- the 64 lane sums of each output, in the tree, 32 outputs at a time: lane L
+    // adds lanes 32 (L / 32) .. + 31 of output L % 32 pairwise, then the two halves
+    float* scr = reinterpret_cast<float*>(smem) + wave * 32 * R::RS;
+    const int ol = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int t = t0 + ty * 4 + a;
-        if (t >= T) continue;
+    for (int c0 = 0; c0 < TW * EW; c0 += 32) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int e = e0 + tx * 4 + b;
-            if (e >= E) continue;
-            float l = acc[a][b];
+        for (int i = 0; i < 32; ++i) scr[i * R::RS + lane] = acc[(c0 + i) / EW][(c0 + i) % EW];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float v[32];
+#pragma unroll
+        for (int m = 0; m < 32; m += 4) {
+            const float4 f = *reinterpret_cast<const float4*>(scr + ol * R::RS + 32 * half + m);
+            v[m] = f.x; v[m + 1] = f.y; v[m + 2] = f.z; v[m + 3] = f.w;
+        }
+#pragma unroll
+        for (int w = 1; w < 32; w <<= 1)
+#pragma unroll
+            for (int m = 0; m < 32; m += 2 * w) v[m] = v[m] + v[m + w];
+        const float other = __shfl_xor(v[0], 32, 64);
+        const float sum = v[0] + other;
+        const int o = c0 + ol, t = t0 + tw0 + o / EW, e = e0 + ew0 + o % EW;
+        if (half == 0 && t < T && e < E) {
+            float l = sum;
             if constexpr (FMT == MOE_FMT_INT8_ROW) l = l * f16_to_f32(scale[e]);
             if (bias) l = l + bias[e];
             logits[(size_t)t * E + e] = l;
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -325,9 +350,24 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
 #undef MOE_GT
         return hipGetLastError();
     }
-    router_gemm_kernel<FMT, NV>
-        <<<dim3((T + RT_TM - 1) / RT_TM, (E + RT_TE - 1) / RT_TE), dim3(256), 0, s>>>(
-            r.w, r.scale, r.bias, x, T, E, d, logits);
+    {
+        using R = RgShape<FMT>;
+        constexpr int kLds = 2 * R::STAGE;
+        constexpr int kMaxDev = 64;
+        static bool attr_set[kMaxDev] = {};
+        int dev = 0;
+        hipError_t err = hipGetDevice(&dev);
+        if (err != hipSuccess) return err;
+        if (dev >= kMaxDev || !attr_set[dev]) {   // more than 64 KiB of LDS: opt in once
+            err = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_gemm_kernel<FMT, NV>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+            if (err != hipSuccess) return err;
+            if (dev < kMaxDev) attr_set[dev] = true;
+        }
+        router_gemm_kernel<FMT, NV>
+            <<<dim3((T + R::BT - 1) / R::BT, (E + R::BE - 1) / R::BE), dim3(512), kLds, s>>>(
+                r.w, r.scale, r.bias, x, T, E, d, logits);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const dim3 grid((T + 3) / 4), block(256);
@@ -349,10 +389,10 @@ hipError_t launch_fmt(const moe_router& r, const uint16_t* x, int T, int k, int3
                       float* weights, float* logits, unsigned* counter, hipStream_t s) {
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
     const int nv = r.d_model / (64 * PV);
-    // chain length per lane must divide the GEMM kernel's 64-element chunk
+    // at most 64 chain elements per lane (the few-token kernel holds them in registers)
 #define MOE_NV(N)                                                                         \
     if (nv == N) {                                                                        \
-        if constexpr (RT_KC % (N * PV) == 0)                                              \
+        if constexpr (N * PV <= 64)                                                       \
             return launch_nv<FMT, N>(r, x, T, k, ids, weights, logits, counter, s);       \
         else                                                                              \
             return hipErrorInvalidValue;                                                  \
