@@ -258,6 +258,10 @@ def main():
         line["prefill_32k"] = [prefill_bench(moe, synth, np, torch, "prefill_32768_mixed", b)
                                for b in ("zipf", "none")]
 
+    # ---- what this chip reaches on plain work, for context next to the spec peaks
+    if not args.no_prefill:
+        line["achievable"] = achievable_peaks(torch)
+
     # ---- CPU oracle on a bounded sample of the decode workload
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(base, toks, w, args.cpu_seconds)
@@ -338,6 +342,34 @@ def prefill_bench(moe, synth, np, torch, name, bias):
             "routed_gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
             "mfma_util": round(flops / (ms_gemm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "active_experts": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())}
+
+
+def achievable_peaks(torch):
+    """Measured ceilings of plain library work on this GPU: a 2 GiB fp32 reduction (HBM
+    read) and torch's dense bf16 matmul at the routed GEMMs' shapes for 8192 tokens (81920
+    pair rows; gate+up K=2048/N=1024, down K=512/N=2048)."""
+    def timed_ms(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+    out = {}
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    out["hbm_read_GBps_torch_sum"] = round(x.numel() * 4 / (timed_ms(lambda: x.sum()) * 1e6), 1)
+    del x
+    for name, (M, K, N) in (("gateup", (81920, 2048, 1024)), ("down", (81920, 512, 2048))):
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+        b = torch.randn((K, N), generator=g, device="cuda").to(torch.bfloat16)
+        ms = timed_ms(lambda: a @ b)
+        out["dense_bf16_matmul_tflops_%s" % name] = round(2.0 * M * K * N / (ms * 1e9), 1)
+        del a, b
+    return out
 
 
 def cpu_baseline(base, toks, w, seconds):
