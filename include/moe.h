@@ -185,18 +185,20 @@ moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const f
  * result, bit for bit, as
  *     moe_route -> moe_permute -> moe_expert_ffn(routed) -> moe_expert_ffn(shared, dense)
  *     -> moe_combine(residual)
- * on the same inputs, in three launches on `stream`: the route kernel, then a gate/up kernel
- * for every (token, expert) pair and every token's shared expert (h rows in the
- * workspace), then a down kernel that produces a few output rows of every pair per block
- * and combines them in registers (y never goes to memory).  Each token is sent to k
- * experts and to the shared one, as the layer the pages describe [Strata 与
- * Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会].
+ * on the same inputs, in three launches on `stream`.  One token: the router GEMV (logits
+ * only), a gate/up kernel whose blocks each select the token's experts (and write ids and
+ * weights), then a down kernel that produces a few output rows of every pair per block and
+ * combines them in registers (y never goes to memory).  Several tokens: moe_route's kernel
+ * (logits and selection), then the same gate/up kernel with the ids given, then the same
+ * down kernel.  Each token is sent to k experts and to the shared one, as the layer the pages
+ * describe [Strata 与 Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会].
  *   routed   the routed expert set; n_experts and d_model must match the router's
  *   shared   the shared expert (n_experts 1, same format, d_model and d_ff) or NULL
  *   x        bf16 [T][d]; ids int32 [T][k] and weights fp32 [T][k] are outputs as in
  *            moe_route; residual bf16 [T][d] or NULL; out bf16 [T][d] (may alias residual)
  *   ws       zero-initialised workspace of moe_workspace_size(MOE_OP_LAYER_DECODE, T, k,
- *            E, d, d_ff) bytes; the route kernel's counter is left zero by every call
+ *            E, d, d_ff) bytes; its first bytes hold moe_route's arrival counter, which
+ *            every call leaves zero again
  * Needs T*k <= 64, the h rows of all T*k (+ T shared) slots within 128 KiB of LDS, and a
  * (d_model, d_ff) pair with a GEMV kernel (see moe_expert_ffn); otherwise
  * MOE_ERR_UNSUPPORTED and the caller uses the four calls.

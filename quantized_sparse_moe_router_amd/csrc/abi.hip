@@ -61,10 +61,10 @@ size_t ffn_ws(int64_t rows, int E, int F) {
     return gemv > mfma ? gemv : mfma;
 }
 
-// decode layer workspace: [router logits [T][E] fp32][h rows of every slot]
+// decode layer workspace: [route workspace: counter, logits [T][E] fp32][h rows of every
+// slot]
 size_t decode_ws(int T, int k, int E, int d, int F) {
-    return round_up((size_t)T * (size_t)E * sizeof(float)) +
-           moe::decode_ws_layout(T, k, d, F).bytes;
+    return round_up(route_ws(T, E, true)) + moe::decode_ws_layout(T, k, d, F).bytes;
 }
 
 // Router descriptor checks shared by moe_route and moe_layer_decode.
@@ -324,11 +324,24 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
                     need, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* base = static_cast<uint8_t*>(ws);
-    float* lg = reinterpret_cast<float*>(base);
-    hipError_t e = moe::launch_route_logits(*r, x, T, lg, s);
-    if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
-    e = moe::launch_decode_ffn(*routed, shared, x, T, k, lg, ids, weights, residual, out,
-                               base + round_up((size_t)T * (size_t)E * sizeof(float)), s);
+    unsigned* counter = reinterpret_cast<unsigned*>(base);
+    float* lg = reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
+    uint8_t* ffn_ws = base + round_up(route_ws(T, E, true));
+    hipError_t e;
+    if (T == 1) {
+        // logits only; every gate/up block selects the token's experts itself
+        e = moe::launch_route_logits(*r, x, T, lg, s);
+        if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
+        e = moe::launch_decode_ffn(*routed, shared, x, T, k, lg, ids, weights, residual, out,
+                                   ffn_ws, s);
+    } else {
+        // several tokens: the route kernel selects once (its last block, one wave per
+        // token) instead of every gate/up block repeating one token's selection
+        e = moe::launch_route(*r, x, T, k, ids, weights, lg, counter, s);
+        if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
+        e = moe::launch_decode_ffn(*routed, shared, x, T, k, nullptr, ids, weights, residual,
+                                   out, ffn_ws, s);
+    }
     return hip_status(e, "moe_layer_decode");
 }
 
