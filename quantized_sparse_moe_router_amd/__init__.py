@@ -46,19 +46,23 @@ class MoeLayer:
     moe_combine; it returns ``out`` (bf16 [T][d]).  For small calls (T*k <= 64) the routed
     experts do not read the grouping, so moe_permute runs on a second side stream beside
     them.  Graph capture records the forks and joins.  Intermediate results stay readable
-    as attributes (logits, ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared).
+    as attributes (ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared, and
+    logits when ``keep_logits``).  Without ``keep_logits``, moe_route gets no logits buffer
+    and, for more than 16 tokens, selects through MFMA logits with an error bound and exact
+    recomputation of the experts near the cut (the same ids and weights, bit for bit).
 
     decode(x) computes the same output bit for bit with moe_layer_decode (three launches, no
     side streams) when T*k <= 64 and the shapes allow it (``can_decode``); it fills ids,
     weights and out only.
     """
 
-    def __init__(self, router, routed, shared, k, T_max, device="cuda"):
+    def __init__(self, router, routed, shared, k, T_max, device="cuda", keep_logits=False):
         self.router = router_desc_of(router)
         self.routed = experts_desc_of(routed)
         self.shared = experts_desc_of(shared) if shared is not None else None
         self.E, self.d, self.F, self.k = routed.E, routed.d, routed.F, k
         self.T_max = T_max
+        self.keep_logits = keep_logits
         dev = torch.device(device)
         T, E, d, F = T_max, self.E, self.d, self.F
         P = T * k
@@ -107,7 +111,8 @@ class MoeLayer:
             self.side.wait_stream(main)
             moe_expert_ffn(self.shared, x, T, 1, None, None, None, self.y_shared,
                            self.ws_shared, stream=self.side)
-        moe_route(self.router, x, T, k, self.ids, self.weights, self.logits, self.ws_route)
+        moe_route(self.router, x, T, k, self.ids, self.weights,
+                  self.logits if self.keep_logits else None, self.ws_route)
         small = T * k <= 64
         if small:
             # small calls of moe_expert_ffn read only ids, so the grouping (needed by the
@@ -127,6 +132,13 @@ class MoeLayer:
         moe_combine(self.y_pairs, self.pair_pos, self.weights,
                     self.y_shared if self.shared is not None else None, residual, T, k, d, out)
         return out
+
+    def route_logits(self, x, ids, weights):
+        """moe_route with the logits requested (the fixed-order path) into self.logits; ids
+        and weights go to the given buffers."""
+        T = x.shape[0]
+        moe_route(self.router, x, T, self.k, ids, weights, self.logits, self.ws_route)
+        return self.logits[:T]
 
     def decode(self, x, residual=None, out=None):
         T = x.shape[0]

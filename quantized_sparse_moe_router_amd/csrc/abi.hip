@@ -48,10 +48,24 @@ constexpr int kMaxK = 64;
 constexpr int64_t kGemvMaxRows = 64;   // pair rows up to which the GEMV path runs
 constexpr int64_t kDecodeMaxPairs = 64; // pairs up to which moe_layer_decode runs
 
-// route workspace: [counter][logits when the caller passes none]
-size_t route_ws(int64_t T, int E, bool need_logits) {
-    return moe::kRouteCounterBytes +
-           (need_logits ? round_up((size_t)T * (size_t)E * sizeof(float)) : 0);
+// route workspace, exact form: [counter][logits]
+size_t route_exact_ws(int64_t T, int E) {
+    return moe::kRouteCounterBytes + round_up((size_t)T * (size_t)E * sizeof(float));
+}
+
+// the bounded form (many tokens, no logits wanted) runs when this holds
+bool route_bounded(int64_t T, const float* logits) {
+    return logits == nullptr && T > moe::kRouteGemvMaxTokens;
+}
+
+// route workspace: [counter]; with no logits from the caller also [logits], and for the
+// bounded form [plane rows][row norm bounds]
+size_t route_ws(int64_t T, int E, int d, bool need_logits) {
+    if (!need_logits) return moe::kRouteCounterBytes;
+    size_t n = route_exact_ws(T, E);
+    if (route_bounded(T, nullptr))
+        n += round_up(moe::route_bounded_planes_bytes(E, d)) + round_up((size_t)E * sizeof(float));
+    return n;
 }
 
 // expert FFN workspace: [counters][h][tile list]
@@ -64,7 +78,7 @@ size_t ffn_ws(int64_t rows, int E, int F) {
 // decode layer workspace: [route workspace: counter, logits [T][E] fp32][h rows of every
 // slot]
 size_t decode_ws(int T, int k, int E, int d, int F) {
-    return round_up(route_ws(T, E, true)) + moe::decode_ws_layout(T, k, d, F).bytes;
+    return round_up(route_exact_ws(T, E)) + moe::decode_ws_layout(T, k, d, F).bytes;
 }
 
 // Router descriptor checks shared by moe_route and moe_layer_decode.
@@ -135,7 +149,7 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
     (void)d;
     if (T <= 0 || k <= 0 || E <= 0) return 0;
     switch (op) {
-        case MOE_OP_ROUTE: return route_ws(T, E, true);
+        case MOE_OP_ROUTE: return route_ws(T, E, d, true);
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes((int64_t)T * k, E);
         case MOE_OP_EXPERT_FFN: return d_ff > 0 ? ffn_ws((int64_t)T * k, E, d_ff) : 0;
         case MOE_OP_LAYER_DECODE:
@@ -163,17 +177,26 @@ moe_status moe_route(const moe_router* r, const uint16_t* x, int32_t T, int32_t 
     if (!x || !aligned16(x))
         return fail(MOE_ERR_INVALID_ARG, "moe_route: x NULL or not 16-byte aligned");
     if (!ids || !weights) return fail(MOE_ERR_INVALID_ARG, "moe_route: ids/weights NULL");
-    const size_t need = route_ws(T, E, logits == nullptr);
+    const size_t need = route_ws(T, E, r->d_model, logits == nullptr);
     if (!ws || ws_bytes < need || !aligned16(ws))
         return fail(MOE_ERR_WORKSPACE,
                     "moe_route: needs a 16-byte aligned workspace of %zu bytes (got %zu)", need,
                     ws_bytes);
-    unsigned* counter = static_cast<unsigned*>(ws);
-    float* lg = logits ? logits
-                       : reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
-                                                  moe::kRouteCounterBytes);
-    return hip_status(moe::launch_route(*r, x, T, k, ids, weights, lg, counter,
-                                        static_cast<hipStream_t>(stream)),
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    unsigned* counter = reinterpret_cast<unsigned*>(base);
+    float* lg = logits ? logits : reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
+    if (route_bounded(T, logits)) {
+        uint8_t* p = base + route_exact_ws(T, E);
+        uint16_t* planes = reinterpret_cast<uint16_t*>(p);
+        float* nw = reinterpret_cast<float*>(
+            p + round_up(moe::route_bounded_planes_bytes(E, r->d_model)));
+        hipError_t e = moe::launch_route_bounded_logits(*r, x, T, planes, nw, lg, s);
+        if (e != hipSuccess) return hip_status(e, "moe_route: bounded logits");
+        return hip_status(moe::launch_route_bounded_select(*r, x, T, k, nw, lg, ids, weights, s),
+                          "moe_route: selection");
+    }
+    return hip_status(moe::launch_route(*r, x, T, k, ids, weights, lg, counter, s),
                       "moe_route");
 }
 
@@ -326,7 +349,7 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
     uint8_t* base = static_cast<uint8_t*>(ws);
     unsigned* counter = reinterpret_cast<unsigned*>(base);
     float* lg = reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
-    uint8_t* ffn_ws = base + round_up(route_ws(T, E, true));
+    uint8_t* ffn_ws = base + round_up(route_exact_ws(T, E));
     hipError_t e;
     if (T == 1) {
         // logits only; every gate/up block selects the token's experts itself

@@ -30,7 +30,7 @@
 // Three LDS stages: loads for step ks + 2 are issued at the start of step ks, so each
 // has about two k-steps to land.  Loads are counted by hand (s_waitcnt vmcnt) because the
 // compiler does not track LDS written by these loads.
-#include "moe_common.h"
+#include "mfma_common.h"
 
 #include <type_traits>
 
@@ -47,12 +47,6 @@ constexpr int MI = BM / 32;      // 32-row MFMA blocks per tile (8)
 constexpr int BK = 64;           // reduction step
 constexpr int kStages = 3;       // LDS pipeline stages
 constexpr int kXcds = 8;         // MI355X: 8 XCDs of 32 CUs, each with its own L2
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));   // plain vector: stays in VGPRs
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 size_t tile_capacity(int64_t rows, int E) { return (size_t)((rows + BM - 1) / BM + E); }
 
@@ -91,11 +85,6 @@ __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __rest
 }
 
 // -------------------------------------------------------------- dequantisation
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    bf16x2_t p = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, p);
-}
-
 // The codes of one 32-code group: int4 = 16 bytes (a), int6 = 24 bytes (a, then b).
 template <int FMT>
 struct GroupCodes {
@@ -137,28 +126,6 @@ __device__ __forceinline__ uint32_t chunk_pair(uint32_t lo, uint32_t hi, int b, 
     const float e1 = (float)((hi >> (8 * b)) & 0xffu);
     return pack_bf16(__builtin_fmaf(e0, s, zc), __builtin_fmaf(e1, s, zc));
 }
-
-// -------------------------------------------------------------- global -> LDS loads
-// lds is the wave-uniform byte address of the destination, set in M0 (the instruction
-// needs one wait state after M0 is written).  Lane l's data lands at lds + 16 l for
-// dwordx4 and dwordx3 (12 bytes used), and at lds + 4 l for ushort (zero-extended to 32
-// bits).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void dma12(const void* g, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-}
-// wait until at most n of this wave's global loads are outstanding (n <= 63) and, with
-// the _LDS form, until its LDS reads are done too (before a barrier after which other
-// waves' loads overwrite what was read)
-#define MOE_WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-#define MOE_WAIT_VMCNT_LDS(n) \
-    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
 
 enum { kGateUp = 0, kDown = 1 };
 

@@ -89,11 +89,26 @@ constexpr size_t kRouteCounterBytes = 256;
 int* device_error_flag();
 hipError_t read_and_clear_device_error(int* flag);
 
+// Tokens up to which moe_route computes logits and selection in one launch (GEMV).
+constexpr int kRouteGemvMaxTokens = 16;
+
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
                         float* weights, float* logits, unsigned* counter, hipStream_t s);
 // Router logits only (fp32 [T][E], the same values launch_route computes), for T <= 64.
 hipError_t launch_route_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
                                hipStream_t s);
+
+// Many tokens, logits not wanted: the bounded form.  launch_route_bounded_logits writes
+// every logit to within 2^-11 (|x_t| nw[e] + |b_e|) of the fixed-order value (MFMA; planes
+// is a workspace of route_bounded_planes_bytes, nw [E] the row norm bounds);
+// launch_route_bounded_select recomputes in the fixed order the experts that bound cannot
+// rule out and selects: ids and weights are those of launch_route, bit for bit.
+size_t route_bounded_planes_bytes(int E, int d);
+hipError_t launch_route_bounded_logits(const moe_router& r, const uint16_t* x, int T,
+                                       uint16_t* planes, float* nw, float* lf, hipStream_t s);
+hipError_t launch_route_bounded_select(const moe_router& r, const uint16_t* x, int T, int k,
+                                       const float* nw, const float* lf, int32_t* ids,
+                                       float* weights, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                           int32_t* sorted_pairs, int32_t* pair_pos, void* ws, hipStream_t s);

@@ -291,6 +291,173 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     }
 }
 
+// ------------------------------------------------------------------ many tokens: bounded
+// Selection from the MFMA logits lf (route_mfma.hip), which satisfy
+//     |lf[t][e] - logit[t][e]| <= B_e = 2^-11 (|x_t| nw[e] + |b_e|)
+// where logit is the fixed-order value.  One wave per token:
+//   1. lo_e = lf - B_e, hi_e = lf + B_e; theta = the k-th largest of the lanes' largest lo
+//      (so at least k experts have logit >= lo >= theta);
+//   2. candidates: hi_e >= theta (any other expert's logit is below theta, hence below k
+//      others: it cannot be selected, and cannot tie a selected one); experts whose
+//      bound is not finite, or whose |x_t| nw[e] is so small (below 2^-90) that products
+//      may underflow, are candidates whatever their value;
+//   3. each candidate's logit recomputed exactly in the fixed order (the wave holds x_t
+//      in the order's layout, as the few-token kernel holds the weight row);
+//   4. the selection (topk_regs) over the row with exact values for the candidates and lf
+//      for the rest: every non-candidate value is below theta and at least k candidates
+//      are at or above it, so the k selected are the k largest exact logits, in the same
+//      order and with the same weights as the exact path computes.
+template <int FMT, int NV, int NPL>
+__global__ void __launch_bounds__(256) route_bounded_select_kernel(
+    const void* __restrict__ W, const uint16_t* __restrict__ scale,
+    const float* __restrict__ bias, const uint16_t* __restrict__ x,
+    const float* __restrict__ nw, const float* __restrict__ lf, int T, int E, int d, int k,
+    int32_t* __restrict__ ids, float* __restrict__ weights) {
+    constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;   // elements per 16-byte vector
+    constexpr int XW = PV / 2;                                 // x words (bf16 pairs) per vector
+    __shared__ uint64_t scratch[4][128];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+
+    // ---- loads: x_t in the fixed order's layout (lane l: vectors l + 64 j), the bounded
+    // logits, the row norms and the bias
+    uint32_t xw[NV][XW];
+    const uint16_t* xt = x + (size_t)t * d;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(xt + (lane + 64 * j) * PV);
+        if constexpr (PV == 4) {
+            const uint2 q = *reinterpret_cast<const uint2*>(src);
+            xw[j][0] = q.x; xw[j][1] = q.y;
+        } else {
+            const uint4 a = reinterpret_cast<const uint4*>(src)[0];
+            const uint4 b = reinterpret_cast<const uint4*>(src)[1];
+            xw[j][0] = a.x; xw[j][1] = a.y; xw[j][2] = a.z; xw[j][3] = a.w;
+            xw[j][4] = b.x; xw[j][5] = b.y; xw[j][6] = b.z; xw[j][7] = b.w;
+        }
+    }
+    float v[NPL], nwe[NPL], be[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+        v[i] = lf[(size_t)t * E + e];
+        nwe[i] = nw[e];
+        be[i] = bias ? bias[e] : 0.0f;
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int w = 0; w < XW; ++w) {
+            const float a = bf16lo(xw[j][w]), b = bf16hi(xw[j][w]);
+            ss = __builtin_fmaf(a, a, ss);
+            ss = __builtin_fmaf(b, b, ss);
+        }
+    const float nx = sqrtf(group_sum<64>(ss)) * (1.0f + 0x1p-10f);
+
+    // ---- 1, 2: threshold and candidates
+    uint32_t lokey[NPL], hikey[NPL];
+    bool force[NPL];
+    uint32_t lmax = 0u;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const bool valid = lane + 64 * i < E;
+        const float xn = nx * nwe[i];
+        const float B = 0x1p-11f * (xn + fabsf(be[i]));
+        const float lo = v[i] - B, hi = v[i] + B;
+        const bool fin = __builtin_isfinite(lo) && __builtin_isfinite(hi);
+        const bool tiny = xn > 0.0f && xn < 0x1p-90f;
+        force[i] = valid && (!fin || tiny);
+        lokey[i] = (valid && fin) ? order_bits(lo) : 0u;
+        hikey[i] = (valid && fin) ? order_bits(hi) : 0u;
+        lmax = lokey[i] > lmax ? lokey[i] : lmax;
+    }
+    uint32_t theta = 0u;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = theta | (1u << b);
+        if (__popcll(__ballot(lmax >= c)) >= k) theta = c;
+    }
+    uint64_t bal[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+        bal[i] = __ballot(lane + 64 * i < E && (force[i] || hikey[i] >= theta));
+
+    // ---- 3: exact logits of the candidates, two at a time
+    auto pop = [&](int& e) __attribute__((always_inline)) {
+        e = -1;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            if (e < 0 && bal[i]) {
+                e = 64 * i + (int)__builtin_ctzll(bal[i]);
+                bal[i] &= bal[i] - 1;
+            }
+    };
+    int ea, eb;
+    pop(ea);
+    pop(eb);
+    while (ea >= 0) {
+        const int ec[2] = {ea, eb >= 0 ? eb : ea};
+        float wv[2][NV][PV];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            if constexpr (FMT == MOE_FMT_INT8_ROW) {
+                const uint4* row = reinterpret_cast<const uint4*>(
+                    static_cast<const int8_t*>(W) + (size_t)ec[c] * d);
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    const uint4 q = row[lane + 64 * j];
+                    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        wv[c][j][u] = (float)(int8_t)((wd[u >> 2] >> (8 * (u & 3))) & 0xffu);
+                }
+            } else {
+                const float4* row = reinterpret_cast<const float4*>(
+                    static_cast<const float*>(W) + (size_t)ec[c] * d);
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    const float4 q = row[lane + 64 * j];
+                    wv[c][j][0] = q.x; wv[c][j][1] = q.y; wv[c][j][2] = q.z; wv[c][j][3] = q.w;
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int w = 0; w < XW; ++w) {
+                    acc = __builtin_fmaf(bf16lo(xw[j][w]), wv[c][j][2 * w], acc);
+                    acc = __builtin_fmaf(bf16hi(xw[j][w]), wv[c][j][2 * w + 1], acc);
+                }
+            acc = group_sum<64>(acc);     // butterfly over xor offsets 1..32
+            const int e = ec[c];
+            float l = acc;
+            if constexpr (FMT == MOE_FMT_INT8_ROW) l = l * f16_to_f32(scale[e]);
+            if (bias) l = l + bias[e];
+            if (lane == (e & 63)) {
+#pragma unroll
+                for (int i = 0; i < NPL; ++i)
+                    if (i == (e >> 6)) v[i] = l;
+            }
+        }
+        pop(ea);
+        pop(eb);
+    }
+
+    // ---- 4: selection and weights
+    int sel_e;
+    float sel_w;
+    topk_regs<NPL>(v, E, k, scratch[wave], sel_e, sel_w);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = sel_e;
+        weights[(size_t)t * k + lane] = sel_w;
+    }
+}
+
 // Few tokens: logits and selection in one launch.  Every block computes its rows' logits
 // for all tokens, writes them with device-scope stores, waits for those stores, then
 // counts itself in; the last block to arrive reads every logit with device-scope loads,
@@ -336,7 +503,7 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
                      float* weights, float* logits, unsigned* counter, hipStream_t s) {
     const int E = r.n_experts, d = r.d_model;
     const int npl = (E + 63) / 64;
-    if (T <= 16) {   // few tokens: one wave per expert row, selection by the last block
+    if (T <= kRouteGemvMaxTokens) {   // one wave per expert row, selection by the last block
         const dim3 grid((E + 3) / 4), block(256);
 #define MOE_GT(N)                                                                         \
     router_gemv_topk_kernel<FMT, NV, N><<<grid, block, 0, s>>>(r.w, r.scale, r.bias, x, T, \
@@ -427,7 +594,55 @@ hipError_t launch_logits_fmt(const moe_router& r, const uint16_t* x, int T, floa
     return hipErrorInvalidValue;
 }
 
+template <int FMT, int NV>
+hipError_t launch_bounded_nv(const moe_router& r, const uint16_t* x, int T, int k,
+                             const float* nw, const float* lf, int32_t* ids, float* weights,
+                             hipStream_t s) {
+    const int E = r.n_experts, npl = (E + 63) / 64;
+    const dim3 grid((T + 3) / 4), block(256);
+#define MOE_BS(N)                                                                          \
+    route_bounded_select_kernel<FMT, NV, N><<<grid, block, 0, s>>>(                        \
+        r.w, r.scale, r.bias, x, nw, lf, T, E, r.d_model, k, ids, weights)
+    if (npl <= 1) MOE_BS(1);
+    else if (npl <= 2) MOE_BS(2);
+    else if (npl <= 4) MOE_BS(4);
+    else if (npl <= 8) MOE_BS(8);
+    else MOE_BS(16);
+#undef MOE_BS
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_bounded_fmt(const moe_router& r, const uint16_t* x, int T, int k,
+                              const float* nw, const float* lf, int32_t* ids, float* weights,
+                              hipStream_t s) {
+    constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
+    const int nv = r.d_model / (64 * PV);
+#define MOE_NV(N)                                                                         \
+    if (nv == N) {                                                                        \
+        if constexpr (N * PV <= 64)                                                       \
+            return launch_bounded_nv<FMT, N>(r, x, T, k, nw, lf, ids, weights, s);        \
+        else                                                                              \
+            return hipErrorInvalidValue;                                                  \
+    }
+    MOE_NV(1)
+    MOE_NV(2)
+    MOE_NV(4)
+    MOE_NV(8)
+    MOE_NV(16)
+#undef MOE_NV
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_route_bounded_select(const moe_router& r, const uint16_t* x, int T, int k,
+                                       const float* nw, const float* lf, int32_t* ids,
+                                       float* weights, hipStream_t s) {
+    if (r.fmt == MOE_FMT_INT8_ROW)
+        return launch_bounded_fmt<MOE_FMT_INT8_ROW>(r, x, T, k, nw, lf, ids, weights, s);
+    return launch_bounded_fmt<MOE_FMT_FP32>(r, x, T, k, nw, lf, ids, weights, s);
+}
 
 hipError_t launch_route_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
                                hipStream_t s) {

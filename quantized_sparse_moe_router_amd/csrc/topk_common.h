@@ -116,21 +116,13 @@ __device__ __forceinline__ uint64_t select_serial(uint64_t (&key)[NPL], int k) {
 // keys have a high word >= T, so every selected key does; these candidates (usually a
 // few more than k) are compacted into LDS and each one's rank among them is counted.  When
 // there are more than 64 candidates (many equal logits) the serial form runs instead.
-template <int NPL, bool COHERENT>
-__device__ __forceinline__ void topk_wave(const float* lt, int E, int k, uint64_t* scratch,
-                                          int& out_e, float& out_w) {
+//
+// topk_regs takes the logits in registers (v[i] = logit of expert lane + 64 i);
+// topk_wave loads them first.
+template <int NPL>
+__device__ __forceinline__ void topk_regs(const float (&v)[NPL], int E, int k,
+                                          uint64_t* scratch, int& out_e, float& out_w) {
     const int lane = threadIdx.x & 63;
-    float v[NPL];
-    // all loads first, unconditionally (clamped index), so they are in flight together
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = min(lane + 64 * i, E - 1);
-        if constexpr (COHERENT)
-            v[i] = __hip_atomic_load(const_cast<float*>(lt) + e, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        else
-            v[i] = lt[e];
-    }
     uint64_t key[NPL];
     uint32_t lmax = 0u;
 #pragma unroll
@@ -187,6 +179,24 @@ __device__ __forceinline__ void topk_wave(const float* lt, int E, int k, uint64_
     const float sum = group_sum<64>(ex);
     out_e = (int)(0xffffffffu - my_lo);
     out_w = ex / sum;
+}
+
+template <int NPL, bool COHERENT>
+__device__ __forceinline__ void topk_wave(const float* lt, int E, int k, uint64_t* scratch,
+                                          int& out_e, float& out_w) {
+    const int lane = threadIdx.x & 63;
+    float v[NPL];
+    // all loads first, unconditionally (clamped index), so they are in flight together
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
+        if constexpr (COHERENT)
+            v[i] = __hip_atomic_load(const_cast<float*>(lt) + e, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        else
+            v[i] = lt[e];
+    }
+    topk_regs<NPL>(v, E, k, scratch, out_e, out_w);
 }
 
 }  // namespace

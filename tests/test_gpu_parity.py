@@ -80,14 +80,20 @@ def _check_layer(name, T=None, sample=None, bias=None, seed=0, stream=0):
     layer, out = _run(moe, lay, w, x)
     k, E = w.k, w.E
 
-    # routing: full size, bit-exact
+    # routing: full size, bit-exact.  forward() selects without logits (for T > 16 the
+    # bounded MFMA form); route_logits() runs the fixed-order path that returns them.
     logits_ref = oracle.router_logits(r_h, x_h)
-    logits = layer.logits[:T].cpu().numpy()
+    ids2 = torch.empty_like(layer.ids)
+    w2 = torch.empty_like(layer.weights)
+    logits = layer.route_logits(x, ids2, w2).cpu().numpy()
+    torch.cuda.synchronize()
     assert np.array_equal(logits.view(np.uint32), logits_ref.view(np.uint32)), \
         "logits differ in %d places" % int((logits != logits_ref).sum())
     ids_ref = oracle.select_topk(logits_ref, k)
     ids = layer.ids[:T].cpu().numpy()
     assert np.array_equal(ids, ids_ref)
+    assert np.array_equal(ids2[:T].cpu().numpy(), ids_ref)
+    assert torch.equal(w2[:T].view(torch.int32), layer.weights[:T].view(torch.int32))
     w_ref = oracle.topk_weights(logits_ref, ids_ref)
     wts = layer.weights[:T].cpu().numpy().astype(np.float64)
     assert np.abs(wts - w_ref).max() <= 1e-6
