@@ -114,16 +114,27 @@ typedef struct moe_experts {
  *           largest; equal logits (+0 == -0) -> lower expert id first
  *   weights fp32 [T][k]: out; softmax over the k selected logits (the full softmax
  *           renormalised over the selected experts); sums to 1 up to rounding
- *   logits  fp32 [T][E]: optional out (NULL: kept in the workspace)
+ *   logits  fp32 [T][E]: optional out (NULL: not returned; see below)
  *   ws      zero-initialised workspace of moe_workspace_size(MOE_OP_ROUTE, T, k, E, d, 0)
  *           bytes (256 bytes are enough when logits != NULL)
- * With T <= 16 the logits and the selection run in one launch (the last block to finish
- * its rows selects); larger T runs an LDS-tiled GEMM and a selection kernel.
- * Logits are computed in one fixed fp32 order, the same for every T: the row is cut
- * into 16-byte vectors dealt round-robin to 64 lanes, each lane runs one
- * fused-multiply-add chain over its vectors in ascending order, and the 64 lane sums
- * are combined by a butterfly with offsets 1, 2, 4, ..., 32; then + bias (FP32), or
- * fl(fl(sum * scale) + bias) (INT8_ROW).  Requires 1 <= k <= min(E, 64).
+ * Logits are defined in one fixed fp32 order, the same for every T: the row is cut into
+ * 16-byte vectors dealt round-robin to 64 lanes, each lane runs one fused-multiply-add
+ * chain over its vectors in ascending order, and the 64 lane sums are combined by a
+ * butterfly with offsets 1, 2, 4, ..., 32; then + bias (FP32), or
+ * fl(fl(sum * scale) + bias) (INT8_ROW).  ids and weights are always those of these
+ * logits.  How they are reached:
+ *   T <= 16: logits and selection in one launch (the last block to finish its rows
+ *            selects);
+ *   T > 16, logits requested: an LDS-tiled fp32 GEMM in the fixed order, then selection;
+ *   T > 16, logits NULL (the bounded form): bf16 MFMA logits (FP32 rows split exactly
+ *            into two bf16 parts plus a dropped remainder below 2^-17 of the weight)
+ *            within 2^-11 (|x_t| |w_e| + |b_e|) of the fixed-order value; per token the
+ *            experts that this bound cannot rule out of the top k are recomputed in the
+ *            fixed order, and the selection runs over exact values for them.  The ids and
+ *            weights are bit for bit those of the other forms.  Three launches; the
+ *            workspace then also holds the logits, bf16 copies of the router rows and
+ *            their norms (moe_workspace_size accounts for them).
+ * Requires 1 <= k <= min(E, 64).
  */
 moe_status moe_route(const moe_router* r, const uint16_t* x, int32_t T, int32_t k,
                      int32_t* ids, float* weights, float* logits, void* ws, size_t ws_bytes,
