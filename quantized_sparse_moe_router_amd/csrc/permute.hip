@@ -7,9 +7,11 @@
 //
 // Work is cut into chunks of kChunk consecutive pairs:
 //   1. per-chunk histograms (LDS integer atomics: the counts do not depend on order);
-//   2. one block scans the histograms per expert over chunks and over experts;
-//   3. each chunk ranks its pairs in pair order, one wave, 64 pairs per round, and
-//      scatters them.
+//   2. per expert, an exclusive scan of the chunk counts (blocks of 64 experts, 16 waves
+//      each over a slice of the chunks) and the expert's total;
+//   3. per chunk (16 waves of 64 pairs): the scan of the totals over experts gives the
+//      offsets; each wave ranks its pairs among equal ids (ballot match on the id bits),
+//      waves before it in the chunk add their counts, and the pairs are scattered.
 // A call with at most kChunk pairs runs all three steps in one block.
 #include "moe_common.h"
 
@@ -192,48 +194,89 @@ __global__ void __launch_bounds__(256) chunk_hist_kernel(const int32_t* __restri
     for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// Step 2: per expert, exclusive scan over chunks; then over experts -> offsets; the
-// chunk table becomes each chunk's starting position per expert.  One block of 1024.
+// Step 2: for experts 64 b .. 64 b + 63, the chunk table becomes each chunk's count of
+// earlier pairs of that expert (exclusive scan over chunks), and tot[e] the expert's
+// total.  Wave g of the 16 takes chunks [g L, g L + L); lane = expert.
 __global__ void __launch_bounds__(1024) chunk_scan_kernel(int* __restrict__ hist, int nchunk,
-                                                          int E,
-                                                          int32_t* __restrict__ offsets) {
-    __shared__ int tot[kMaxE];
-    __shared__ int off[kMaxE + 1];
-    const int e = threadIdx.x;
+                                                          int E, int* __restrict__ tot) {
+    __shared__ int part[16][64];
+    const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;
+    const int L = (nchunk + 15) / 16;
+    const int c0 = g * L, c1 = min(nchunk, c0 + L);
+    int sum = 0;
+    if (e < E)
+        for (int c = c0; c < c1; ++c) sum += hist[(size_t)c * E + e];
+    part[g][lane] = sum;
+    __syncthreads();
+    int run = 0;
+    for (int i = 0; i < g; ++i) run += part[i][lane];
     if (e < E) {
-        int run = 0;
-        for (int c = 0; c < nchunk; ++c) {
+        for (int c = c0; c < c1; ++c) {
             const int v = hist[(size_t)c * E + e];
             hist[(size_t)c * E + e] = run;
             run += v;
         }
-        tot[e] = run;
+        if (g == 15) tot[e] = run;
     }
-    __syncthreads();
-    block_exclusive_scan(tot, off, E);
-    for (int i = e; i <= E; i += blockDim.x) offsets[i] = off[i];
-    if (e < E)
-        for (int c = 0; c < nchunk; ++c) hist[(size_t)c * E + e] += off[e];
 }
 
-// Step 3: scatter each chunk.  blockDim.x = 64.
-__global__ void __launch_bounds__(64) chunk_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t P, int E, const int* __restrict__ start,
-    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
-    __shared__ int base[kMaxE];
-    for (int e = threadIdx.x; e < E; e += 64) base[e] = start[(size_t)blockIdx.x * E + e];
+// Lanes of the wave holding the same id as this lane (valid lanes only): a ballot per id
+// bit, kept where the lane's bit agrees.
+__device__ __forceinline__ uint64_t match_id(int id, bool valid, int nbits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+
+// Step 3: chunk blockIdx.x, 16 waves of 64 consecutive pairs.  Block 0 also writes the
+// offsets.
+__global__ void __launch_bounds__(1024) chunk_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t P, int E, int nbits,
+    const int* __restrict__ start, const int* __restrict__ tot,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ pair_pos) {
+    __shared__ int off[kMaxE + 1];
+    __shared__ int tl[kMaxE];
+    __shared__ __attribute__((aligned(16))) uint8_t wcnt[16][kMaxE];   // pairs of wave w with id e (<= 64)
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid < E) tl[tid] = tot[tid];
+    for (int i = tid; i < 16 * kMaxE / 4; i += 1024) reinterpret_cast<uint32_t*>(wcnt)[i] = 0;
+    const int64_t p = (int64_t)blockIdx.x * kChunk + tid;
+    const bool inrange = p < P;
+    const int id = inrange ? ids[p] : -1;
+    const bool valid = inrange && id >= 0 && id < E;
+    if (inrange && !valid) {
+        pair_pos[p] = -1;
+        atomicOr(&g_bad_id_flag, 1);
+    }
     __syncthreads();
-    const int64_t p0 = (int64_t)blockIdx.x * kChunk;
-    const int64_t p1 = min(P, p0 + kChunk);
-    scatter_chunk(ids, p0, p1, E, base, sorted_pairs, pair_pos);
+    block_exclusive_scan(tl, off, E);     // ends with a barrier
+    if (blockIdx.x == 0)
+        for (int e = tid; e <= E; e += 1024) offsets[e] = off[e];
+    const uint64_t m = match_id(id, valid, nbits);
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) wcnt[w][id] = (uint8_t)__popcll(m);
+    __syncthreads();
+    if (valid) {
+        int pos = off[id] + start[(size_t)blockIdx.x * E + id] + rank;
+        for (int i = 0; i < w; ++i) pos += wcnt[i][id];
+        sorted_pairs[pos] = (int32_t)p;
+        pair_pos[p] = pos;
+    }
 }
 
 }  // namespace
 
+// workspace: [chunk table nchunk x E][expert totals E]
 size_t permute_ws_bytes(int64_t P, int E) {
     if (P <= kChunk) return 0;
     const int64_t nchunk = (P + kChunk - 1) / kChunk;
-    return (size_t)nchunk * (size_t)E * sizeof(int);
+    return (size_t)(nchunk + 1) * (size_t)E * sizeof(int);
 }
 
 hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offsets,
@@ -250,9 +293,13 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
     }
     const int nchunk = (int)((P + kChunk - 1) / kChunk);
     int* hist = static_cast<int*>(ws);
+    int* tot = hist + (size_t)nchunk * E;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
     chunk_hist_kernel<<<nchunk, 256, 0, s>>>(ids, P, E, hist);
-    chunk_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunk, E, offsets);
-    chunk_scatter_kernel<<<nchunk, 64, 0, s>>>(ids, P, E, hist, sorted_pairs, pair_pos);
+    chunk_scan_kernel<<<(E + 63) / 64, 1024, 0, s>>>(hist, nchunk, E, tot);
+    chunk_scatter_kernel<<<nchunk, 1024, 0, s>>>(ids, P, E, nbits, hist, tot, offsets,
+                                                 sorted_pairs, pair_pos);
     return hipGetLastError();
 }
 
