@@ -234,9 +234,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
     const uint32_t own_b = (uint32_t)(wave * NI) * L::B_WJ + lane * 16;
     const uint32_t own_s = (uint32_t)(wave * NI) * L::S_WJ + lane * 4;
 
-    // load number q (0..NG-1) of k-step `step` (clamped to the last step) into stage st
+    // load number q (0..NG-1) of k-step `step` into stage st
     auto issue = [&](int q, int step, int st) __attribute__((always_inline)) {
-        const int kk = min(step, nk - 1);
+        const int kk = step;
         const uint32_t base = lds0 + st * L::BYTES;
         if (q < MB) {
             dma16(a_src[q] + kk * BK, base + (32 * q + 8 * wave) * 128);
@@ -329,25 +329,32 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
     // the next sub-step.  A 32x32x16 MFMA leaves its wave free to issue for about 16 of its
     // 32 cycles, so this keeps the matrix pipe fed; sched_barrier keeps the compiler from
     // regrouping the slots.
+    // One k-step; PF: the loads of step ks + 2 are issued (every step but the last two,
+    // which wait for everything outstanding instead).
     int st = 0;                                   // stage of step ks
-    for (int ks = 0; ks < nk; ++ks) {
+    auto kstep = [&](int ks, auto pf) __attribute__((always_inline)) {
+        constexpr bool PF = decltype(pf)::value;
         const int st1 = st == kStages - 1 ? 0 : st + 1;
         const int st2 = st1 == kStages - 1 ? 0 : st1 + 1;
 #pragma unroll
         for (int u = 0; u < 48; ++u) {            // sub-steps 0..2
             const int ss = u / 16, t = u % 16, F = ss & 1;
             if (t < MB * NI) mfma(F, t);
-            if (ss == 0 && t < NG) issue(t, ks + 2, st2);
+            if (PF && ss == 0 && t < NG) issue(t, ks + 2, st2);
             if (t % 2 == 0 && t / 2 < MB) fa[F ^ 1][t / 2] = read_a(st, t / 2, ss + 1);
             dequant_half(codes, scale, F ^ 1, t / 8, ss + 1, (t / 2) % 4, t % 2);
             // this wave's loads of step ks + 1 are done; its codes are private to the wave
-            if (ss == 2 && t == 0) MOE_WAIT_VMCNT(NG);
+            if (ss == 2 && t == 0) {
+                if constexpr (PF) MOE_WAIT_VMCNT(NG);
+                else MOE_WAIT_VMCNT(0);
+            }
             if (ss == 2 && (t == 1 || t == 3)) read_codes(st1, t / 2, codes_n[t / 2], scale_n[t / 2]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // every wave's loads of step ks + 1 have landed once all pass the barrier; stage st
         // is not read after it
-        MOE_WAIT_VMCNT_LDS(NG);
+        if constexpr (PF) MOE_WAIT_VMCNT_LDS(NG);
+        else MOE_WAIT_VMCNT_LDS(0);
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < 16; ++t) {            // sub-step 3, and step ks + 1's sub-step 0
@@ -362,10 +369,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
             scale[j] = scale_n[j];
         }
         st = st1;
-    }
-    // the last two steps' loads (re-reads of the last step) are still in flight; after the
-    // barrier no wave reads the stages and LDS holds the output tile
-    MOE_WAIT_VMCNT(0);
+    };
+    for (int ks = 0; ks + 2 < nk; ++ks) kstep(ks, std::true_type{});
+    for (int ks = nk - 2; ks < nk; ++ks) kstep(ks, std::false_type{});
+    // nothing is in flight; after the barrier no wave reads the stages and LDS holds the
+    // output tile
     __syncthreads();
 
     // ---- epilogue: accumulator r of lane l in block (i, j) is tile row 32 i + l % 32 and
