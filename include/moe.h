@@ -170,7 +170,8 @@ moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  * expert's weights once (two launches: gate/up + SwiGLU, then down); they derive each
  * pair's row from ids alone and do not read offsets or sorted_pairs, so moe_permute may
  * run concurrently with them.  Larger calls run a grouped MFMA GEMM that reads offsets
- * and sorted_pairs.
+ * and sorted_pairs; it needs T*d_model and T*k*d_ff (dense: T*d_ff) below 2^31 elements
+ * (MOE_ERR_UNSUPPORTED otherwise: split the call).
  * ws: moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, d_ff) bytes (pass k = 1, E = 1
  * for dense mode).
  */

@@ -248,10 +248,17 @@ moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, i
                     need, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (rows <= kGemvMaxRows && moe::ffn_gemv_has_shape(d, F))
+    if (rows <= kGemvMaxRows && moe::ffn_gemv_has_shape(d, F)) {
         e = moe::launch_ffn_gemv(*ex, x, T, grouped ? k : 1, ids, y, ws, s);
-    else
+    } else {
+        // the grouped GEMM addresses x and h rows with 32-bit byte offsets
+        if ((uint64_t)T * (uint64_t)d * 2 >= (1ull << 32) ||
+            (uint64_t)rows * (uint64_t)F * 2 >= (1ull << 32))
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "moe_expert_ffn: x (T*d_model) and h (rows*d_ff) must each be under "
+                        "4 GiB of bf16; split the call");
         e = moe::launch_ffn_mfma(*ex, x, T, grouped ? k : 1, offsets, sorted_pairs, y, ws, s);
+    }
     return hip_status(e, "moe_expert_ffn");
 }
 

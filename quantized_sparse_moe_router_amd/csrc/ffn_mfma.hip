@@ -185,40 +185,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
     // into LDS chunk position lane % 8 of that row.  Position p of row r holds logical
     // 16-byte chunk p ^ ((r / 2) % 8): the 16 rows an MFMA operand read touches per LDS
     // cycle then cover all 64 banks.
-    const uint16_t* a_src[MB];
+    // Addresses: a wave-uniform base per source (SGPRs, advanced per k-step) plus a per-lane
+    // 32-bit byte offset (activations: at most T * K * 2 bytes; weights: within one
+    // expert's rows).
+    const uint16_t* a_base = uniform_ptr(g.act);
+    uint32_t a_off[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
         const int r = 32 * i + 8 * wave + (lane >> 3);
         const int pos = min(m0 + r, m1 - 1);
-        size_t arow;
+        uint32_t arow;
         if (MODE == kGateUp && g.sorted_pairs)
-            arow = (size_t)(g.sorted_pairs[pos] / g.topk);
+            arow = (uint32_t)(g.sorted_pairs[pos] / g.topk);
         else
-            arow = (size_t)pos;
-        a_src[i] = g.act + arow * K + 8 * ((lane & 7) ^ ((r >> 1) & 7));
+            arow = (uint32_t)pos;
+        a_off[i] = (arow * (uint32_t)K + 8u * (uint32_t)((lane & 7) ^ ((r >> 1) & 7))) * 2u;
     }
-    // ---- weight rows of this lane's two MFMA columns (column lane % 32 of block j)
-    const uint8_t* b_src[NI];
-    const uint16_t* s_src[NI];
-    {
-        const size_t row_bytes = (size_t)K / 32 * GB;
+    // ---- weight rows of this lane's two MFMA columns (column lane % 32 of block j): the
+    // wave's first row of block j as the base, lane % 32 rows further as the offset
+    const uint8_t* b_base[NI];
+    const uint16_t* s_base[NI];
+    const uint32_t row_bytes = (uint32_t)(K / 32 * GB);
+    const uint32_t b_off = (uint32_t)(lane & 31) * row_bytes + (uint32_t)(h * GB);
+    const uint32_t s_off = ((uint32_t)(lane & 31) * (uint32_t)(K / 32) + (uint32_t)h) * 2u;
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            size_t grow;
-            const uint8_t* wm;
-            const uint16_t* sm;
-            if (MODE == kGateUp) {
-                grow = (size_t)e * g.n_out + ny * (BN / 2) + 32 * wave + (lane & 31);
-                wm = j == 0 ? g.wa : g.wb;
-                sm = j == 0 ? g.sa : g.sb;
-            } else {
-                grow = (size_t)e * g.n_out + ny * BN + TN * wave + 32 * j + (lane & 31);
-                wm = g.wa;
-                sm = g.sa;
-            }
-            b_src[j] = wm + grow * row_bytes + h * GB;
-            s_src[j] = sm + grow * (K / 32) + h;
+    for (int j = 0; j < NI; ++j) {
+        size_t grow0;
+        const uint8_t* wm;
+        const uint16_t* sm;
+        if (MODE == kGateUp) {
+            grow0 = (size_t)e * g.n_out + ny * (BN / 2) + 32 * wave;
+            wm = j == 0 ? g.wa : g.wb;
+            sm = j == 0 ? g.sa : g.sb;
+        } else {
+            grow0 = (size_t)e * g.n_out + ny * BN + TN * wave + 32 * j;
+            wm = g.wa;
+            sm = g.sa;
         }
+        b_base[j] = uniform_ptr(wm + grow0 * row_bytes);
+        s_base[j] = uniform_ptr(sm + grow0 * (size_t)(K / 32));
     }
 
     f32x16_t acc[MB][NI];
@@ -239,18 +244,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
         const int kk = step;
         const uint32_t base = lds0 + st * L::BYTES;
         if (q < MB) {
-            dma16(a_src[q] + kk * BK, base + (32 * q + 8 * wave) * 128);
+            dma16s(a_base + kk * BK, a_off[q], base + (32 * q + 8 * wave) * 128);
         } else if (q < MB + NI * L::DMA_B) {
             const int j = (q - MB) / L::DMA_B, part = (q - MB) % L::DMA_B;
-            const uint8_t* src = b_src[j] + (size_t)kk * 2 * GB;
+            const uint8_t* src = b_base[j] + kk * 2 * GB;
             const uint32_t dst = base + L::A + (wave * NI + j) * L::B_WJ;
             if (L::DMA_B == 1)
-                dma16(src, dst);
+                dma16s(src, b_off, dst);
             else
-                dma12(src + 12 * part, dst + 1024 * part);
+                dma12s(src, b_off + 12 * part, dst + 1024 * part);
         } else {
             const int j = q - MB - NI * L::DMA_B;
-            dma2(s_src[j] + kk * 2, base + L::A + L::B + (wave * NI + j) * L::S_WJ);
+            dma2s(s_base[j] + kk * 2, s_off, base + L::A + L::B + (wave * NI + j) * L::S_WJ);
         }
     };
     // this lane's group codes and scale of MFMA column block j, from stage st

@@ -34,6 +34,31 @@ __device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 
+// The same with the address split into a wave-uniform base (SGPR pair) and a per-lane
+// 32-bit byte offset: per k-step only the base moves, a scalar add.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma12s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx3 %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma2s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"(lds) : "memory");
+}
+
+// a pointer made wave-uniform (both halves read from the first active lane), so that it
+// lives in SGPRs
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 }  // namespace
 }  // namespace moe
 
