@@ -172,7 +172,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
     using L = StageLayout<FMT>;
     constexpr int GB = L::GB;
     constexpr int NG = MB + NI * L::DMA_B + NI;   // global loads per wave per k-step
-    static_assert(NG <= 16, "one load per slot of sub-step 0");
+    static_assert(NG <= 16, "one load every third slot of sub-steps 0..2");
+    constexpr int kIssuedBySs2 = NG < 11 ? NG : 11;   // loads issued in slots 0..31
     const int K = g.K;
     const int nk = K / BK;
 
@@ -345,12 +346,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
         for (int u = 0; u < 48; ++u) {            // sub-steps 0..2
             const int ss = u / 16, t = u % 16, F = ss & 1;
             if (t < MB * NI) mfma(F, t);
-            if (PF && ss == 0 && t < NG) issue(t, ks + 2, st2);
+            // the loads of step ks + 2 are spread over the first 48 slots, one every third:
+            // issued in one burst they queue in the address path and the waves fall out
+            // of step, which the barrier then pays for
+            if (PF && u % 3 == 0 && u / 3 < NG) issue(u / 3, ks + 2, st2);
             if (t % 2 == 0 && t / 2 < MB) fa[F ^ 1][t / 2] = read_a(st, t / 2, ss + 1);
             dequant_half(codes, scale, F ^ 1, t / 8, ss + 1, (t / 2) % 4, t % 2);
-            // this wave's loads of step ks + 1 are done; its codes are private to the wave
+            // this wave's loads of step ks + 1 are done (the loads of step ks + 2 issued so
+            // far, slots 0, 3, .., 30, may still be in flight); its codes are private to the
+            // wave
             if (ss == 2 && t == 0) {
-                if constexpr (PF) MOE_WAIT_VMCNT(NG);
+                if constexpr (PF) MOE_WAIT_VMCNT(kIssuedBySs2);
                 else MOE_WAIT_VMCNT(0);
             }
             if (ss == 2 && (t == 1 || t == 3)) read_codes(st1, t / 2, codes_n[t / 2], scale_n[t / 2]);
