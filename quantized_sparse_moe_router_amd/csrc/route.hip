@@ -384,74 +384,83 @@ __global__ void __launch_bounds__(256) route_bounded_select_kernel(
     for (int i = 0; i < NPL; ++i)
         bal[i] = __ballot(lane + 64 * i < E && (force[i] || hikey[i] >= theta));
 
-    // ---- 3: exact logits of the candidates, two at a time
-    auto pop = [&](int& e) __attribute__((always_inline)) {
-        e = -1;
+    // ---- 3: exact logits of the candidates, NB at a time (raw 16-byte vectors of their
+    // rows in flight together, converted inside the chain)
+    constexpr int NB = (FMT == MOE_FMT_INT8_ROW) ? 4 : 2;
+    uint64_t rest[NPL];
+    int C = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        rest[i] = bal[i];
+        C += __popcll(bal[i]);
+    }
+    auto pop = [&]() __attribute__((always_inline)) {
+        int e = -1;
 #pragma unroll
         for (int i = 0; i < NPL; ++i)
-            if (e < 0 && bal[i]) {
-                e = 64 * i + (int)__builtin_ctzll(bal[i]);
-                bal[i] &= bal[i] - 1;
+            if (e < 0 && rest[i]) {
+                e = 64 * i + (int)__builtin_ctzll(rest[i]);
+                rest[i] &= rest[i] - 1;
             }
+        return e;
     };
-    int ea, eb;
-    pop(ea);
-    pop(eb);
-    while (ea >= 0) {
-        const int ec[2] = {ea, eb >= 0 ? eb : ea};
-        float wv[2][NV][PV];
+    for (int done = 0; done < C; done += NB) {
+        int ec[NB];
+        uint4 raw[NB][NV];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            if constexpr (FMT == MOE_FMT_INT8_ROW) {
-                const uint4* row = reinterpret_cast<const uint4*>(
-                    static_cast<const int8_t*>(W) + (size_t)ec[c] * d);
+        for (int c = 0; c < NB; ++c) {
+            const int e = pop();
+            ec[c] = e;
+            const int er = e >= 0 ? e : 0;
+            const uint4* row = reinterpret_cast<const uint4*>(
+                static_cast<const uint8_t*>(W) + (size_t)er * d * (PV == 4 ? 4 : 1));
 #pragma unroll
-                for (int j = 0; j < NV; ++j) {
-                    const uint4 q = row[lane + 64 * j];
-                    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        wv[c][j][u] = (float)(int8_t)((wd[u >> 2] >> (8 * (u & 3))) & 0xffu);
-                }
-            } else {
-                const float4* row = reinterpret_cast<const float4*>(
-                    static_cast<const float*>(W) + (size_t)ec[c] * d);
-#pragma unroll
-                for (int j = 0; j < NV; ++j) {
-                    const float4 q = row[lane + 64 * j];
-                    wv[c][j][0] = q.x; wv[c][j][1] = q.y; wv[c][j][2] = q.z; wv[c][j][3] = q.w;
-                }
-            }
+            for (int j = 0; j < NV; ++j) raw[c][j] = row[lane + 64 * j];
         }
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NB; ++c) {
             float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < NV; ++j)
+            for (int j = 0; j < NV; ++j) {
+                const uint32_t wd[4] = {raw[c][j].x, raw[c][j].y, raw[c][j].z, raw[c][j].w};
 #pragma unroll
                 for (int w = 0; w < XW; ++w) {
-                    acc = __builtin_fmaf(bf16lo(xw[j][w]), wv[c][j][2 * w], acc);
-                    acc = __builtin_fmaf(bf16hi(xw[j][w]), wv[c][j][2 * w + 1], acc);
+                    float w0, w1;
+                    if constexpr (FMT == MOE_FMT_INT8_ROW) {
+                        w0 = (float)(int8_t)((wd[w >> 1] >> (16 * (w & 1))) & 0xffu);
+                        w1 = (float)(int8_t)((wd[w >> 1] >> (16 * (w & 1) + 8)) & 0xffu);
+                    } else {
+                        w0 = __uint_as_float(wd[2 * w]);
+                        w1 = __uint_as_float(wd[2 * w + 1]);
+                    }
+                    acc = __builtin_fmaf(bf16lo(xw[j][w]), w0, acc);
+                    acc = __builtin_fmaf(bf16hi(xw[j][w]), w1, acc);
                 }
+            }
             acc = group_sum<64>(acc);     // butterfly over xor offsets 1..32
             const int e = ec[c];
-            float l = acc;
-            if constexpr (FMT == MOE_FMT_INT8_ROW) l = l * f16_to_f32(scale[e]);
-            if (bias) l = l + bias[e];
-            if (lane == (e & 63)) {
+            if (e >= 0) {
+                float l = acc;
+                if constexpr (FMT == MOE_FMT_INT8_ROW) l = l * f16_to_f32(scale[e]);
+                if (bias) l = l + bias[e];
+                if (lane == (e & 63)) {
 #pragma unroll
-                for (int i = 0; i < NPL; ++i)
-                    if (i == (e >> 6)) v[i] = l;
+                    for (int i = 0; i < NPL; ++i)
+                        if (i == (e >> 6)) v[i] = l;
+                }
             }
         }
-        pop(ea);
-        pop(eb);
     }
 
-    // ---- 4: selection and weights
+    // ---- 4: selection and weights among the candidates (exact values); more than 64
+    // candidates (many equal logits) take the general selection over the whole row
     int sel_e;
     float sel_w;
-    topk_regs<NPL>(v, E, k, scratch[wave], sel_e, sel_w);
+    uint64_t key[NPL];
+    make_keys<NPL>(v, E, key);
+    const uint64_t mine = C <= 64 ? rank_candidates<NPL>(key, bal, C, k, scratch[wave])
+                                  : select_keys<NPL>(key, k, scratch[wave]);
+    finish_selection(mine, k, sel_e, sel_w);
     if (lane < k) {
         ids[(size_t)t * k + lane] = sel_e;
         weights[(size_t)t * k + lane] = sel_w;

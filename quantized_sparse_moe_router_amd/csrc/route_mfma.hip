@@ -26,6 +26,8 @@
 // sum |x_k w_k| <= |x|·|w|.
 #include "mfma_common.h"
 
+#include <type_traits>
+
 #pragma clang fp contract(off)
 
 namespace moe {
@@ -98,7 +100,7 @@ __global__ void __launch_bounds__(256) router_planes_kernel(const void* __restri
 // accumulators).  Per k-step of 64, x rows and plane rows are copied global -> LDS
 // directly, 128 bytes per row with the 16-byte chunks XOR-swizzled by (row / 2) % 8 so
 // that operand reads are free of bank conflicts; three stages, the loads of step ks + 2
-// issued at the start of step ks.  Inside a step, lane half h of every operand covers
+// issued during step ks.  Inside a step, lane half h of every operand covers
 // k = 32 h + 8 ss .. + 7 in sub-step ss (the same permutation on both sides).
 constexpr int RBM = 128;              // tokens per tile
 constexpr int RBN = 256;              // plane rows per tile
@@ -151,14 +153,10 @@ __global__ void __launch_bounds__(256, 1) router_mfma_kernel(
         else
             src[q] = planes + (size_t)min(p0 + r, NP - 1) * d + 8 * chunk;
     }
-    auto issue = [&](int step, int st) __attribute__((always_inline)) {
-        const int kk = min(step, nk - 1);
+    auto issue = [&](int q, int step, int st) __attribute__((always_inline)) {
         const uint32_t base = lds0 + st * RSTAGE;
-#pragma unroll
-        for (int q = 0; q < RNG; ++q) {
-            const int qq = q < 4 ? q : q - 4;
-            dma16(src[q] + kk * RBK, base + (q < 4 ? 0 : RA) + (32 * qq + 8 * wave) * 128);
-        }
+        const int qq = q < 4 ? q : q - 4;
+        dma16(src[q] + step * RBK, base + (q < 4 ? 0 : RA) + (32 * qq + 8 * wave) * 128);
     };
     // operand of 32-row block rb (of the x or plane region), sub-step ss
     const uint32_t rd = (uint32_t)(lane & 31) * 128;
@@ -176,38 +174,61 @@ __global__ void __launch_bounds__(256, 1) router_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    issue(0, 0);
-    issue(1, 1);
+    // operands of the current sub-step (buffer B) and the next (B ^ 1)
+    bf16x8_t fa[2][2], fb[2][4];
+    auto read_ops = [&](int st, int ss, int B, int t) __attribute__((always_inline)) {
+        if (t < 2) fa[B][t] = frag(st, 0, 2 * wm + t, ss);
+        else if (t < 6) fb[B][t - 2] = frag(st, RA, 4 * wn + t - 2, ss);
+    };
+    // plane rows as the first operand: lane l of block (i, j) then holds token 32 i + l % 32
+    // and plane rows 32 j + 8 (r / 4) + 4 (l / 32) + r % 4
+    auto mfma = [&](int B, int t) __attribute__((always_inline)) {
+        const int i = t / 4, j = t % 4;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[B][j], fa[B][i], acc[i][j],
+                                                            0, 0, 0);
+    };
+
+#pragma unroll
+    for (int q = 0; q < RNG; ++q) issue(q, 0, 0);
+#pragma unroll
+    for (int q = 0; q < RNG; ++q) issue(q, 1, 1);
     MOE_WAIT_VMCNT(RNG);
     __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 6; ++t) read_ops(0, 0, 0, t);
+
+    // One k-step = 4 sub-steps x 8 slots, each slot one MFMA; the next sub-step's operands
+    // are read from LDS during the current one, and the 12 loads of step ks + 2 go out one
+    // every other slot of sub-steps 0..2 (PF: all but the last two steps, which wait for
+    // everything instead).  sched_barrier keeps the compiler from regrouping the slots.
     int st = 0;
-    for (int ks = 0; ks < nk; ++ks) {
+    auto kstep = [&](int ks, auto pf) __attribute__((always_inline)) {
+        constexpr bool PF = decltype(pf)::value;
         const int st1 = st == RSTAGES - 1 ? 0 : st + 1;
         const int st2 = st1 == RSTAGES - 1 ? 0 : st1 + 1;
-        issue(ks + 2, st2);
 #pragma unroll
-        for (int ss = 0; ss < 4; ++ss) {
-            bf16x8_t fa[2], fb[4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = frag(st, 0, 2 * wm + i, ss);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j] = frag(st, RA, 4 * wn + j, ss);
-            // plane rows as the first operand: lane l of block (i, j) then holds token
-            // 32 i + l % 32 and plane rows 32 j + 8 (r / 4) + 4 (l / 32) + r % 4
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i],
-                                                                        acc[i][j], 0, 0, 0);
+        for (int u = 0; u < 24; ++u) {            // sub-steps 0..2
+            const int ss = u / 8, t = u % 8, B = ss & 1;
+            mfma(B, t);
+            read_ops(st, ss + 1, B ^ 1, t);
+            if (PF && u % 2 == 0) issue(u / 2, ks + 2, st2);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // this wave's loads of step ks + 1 have landed and its reads of stage st are done;
         // after the barrier every wave's have
-        MOE_WAIT_VMCNT_LDS(RNG);
+        if constexpr (PF) MOE_WAIT_VMCNT_LDS(RNG);
+        else MOE_WAIT_VMCNT_LDS(0);
         __syncthreads();
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {             // sub-step 3, and step ks + 1's operands
+            mfma(1, t);
+            read_ops(st1, 0, 0, t);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         st = st1;
-    }
-    MOE_WAIT_VMCNT(0);   // the clamped re-reads of the last step
+    };
+    for (int ks = 0; ks + 2 < nk; ++ks) kstep(ks, std::true_type{});
+    for (int ks = nk - 2; ks < nk; ++ks) kstep(ks, std::false_type{});
 
     // ---- epilogue: planes of an expert are adjacent accumulators of one lane
     const bool vec = (E % 4) == 0;

@@ -118,18 +118,71 @@ __device__ __forceinline__ uint64_t select_serial(uint64_t (&key)[NPL], int k) {
 // there are more than 64 candidates (many equal logits) the serial form runs instead.
 //
 // topk_regs takes the logits in registers (v[i] = logit of expert lane + 64 i);
-// topk_wave loads them first.
+// topk_wave loads them first.  The pieces below are also used on their own by a caller
+// that already knows a candidate set containing the k largest (route.hip).
+
+// keys of the lane's experts lane + 64 i (padding keys 0)
 template <int NPL>
-__device__ __forceinline__ void topk_regs(const float (&v)[NPL], int E, int k,
-                                          uint64_t* scratch, int& out_e, float& out_w) {
+__device__ __forceinline__ void make_keys(const float (&v)[NPL], int E, uint64_t (&key)[NPL]) {
     const int lane = threadIdx.x & 63;
-    uint64_t key[NPL];
-    uint32_t lmax = 0u;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = lane + 64 * i;
         key[i] = (e < E) ? (((uint64_t)order_bits(v[i]) << 32) | (0xffffffffu - (uint32_t)e))
                          : 0ull;                       // padding keys lose to every id
+    }
+}
+
+// The k largest of the C <= 64 candidate keys marked by bal (one ballot per key slot i),
+// which must include the k largest keys overall: lane j < k returns the j-th, others 0.
+// Compaction in (i, lane) order, then each candidate's rank among the candidates (keys
+// are unique).
+template <int NPL>
+__device__ __forceinline__ uint64_t rank_candidates(const uint64_t (&key)[NPL],
+                                                    const uint64_t (&bal)[NPL], int C, int k,
+                                                    uint64_t* scratch) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        if ((bal[i] >> lane) & 1ull)
+            scratch[base + __popcll(bal[i] & ((1ull << lane) - 1ull))] = key[i];
+        base += __popcll(bal[i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint64_t ck = lane < C ? scratch[lane] : 0ull;
+    int rank = 0;
+    for (int c = 0; c < C; ++c) rank += scratch[c] > ck ? 1 : 0;
+    if (lane < C && rank < k) scratch[64 + rank] = ck;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return lane < k ? scratch[64 + lane] : 0ull;
+}
+
+// expert and weight of the selection's lane j < k: softmax over the k selected logits in
+// fp32, shifted by the largest
+__device__ __forceinline__ void finish_selection(uint64_t mine, int k, int& out_e,
+                                                 float& out_w) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t my_hi = (uint32_t)(mine >> 32), my_lo = (uint32_t)mine;
+    const uint32_t vbits = (my_hi & 0x80000000u) ? (my_hi & 0x7fffffffu) : ~my_hi;
+    const float my_v = (lane < k) ? __uint_as_float(vbits) : 0.0f;
+    const float vmax = __shfl(my_v, 0, 64);
+    const float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
+    const float sum = group_sum<64>(ex);
+    out_e = (int)(0xffffffffu - my_lo);
+    out_w = ex / sum;
+}
+
+// The whole selection from keys: fast form when at most 64 keys reach the threshold T,
+// serial form otherwise.
+template <int NPL>
+__device__ __forceinline__ uint64_t select_keys(uint64_t (&key)[NPL], int k,
+                                                uint64_t* scratch) {
+    uint32_t lmax = 0u;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
         const uint32_t h = (uint32_t)(key[i] >> 32);
         lmax = h > lmax ? h : lmax;
     }
@@ -147,38 +200,16 @@ __device__ __forceinline__ void topk_regs(const float (&v)[NPL], int E, int k,
         bal[i] = __ballot((uint32_t)(key[i] >> 32) >= T);
         C += __popcll(bal[i]);
     }
-    uint64_t mine;
-    if (C <= 64) {
-        // compaction in (i, lane) order
-        int base = 0;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            if ((bal[i] >> lane) & 1ull)
-                scratch[base + __popcll(bal[i] & ((1ull << lane) - 1ull))] = key[i];
-            base += __popcll(bal[i]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // rank of candidate `lane` among the C candidates (keys are unique)
-        const uint64_t ck = lane < C ? scratch[lane] : 0ull;
-        int rank = 0;
-        for (int c = 0; c < C; ++c) rank += scratch[c] > ck ? 1 : 0;
-        if (lane < C && rank < k) scratch[64 + rank] = ck;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        mine = lane < k ? scratch[64 + lane] : 0ull;
-    } else {
-        mine = select_serial<NPL>(key, k);
-    }
-    // weights: softmax over the k selected logits in fp32, shifted by the largest
-    const uint32_t my_hi = (uint32_t)(mine >> 32), my_lo = (uint32_t)mine;
-    const uint32_t vbits = (my_hi & 0x80000000u) ? (my_hi & 0x7fffffffu) : ~my_hi;
-    const float my_v = (lane < k) ? __uint_as_float(vbits) : 0.0f;
-    const float vmax = __shfl(my_v, 0, 64);
-    const float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
-    const float sum = group_sum<64>(ex);
-    out_e = (int)(0xffffffffu - my_lo);
-    out_w = ex / sum;
+    if (C <= 64) return rank_candidates<NPL>(key, bal, C, k, scratch);
+    return select_serial<NPL>(key, k);
+}
+
+template <int NPL>
+__device__ __forceinline__ void topk_regs(const float (&v)[NPL], int E, int k,
+                                          uint64_t* scratch, int& out_e, float& out_w) {
+    uint64_t key[NPL];
+    make_keys<NPL>(v, E, key);
+    finish_selection(select_keys<NPL>(key, k, scratch), k, out_e, out_w);
 }
 
 template <int NPL, bool COHERENT>
