@@ -51,6 +51,11 @@ def test_workspace_sizes(L):
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 1, 10, 512, 2048, 512) == 0
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 8192, 10, 512, 2048, 512) >= 80 * 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 1, 10, 512, 2048, 512) >= 10 * 512 * 2
+    # more than 16 tokens without a logits output: the bounded form also keeps bf16 plane
+    # rows of the router (two per fp32 row) and one norm bound per expert
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 8192, 10, 512, 2048, 0) == \
+        256 + 8192 * 512 * 4 + 512 * 2 * 2048 * 2 + 512 * 4
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 16, 10, 512, 2048, 0) == 256 + 16 * 512 * 4
 
 
 def _router(fmt=0, E=512, d=2048, w=16, scale=None, reserved=0):
@@ -95,6 +100,9 @@ def test_route_null_descriptor_and_workspace(L):
     assert st == -3 and "workspace" in _err(L)
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, None, 16, 100, None)
     assert st == -3
+    # bounded form (17 tokens, no logits): counter + logits alone are not enough
+    st = L.moe_route(ctypes.byref(r), 16, 17, 10, 16, 16, None, 16, 256 + 17 * 512 * 4, None)
+    assert st == -3 and "workspace" in _err(L)
     # with a logits output the workspace still holds the arrival counter
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, 16, None, 0, None)
     assert st == -3
@@ -134,6 +142,10 @@ def test_expert_ffn_rejects(L):
     assert call(_experts(), wsb=10) == -3
     assert call(_experts(), T=-1) == -1
     assert call(_experts(), T=0) == 0
+    # the grouped GEMM addresses x and h with 32-bit byte offsets: 2^20 tokens of d 2048
+    # bf16 are 4 GiB
+    assert call(_experts(), T=1 << 20, k=1, wsb=1 << 62) == -2
+    assert "4 GiB" in _err(L)
 
 
 def test_combine_rejects(L):
