@@ -47,3 +47,40 @@ def test_graph_replays_match_eager():
         assert torch.equal(outs[0], eager[0]), rep
         assert torch.equal(outs[1], eager[1]), rep
     moe.moe_check_device_error()
+
+
+def test_graph_replays_match_eager_prefill_path():
+    # 300 tokens x top-10: the bounded router (planes, MFMA logits, selection), the chunked
+    # grouping (3000 pairs), the grouped MFMA GEMM and the combine, all inside one graph
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_sparse_moe_router_amd as moe
+    w = synth.WORKLOADS["decode_d2048_e512_top10_t1"]
+    lay = synth.make_layer(w, seed=5, device="cuda", bias="zipf")
+    T = 300
+    x = synth.make_tokens(w, T=T, seed=5, device="cuda")
+    layer = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, T)
+    print("case graph prefill T=%d" % T, flush=True)
+    eager = layer.forward(x).clone()
+    eager_ids = layer.ids[:T].clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, out=out)
+    for rep in range(4):
+        out.zero_()
+        layer.ids.zero_()
+        _ = torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        assert torch.equal(layer.ids[:T], eager_ids), rep
+    moe.moe_check_device_error()
