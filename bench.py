@@ -258,9 +258,15 @@ def main():
         line["prefill_32k"] = [prefill_bench(moe, synth, np, torch, "prefill_32768_mixed", b)
                                for b in ("zipf", "none")]
 
-    # ---- what this chip reaches on plain work, for context next to the spec peaks
-    if not args.no_prefill:
-        line["achievable"] = achievable_peaks(torch)
+    # ---- what this chip reaches on plain work, next to the spec peaks: the rates above as
+    # fractions of the measured stream read and MFMA loop too
+    ach = achievable_peaks(torch)
+    line["achievable"] = ach
+    line["roofline"]["frac_of_measured_stream"] = round(
+        line["roofline"]["achieved"] / ach["hbm_read_GBps_stream_kernel"], 4)
+    for p in ([line["prefill"]] + line["prefill_32k"]) if "prefill" in line else []:
+        p["mfma_util_of_measured_loop"] = round(
+            p["routed_gemm_tflops"] / ach["mfma_bf16_tflops_loop"], 4)
 
     # ---- CPU oracle on a bounded sample of the decode workload
     if not args.no_cpu_baseline:
@@ -345,9 +351,12 @@ def prefill_bench(moe, synth, np, torch, name, bias):
 
 
 def achievable_peaks(torch):
-    """Measured ceilings of plain library work on this GPU: a 2 GiB fp32 reduction (HBM
-    read) and torch's dense bf16 matmul at the routed GEMMs' shapes for 8192 tokens (81920
-    pair rows; gate+up K=2048/N=1024, down K=512/N=2048)."""
+    """Measured ceilings on this GPU, next to the spec peaks: our stream-read kernel over
+    4 GiB of HBM and our loop of bf16 MFMAs (libmoe_peaks.so, with the shader clock it runs
+    at), plus torch's dense bf16 matmul (the vendor GEMM library) at the routed GEMMs'
+    shapes for 8192 tokens (81920 pair rows; gate+up K=2048/N=1024, down K=512/N=2048)."""
+    import ctypes
+
     def timed_ms(fn, reps=10):
         fn()
         torch.cuda.synchronize()
@@ -359,6 +368,32 @@ def achievable_peaks(torch):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
     out = {}
+    P = ctypes.CDLL(os.path.join(ROOT, "quantized_sparse_moe_router_amd", "libmoe_peaks.so"))
+    P.moe_peaks_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    P.moe_peaks_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(P.moe_peaks_stream_blocks(), dtype=torch.int32, device="cuda")
+
+    def stream_read():
+        assert P.moe_peaks_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream) == 0
+    out["hbm_read_GBps_stream_kernel"] = round(nbytes / (timed_ms(stream_read) * 1e6), 1)
+    del buf, sink
+    blocks, iters = 2048, 20000
+    fsink = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    clk = torch.empty(blocks * 2, dtype=torch.int64, device="cuda")
+
+    def mfma_loop():
+        assert P.moe_peaks_mfma_loop(blocks, iters, fsink.data_ptr(), clk.data_ptr(),
+                                     stream) == 0
+    ms = timed_ms(mfma_loop, reps=5)
+    flops = blocks * 4.0 * iters * 8 * 32768
+    out["mfma_bf16_tflops_loop"] = round(flops / (ms * 1e9), 1)
+    c = clk.view(blocks, 2).double()
+    out["sclk_mhz_mfma_loop"] = round(float((c[:, 0] / c[:, 1]).mean()) * 100.0, 0)
     x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
     out["hbm_read_GBps_torch_sum"] = round(x.numel() * 4 / (timed_ms(lambda: x.sum()) * 1e6), 1)
     del x

@@ -11,6 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")   # bench.py's measurement helpers
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 add/mul/fma.
@@ -44,6 +46,10 @@ def build(verbose=False):
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
                            *[o for o, _ in results]])
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, *FLAGS, "-shared", "-o", tmp, PEAKS_SRC],
+                          stderr=subprocess.DEVNULL)
+    os.replace(tmp, PEAKS_LIB)
     return LIB
 
 

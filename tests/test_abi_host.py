@@ -37,6 +37,21 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+def test_peaks_library_exports_its_declared_symbols():
+    # bench.py's measurement helpers: a library of their own, declared in moe_peaks.h
+    import re
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = open(os.path.join(root, "include", "moe_peaks.h")).read()
+    names = re.findall(r"^int\s+(moe_peaks_\w+)\(", hdr, re.M)
+    assert set(names) == {"moe_peaks_stream_blocks", "moe_peaks_stream_read",
+                          "moe_peaks_mfma_loop"}
+    P = ctypes.CDLL(os.path.join(root, "quantized_sparse_moe_router_amd", "libmoe_peaks.so"))
+    for n in names:
+        assert hasattr(P, n), n
+    assert P.moe_peaks_stream_blocks() > 0
+
+
 def test_version_and_status_strings(L):
     assert b"gfx950" in L.moe_version()
     assert L.moe_status_string(0) == b"ok"
