@@ -48,7 +48,12 @@ constexpr int BK = 64;           // reduction step
 constexpr int kStages = 3;       // LDS pipeline stages
 constexpr int kXcds = 8;         // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
-size_t tile_capacity(int64_t rows, int E) { return (size_t)((rows + BM - 1) / BM + E); }
+// entries of the work list: at most ceil(rows / BM) + E tiles, rounded up to whole XCD groups
+// so that every block of the grid can read its entry before checking the count
+size_t tile_capacity(int64_t rows, int E) {
+    const size_t n = (size_t)((rows + BM - 1) / BM + E);
+    return (n + kXcds - 1) / kXcds * kXcds;
+}
 
 // -------------------------------------------------------------- work list
 __global__ void __launch_bounds__(1024) build_tiles_kernel(const int32_t* __restrict__ offsets,
@@ -458,8 +463,9 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(
     const int tile = (q / n_ny) * kXcds + xcd, ny = q % n_ny;
     int e, m0, m1;
     if (tiles) {
-        if (tile >= *tile_count) return;
+        // the entry (in bounds for every block of the grid) and the count load together
         const int4 t = tiles[tile];
+        if (tile >= *tile_count) return;
         e = t.x; m0 = t.y; m1 = t.z;
     } else {
         e = 0;
