@@ -165,3 +165,29 @@ def test_bounded_logits_within_bound(name):
     ratio = np.abs(lf.astype(np.float64) - ref) / bound
     print("%s: max |lf - logit| / bound = %.3g" % (name, ratio.max()), flush=True)
     assert ratio.max() <= 0.25
+
+
+@pytest.mark.parametrize("scale", [1e-31, 1e30])
+def test_bounded_selection_tiny_and_huge_rows(scale):
+    # Rows scaled so that |x| |w_e| falls below the bounded form's underflow guard (every
+    # expert is then recomputed in the fixed order, more than 64 candidates: the general
+    # selection runs), or is huge (the bound is wide; more candidates, still exact).
+    moe = _gpu()
+    w = synth.WORKLOADS["decode_d2048_e512_top10_t1"]
+    lay = synth.make_layer(w, seed=0, device="cuda")
+    gen = torch.Generator().manual_seed(29)
+    rw = (torch.randn((w.E, w.d), generator=gen) * 0.02 * scale).contiguous()
+    router = si.Router("fp32", w.E, w.d, rw.cuda(), None, None)
+    r_h = router.host()
+    T = 40
+    print("case scale %g T=%d" % (scale, T), flush=True)
+    x = _tokens("normal", T, w.d, gen).cuda()
+    logits_ref = oracle.router_logits(r_h, si.bits16(x))
+    assert np.isfinite(logits_ref).all()
+    ids_ref = oracle.select_topk(logits_ref, w.k)
+    w_ref = oracle.topk_weights(logits_ref, ids_ref)
+    layer = moe.MoeLayer(router, lay.routed, lay.shared, w.k, T)
+    layer.forward(x)
+    torch.cuda.synchronize()
+    moe.moe_check_device_error()
+    _check_both_forms(layer, x, T, logits_ref, ids_ref, w_ref)
