@@ -5,9 +5,11 @@
 //  Strata 与 Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会].  They fix no
 // summation order; selection compares fp32 logits, so the order is part of the contract
 // (see include/moe.h): 16-byte vectors dealt round-robin to 64 lanes, one fused
-// multiply-add chain per lane, then a butterfly over lanes with offsets 1..32.  Both
-// kernels below realise exactly that order, so decode (few tokens) and prefill (many
-// tokens) produce identical logits for the same token.
+// multiply-add chain per lane, then a butterfly over lanes with offsets 1..32.  The GEMV
+// (few tokens) and the LDS-tiled GEMM (many tokens, logits wanted) realise exactly that
+// order, so they produce identical logits for the same token; the bounded selection (many
+// tokens, no logits wanted) recomputes in that order every expert its MFMA logits cannot
+// rule out, so all forms select alike.
 #include "moe_common.h"
 #include "topk_common.h"
 
@@ -303,10 +305,10 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
 //      may underflow, are candidates whatever their value;
 //   3. each candidate's logit recomputed exactly in the fixed order (the wave holds x_t
 //      in the order's layout, as the few-token kernel holds the weight row);
-//   4. the selection (topk_regs) over the row with exact values for the candidates and lf
-//      for the rest: every non-candidate value is below theta and at least k candidates
-//      are at or above it, so the k selected are the k largest exact logits, in the same
-//      order and with the same weights as the exact path computes.
+//   4. the selection among the candidates (exact values; rank_candidates, or the general
+//      selection over the row when more than 64): every non-candidate value is below theta
+//      and at least k candidates are at or above it, so the k selected are the k largest
+//      exact logits, in the same order and with the same weights as the exact path computes.
 template <int FMT, int NV, int NPL>
 __global__ void __launch_bounds__(256) route_bounded_select_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
