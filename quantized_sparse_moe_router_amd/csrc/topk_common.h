@@ -111,11 +111,12 @@ __device__ __forceinline__ uint64_t select_serial(uint64_t (&key)[NPL], int k) {
 // calling wave.  COHERENT: the logits were just stored by other blocks of the same launch
 // (device-scope stores), so they are read device-scope.
 //
-// Fast form (exact, for any input): let T be the k-th largest of the 64 lanes' largest high
-// words (a bitwise search, most significant bit first, on one value per lane).  At least k
-// keys have a high word >= T, so every selected key does; these candidates (usually a
-// few more than k) are compacted into LDS and each one's rank among them is counted.  When
-// there are more than 64 candidates (many equal logits) the serial form runs instead.
+// Fast form (exact, for any input): let T be the largest multiple of 2^16 such that at
+// least k of the 64 lanes' largest high words are >= T (a bitwise search over the top 16
+// bits, one value per lane).  At least k keys have a high word >= T, so every selected key
+// does; these candidates (usually a few more than k) are compacted into LDS and each one's
+// rank among them is counted.  When there are more than 64 candidates (many equal logits)
+// the serial form runs instead.
 //
 // topk_regs takes the logits in registers (v[i] = logit of expert lane + 64 i);
 // topk_wave loads them first.  The pieces below are also used on their own by a caller
@@ -151,9 +152,15 @@ __device__ __forceinline__ uint64_t rank_candidates(const uint64_t (&key)[NPL],
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane c holds candidate c; its rank counts the larger candidates, read lane by lane
     const uint64_t ck = lane < C ? scratch[lane] : 0ull;
+    const uint32_t ck_hi = (uint32_t)(ck >> 32), ck_lo = (uint32_t)ck;
     int rank = 0;
-    for (int c = 0; c < C; ++c) rank += scratch[c] > ck ? 1 : 0;
+    for (int c = 0; c < C; ++c) {
+        const uint32_t o_hi = (uint32_t)__builtin_amdgcn_readlane((int)ck_hi, c);
+        const uint32_t o_lo = (uint32_t)__builtin_amdgcn_readlane((int)ck_lo, c);
+        rank += (o_hi > ck_hi || (o_hi == ck_hi && o_lo > ck_lo)) ? 1 : 0;
+    }
     if (lane < C && rank < k) scratch[64 + rank] = ck;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -168,9 +175,14 @@ __device__ __forceinline__ void finish_selection(uint64_t mine, int k, int& out_
     const uint32_t my_hi = (uint32_t)(mine >> 32), my_lo = (uint32_t)mine;
     const uint32_t vbits = (my_hi & 0x80000000u) ? (my_hi & 0x7fffffffu) : ~my_hi;
     const float my_v = (lane < k) ? __uint_as_float(vbits) : 0.0f;
-    const float vmax = __shfl(my_v, 0, 64);
+    const float vmax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                     __builtin_bit_cast(int, my_v), 0));
     const float ex = (lane < k) ? expf(my_v - vmax) : 0.0f;
-    const float sum = group_sum<64>(ex);
+    // lanes k.. hold exact zeros: for k <= 16 the sum over the first 16 lanes is the same
+    // value the full butterfly gives (its further levels add zeros)
+    const float sum = k <= 16 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                    __builtin_bit_cast(int, group_sum<16>(ex)), 0))
+                              : group_sum<64>(ex);
     out_e = (int)(0xffffffffu - my_lo);
     out_w = ex / sum;
 }
@@ -186,10 +198,11 @@ __device__ __forceinline__ uint64_t select_keys(uint64_t (&key)[NPL], int k,
         const uint32_t h = (uint32_t)(key[i] >> 32);
         lmax = h > lmax ? h : lmax;
     }
-    // T: the largest value with at least k lane maxima >= T
+    // T: the largest multiple of 2^16 with at least k lane maxima >= T (a search over the
+    // top 16 bits; a lower threshold only admits a few more candidates)
     uint32_t T = 0u;
 #pragma unroll
-    for (int b = 31; b >= 0; --b) {
+    for (int b = 31; b >= 16; --b) {
         const uint32_t c = T | (1u << b);
         if (__popcll(__ballot(lmax >= c)) >= k) T = c;
     }
