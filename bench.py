@@ -132,9 +132,9 @@ def time_graph(fn, reps, warm=2):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (--gpus %d requested); the layer "
-              "shards by tokens with no communication, see DESIGN.md" % args.gpus,
-              file=sys.stderr)
+        print("bench.py measures one GPU (--gpus %d requested): the layer shards by tokens "
+              "with no communication between GPUs, so one GPU's throughput is the measure"
+              % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -203,3 +203,14 @@ def test_layer_decode_rejects(L):
     assert need > 256 + 512 * 4
     assert call(wsb=need - 1) == -3
     assert L.moe_workspace_size(_lib.MOE_OP_LAYER_DECODE, 7, 10, 512, 2048, 512) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
