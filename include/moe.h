@@ -56,7 +56,7 @@ typedef int32_t moe_status;
 enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, bad format */
-    MOE_ERR_UNSUPPORTED = -2,   /* valid request this build has no kernel for */
+    MOE_ERR_UNSUPPORTED = -2,   /* valid request this library has no kernel for */
     MOE_ERR_WORKSPACE = -3,     /* workspace missing or smaller than moe_workspace_size */
     MOE_ERR_HIP = -4,           /* a HIP runtime call failed (launch, sync, copy) */
     MOE_ERR_DEVICE = -5         /* a kernel reported bad data (expert id out of range) */

@@ -54,7 +54,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError("libmoe_mi355x.so is not built (%s); run "
-                              "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+                              "`python -m quantized_sparse_moe_router_amd.build`" % LIB_PATH)
         L = ctypes.CDLL(LIB_PATH)
         P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         sig = {
