@@ -51,6 +51,13 @@ struct GuShape {
     static constexpr int RPB = GU_WAVES * (64 / LPR);   // rows per block
 };
 
+// 8 activations (16 bytes) as group_dot_int4 / group_dot_int6 take them from LDS
+template <int FMT>
+__device__ __forceinline__ uint4 paired(uint4 v) {
+    if constexpr (FMT == MOE_FMT_INT4_G32) return nibble_pairs(v.x, v.y, v.z, v.w);
+    return v;
+}
+
 // ---- down: 4 output rows per block for every slot, then their combine.  16 waves: wave w
 // takes row w % 4 and every 4th wave load of that row (part w / 4).  A row's K = d_ff
 // codes are read by LPR lanes exactly as in gemv_rows; the 64 / LPR lane groups of a wave
@@ -179,11 +186,14 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     load_batch(0);
     __builtin_amdgcn_sched_barrier(0);
     if (threadIdx.x < P) w_lds[threadIdx.x] = gate_w;
-    // h rows -> LDS.  An index past the end is clamped to the last chunk, which then
-    // stores the same value twice: no branch, so no wait per chunk.
+    // h rows -> LDS (int4: in nibble_pairs order).  An index past the end is clamped to the
+    // last chunk, which then stores the same value twice: no branch, so no wait per chunk.
+    auto to_lds = [&](int c, u32x4 v) __attribute__((always_inline)) {
+        const uint4 p = paired<FMT>(make_uint4(v[0], v[1], v[2], v[3]));
+        hdst[c] = u32x4{p.x, p.y, p.z, p.w};
+    };
 #pragma unroll
-    for (int u = 0; u < kHPass; ++u)
-        hdst[min(u * DN_THREADS + (int)threadIdx.x, n16 - 1)] = hv[u];
+    for (int u = 0; u < kHPass; ++u) to_lds(min(u * DN_THREADS + (int)threadIdx.x, n16 - 1), hv[u]);
     for (int c0 = kHPass * DN_THREADS; c0 < n16; c0 += kHPass * DN_THREADS) {
         u32x4 hw[kHPass];
 #pragma unroll
@@ -191,7 +201,7 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
             hw[u] = hsrc[min(c0 + u * DN_THREADS + (int)threadIdx.x, n16 - 1)];
 #pragma unroll
         for (int u = 0; u < kHPass; ++u)
-            hdst[min(c0 + u * DN_THREADS + (int)threadIdx.x, n16 - 1)] = hw[u];
+            to_lds(min(c0 + u * DN_THREADS + (int)threadIdx.x, n16 - 1), hw[u]);
     }
     __syncthreads();
     // group sums of h, once per (slot, group), in group_sum_x's order
@@ -247,14 +257,18 @@ __global__ void __launch_bounds__(GU_WAVES * 64) decode_gateup_kernel(DecodeArgs
     const int s = blockIdx.x / n_gu, rb = blockIdx.x % n_gu;
     const bool pair = s < P;
     // the slot's activation row (token s / k, or s - P for the shared expert) goes to LDS
-    // once per block; requested first, so it is in flight during the selection
+    // once per block, one 16-byte piece per thread: requested first and stored only after
+    // the expert id (or the selection's logits) has been requested too, so that the two
+    // round trips overlap instead of following each other
+    static_assert(D / 8 <= GU_WAVES * 64, "one x piece per thread");
     __shared__ __attribute__((aligned(16))) uint16_t x_lds[D];
-    {
-        const int t = pair ? s / a.k : s - P;
-        const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * D);
-        for (int i = threadIdx.x; i < D / 8; i += GU_WAVES * 64)
-            reinterpret_cast<uint4*>(x_lds)[i] = src[i];
-    }
+    const int xi = min((int)threadIdx.x, D / 8 - 1);
+    const uint4 xq =
+        reinterpret_cast<const uint4*>(a.x + (size_t)(pair ? s / a.k : s - P) * D)[xi];
+    auto store_x = [&]() __attribute__((always_inline)) {
+        if ((int)threadIdx.x < D / 8)
+            reinterpret_cast<uint4*>(x_lds)[xi] = paired<FMT>(xq);
+    };
     // dense form of gemv_rows: one token, activation row 0 (x_lds), output row 0 of `out`
     Slot sl;
     sl.first = 0;
@@ -282,20 +296,23 @@ __global__ void __launch_bounds__(GU_WAVES * 64) decode_gateup_kernel(DecodeArgs
                     a.weights[(size_t)t * a.k + threadIdx.x] = sel_w;
                 }
             }
+            store_x();
             __syncthreads();
             e = sel_lds;
         } else {
             e = a.ids[s];
+            store_x();
             __syncthreads();
         }
         sl.e = (e >= 0 && e < a.E) ? e : 0;
         if (sl.e != e && threadIdx.x == 0 && rb == 0) atomicOr(a.err, 1);
-        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, 1, 1, GU_WAVES>(
+        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, 1, 1, GU_WAVES, true>(
             a.rg, a.rsg, a.ru, a.rsu, x_lds, a.k, F, rb, sl, a.h + (size_t)s * F);
     } else {
+        store_x();
         __syncthreads();
         sl.e = 0;
-        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, 1, 1, GU_WAVES>(
+        gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, 1, 1, GU_WAVES, true>(
             a.sg, a.ssg, a.su, a.ssu, x_lds, a.k, F, rb, sl, a.h + (size_t)s * F);
     }
 }

@@ -6,7 +6,9 @@
 // A row of K packed codes is read by LPR = min(64, K/32) lanes, one 32-code group (16
 // bytes int4, 24 bytes int6) per lane per step, so a wave covers 64/LPR rows per load
 // instruction with fully used 16-byte loads.  Codes become bf16 pairs (128 + u) with a
-// byte permute, are multiplied against bf16 activation pairs by v_dot2_f32_bf16, and the
+// shift and one and-or (int4: the two nibbles 16 bits apart in a word of codes, i.e.
+// elements p and p + 4 of its 8, so the activations are paired the same way, see
+// nibble_pairs), are multiplied against bf16 activation pairs by v_dot2_f32_bf16, and the
 // offset (128 + zero point) times the group's activation sum is removed afterwards; the
 // fp16 group scale is applied once per group.
 //
@@ -27,19 +29,41 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// 16 bytes of int4 codes (32 elements) against 32 bf16 activations (16 pairs).
-// Returns sum_i (128 + u_i) * x_i.
+// Activation pairs in the order group_dot_int4 takes them: within each block of 8
+// elements, (x_p, x_{p+4}) for p = 0..3.  a0..a3: the block's pairs in natural order,
+// (x0, x1) .. (x6, x7).  v_perm_b32 bytes 0-3 come from its second operand, 4-7 from its
+// first.
+__device__ __forceinline__ uint4 nibble_pairs(uint32_t a0, uint32_t a1, uint32_t a2,
+                                              uint32_t a3) {
+    return make_uint4(__builtin_amdgcn_perm(a2, a0, 0x05040100u),
+                      __builtin_amdgcn_perm(a2, a0, 0x07060302u),
+                      __builtin_amdgcn_perm(a3, a1, 0x05040100u),
+                      __builtin_amdgcn_perm(a3, a1, 0x07060302u));
+}
+__device__ __forceinline__ void nibble_pairs16(uint32_t* xp) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 v = nibble_pairs(xp[4 * q], xp[4 * q + 1], xp[4 * q + 2], xp[4 * q + 3]);
+        xp[4 * q] = v.x; xp[4 * q + 1] = v.y; xp[4 * q + 2] = v.z; xp[4 * q + 3] = v.w;
+    }
+}
+
+// 16 bytes of int4 codes (32 elements, element i in bits 4i..4i+3 of the group) against 32
+// bf16 activations in nibble_pairs order.  Returns sum_i (128 + u_i) * x_i, accumulated
+// pair by pair: (0, 4), (1, 5), (2, 6), (3, 7), (8, 12), ...
 __device__ __forceinline__ float group_dot_int4(const uint4 w, const uint32_t* xp) {
+    // the two constants live in registers so that each pair is one v_and_or_b32 (after a
+    // shift): a VOP3 instruction cannot take literal operands on gfx9
+    uint32_t mask, bias;
+    asm("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(bias));
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     float acc = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = wd[q] & 0x0f0f0f0fu;
-        const uint32_t hi = (wd[q] >> 4) & 0x0f0f0f0fu;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const uint32_t sel = 0x0c000c00u | (uint32_t)p | ((uint32_t)(4 + p) << 16);
-            const uint32_t pair = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+            const uint32_t pair = ((wd[q] >> (4 * p)) & mask) | bias;
             acc = dot2(pair, xp[4 * q + p], acc);
         }
     }
@@ -170,7 +194,10 @@ __device__ __forceinline__ bool resolve_slot(int s, int T, int k, const int32_t*
 //   Down  : rows = d_model, inputs = h rows of the pairs, output y (bf16) per pair row.
 // MT = tokens per pass over the weights (a slot's pairs are taken MT at a time).
 // NW = waves per block; wave w owns ITERS consecutive groups of 64 / LPR rows.
-template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT, int NW = 4>
+// PAIRED: int4 activations are already in nibble_pairs order (else they are put in it
+// after loading).
+template <int FMT, int MODE, int LPR, int GPL, int ITERS, int MT, int NW = 4,
+          bool PAIRED = false>
 __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                                           const uint16_t* __restrict__ sa,
                                           const uint8_t* __restrict__ wb,
@@ -236,6 +263,7 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                         xv[m][i][4 * v + 2] = q.z;
                         xv[m][i][4 * v + 3] = q.w;
                     }
+                    if constexpr (FMT == MOE_FMT_INT4_G32 && !PAIRED) nibble_pairs16(xv[m][i]);
                 }
             }
         }
