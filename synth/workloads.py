@@ -43,5 +43,12 @@ WORKLOADS = {
         Workload("prefill_32768_mixed", 4, d=2048, E=512, k=10, F=512, T=32768,
                  routed_fmt="int4_g32", shared_fmt="int6_g32", router_fmt="int8_row",
                  bias="zipf"),
+        # parity cases only: every expert at 6 bit, at decode sizes, so that the few-token
+        # kernels' int6 path is checked (the prefill workload reaches int6 only through the
+        # grouped GEMM); the 8-bit router where its kernels have the width (d = 2048)
+        Workload("int6_d2048_e64_top10", 5, d=2048, E=64, k=10, F=512, T=4,
+                 routed_fmt="int6_g32", shared_fmt="int6_g32", router_fmt="int8_row"),
+        Workload("int6_tiny_d256_e16_top2", 6, d=256, E=16, k=2, F=128, T=33,
+                 routed_fmt="int6_g32", shared_fmt="int6_g32"),
     ]
 }

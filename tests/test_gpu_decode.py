@@ -43,6 +43,9 @@ def _same(a, b):
     ("decode_sweep_48_layers", 4, "zipf"),
     ("decode_sweep_48_layers", 6, "zipf"),
     ("decode_d2048_e512_top10_t1", 2, None),
+    ("int6_tiny_d256_e16_top2", 4, None),
+    ("int6_d2048_e64_top10", 1, None),
+    ("int6_d2048_e64_top10", 4, None),
 ])
 def test_decode_equals_composition(name, T, bias):
     moe = _gpu()

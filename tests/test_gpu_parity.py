@@ -150,6 +150,24 @@ def test_decode_sweep_layer_batch4():
     _check_layer("decode_sweep_48_layers", T=4)
 
 
+@pytest.mark.parametrize("T", [1, 4, 17])
+def test_int6_experts_int8_router_small_batches(T):
+    # int6 routed and shared experts through the GEMV kernels; T = 17 routes through the
+    # bounded MFMA router in its int8 form
+    _check_layer("int6_d2048_e64_top10", T=T, stream=T)
+
+
+def test_int6_tiny_layer_all_tokens():
+    _check_layer("int6_tiny_d256_e16_top2")
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_mixed_precision_layer_at_decode_sizes(T):
+    # int4 routed, int6 shared, int8 router with few tokens: the four calls on the GEMV
+    # kernels (the mixed formats do not take the decode layer's two launches)
+    _check_layer("prefill_32768_mixed", T=T, stream=T, sample=T)
+
+
 def test_prefill_8192_zipf():
     _check_layer("prefill_8192_zipf", sample=24)
 
