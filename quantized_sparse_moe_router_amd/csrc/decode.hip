@@ -72,9 +72,11 @@ struct DnShape {
     static constexpr int ROWS = 4;               // rows per block
     static constexpr int SPLIT = DN_WAVES / ROWS;   // waves per row
     // wave loads per wave in registers at once: one when every slot fits in one load per
-    // wave (a token with 10 experts and the shared one), else a batch of 4
+    // wave (a token with 10 experts and the shared one), else batches of 3 (four tokens
+    // with 10 experts and the shared one: 44 slots, 11 wave loads per row, at most 3 per
+    // wave, so one batch and no load beyond the last slot's)
     static constexpr int ITB_SMALL = 1;
-    static constexpr int ITB_LARGE = 4;
+    static constexpr int ITB_LARGE = 3;
 };
 
 template <int FMT, int D, int F, int ITB>
@@ -115,6 +117,9 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
 #pragma unroll
     for (int u = 0; u < kHPass; ++u)
         hv[u] = hsrc[min(u * DN_THREADS + (int)threadIdx.x, n16 - 1)];
+    // all of the above in flight before the wait for the expert ids: left to itself the
+    // scheduler may place that wait first and request the h chunks only after it
+    __builtin_amdgcn_sched_barrier(0);
     my_e = (lane < P && my_e >= 0 && my_e < a.E) ? my_e : 0;
 
     GroupBits<FMT> wbits[ITB][GPL];
