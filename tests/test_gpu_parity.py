@@ -97,6 +97,10 @@ def _check_layer(name, T=None, sample=None, bias=None, seed=0, stream=0):
     w_ref = oracle.topk_weights(logits_ref, ids_ref)
     wts = layer.weights[:T].cpu().numpy().astype(np.float64)
     assert np.abs(wts - w_ref).max() <= 1e-6
+    # the invariants on the GPU's own outputs: k distinct experts per token, gate weights
+    # positive and summing to 1 up to fp32 rounding
+    assert all(len(set(row)) == k for row in ids.tolist())
+    assert (wts > 0).all() and np.abs(wts.sum(axis=1) - 1.0).max() <= 1e-5
     off_ref, sp_ref, pp_ref, bad = oracle.permute(ids_ref, E)
     assert bad == 0
     assert np.array_equal(layer.offsets.cpu().numpy(), off_ref)
