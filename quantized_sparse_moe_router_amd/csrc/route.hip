@@ -22,14 +22,14 @@ namespace {
 // One wave per expert row.  Lane l holds its vectors v = l + 64 j of the row in
 // registers and walks them for every token; the butterfly is a shuffle-xor tree.
 // PV = elements per 16-byte vector (4 fp32 or 16 int8); NV = vectors per lane.
-template <int FMT, int NV, bool DEVICE_SCOPE_STORE>
+template <int FMT, int NV, bool DEVICE_SCOPE_STORE, int WPB = 4>
 __device__ __forceinline__ void router_gemv_rows(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
     float* logits) {
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int e = blockIdx.x * WPB + (threadIdx.x >> 6);   // WPB rows (waves) per block
     if (e >= E) return;
 
     float w[NV][PV];
@@ -500,13 +500,15 @@ __global__ void __launch_bounds__(256) router_gemv_topk_kernel(
     if (threadIdx.x == 0) atomicExch(counter, 0u);
 }
 
-// Logits only, for a consumer that runs the selection itself (the decode layer).
+// Logits only, for a consumer that runs the selection itself (the decode layer).  One
+// wave (one expert row) per block: E blocks reach every CU, where blocks of 4 rows would
+// leave half of them idle at E = 512.
 template <int FMT, int NV>
-__global__ void __launch_bounds__(256) router_gemv_kernel(
+__global__ void __launch_bounds__(64) router_gemv_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
     float* __restrict__ logits) {
-    router_gemv_rows<FMT, NV, false>(W, scale, bias, x, T, E, d, logits);
+    router_gemv_rows<FMT, NV, false, 1>(W, scale, bias, x, T, E, d, logits);
 }
 
 template <int FMT, int NV>
@@ -589,7 +591,7 @@ hipError_t launch_logits_fmt(const moe_router& r, const uint16_t* x, int T, floa
                              hipStream_t s) {
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
     const int nv = r.d_model / (64 * PV);
-    const dim3 grid((r.n_experts + 3) / 4), block(256);
+    const dim3 grid(r.n_experts), block(64);
 #define MOE_NV(N)                                                                         \
     if (nv == N) {                                                                        \
         router_gemv_kernel<FMT, N><<<grid, block, 0, s>>>(r.w, r.scale, r.bias, x, T,     \
