@@ -60,6 +60,25 @@ __device__ __forceinline__ int dpp(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
 }
 
+// v + v of lane (lane ^ M), M = 16 or 32, with gfx950's v_permlane16/32_swap instead of a
+// round trip through the LDS crossbar: swapping a copy of v with v leaves one operand
+// holding the lower lane of each pair and the other the upper, and fp addition is
+// commutative, so every lane gets the same bits as v + shfl_xor(v, M).
+template <int M>
+__device__ __forceinline__ float add_swapped(float v) {
+    const uint32_t u = __float_as_uint(v);
+    uint32_t lo, hi;
+    if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        lo = r[0]; hi = r[1];
+    } else {
+        static_assert(M == 32, "offset 16 or 32");
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        lo = r[0]; hi = r[1];
+    }
+    return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
 // Sum over aligned groups of G lanes (G a power of two <= 64); every lane of the group
 // ends with the group's sum, combined as the butterfly tree over xor offsets 1..G/2.
 template <int G>
@@ -68,8 +87,8 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (G >= 4) v = v + dpp<kDppXor2>(v);
     if constexpr (G >= 8) v = v + dpp<kDppHalfMirror>(v);
     if constexpr (G >= 16) v = v + dpp<kDppMirror>(v);
-    if constexpr (G >= 32) v = v + shfl_xor(v, 16);
-    if constexpr (G >= 64) v = v + shfl_xor(v, 32);
+    if constexpr (G >= 32) v = add_swapped<16>(v);
+    if constexpr (G >= 64) v = add_swapped<32>(v);
     return v;
 }
 
