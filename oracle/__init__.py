@@ -71,6 +71,7 @@ def _declare(L):
     sig = {
         "oracle_half_to_double": (ctypes.c_double, [ctypes.c_uint16]),
         "oracle_double_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
+        "oracle_double_to_bf16_n": (None, [_P, _I64, _P]),
         "oracle_code": (_I, [_I, _P, _I]),
         "oracle_dequant_row": (None, [_I, _P, _P, _I, _I64, _P]),
         "oracle_router_logits": (None, [_P, _P, _I64, _P]),
@@ -84,6 +85,7 @@ def _declare(L):
         "oracle_layer_tokens": (None, [_P, _P, _P, _P, _P, _I64, _I, _P, _P, _P, _P, _P]),
         "oracle_residual": (None, [_P, _P, _I64, _P]),
         "oracle_num_threads": (_I, []),
+        "oracle_set_num_threads": (None, [_I]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -137,6 +139,14 @@ def half_to_double(h):
 
 def double_to_bf16(v):
     return lib().oracle_double_to_bf16(float(v))
+
+
+def double_to_bf16_array(v):
+    """double_to_bf16 over an array: uint16 bit patterns of the same shape."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_double_to_bf16_n(_ptr(v), v.size, _ptr(out))
+    return out
 
 
 def code(fmt, row_bytes, c):
@@ -273,3 +283,7 @@ def residual(x_bits, out):
 
 def num_threads():
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n):
+    lib().oracle_set_num_threads(int(n))

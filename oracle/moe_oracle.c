@@ -117,6 +117,12 @@ uint16_t oracle_double_to_bf16(double v)
     return (uint16_t)(u >> 16);
 }
 
+/* The same rounding over an array (n values). */
+void oracle_double_to_bf16_n(const double* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_double_to_bf16(v[i]);
+}
+
 /* ------------------------------------------------------------------ weight codes */
 
 /* Signed code of element c of one packed row. */
@@ -433,6 +439,16 @@ void oracle_residual(const uint16_t* x, const double* out, int64_t n, uint16_t* 
         double s = (double)bf16_to_float(x[i]) + o;   /* exact: two bf16 values */
         x_next[i] = oracle_double_to_bf16(s);
     }
+}
+
+/* Threads the OpenMP loops above use from now on (n >= 1). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
 }
 
 int oracle_num_threads(void)

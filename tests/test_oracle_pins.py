@@ -59,6 +59,17 @@ def test_bf16_rounding_golden():
             assert oracle.double_to_bf16(float(a)) == int(b, 16), ln
 
 
+def test_bf16_array_rounding_golden():
+    vals, want = [], []
+    for ln in _lines("fp16_bf16.txt"):
+        kind, a, b = ln.split()
+        if kind == "bf16":
+            vals.append(float(a))
+            want.append(int(b, 16))
+    got = oracle.double_to_bf16_array(np.array(vals))
+    assert got.tolist() == want
+
+
 def test_bf16_rounding_matches_torch_on_fp32_values():
     g = torch.Generator().manual_seed(7)
     v = torch.randn(20000, generator=g) * torch.exp(torch.randn(20000, generator=g) * 8)
@@ -185,6 +196,33 @@ def test_router_int8_exact_on_integers():
     got = oracle.router_logits(r, si.bits16(x))
     ref = ((x.double() @ q.double().T) * 0.25 + b.double()).numpy()
     assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_router_int8_order_golden():
+    # hand-derived int8 cases (tests/golden/router_int8_order.txt): the code dealing (16
+    # per vector), the chain order, the butterfly and the two roundings of scale and bias
+    # each change the expected bits
+    n = 0
+    for ln in _lines("router_int8_order.txt"):
+        head, *trip = [p.strip() for p in ln.split("|")]
+        name, d, s_hex, bias, expect = head.split()
+        d = int(d)
+        x = torch.zeros((1, d), dtype=torch.bfloat16)
+        q = torch.zeros((1, d), dtype=torch.int8)
+        for t in trip:
+            idx, xv, qv = t.split()
+            assert float(torch.tensor(float(xv)).to(torch.bfloat16)) == float(xv)
+            assert -127 <= int(qv) <= 127
+            x[0, int(idx)] = float(xv)
+            q[0, int(idx)] = int(qv)
+        assert float(np.float32(float(bias))) == float(bias)
+        r = {"fmt": oracle.FMT_INT8_ROW, "E": 1, "d": d, "w": q.numpy(),
+             "scale": np.array([int(s_hex, 16)], np.uint16),
+             "bias": np.array([float(bias)], np.float32)}
+        got = oracle.router_logits(r, si.bits16(x))[0, 0]
+        assert got == np.float32(float(expect)), (name, got)
+        n += 1
+    assert n == 4
 
 
 def test_router_fp32_within_rounding_bound_of_exact():
