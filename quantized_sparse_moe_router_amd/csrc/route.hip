@@ -470,21 +470,28 @@ __global__ void __launch_bounds__(256) route_bounded_select_kernel(
 }
 
 // Few tokens: logits and selection in one launch.  Every block computes its rows' logits
-// for all tokens, writes them with device-scope stores, waits for those stores, then
-// counts itself in; the last block to arrive reads every logit with device-scope loads,
+// for all tokens and writes them with device-scope atomic stores, which go through to the
+// device's point of coherence.  Each wave then waits until its stores have completed
+// (s_waitcnt vmcnt(0)), the block meets at a barrier, and one thread counts the block in
+// with a device-scope atomic increment.  The last block to arrive reads every logit with
+// device-scope atomic loads (served from the point of coherence, not from a stale cache),
 // runs the selection for all tokens and resets the counter, leaving the workspace as it
-// found it.  No cache-wide flush or invalidation is involved.
+// found it.  A release fence at device scope would also write back the whole L2 of each
+// XCD (buffer_wbl2), measured at 3.7 us per call here; the completed device-scope
+// stores already give the last block every logit.
 template <int FMT, int NV, int NPL>
 __global__ void __launch_bounds__(256) router_gemv_topk_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d, int k,
     float* logits, int32_t* __restrict__ ids, float* __restrict__ weights, unsigned* counter) {
     router_gemv_rows<FMT, NV, true>(W, scale, bias, x, T, E, d, logits);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // this block's stores done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
     __syncthreads();
     __shared__ int is_last;
     __shared__ uint64_t scratch[4][128];
-    if (threadIdx.x == 0) is_last = (atomicAdd(counter, 1u) == gridDim.x - 1) ? 1 : 0;
+    if (threadIdx.x == 0)
+        is_last = (__hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) ? 1 : 0;
     __syncthreads();
     if (!is_last) return;
     const int lane = threadIdx.x & 63;
