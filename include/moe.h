@@ -233,6 +233,25 @@ moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shar
                               const float* weights, const uint16_t* residual, uint16_t* out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_dequant_probe -- a verification entry point: runs the weight decoder of one of the
+ * two expert paths over n_groups consecutive 32-code groups of a packed matrix, so that
+ * every decoded weight can be compared bit for bit with its exact value s * q (expert
+ * weights at 4 and 6 bit [本地部署Qwen3.8-Flash-Next模型的两条路线 (blog.cycleuser.org),
+ * section 精度和内存占用]).
+ *   fmt   MOE_FMT_INT4_G32 or MOE_FMT_INT6_G32
+ *   w     packed codes of n_groups groups (16 or 24 bytes each), device, 16-byte aligned
+ *   s     fp16 scales [n_groups], device
+ *   form 0: out fp32 [n_groups][32]: the few-token (GEMV) kernels' group arithmetic
+ *           (dot product on offset codes, zero-point removal, scale) evaluated on one-hot
+ *           activations; equals s * q exactly when the decoder is right.
+ *   form 1: out bf16 [n_groups][32]: the grouped GEMM's MFMA operand, bf16(s * q) rounded
+ *           to nearest even.
+ * Enqueues one launch on `stream`.  n_groups = 0 is a no-op; above 2^31 is rejected.
+ */
+moe_status moe_dequant_probe(int32_t fmt, int32_t form, const uint8_t* w, const uint16_t* s,
+                             int64_t n_groups, void* out, void* stream);
+
 /* Workspace bytes an operation needs for these sizes (0 = none).  Pure host function. */
 size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d,
                           int32_t d_ff);

@@ -14,7 +14,7 @@ from ._lib import (  # noqa: F401
     MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE,
     MOE_OP_EXPERTS_DECODE, MoeError,
     moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_layer_decode, moe_experts_decode,
-    moe_workspace_size,
+    moe_dequant_probe, moe_workspace_size,
     moe_check_device_error, moe_status_string, moe_last_error, moe_version,
     router_desc, experts_desc,
 )
@@ -139,6 +139,12 @@ class MoeLayer:
         T = x.shape[0]
         moe_route(self.router, x, T, self.k, ids, weights, self.logits, self.ws_route)
         return self.logits[:T]
+
+    def route_only(self, x):
+        """moe_route alone (no logits returned) into ids and weights."""
+        T = x.shape[0]
+        moe_route(self.router, x, T, self.k, self.ids, self.weights, None, self.ws_route)
+        return self.ids[:T]
 
     def decode(self, x, residual=None, out=None):
         T = x.shape[0]

@@ -21,7 +21,8 @@ MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE, MOE_OP_EXP
     0, 1, 2, 3, 4
 
 EXPORTED = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-            "moe_layer_decode", "moe_experts_decode", "moe_workspace_size", "moe_check_device_error", "moe_status_string",
+            "moe_layer_decode", "moe_experts_decode", "moe_dequant_probe",
+            "moe_workspace_size", "moe_check_device_error", "moe_status_string",
             "moe_last_error", "moe_version")
 
 
@@ -64,6 +65,7 @@ def lib():
             "moe_combine": [P, P, P, P, P, I32, I32, I32, P, P],
             "moe_layer_decode": [P, P, P, P, I32, I32, P, P, P, P, P, SZ, P],
             "moe_experts_decode": [P, P, P, I32, I32, P, P, P, P, P, SZ, P],
+            "moe_dequant_probe": [I32, I32, P, P, ctypes.c_int64, P, P],
             "moe_workspace_size": [I32, I32, I32, I32, I32, I32],
             "moe_check_device_error": [P],
             "moe_status_string": [I32],
@@ -169,6 +171,12 @@ def moe_experts_decode(routed, shared, x, T, k, ids, weights, residual, out, ws,
                                   _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream))
     _check(st, "moe_experts_decode")
+
+
+def moe_dequant_probe(fmt, form, w, s, n_groups, out, stream=None):
+    st = lib().moe_dequant_probe(int(fmt), int(form), _ptr(w), _ptr(s), int(n_groups),
+                                 _ptr(out), _stream(stream))
+    _check(st, "moe_dequant_probe")
 
 
 def moe_check_device_error(stream=None):

@@ -375,6 +375,25 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
     return hip_status(e, "moe_layer_decode");
 }
 
+moe_status moe_dequant_probe(int32_t fmt, int32_t form, const uint8_t* w, const uint16_t* s,
+                             int64_t n_groups, void* out, void* stream) {
+    if (fmt != MOE_FMT_INT4_G32 && fmt != MOE_FMT_INT6_G32)
+        return fail(MOE_ERR_INVALID_ARG, "moe_dequant_probe: format %d is not INT4_G32/INT6_G32",
+                    fmt);
+    if (form != 0 && form != 1)
+        return fail(MOE_ERR_INVALID_ARG, "moe_dequant_probe: form %d is not 0 or 1", form);
+    if (n_groups < 0 || n_groups > ((int64_t)1 << 31))
+        return fail(MOE_ERR_INVALID_ARG, "moe_dequant_probe: n_groups = %lld",
+                    (long long)n_groups);
+    if (n_groups == 0) return ok();
+    if (!w || !s || !out || !aligned16(w) || !aligned16(out) || ((uintptr_t)s & 1u))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_dequant_probe: w/out NULL or not 16-byte aligned, or s NULL/odd");
+    return hip_status(moe::launch_dequant_probe(fmt, form, w, s, n_groups, out,
+                                                static_cast<hipStream_t>(stream)),
+                      "moe_dequant_probe");
+}
+
 moe_status moe_check_device_error(void* stream) {
     hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_status(e, "moe_check_device_error: sync");

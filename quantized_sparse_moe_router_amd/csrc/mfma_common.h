@@ -59,6 +59,50 @@ __device__ __forceinline__ P* uniform_ptr(P* p) {
     return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
 
+// ---- dequantisation of packed weight codes into bf16 MFMA operands (the grouped GEMM
+// and the dequantisation probe call these same functions)
+// The codes of one 32-code group: int4 = 16 bytes (a), int6 = 24 bytes (a, then b).
+template <int FMT>
+struct GroupCodes {
+    u32x4_t a;
+    u32x2_t b;
+};
+
+// Chunk c (codes 8c..8c+7) of a group, split into byte-aligned code fields: lo holds
+// codes 8c, 8c+2, 8c+4, 8c+6 in bytes 0..3, hi codes 8c+1, 8c+3, 8c+5, 8c+7.
+template <int FMT>
+__device__ __forceinline__ void chunk_codes(const GroupCodes<FMT>& g, int c, uint32_t& lo,
+                                            uint32_t& hi) {
+    if constexpr (FMT == MOE_FMT_INT4_G32) {
+        const uint32_t w = g.a[c];      // byte i: code 8c+2i (low nibble), 8c+2i+1 (high)
+        lo = w & 0x0f0f0f0fu;
+        hi = (w >> 4) & 0x0f0f0f0fu;
+    } else {
+        // 8 six-bit codes = bits [48c, 48c + 48) of the 24-byte group
+        const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
+        const int bit = 48 * c, wi = bit / 32, sh = bit % 32;
+        const uint64_t v = ((uint64_t)w6[wi] | ((uint64_t)w6[wi + 1] << 32)) >> sh;
+        uint32_t l = 0, h = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            l |= (uint32_t)((v >> (12 * p)) & 63u) << (8 * p);
+            h |= (uint32_t)((v >> (12 * p + 6)) & 63u) << (8 * p);
+        }
+        lo = l;
+        hi = h;
+    }
+    asm volatile("" : "+v"(lo), "+v"(hi));   // keep the byte fields for byte-to-float ops
+}
+
+// Codes 8c+2b and 8c+2b+1 -> packed bf16 pair s * (code - zero point).
+template <int FMT>
+__device__ __forceinline__ uint32_t chunk_pair(uint32_t lo, uint32_t hi, int b, float s) {
+    const float zc = (FMT == MOE_FMT_INT4_G32) ? -8.0f * s : -32.0f * s;
+    const float e0 = (float)((lo >> (8 * b)) & 0xffu);
+    const float e1 = (float)((hi >> (8 * b)) & 0xffu);
+    return pack_bf16(__builtin_fmaf(e0, s, zc), __builtin_fmaf(e1, s, zc));
+}
+
 }  // namespace
 }  // namespace moe
 

@@ -164,4 +164,10 @@ hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* share
                              int32_t* ids, float* weights, const uint16_t* residual,
                              uint16_t* out, void* ws, hipStream_t s);
 
+// The two expert paths' weight decoders over n_groups consecutive 32-code groups (form 0:
+// fp32 out[n_groups][32], the GEMV arithmetic on one-hot activations; form 1: bf16
+// out[n_groups][32], the grouped GEMM's operand conversion).
+hipError_t launch_dequant_probe(int fmt, int form, const uint8_t* w, const uint16_t* s,
+                                int64_t n_groups, void* out, hipStream_t st);
+
 }  // namespace moe

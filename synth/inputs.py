@@ -213,6 +213,56 @@ def make_layer(w, seed=0, layer=0, device="cpu", bias=None, with_shared=True,
     return Layer(router, routed, shared)
 
 
+_QRANGE = {"int4_g32": (-8, 7), "int6_g32": (-32, 31)}
+_PACK = {"int4_g32": pack_int4, "int6_g32": pack_int6}
+
+
+def _all_codes_matrix(fmt, E, N, K, gen, device):
+    """Packed codes and fp16 scales of E matrices [N][K] in which every code of the format,
+    the lowest included (int4 -8, int6 -32), sits at every position of a group: row n,
+    element c of matrix e holds qmin + ((n + c + e) mod ncodes) for the first ncodes rows,
+    uniform random codes elsewhere.  Scales are fp16 of U(0.5, 1.5) * 0.02 / sd, sd the
+    standard deviation of a code drawn uniformly from the format's range (int4 4.61, int6
+    18.47), so the weights spread like the N(0, 0.02) draws of make_layer; every 7th group
+    of a matrix (in row-major group order, from a random start) has scale 0."""
+    qmin, qmax = _QRANGE[fmt]
+    nc = qmax - qmin + 1
+    q = torch.randint(qmin, qmax + 1, (E, N, K), generator=gen, device=device,
+                      dtype=torch.int32)
+    n = torch.arange(min(nc, N), device=device, dtype=torch.int32)[:, None]
+    c = torch.arange(K, device=device, dtype=torch.int32)[None, :]
+    for e in range(E):
+        q[e, :min(nc, N)] = qmin + (n + c + e) % nc
+    sd = ((nc * nc - 1) / 12.0) ** 0.5
+    s = (torch.rand((E, N, K // 32), generator=gen, device=device) + 0.5) * (0.02 / sd)
+    s = s.to(torch.float16)
+    start = int(torch.randint(0, 7, (1,), generator=gen, device=device))
+    flat = s.view(-1)
+    flat[start::7] = 0
+    return _PACK[fmt](q), s.contiguous()
+
+
+def make_layer_all_codes(w, seed=0, device="cpu", with_shared=True):
+    """A layer of workload ``w``'s shapes whose expert codes cover the whole code range at
+    every group position, with some all-zero-scale groups (see _all_codes_matrix); the
+    router is drawn as in make_layer.  For parity tests of the decoders."""
+    dev = torch.device(device)
+    base = make_layer(w, seed=seed, device=device, with_shared=False)
+    tid = 1 << 21
+
+    def ex(fmt, E, salt):
+        mats = []
+        for t, (N, K) in enumerate(((w.F, w.d), (w.F, w.d), (w.d, w.F))):
+            mats.append(_all_codes_matrix(fmt, E, N, K,
+                                          _gen(dev, w.wid, seed, tid, salt, t), dev))
+        (pg, sg), (pu, su), (pd, sd) = mats
+        return ExpertSet(fmt, E, w.d, w.F, pg, pu, pd, sg, su, sd)
+
+    routed = ex(w.routed_fmt, w.E, 0)
+    shared = ex(w.shared_fmt, 1, 1) if with_shared else None
+    return Layer(base.router, routed, shared)
+
+
 def make_tokens(w, T=None, seed=0, layer=0, device="cpu", stream=0):
     """bf16 [T][d] activations, N(0, 1) rounded to bf16."""
     T = w.T if T is None else T

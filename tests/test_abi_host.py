@@ -205,6 +205,18 @@ def test_layer_decode_rejects(L):
     assert L.moe_workspace_size(_lib.MOE_OP_LAYER_DECODE, 7, 10, 512, 2048, 512) == 0
 
 
+def test_dequant_probe_rejects(L):
+    P = ctypes.c_void_p
+    dummy = P(16)
+    # bad format, bad form, negative count, NULL pointers: rejected before any launch
+    assert L.moe_dequant_probe(0, 0, dummy, dummy, 1, dummy, None) == -1
+    assert L.moe_dequant_probe(2, 2, dummy, dummy, 1, dummy, None) == -1
+    assert L.moe_dequant_probe(2, 0, dummy, dummy, -1, dummy, None) == -1
+    assert L.moe_dequant_probe(3, 1, None, dummy, 1, dummy, None) == -1
+    assert L.moe_dequant_probe(2, 0, P(8), dummy, 1, dummy, None) == -1   # misaligned
+    assert L.moe_dequant_probe(2, 0, None, None, 0, None, None) == 0      # no-op
+
+
 def test_bench_refuses_more_than_one_gpu():
     import os
     import subprocess

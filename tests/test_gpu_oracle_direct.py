@@ -1,0 +1,238 @@
+"""GPU parity of the paths the bench times, against the CPU oracle directly:
+
+  - moe_layer_decode and moe_experts_decode (one token and four tokens) on the decode
+    layer and on a Zipf-biased layer of the 48-layer sweep;
+  - the 48-layer chained decode sweep at one and four tokens per step, teacher-forced:
+    every layer's input x_l is downloaded from the GPU's own chain and the oracle evaluates
+    that layer on it, so output differences within tolerance cannot cascade into routing
+    differences at the next layer;
+  - layers whose codes cover the whole code range at every group position (int4 -8 and
+    int6 -32 included) with some all-zero-scale groups, through the GEMV, decode-layer and
+    MFMA paths, and the two weight decoders bit for bit (moe_dequant_probe).
+
+The layer: 512 routed experts, 10 of them plus one shared expert per token, 48 layers
+[Strata 与 Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会]; 4- and 6-bit expert
+weights [本地部署Qwen3.8-Flash-Next模型的两条路线 (blog.cycleuser.org), section 精度和内存占用].
+Bar: ids bit-exact, |dw| <= 1e-6, outputs |g - r| <= 2e-2 + 1e-2 |r| and
+rel-Frobenius <= 1e-2 (the layer tolerance), decoded weights bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import inputs as si
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL, FROB = 2e-2, 1e-2, 1e-2
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_sparse_moe_router_amd as moe
+    return moe
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _bits_to_f64(b):
+    return (np.asarray(b, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _close(got, ref, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    assert not bad.any(), "%s: %d elements out of tolerance, max err %.3g" % (
+        what, int(bad.sum()), float(err.max()))
+    frob = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert frob <= FROB, "%s: rel-Frobenius %.3g" % (what, frob)
+    return float(err.max())
+
+
+def _check_routing(ids, wts, res, k, what):
+    assert np.array_equal(ids, res["ids"]), what + ": ids differ"
+    assert np.abs(wts.astype(np.float64) - res["w"]).max() <= 1e-6, what + ": weights"
+    assert all(len(set(r)) == k for r in ids.tolist())
+
+
+# ---------------------------------------------------------------- decode entry points
+
+@pytest.mark.parametrize("name,bias,T", [
+    ("decode_d2048_e512_top10_t1", None, 1),
+    ("decode_d2048_e512_top10_t1", None, 4),
+    ("decode_sweep_48_layers", "zipf", 1),
+    ("decode_sweep_48_layers", "zipf", 4),
+])
+def test_decode_entry_points_against_oracle(name, bias, T):
+    moe = _gpu()
+    w = synth.WORKLOADS[name]
+    print("case %s bias=%s T=%d" % (name, bias, T), flush=True)
+    lay = synth.make_layer(w, seed=0, layer=7, device="cuda", bias=bias)
+    r_h, ex_h, sh_h = lay.router.host(), lay.routed.host(), lay.shared.host()
+    x = synth.make_tokens(w, T=T, seed=21, device="cuda")
+    res_in = synth.make_tokens(w, T=T, seed=22, device="cuda")
+    m = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, T)
+    assert m.can_decode
+    out = m.decode(x).clone()
+    torch.cuda.synchronize()
+    moe.moe_check_device_error()
+    ref = oracle.layer_tokens(r_h, ex_h, sh_h, si.bits16(x), np.arange(T, dtype=np.int32),
+                              w.k)
+    _check_routing(m.ids[:T].cpu().numpy(), m.weights[:T].cpu().numpy(), ref, w.k,
+                   "moe_layer_decode")
+    _close(_f64(out), ref["out"], "moe_layer_decode out")
+    # the same with the residual folded in: x_next = bf16(res + bf16(out))
+    nxt = m.decode(x, residual=res_in).clone()
+    want = oracle.residual(si.bits16(res_in), ref["out"])
+    _close(_f64(nxt), _bits_to_f64(want), "moe_layer_decode residual")
+    # moe_experts_decode from the ids and weights of that call
+    out2 = m.experts_decode(x).clone()
+    torch.cuda.synchronize()
+    moe.moe_check_device_error()
+    _close(_f64(out2), ref["out"], "moe_experts_decode out")
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+
+
+# ---------------------------------------------------------------- 48-layer chain
+
+# A plain residual x_{l+1} = bf16(x_l + bf16(out_l)) with no normalisation grows the stream
+# like x + c x^2 (the expert FFN is quadratic in its input through SwiGLU): measured with
+# the oracle on these layers, rms(out) is 0.26 at layer 0, 0.65 at layer 10, 19.7 at layer
+# 16 and 336 at layer 17, after which bf16 overflows.  The layer tolerance (max-abs 2e-2)
+# is stated for outputs of the configured scale, so the plain chain is checked over its
+# first CHAIN_PLAIN layers, where rms(out) stays below 0.7.
+CHAIN_PLAIN = 10
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_sweep_chain_teacher_forced():
+    moe = _gpu()
+    w = synth.WORKLOADS["decode_sweep_48_layers"]
+    n_layers = CHAIN_PLAIN
+    lays = [synth.make_layer(w, seed=0, layer=l, device="cuda") for l in range(n_layers)]
+    chains = {}
+    for T in (1, 4):                                  # the chains as the bench runs them
+        mls = [moe.MoeLayer(L.router, L.routed, L.shared, w.k, T) for L in lays]
+        xs = [synth.make_tokens(w, T=T, seed=0, device="cuda")]
+        xs += [torch.empty_like(xs[0]) for _ in range(n_layers)]
+        for l in range(n_layers):
+            mls[l].decode(xs[l], residual=xs[l], out=xs[l + 1])
+        torch.cuda.synchronize()
+        moe.moe_check_device_error()
+        ids = [m.ids[:T].cpu().numpy().copy() for m in mls]
+        wts = [m.weights[:T].cpu().numpy().copy() for m in mls]
+        chains[T] = (mls, xs, ids, wts)
+        print("chain T=%d built" % T, flush=True)
+    worst = {1: 0.0, 4: 0.0}
+    for l in range(n_layers):
+        L = lays[l]
+        r_h, ex_h, sh_h = L.router.host(), L.routed.host(), L.shared.host()
+        for T, (mls, xs, ids, wts) in chains.items():
+            # teacher forcing: layer l on the GPU's own x_l, plain output
+            plain = mls[l].decode(xs[l]).clone()
+            torch.cuda.synchronize()
+            assert np.array_equal(mls[l].ids[:T].cpu().numpy(), ids[l])
+            # the chain's x_{l+1} is bf16(x_l + plain), two fp32 steps done here by torch
+            host_next = (xs[l].cpu().float() + plain.cpu().float()).to(torch.bfloat16)
+            assert torch.equal(xs[l + 1].cpu().view(torch.int16),
+                               host_next.view(torch.int16)), "T %d layer %d residual" % (T, l)
+            ref = oracle.layer_tokens(r_h, ex_h, sh_h, si.bits16(xs[l]),
+                                      np.arange(T, dtype=np.int32), w.k)
+            _check_routing(ids[l], wts[l], ref, w.k, "T %d layer %d" % (T, l))
+            worst[T] = max(worst[T], _close(_f64(plain), ref["out"],
+                                            "T %d layer %d out" % (T, l)))
+        del r_h, ex_h, sh_h
+    print("chains: %d layers at T = 1 and 4, ids bit-exact, max |out - oracle| %.3g / %.3g"
+          % (n_layers, worst[1], worst[4]), flush=True)
+
+
+# ---------------------------------------------------------------- every code value
+
+def _all_codes(name):
+    w = synth.WORKLOADS[name]
+    return w, synth.make_layer_all_codes(w, seed=0, device="cuda")
+
+
+@pytest.mark.parametrize("name", ["tiny_d256_e16_top2", "int6_tiny_d256_e16_top2",
+                                  "decode_d2048_e512_top10_t1"])
+def test_dequant_probe_every_code(name):
+    moe = _gpu()
+    w, lay = _all_codes(name)
+    for ex in (lay.routed, lay.shared):
+        fmt = si.FMT_BY_NAME[ex.fmt]
+        for mat, sc, K in ((ex.w_gate, ex.s_gate, ex.d), (ex.w_up, ex.s_up, ex.d),
+                           (ex.w_down, ex.s_down, ex.F)):
+            if ex.E > 16:      # the large set: its first 16 experts are enough
+                mat, sc = mat[:16].contiguous(), sc[:16].contiguous()
+            n_groups = sc.numel()
+            g32 = torch.empty((n_groups, 32), dtype=torch.float32, device="cuda")
+            b16 = torch.empty((n_groups, 32), dtype=torch.bfloat16, device="cuda")
+            moe.moe_dequant_probe(fmt, 0, mat, sc, n_groups, g32)
+            moe.moe_dequant_probe(fmt, 1, mat, sc, n_groups, b16)
+            torch.cuda.synchronize()
+            s_h = si.bits16(sc).reshape(-1)
+            ref = oracle.dequant_rows(fmt, mat.cpu().numpy(), s_h, K).reshape(-1)
+            # every code occurs, the lowest included, and so do zero-scale groups
+            s64 = np.repeat(si.bits16(sc).reshape(-1).view(np.float16).astype(np.float64), 32)
+            q = ref[s64 > 0] / s64[s64 > 0]
+            qmin, qmax = (-8, 7) if ex.fmt == "int4_g32" else (-32, 31)
+            assert q.min() == qmin and q.max() == qmax and (s64 == 0).any()
+            # s * q is exact in fp32 (11-bit scale times a code of at most 6 bits)
+            got32 = g32.cpu().numpy().reshape(-1)
+            assert np.array_equal(got32.astype(np.float64), ref), "%s GEMV decode" % ex.fmt
+            # bf16 bit patterns equal, except that +0 and -0 (the same value) are not told
+            # apart: a zero-scale group gives the oracle s * q = -0 for q < 0, while the
+            # kernel's u * s - 8 s gives +0
+            want16 = oracle.double_to_bf16_array(ref)
+            got16 = si.bits16(b16).reshape(-1)
+            zero = np.uint16(0x7fff)
+            want16 = np.where((want16 & zero) == 0, 0, want16)
+            got16 = np.where((got16 & zero) == 0, 0, got16)
+            assert np.array_equal(got16, want16), "%s MFMA decode: %d differ" % (
+                ex.fmt, int((got16 != want16).sum()))
+
+
+@pytest.mark.parametrize("name,T", [
+    ("tiny_d256_e16_top2", 4),          # GEMV path and the decode layer
+    ("tiny_d256_e16_top2", 100),        # grouped MFMA GEMM
+    ("int6_tiny_d256_e16_top2", 4),
+    ("int6_tiny_d256_e16_top2", 100),
+    ("decode_d2048_e512_top10_t1", 1),
+    ("decode_d2048_e512_top10_t1", 17),
+])
+def test_every_code_through_the_layer(name, T):
+    moe = _gpu()
+    w, lay = _all_codes(name)
+    print("case all-codes %s T=%d" % (name, T), flush=True)
+    # the lowest codes are present in every matrix
+    for ex in (lay.routed, lay.shared):
+        if ex.fmt == "int4_g32":
+            g = ex.w_gate[:1].cpu().numpy()
+            assert ((g & 15) == 0).any() and ((g >> 4) == 0).any()
+        assert (ex.s_gate == 0).any() and (ex.s_down == 0).any()
+    r_h, ex_h, sh_h = lay.router.host(), lay.routed.host(), lay.shared.host()
+    x = synth.make_tokens(w, T=T, seed=31, device="cuda")
+    m = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, T)
+    out = m.forward(x).clone()
+    torch.cuda.synchronize()
+    moe.moe_check_device_error()
+    ref = oracle.layer_tokens(r_h, ex_h, sh_h, si.bits16(x), np.arange(T, dtype=np.int32),
+                              w.k, keep_pairs=True)
+    _check_routing(m.ids[:T].cpu().numpy(), m.weights[:T].cpu().numpy(), ref, w.k, name)
+    _, _, pp_ref, _ = oracle.permute(ref["ids"], w.E)
+    got_pairs = _f64(m.y_pairs[torch.from_numpy(pp_ref).long().cuda()])
+    _close(got_pairs, ref["y_sel"].reshape(-1, w.d), name + " pair rows")
+    _close(_f64(m.y_shared[:T]), ref["y_shared"], name + " shared rows")
+    _close(_f64(out), ref["out"], name + " out")
+    if m.can_decode:
+        dec = m.decode(x).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.view(torch.int16), out.view(torch.int16))

@@ -70,7 +70,33 @@ def _run(moe, lay, w, x):
     return layer, out
 
 
-def _check_layer(name, T=None, sample=None, bias=None, seed=0, stream=0):
+def _check_tiles(layer, w, x_h, ex_h, sh_h, ids_ref, off_ref, sp_ref, T):
+    """Pair rows at the first and last row of every (expert, 256-row tile) entry of the
+    grouped GEMM's work list, which includes every expert's last row, and shared-expert
+    rows at the first and last token of every 256-token tile, against the oracle."""
+    k, BM = w.k, 256
+    pos = []
+    for e in range(w.E):
+        for m0 in range(int(off_ref[e]), int(off_ref[e + 1]), BM):
+            pos += [m0, min(m0 + BM, int(off_ref[e + 1])) - 1]
+    pos = np.unique(np.array(pos, np.int64))
+    pairs = sp_ref[pos]
+    tok = (pairs // k).astype(np.int32)
+    exp = ids_ref.reshape(-1)[pairs].astype(np.int32)
+    ref = oracle.expert_ffn_pairs(ex_h, x_h, tok, exp)
+    got = _bf16_np(layer.y_pairs[torch.from_numpy(pos).long().cuda()])
+    _close(got, ref, "pair rows at every tile's first and last row (%d rows)" % pos.size)
+    nrm = np.linalg.norm(got - ref, axis=1) <= FROB * np.linalg.norm(ref, axis=1) + 1e-6
+    assert nrm.all(), "%d pair rows above the per-pair bound" % int((~nrm).sum())
+    st = np.unique(np.concatenate([np.arange(0, T, BM), np.minimum(np.arange(0, T, BM) + BM,
+                                                                   T) - 1])).astype(np.int32)
+    ref_sh = oracle.expert_ffn_pairs(sh_h, x_h, st, np.zeros_like(st))
+    got_sh = _bf16_np(layer.y_shared[torch.from_numpy(st).long().cuda()])
+    _close(got_sh, ref_sh, "shared rows at every tile's first and last token")
+    print("tile coverage: %d pair rows, %d shared rows" % (pos.size, st.size), flush=True)
+
+
+def _check_layer(name, T=None, sample=None, bias=None, seed=0, stream=0, tiles=False):
     moe = _gpu()
     w, lay, (r_h, ex_h, sh_h) = _setup(name, bias=bias, seed=seed)
     T = w.T if T is None else T
@@ -106,6 +132,9 @@ def _check_layer(name, T=None, sample=None, bias=None, seed=0, stream=0):
     assert np.array_equal(layer.offsets.cpu().numpy(), off_ref)
     assert np.array_equal(layer.sorted_pairs[:T * k].cpu().numpy(), sp_ref)
     assert np.array_equal(layer.pair_pos[:T * k].cpu().numpy(), pp_ref)
+
+    if tiles:
+        _check_tiles(layer, w, x_h, ex_h, sh_h, ids_ref, off_ref, sp_ref, T)
 
     # experts and combine: every token, or a sample
     if sample is None or sample >= T:
@@ -173,15 +202,15 @@ def test_mixed_precision_layer_at_decode_sizes(T):
 
 
 def test_prefill_8192_zipf():
-    _check_layer("prefill_8192_zipf", sample=24)
+    _check_layer("prefill_8192_zipf", sample=24, tiles=True)
 
 
 def test_prefill_32768_mixed_zipf():
-    _check_layer("prefill_32768_mixed", sample=16)
+    _check_layer("prefill_32768_mixed", sample=16, tiles=True)
 
 
 def test_prefill_32768_mixed_uniform():
-    _check_layer("prefill_32768_mixed", sample=16, bias="none")
+    _check_layer("prefill_32768_mixed", sample=16, bias="none", tiles=True)
 
 
 def test_batch_invariance_and_rerun_determinism():
