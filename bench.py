@@ -73,6 +73,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=640)
     p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--reps", type=int, default=20,
+                   help="repetitions (at least 20) of each timed region for median and min")
     p.add_argument("--copies", type=int, default=32,
                    help="distinct layer copies rotated through (defeats the 256 MB MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -105,28 +107,48 @@ def expert_bytes(ex):
     return ex.nbytes() // ex.E
 
 
-def time_graph(fn, reps, warm=2):
-    """Capture fn() in a graph, replay; returns ms per replay (HIP events)."""
+def capture(fn, eager=True):
+    """Capture fn() into a HIP graph (after one eager pass on a side stream, unless the
+    calls have run eagerly before)."""
     import torch
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn()                                  # eager warm-up on the capture stream
-    torch.cuda.current_stream().wait_stream(s)
+    if eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_replay(g, lead_cycles=2_000_000):
+    """GPU time (ms) of one replay of g between two events on the current stream.  A GPU
+    sleep is queued ahead of the first event so that the host has enqueued the replay
+    before the GPU reaches it: the events then bracket GPU work only."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(lead_cycles)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def time_graph(fn, reps, warm=2):
+    """Capture fn() in a graph; returns (median ms per replay over `reps` replays, each
+    timed on its own, min, graph)."""
+    import statistics
+    g = capture(fn)
     for _ in range(warm):
         g.replay()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / reps, g
+    ts = [timed_replay(g) for _ in range(reps)]
+    return statistics.median(ts), min(ts), g
 
 
 def main():
@@ -181,49 +203,92 @@ def main():
         if not torch.equal(layers[i].out[:1].view(torch.int16), ref[i].view(torch.int16)):
             raise SystemExit("bench.py: moe_layer_decode differs from the four calls")
 
-    reps = max(1, -(-args.steps // L))
-    warm = max(1, -(-args.warmup // L))
-    steps = reps * L
+    K, W = max(1, args.steps), max(0, args.warmup)
+    REPS = max(20, args.reps)
 
-    def timed(fn, n_reps):
-        if args.eager:
-            for _ in range(warm):
-                fn()
-            torch.cuda.synchronize()
-            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            t0.record()
-            for _ in range(n_reps):
-                fn()
-            t1.record()
-            torch.cuda.synchronize()
-            return t0.elapsed_time(t1) / n_reps
-        return time_graph(fn, n_reps, warm)[0]
+    def steps_fn(first, n, call):
+        def fn():
+            for i in range(first, first + n):
+                call(i % L)
+        return fn
 
-    ms_step = timed(step_all, reps) / L
+    if args.eager:
+        def run_region(first, n, call):
+            import statistics
+            steps_fn(first, n, call)()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(REPS):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                steps_fn(first, n, call)()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return statistics.median(ts), min(ts)
+    else:
+        def run_region(first, n, call):
+            med, mn, _ = time_graph(steps_fn(first, n, call), REPS)
+            return med, mn
+
+    decode_call = lambda i: layers[i].decode(xs[i])          # noqa: E731
+    # the headline: W untimed warm-up steps (one graph), then exactly K timed steps (one
+    # graph, its first replay), continuing the rotation over the copies.  Every copy ran
+    # eagerly above, so the graphs are captured without another eager pass: the timed
+    # steps' copies were last read before the warm-up and the checks' later copies, more
+    # than the 256 MB cache holds.
+    if args.eager:
+        steps_fn(0, W, decode_call)()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(2_000_000)
+        a.record()
+        steps_fn(W, K, decode_call)()
+        b.record()
+        torch.cuda.synchronize()
+        ms_region = a.elapsed_time(b)
+        g_k = None
+    else:
+        g_w = capture(steps_fn(0, W, decode_call), eager=False) if W > 0 else None
+        g_k = capture(steps_fn(W, K, decode_call), eager=False)
+        torch.cuda.synchronize()
+        if g_w is not None:
+            g_w.replay()
+        ms_region = timed_replay(g_k)
+    ms_step = ms_region / K
     tok_s = 1000.0 / ms_step
-    ms_step_calls = timed(step_all_calls, max(4, reps // 2)) / L
+    # the same K-step region repeated REPS times, each replay timed on its own
+    if g_k is not None:
+        import statistics
+        rep_ms = [timed_replay(g_k) / K for _ in range(REPS)]
+        ms_med, ms_min = statistics.median(rep_ms), min(rep_ms)
+    else:
+        ms_med, ms_min = run_region(W, K, decode_call)
+        ms_med, ms_min = ms_med / K, ms_min / K
+    ms_calls, _ = run_region(0, L, lambda i: layers[i].forward(xs[i]))
+    ms_step_calls = ms_calls / L
 
     # ---- roofline: the expert kernels of the decode step (moe_experts_decode: the routed
     # experts and the shared one streamed once, SwiGLU, combine) -- two launches per call
     E_b = expert_bytes(base.routed)
     alg_bytes_exp = (w.k + 1) * E_b + 2 * w.d * 2
-
-    def experts_all():
-        for i in range(L):
-            layers[i].experts_decode(xs[i])
-
-    ms_exp = timed(experts_all, max(4, reps // 2)) / L
+    ms_exp_med, ms_exp_min = run_region(0, L, lambda i: layers[i].experts_decode(xs[i]))
+    ms_exp = ms_exp_med / L
     achieved = alg_bytes_exp / (ms_exp * 1e-3) / 1e9
     alg_bytes_step = (base.router.w.numel() * base.router.w.element_size()
                       + (w.k + 1) * E_b + 2 * w.d * 2)
+    # per-leg split of the step, event-timed: the router alone (moe_route at one token:
+    # logits and selection in one launch) and the expert side (moe_experts_decode)
+    ms_route, _ = run_region(0, L, lambda i: layers[i].route_only(xs[i]))
+    ms_route /= L
 
     line = {
         "metric": "moe_layer_decode_tokens_per_s",
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warm * L,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -236,14 +301,21 @@ def main():
                    "entry_point": "moe_layer_decode",
                    "step_weight_stream_GBps": round(alg_bytes_step / (ms_step * 1e-3) / 1e9, 1),
                    "alg_bytes_per_step": alg_bytes_step,
-                   "ms_per_step_four_calls": round(ms_step_calls, 5)},
+                   "ms_per_step_median": round(ms_med, 5), "ms_per_step_min": round(ms_min, 5),
+                   "repetitions": REPS,
+                   "ms_per_step_four_calls": round(ms_step_calls, 5),
+                   "step_split_us": {
+                       "moe_route_one_launch": round(ms_route * 1e3, 3),
+                       "moe_experts_decode": round(ms_exp * 1e3, 3),
+                       "step": round(ms_med * 1e3, 3)}},
         "roofline": {"bound": "hbm",
                      "kernel": "decode_gateup_kernel + decode_down_kernel (moe_experts_decode:"
                                " 10 routed + 1 shared expert FFN and combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "alg_bytes_per_launch": alg_bytes_exp,
-                     "avg_launch_us": round(ms_exp * 1e3, 3)},
+                     "avg_launch_us": round(ms_exp * 1e3, 3),
+                     "min_launch_us": round(ms_exp_min / L * 1e3, 3)},
     }
 
     # ---- 48 chained layers, 1 and 4 tokens per step
@@ -298,11 +370,10 @@ def decode_sweep(moe, synth, np, torch, args):
         moe.moe_check_device_error()
         # distinct routed experts per layer (the bytes a step must stream)
         U = [int(np.unique(m.ids[:T].cpu().numpy()).size) for m in mls]
-        reps = max(4, args.steps // (8 * w.layers))
-        ms = time_graph(step, reps, 2)[0]
+        ms, ms_min, _ = time_graph(step, max(20, args.reps), 2)
         bytes_step = sum(r_b + (u + 1) * E_b + 2 * T * w.d * 2 for u in U)
         out["T%d" % T] = {"tokens_per_s": round(T / (ms * 1e-3), 1),
-                          "ms_per_step": round(ms, 4),
+                          "ms_per_step": round(ms, 4), "ms_per_step_min": round(ms_min, 4),
                           "us_per_layer": round(ms * 1e3 / w.layers, 3),
                           "distinct_experts_per_layer_mean": round(float(np.mean(U)), 2),
                           "alg_bytes_per_step": bytes_step,
@@ -320,31 +391,34 @@ def prefill_bench(moe, synth, np, torch, name, bias):
     layer.forward(x)
     torch.cuda.synchronize()
     moe.moe_check_device_error()
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    reps = 10
-    t0, t1 = ev(), ev()
-    t0.record()
-    for _ in range(reps):
-        layer.forward(x)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_layer = t0.elapsed_time(t1) / reps
+    import statistics
+
+    def each(fn, reps=20):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(2_000_000)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts), min(ts)
+    ms_layer, ms_layer_min = each(lambda: layer.forward(x))
     # grouped GEMM (routed experts): useful flops 6 * pairs * d * F
     P = w.T * w.k
-    t0, t1 = ev(), ev()
-    t0.record()
-    for _ in range(reps):
-        moe.moe_expert_ffn(layer.routed, x, w.T, w.k, layer.ids, layer.offsets,
-                           layer.sorted_pairs, layer.y_pairs, layer.ws_ffn)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_gemm = t0.elapsed_time(t1) / reps
+    ms_gemm, ms_gemm_min = each(lambda: moe.moe_expert_ffn(
+        layer.routed, x, w.T, w.k, layer.ids, layer.offsets, layer.sorted_pairs,
+        layer.y_pairs, layer.ws_ffn))
     flops = 6.0 * P * w.d * w.F
     counts = np.diff(layer.offsets.cpu().numpy())
     del layer, lay
     return {"workload": name, "router_bias": bias or w.bias, "tokens": w.T,
             "tokens_per_s": round(w.T / (ms_layer * 1e-3), 1),
-            "ms_layer": round(ms_layer, 4), "ms_routed_grouped_gemm": round(ms_gemm, 4),
+            "ms_layer": round(ms_layer, 4), "ms_layer_min": round(ms_layer_min, 4),
+            "ms_routed_grouped_gemm": round(ms_gemm, 4),
+            "ms_routed_grouped_gemm_min": round(ms_gemm_min, 4),
             "routed_gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
             "mfma_util": round(flops / (ms_gemm * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "active_experts": int((counts > 0).sum()), "max_rows_per_expert": int(counts.max())}
@@ -407,10 +481,22 @@ def achievable_peaks(torch):
     return out
 
 
-def cpu_baseline(base, toks, w, seconds):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(base, toks, w, seconds, prefill_every=64):
     import numpy as np
 
     import oracle
+    import synth
     from synth import inputs as si
     r_h, ex_h, sh_h = base.router.host(), base.routed.host(), base.shared.host()
     x_h = si.bits16(toks)
@@ -426,9 +512,31 @@ def cpu_baseline(base, toks, w, seconds):
     t = time.perf_counter()
     oracle.layer_tokens(r_h, ex_h, sh_h, x_h, tok_idx, w.k)
     dt = time.perf_counter() - t
-    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d single-token decode calls of the same layer (fp64 oracle, OpenMP "
-                      "over tokens), %.1f s" % (n, dt)}
+    out = {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+           "sample": "%d single-token decode calls of the same layer (fp64 oracle, OpenMP "
+                     "over tokens), %.1f s" % (n, dt)}
+    # one thread on every `prefill_every`-th token of the 8192-token prefill, extrapolated
+    pw = synth.WORKLOADS["prefill_8192_zipf"]
+    lay = synth.make_layer(pw, seed=0, device="cuda")
+    xp = si.bits16(synth.make_tokens(pw, seed=0, device="cuda"))
+    sel = np.arange(0, pw.T, prefill_every, dtype=np.int32)
+    oracle.set_num_threads(1)
+    try:
+        t = time.perf_counter()
+        oracle.layer_tokens(lay.router.host(), lay.routed.host(), lay.shared.host(), xp, sel,
+                            pw.k)
+        dt1 = time.perf_counter() - t
+    finally:
+        oracle.set_num_threads(threads)
+    del lay, xp
+    out["prefill_8192_single_thread_extrapolated"] = {
+        "tokens_per_s": round(sel.size / dt1, 3),
+        "seconds_for_8192_tokens": round(dt1 * pw.T / sel.size, 1),
+        "sample": "every %dth token (%d tokens) of the 8192-token Zipf prefill on 1 thread, "
+                  "%.1f s, extrapolated to 8192 tokens (label: extrapolated)"
+                  % (prefill_every, sel.size, dt1)}
+    return out
 
 
 if __name__ == "__main__":
