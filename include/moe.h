@@ -221,6 +221,24 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer_decode_noalloc -- moe_layer_decode for callers that cannot allocate device
+ * memory or pass a workspace: code recorded under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, checks and results (bit for bit) as
+ * moe_layer_decode, without ws / ws_bytes: the workspace is a fixed 512 KiB array inside
+ * the library, one per GPU, held until the process ends.  Every valid decode call fits
+ * (moe_workspace_size(MOE_OP_LAYER_DECODE, ...) is at most 472.25 KiB over every shape
+ * moe_layer_decode accepts); a larger need would return MOE_ERR_UNSUPPORTED.  The call allocates nothing.  Its first call on a GPU looks
+ * up that GPU's array and enqueues one small kernel on `stream` that clears its counter
+ * area.  All calls on one GPU share the array, so two calls whose work overlaps on the
+ * GPU (different streams, no ordering between them) race and give undefined results;
+ * calls ordered on one stream are safe.
+ */
+moe_status moe_layer_decode_noalloc(const moe_router* r, const moe_experts* routed,
+                                    const moe_experts* shared, const uint16_t* x, int32_t T,
+                                    int32_t k, int32_t* ids, float* weights,
+                                    const uint16_t* residual, uint16_t* out, void* stream);
+
+/*
  * moe_experts_decode -- the last two launches of moe_layer_decode on their own: given ids
  * and weights from moe_route, the routed and shared expert FFNs and the combine, bit for
  * bit equal to moe_permute -> moe_expert_ffn x 2 -> moe_combine.  Arguments as in

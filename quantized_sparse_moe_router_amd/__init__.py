@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE,
     MOE_OP_EXPERTS_DECODE, MoeError,
     moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_layer_decode, moe_experts_decode,
+    moe_layer_decode_noalloc,
     moe_dequant_probe, moe_workspace_size,
     moe_check_device_error, moe_status_string, moe_last_error, moe_version,
     router_desc, experts_desc,

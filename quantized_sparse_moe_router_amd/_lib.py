@@ -21,7 +21,8 @@ MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE, MOE_OP_EXP
     0, 1, 2, 3, 4
 
 EXPORTED = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-            "moe_layer_decode", "moe_experts_decode", "moe_dequant_probe",
+            "moe_layer_decode", "moe_layer_decode_noalloc", "moe_experts_decode",
+            "moe_dequant_probe",
             "moe_workspace_size", "moe_check_device_error", "moe_status_string",
             "moe_last_error", "moe_version")
 
@@ -65,6 +66,7 @@ def lib():
             "moe_combine": [P, P, P, P, P, I32, I32, I32, P, P],
             "moe_layer_decode": [P, P, P, P, I32, I32, P, P, P, P, P, SZ, P],
             "moe_experts_decode": [P, P, P, I32, I32, P, P, P, P, P, SZ, P],
+            "moe_layer_decode_noalloc": [P, P, P, P, I32, I32, P, P, P, P, P],
             "moe_dequant_probe": [I32, I32, P, P, ctypes.c_int64, P, P],
             "moe_workspace_size": [I32, I32, I32, I32, I32, I32],
             "moe_check_device_error": [P],
@@ -161,6 +163,15 @@ def moe_layer_decode(router, routed, shared, x, T, k, ids, weights, residual, ou
                                 _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream))
     _check(st, "moe_layer_decode")
+
+
+def moe_layer_decode_noalloc(router, routed, shared, x, T, k, ids, weights, residual, out,
+                             stream=None):
+    st = lib().moe_layer_decode_noalloc(
+        ctypes.byref(router), ctypes.byref(routed),
+        ctypes.byref(shared) if shared is not None else None, _ptr(x), int(T), int(k),
+        _ptr(ids), _ptr(weights), _ptr(residual), _ptr(out), _stream(stream))
+    _check(st, "moe_layer_decode_noalloc")
 
 
 def moe_experts_decode(routed, shared, x, T, k, ids, weights, residual, out, ws, stream=None):

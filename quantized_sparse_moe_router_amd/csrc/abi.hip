@@ -2,9 +2,17 @@
 // shape-based dispatch to the gfx950 kernels.  See include/moe.h for the contract.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "moe_common.h"
+
+// Workspace of moe_layer_decode_noalloc: one copy per GPU, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name is a
+// stand-in, not a device address); it passes the address hipGetSymbolAddress returns
+// for the current device (scratch_base below).
+constexpr size_t kNoAllocScratchBytes = 512 * 1024;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -279,6 +287,10 @@ moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const f
                       "moe_combine");
 }
 
+}  // extern "C"
+
+namespace {
+
 // Checks shared by moe_experts_decode and moe_layer_decode (routed, shared, T, k, rows).
 moe_status check_decode(const moe_experts* routed, const moe_experts* shared, int T, int k,
                         const uint16_t* x, const uint16_t* residual, const uint16_t* out,
@@ -311,6 +323,10 @@ moe_status check_decode(const moe_experts* routed, const moe_experts* shared, in
     return MOE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shared,
                               const uint16_t* x, int32_t T, int32_t k, const int32_t* ids,
                               const float* weights, const uint16_t* residual, uint16_t* out,
@@ -333,26 +349,36 @@ moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shar
                       "moe_experts_decode");
 }
 
-moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
-                            const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
-                            int32_t* ids, float* weights, const uint16_t* residual,
-                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
-    moe_status st = check_router(r, "moe_layer_decode");
+}  // extern "C"
+
+namespace {
+
+// Argument checks of moe_layer_decode and moe_layer_decode_noalloc; *need = workspace bytes.
+moe_status check_layer_decode(const moe_router* r, const moe_experts* routed,
+                              const moe_experts* shared, const uint16_t* x, int32_t T,
+                              int32_t k, int32_t* ids, float* weights,
+                              const uint16_t* residual, uint16_t* out, const char* who,
+                              size_t* need) {
+    moe_status st = check_router(r, who);
     if (st != MOE_OK) return st;
-    st = check_decode(routed, shared, T, k, x, residual, out, "moe_layer_decode");
+    st = check_decode(routed, shared, T, k, x, residual, out, who);
     if (st != MOE_OK) return st;
     const int E = r->n_experts, d = r->d_model, F = routed->d_ff;
     if (routed->n_experts != E || routed->d_model != d)
         return fail(MOE_ERR_INVALID_ARG,
-                    "moe_layer_decode: router (E %d, d %d) and experts (E %d, d %d) differ", E,
-                    d, routed->n_experts, routed->d_model);
-    if (T == 0) return ok();
-    if (!ids || !weights) return fail(MOE_ERR_INVALID_ARG, "moe_layer_decode: ids/weights NULL");
-    const size_t need = decode_ws(T, k, E, d, F);
-    if (!ws || ws_bytes < need || !aligned16(ws))
-        return fail(MOE_ERR_WORKSPACE, "moe_layer_decode: needs %zu workspace bytes (got %zu)",
-                    need, ws_bytes);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+                    "%s: router (E %d, d %d) and experts (E %d, d %d) differ", who, E, d,
+                    routed->n_experts, routed->d_model);
+    *need = T > 0 ? decode_ws(T, k, E, d, F) : 0;
+    if (T > 0 && (!ids || !weights)) return fail(MOE_ERR_INVALID_ARG, "%s: ids/weights NULL", who);
+    return MOE_OK;
+}
+
+// The three launches of the decode layer on a workspace of decode_ws bytes.
+moe_status run_layer_decode(const moe_router* r, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
+                            int32_t* ids, float* weights, const uint16_t* residual,
+                            uint16_t* out, void* ws, hipStream_t s) {
+    const int E = r->n_experts;
     uint8_t* base = static_cast<uint8_t*>(ws);
     unsigned* counter = reinterpret_cast<unsigned*>(base);
     float* lg = reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
@@ -373,6 +399,89 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
                                    out, ffn_ws, s);
     }
     return hip_status(e, "moe_layer_decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
+                            int32_t* ids, float* weights, const uint16_t* residual,
+                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    const moe_status st = check_layer_decode(r, routed, shared, x, T, k, ids, weights,
+                                             residual, out, "moe_layer_decode", &need);
+    if (st != MOE_OK) return st;
+    if (T == 0) return ok();
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(MOE_ERR_WORKSPACE, "moe_layer_decode: needs %zu workspace bytes (got %zu)",
+                    need, ws_bytes);
+    return run_layer_decode(r, routed, shared, x, T, k, ids, weights, residual, out, ws,
+                            static_cast<hipStream_t>(stream));
+}
+
+// ---- moe_layer_decode_noalloc: the workspace is the file-scope array `scratch`
+}  // extern "C"
+
+namespace {
+
+__global__ void zero_words_kernel(unsigned* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_base[kMaxDevices] = {};
+
+// Device address of this GPU's `scratch`, looked up once per device with that device
+// current.  The first call on a device also clears the route counter area (the only part
+// that must start at zero; every call leaves it zero again) with a fill kernel on `s`.
+hipError_t scratch_base(hipStream_t s, void** base) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_base[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        constexpr int n = (int)(moe::kRouteCounterBytes / sizeof(unsigned));
+        zero_words_kernel<<<1, n, 0, s>>>(static_cast<unsigned*>(p), n);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch_base[dev] = p;
+    }
+    *base = g_scratch_base[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_decode_noalloc(const moe_router* r, const moe_experts* routed,
+                                    const moe_experts* shared, const uint16_t* x, int32_t T,
+                                    int32_t k, int32_t* ids, float* weights,
+                                    const uint16_t* residual, uint16_t* out, void* stream) {
+    size_t need = 0;
+    const moe_status st = check_layer_decode(r, routed, shared, x, T, k, ids, weights,
+                                             residual, out, "moe_layer_decode_noalloc", &need);
+    if (st != MOE_OK) return st;
+    if (T == 0) return ok();
+    if (need > kNoAllocScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_layer_decode_noalloc: this call needs %zu workspace bytes, more than "
+                    "the %zu of the library's fixed workspace; use moe_layer_decode", need,
+                    kNoAllocScratchBytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* base = nullptr;
+    const hipError_t e = scratch_base(s, &base);
+    if (e != hipSuccess) return hip_status(e, "moe_layer_decode_noalloc: fixed workspace");
+    return run_layer_decode(r, routed, shared, x, T, k, ids, weights, residual, out, base, s);
 }
 
 moe_status moe_dequant_probe(int32_t fmt, int32_t form, const uint8_t* w, const uint16_t* s,
