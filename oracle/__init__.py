@@ -84,6 +84,9 @@ def _declare(L):
         "oracle_combine": (None, [_P, _P, _P, _P, _I64, _I, _I, _P]),
         "oracle_layer_tokens": (None, [_P, _P, _P, _P, _P, _I64, _I, _P, _P, _P, _P, _P]),
         "oracle_residual": (None, [_P, _P, _I64, _P]),
+        "oracle_rms_sumsq": (ctypes.c_float, [_P, _I]),
+        "oracle_rmsnorm": (None, [_P, _I64, _I, _P, ctypes.c_float, _P, _P]),
+        "oracle_gated_residual": (None, [_P, _P, _P, _I64, _I, _P]),
         "oracle_num_threads": (_I, []),
         "oracle_set_num_threads": (None, [_I]),
     }
@@ -271,6 +274,58 @@ def layer_tokens(router, routed, shared, x_bits, tokens, k, keep_pairs=False):
                               _ptr(tokens), n, int(k), _ptr(ids), _ptr(w), _ptr(y_sel),
                               _ptr(y_sh), _ptr(out))
     return {"ids": ids, "w": w, "y_sel": y_sel, "y_shared": y_sh, "out": out}
+
+
+def rms_sumsq(x_row_bits):
+    x = _c(x_row_bits, np.uint16)
+    return lib().oracle_rms_sumsq(_ptr(x), x.size)
+
+
+def rmsnorm(x_bits, gamma, eps):
+    """(xn bf16 bits [T][d], r fp32 [T]) of the pre-layer RMS norm."""
+    x = _c(x_bits, np.uint16)
+    T, d = x.shape
+    g = _c(gamma, np.float32)
+    xn = np.empty_like(x)
+    r = np.empty(T, np.float32)
+    lib().oracle_rmsnorm(_ptr(x), T, d, _ptr(g), float(np.float32(eps)), _ptr(xn), _ptr(r))
+    return xn, r
+
+
+def gate_logits(gate_w, gate_b, xn_bits):
+    """z [T] fp32: the gate row through the router's fixed fp32 order, plus its bias."""
+    gw = _c(gate_w, np.float32).reshape(1, -1)
+    r = {"fmt": FMT_FP32, "E": 1, "d": gw.shape[1], "w": gw,
+         "bias": np.array([gate_b], np.float32)}
+    return router_logits(r, xn_bits)[:, 0].copy()
+
+
+def gated_residual(x_bits, out, z=None):
+    x = _c(x_bits, np.uint16)
+    out = _c(out, np.float64)
+    T, d = x.shape
+    zz = None if z is None else _c(z, np.float32)
+    xn = np.empty_like(x)
+    lib().oracle_gated_residual(_ptr(x), _ptr(out), _ptr(zz), T, d, _ptr(xn))
+    return xn
+
+
+def block_tokens(norm, router, routed, shared, x_bits, tokens, k, keep_pairs=False):
+    """One MoE block on the listed tokens: xn = RMSNorm(x), the layer on xn, and the gated
+    residual x_next = bf16(x + bf16(g * out)).  norm: {gamma, eps, gate_w, gate_b}
+    (gate_w None: g = 1).  Returns layer_tokens' dict plus xn, z, x_next."""
+    x = _c(x_bits, np.uint16)
+    tokens = _c(tokens, np.int32)
+    xs = x[tokens]
+    xn, _ = rmsnorm(xs, norm["gamma"], norm["eps"])
+    res = layer_tokens(router, routed, shared, xn, np.arange(tokens.size, dtype=np.int32), k,
+                       keep_pairs=keep_pairs)
+    z = None
+    if norm.get("gate_w") is not None:
+        z = gate_logits(norm["gate_w"], norm.get("gate_b", 0.0), xn)
+    res["xn"], res["z"] = xn, z
+    res["x_next"] = gated_residual(xs, res["out"], z)
+    return res
 
 
 def residual(x_bits, out):

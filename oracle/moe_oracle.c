@@ -253,6 +253,78 @@ void oracle_router_logits_fp64(const oracle_router* r, const uint16_t* x, int64_
     }
 }
 
+/* ------------------------------------------------------------------ pre-MoE norm */
+
+/*
+ * The pages put a gated residual on the GPU next to the router and the shared expert
+ * [本地部署Qwen3.8-Flash-Next模型的两条路线 (blog.cycleuser.org), section 硬件形态决定了各自的走法]
+ * but give no formula for it or for the normalisation in front of the layer.  Reading: the
+ * MoE layer runs on xn = RMSNorm(x), and its output joins the residual stream through a
+ * per-token sigmoid gate (see oracle_gated_residual).  The norm, in fp32 with a fixed
+ * order so that the routing that follows is reproducible bit for bit:
+ *   ss  = sum_c x_c^2: the row cut into chunks of 4 elements, chunk v belongs to lane
+ *         (v mod 64), each lane runs acc = fma(x_c, x_c, acc) over its chunks in ascending
+ *         order (elements ascending), then the butterfly over lanes with offsets 1..32
+ *         (the router's tree);
+ *   r   = fl(1 / fl(sqrt(fl(fl(ss / d) + eps))))  (IEEE division and square root);
+ *   xn_c = bf16(fl(fl(x_c * r) * gamma_c)).
+ */
+float oracle_rms_sumsq(const uint16_t* x, int d)
+{
+    float lane[64], nxt[64];
+    int nchunk = d / 4;
+    for (int l = 0; l < 64; ++l) {
+        float acc = 0.0f;
+        for (int v = l; v < nchunk; v += 64)
+            for (int i = 0; i < 4; ++i) {
+                float xv = bf16_to_float(x[v * 4 + i]);
+                acc = fmaf(xv, xv, acc);
+            }
+        lane[l] = acc;
+    }
+    for (int off = 1; off < 64; off *= 2) {
+        for (int l = 0; l < 64; ++l)
+            nxt[l] = lane[l] + lane[l ^ off];
+        memcpy(lane, nxt, sizeof lane);
+    }
+    return lane[0];
+}
+
+/* xn [T][d] (bf16 bits) and the scale r [T] (may be NULL) of T rows. */
+void oracle_rmsnorm(const uint16_t* x, int64_t T, int d, const float* gamma, float eps,
+                    uint16_t* xn, float* r_out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* xr = x + (size_t)t * d;
+        float ss = oracle_rms_sumsq(xr, d);
+        float ms = ss / (float)d;
+        float den = sqrtf(ms + eps);
+        float r = 1.0f / den;
+        if (r_out) r_out[t] = r;
+        for (int c = 0; c < d; ++c) {
+            float a = bf16_to_float(xr[c]) * r;
+            float b = a * gamma[c];
+            xn[(size_t)t * d + c] = oracle_double_to_bf16((double)b);
+        }
+    }
+}
+
+/* Gated residual: x_next = bf16(x + bf16(g_t * out)), g_t = 1 / (1 + exp(-z_t)) in double
+ * (z = gate logits [T], or NULL for g = 1, the plain residual).  x + bf16(...) is exact in
+ * double (two bf16 values), so one rounding remains. */
+void oracle_gated_residual(const uint16_t* x, const double* out, const float* z, int64_t T,
+                           int d, uint16_t* x_next)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        double g = z ? 1.0 / (1.0 + exp(-(double)z[t])) : 1.0;
+        for (int c = 0; c < d; ++c) {
+            size_t i = (size_t)t * d + c;
+            double o = (double)bf16_to_float(oracle_double_to_bf16(g * out[i]));
+            x_next[i] = oracle_double_to_bf16((double)bf16_to_float(x[i]) + o);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ selection */
 
 /* "a ranks before b": larger logit first; equal logits (+0 and -0 are equal) -> lower id. */

@@ -244,6 +244,105 @@ def test_router_fp32_within_rounding_bound_of_exact():
     assert np.all(np.abs(l32 - exact.numpy()) <= gamma * mag)
 
 
+# ---------------------------------------------------------------- pre-layer norm, gate
+
+def _bf16_bits(v):
+    return int(si.bits16(torch.tensor([v], dtype=torch.float32).to(torch.bfloat16))[0])
+
+
+def test_rms_sumsq_order_golden():
+    n = 0
+    for ln in _lines("rmsnorm.txt"):
+        if not ln.startswith("S "):
+            continue
+        head, *items = [p.strip() for p in ln.split("|")]
+        _, name, d, expect = head.split()
+        x = np.zeros(int(d), np.uint16)
+        for it in items:
+            idx, xv = it.split()
+            assert float(torch.tensor(float(xv)).to(torch.bfloat16)) == float(xv)
+            x[int(idx)] = _bf16_bits(float(xv))
+        assert oracle.rms_sumsq(x) == np.float32(float(expect)), name
+        n += 1
+    assert n == 2
+
+
+def test_rmsnorm_golden():
+    n = 0
+    for ln in _lines("rmsnorm.txt"):
+        if not ln.startswith("N "):
+            continue
+        head, *items = [p.strip() for p in ln.split("|")]
+        _, name, d, eps, xv, r_hex = head.split()
+        d = int(d)
+        x = np.full((1, d), _bf16_bits(float(xv)), np.uint16)
+        gamma = np.ones(d, np.float32)
+        want = {}
+        for it in items:
+            idx, g, xn_hex = it.split()
+            assert float(np.float32(float(g))) == float(g)
+            gamma[int(idx)] = float(g)
+            want[int(idx)] = int(xn_hex, 16)
+        xn, r = oracle.rmsnorm(x, gamma, float(eps))
+        assert r.view(np.uint32)[0] == int(r_hex, 16), (name, hex(r.view(np.uint32)[0]))
+        for idx, h in want.items():
+            assert xn[0, idx] == h, (name, idx, hex(xn[0, idx]))
+        if gamma[0] == 1:
+            assert (xn[0, gamma == 1] == xn[0, 0]).all()
+        n += 1
+    assert n == 3
+
+
+def test_rmsnorm_zero_row_and_eps():
+    x = np.zeros((2, 512), np.uint16)
+    x[1, 7] = _bf16_bits(1e-3)
+    xn, r = oracle.rmsnorm(x, np.ones(512, np.float32), 1e-6)
+    assert (xn[0] == 0).all() and np.isfinite(r).all() and (r > 0).all()
+    # 1 / sqrt(eps) within two ulps of fp32 (the eps of the empty row dominates)
+    assert abs(float(r[0]) - 1.0 / math.sqrt(float(np.float32(1e-6)))) <= 2 * 2.0 ** -24 * 1000
+    # a lone element far below sqrt(eps): xn = x * r, r ~ 1/sqrt(1e-6 + 1e-6/512)
+    assert xn[1, 7] != 0 and (np.delete(xn[1], 7) == 0).all()
+
+
+def test_rmsnorm_scale_invariance_and_exact_value():
+    # eps = 0: scaling a row by a power of two scales ss by its square exactly, so r and
+    # x * r, hence xn, do not change; and xn is within half a bf16 ulp (plus the fp32
+    # roundings before it) of the real-number value x * gamma / sqrt(mean(x^2)), which a
+    # dropped factor (mean vs sum, a missing square root, gamma unused) would break
+    g = torch.Generator().manual_seed(21)
+    T, d = 64, 2048
+    x = torch.randn((T, d), generator=g).to(torch.bfloat16)
+    gamma = (1 + 0.1 * torch.randn(d, generator=g)).numpy().astype(np.float32)
+    xn, _ = oracle.rmsnorm(si.bits16(x), gamma, 0.0)
+    for k in (-20, -3, 5, 30):
+        xs = (x.float() * 2.0 ** k).to(torch.bfloat16)
+        assert torch.equal(xs.float(), x.float() * 2.0 ** k)
+        assert np.array_equal(oracle.rmsnorm(si.bits16(xs), gamma, 0.0)[0], xn)
+    xd = x.double().numpy()
+    exact = xd * gamma / np.sqrt((xd ** 2).mean(axis=1, keepdims=True))
+    got = (xn.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    # half a bf16 ulp is at most 2^-8 of the value; the fp32 steps before the rounding add
+    # well under 2^-16 of it
+    assert np.all(np.abs(got - exact) <= (2.0 ** -8 + 2.0 ** -16) * np.abs(exact) + 1e-30)
+
+
+def test_gated_residual_closed_forms():
+    g = torch.Generator().manual_seed(22)
+    T, d = 3, 256
+    x = torch.randn((T, d), generator=g).to(torch.bfloat16)
+    out = torch.randn((T, d), generator=g, dtype=torch.float64).numpy()
+    xb = si.bits16(x)
+    plain = oracle.residual(xb, out)
+    # z large: g = 1 exactly in double -> the plain residual
+    assert np.array_equal(oracle.gated_residual(xb, out, np.full(T, 100.0, np.float32)), plain)
+    assert np.array_equal(oracle.gated_residual(xb, out, None), plain)
+    # z = 0: g = 1/2 exactly -> the plain residual of out / 2
+    assert np.array_equal(oracle.gated_residual(xb, out, np.zeros(T, np.float32)),
+                          oracle.residual(xb, out / 2))
+    # z very negative: g * out rounds to 0 in bf16 -> x unchanged
+    assert np.array_equal(oracle.gated_residual(xb, out, np.full(T, -200.0, np.float32)), xb)
+
+
 # ---------------------------------------------------------------- selection + weights
 
 def _brute_topk(row, k):
