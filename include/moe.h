@@ -70,7 +70,8 @@ enum {
     MOE_OP_PERMUTE = 1,
     MOE_OP_EXPERT_FFN = 2,
     MOE_OP_LAYER_DECODE = 3,
-    MOE_OP_EXPERTS_DECODE = 4
+    MOE_OP_EXPERTS_DECODE = 4,
+    MOE_OP_BLOCK_DECODE = 5
 };
 
 /* Router: logits = W x (+ bias).  fmt FP32: w = fp32 [E][d], scale unused.
@@ -106,6 +107,37 @@ typedef struct moe_experts {
     const uint16_t* s_up;
     const uint16_t* s_down;
 } moe_experts;
+
+/* The pre-layer RMS norm and the residual gate of a MoE block (moe_rmsnorm,
+ * moe_combine_gated, moe_block_decode).  The pages keep a gated residual on the GPU next to
+ * the router and the shared expert [本地部署Qwen3.8-Flash-Next模型的两条路线
+ * (blog.cycleuser.org), section 硬件形态决定了各自的走法] without a formula; the reading
+ * here: the layer runs on xn = RMSNorm(x) and its output joins the residual stream as
+ * x_next = bf16(x + bf16(sigmoid(z) * out)), z = <gate_w, xn> + gate_b per token.
+ *   gamma   fp32 [d] per-channel scale of the norm (16-byte aligned)
+ *   gate_w  fp32 [d] residual-gate row (16-byte aligned), or NULL: no gate (factor 1)
+ *   eps     added to the mean square (finite, >= 0)
+ *   gate_b  residual-gate bias (finite) */
+typedef struct moe_norm {
+    const float* gamma;
+    const float* gate_w;
+    float eps;
+    float gate_b;
+} moe_norm;
+
+/*
+ * moe_rmsnorm -- xn = RMSNorm(x) for T tokens, and their residual-gate logits.
+ *   x   bf16 [T][d]; xn bf16 [T][d] out; z fp32 [T] out (needed when gate_w != NULL,
+ *       ignored otherwise).  d = 256, 512, 1024, 2048 or 4096.
+ * Fixed fp32 arithmetic, so that routing on xn is reproducible bit for bit: ss = sum of
+ * x_c^2 with the row cut into chunks of 4 elements, chunk v to lane v mod 64, one fused
+ * multiply-add chain per lane over its chunks in ascending order, then a butterfly over the
+ * 64 lanes with offsets 1..32; r = fl(1 / fl(sqrt(fl(fl(ss / d) + eps)))) with IEEE
+ * division and square root; xn_c = bf16(fl(fl(x_c * r) * gamma_c)).  z = <gate_w, xn> +
+ * gate_b in moe_route's fixed fp32 order.  One launch.
+ */
+moe_status moe_rmsnorm(const moe_norm* n, const uint16_t* x, int32_t T, int32_t d,
+                       uint16_t* xn, float* z, void* stream);
 
 /*
  * moe_route -- router logits, top-k selection and gate weights for T tokens.
@@ -193,6 +225,18 @@ moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const f
                        int32_t k, int32_t d, uint16_t* out, void* stream);
 
 /*
+ * moe_combine_gated -- moe_combine with the residual gate: the fp32 sum of moe_combine
+ * (slots in order, then the shared row) is scaled once by g = sigmoid(z[t]) =
+ * 1 / (1 + exp(-z[t])) before its rounding: out = bf16(residual + bf16(fl(g * sum))), or
+ * bf16(fl(g * sum)) without a residual.  z fp32 [T] (required); other arguments as in
+ * moe_combine.
+ */
+moe_status moe_combine_gated(const uint16_t* y_pairs, const int32_t* pair_pos,
+                             const float* weights, const uint16_t* y_shared, const float* z,
+                             const uint16_t* residual, int32_t T, int32_t k, int32_t d,
+                             uint16_t* out, void* stream);
+
+/*
  * moe_layer_decode -- the whole layer for a few tokens (decode, MTP verification): the same
  * result, bit for bit, as
  *     moe_route -> moe_permute -> moe_expert_ffn(routed) -> moe_expert_ffn(shared, dense)
@@ -219,6 +263,29 @@ moe_status moe_layer_decode(const moe_router* r, const moe_experts* routed,
                             const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
                             int32_t* ids, float* weights, const uint16_t* residual,
                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_block_decode -- one MoE block of a stacked model for a few tokens: the pre-layer norm,
+ * the layer, and the gated residual, fused into moe_layer_decode's three launches (the norm
+ * inside the router kernel, the gate inside the down kernel's combine).  The result equals,
+ * bit for bit,
+ *     moe_rmsnorm -> moe_route(xn) -> moe_permute -> moe_expert_ffn(routed, xn)
+ *     -> moe_expert_ffn(shared, dense, xn) -> moe_combine_gated(z, residual = x)
+ * (without a gate row: moe_combine with residual = x).  48 such blocks are stacked in the
+ * model the pages describe [Strata 与 Qwen3.8-Flash-Next (telli.sh), section
+ * 稀疏架构创造了机会].
+ *   n        the block's norm and residual gate; r, routed, shared as in moe_layer_decode
+ *   x        bf16 [T][d], the block's input (the residual stream)
+ *   ids, weights  out, as in moe_route (of xn)
+ *   out      bf16 [T][d]: x_next; may alias x
+ *   ws       zero-initialised workspace of moe_workspace_size(MOE_OP_BLOCK_DECODE, T, k, E,
+ *            d, d_ff) bytes (it holds xn and z too); its counter is left zero by every call
+ * Needs what moe_layer_decode needs and T <= 16 (MOE_ERR_UNSUPPORTED otherwise).
+ */
+moe_status moe_block_decode(const moe_norm* n, const moe_router* r, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
+                            int32_t* ids, float* weights, uint16_t* out, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /*
  * moe_layer_decode_noalloc -- moe_layer_decode for callers that cannot allocate device

@@ -325,6 +325,9 @@ def block_tokens(norm, router, routed, shared, x_bits, tokens, k, keep_pairs=Fal
         z = gate_logits(norm["gate_w"], norm.get("gate_b", 0.0), xn)
     res["xn"], res["z"] = xn, z
     res["x_next"] = gated_residual(xs, res["out"], z)
+    # the unrounded update g * out (fp64): x_next is bf16(x + bf16(update))
+    g = np.ones(tokens.size) if z is None else 1.0 / (1.0 + np.exp(-z.astype(np.float64)))
+    res["update"] = g[:, None] * res["out"]
     return res
 
 

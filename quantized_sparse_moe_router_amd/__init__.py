@@ -12,12 +12,12 @@ from . import _lib
 from ._lib import (  # noqa: F401
     MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32,
     MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE,
-    MOE_OP_EXPERTS_DECODE, MoeError,
+    MOE_OP_EXPERTS_DECODE, MOE_OP_BLOCK_DECODE, MoeError,
     moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_layer_decode, moe_experts_decode,
     moe_layer_decode_noalloc,
-    moe_dequant_probe, moe_workspace_size,
+    moe_dequant_probe, moe_rmsnorm, moe_combine_gated, moe_block_decode, moe_workspace_size,
     moe_check_device_error, moe_status_string, moe_last_error, moe_version,
-    router_desc, experts_desc,
+    router_desc, experts_desc, norm_desc,
 )
 
 _FMT = {"fp32": MOE_FMT_FP32, "int8_row": MOE_FMT_INT8_ROW, "int4_g32": MOE_FMT_INT4_G32,
@@ -57,8 +57,13 @@ class MoeLayer:
     weights and out only.
     """
 
-    def __init__(self, router, routed, shared, k, T_max, device="cuda", keep_logits=False):
+    def __init__(self, router, routed, shared, k, T_max, device="cuda", keep_logits=False,
+                 norm=None):
         self.router = router_desc_of(router)
+        # the block's pre-layer norm and residual gate (an object with gamma, eps, gate_w,
+        # gate_b), for block_forward / block_decode
+        self.norm = None if norm is None else norm_desc(norm.gamma, norm.eps, norm.gate_w,
+                                                        norm.gate_b)
         self.routed = experts_desc_of(routed)
         self.shared = experts_desc_of(shared) if shared is not None else None
         self.E, self.d, self.F, self.k = routed.E, routed.d, routed.F, k
@@ -97,6 +102,12 @@ class MoeLayer:
         ws_xd = moe_workspace_size(MOE_OP_EXPERTS_DECODE, T, k, E, d, F) if self.can_decode \
             else 0
         self.ws_experts_decode = torch.zeros((max(ws_xd, 256),), dtype=u8, device=dev)
+        if norm is not None:
+            self.xn = torch.empty((T, d), dtype=bf, device=dev)
+            self.z = torch.empty((T,), dtype=f32, device=dev)
+            ws_blk = moe_workspace_size(MOE_OP_BLOCK_DECODE, T, k, E, d, F) \
+                if self.can_decode else 0
+            self.ws_block = torch.zeros((max(ws_blk, 256),), dtype=u8, device=dev)
         self.side = torch.cuda.Stream(device=dev)     # default priority
         self.side2 = torch.cuda.Stream(device=dev)
 
@@ -104,8 +115,43 @@ class MoeLayer:
         T = x.shape[0]
         if T > self.T_max:
             raise ValueError("T = %d exceeds T_max = %d" % (T, self.T_max))
-        k, E, d = self.k, self.E, self.d
         out = self.out[:T] if out is None else out
+        self._experts(x, T)
+        moe_combine(self.y_pairs, self.pair_pos, self.weights,
+                    self.y_shared if self.shared is not None else None, residual, T, self.k,
+                    self.d, out)
+        return out
+
+    def block_forward(self, x, out=None):
+        """One block of a stack: xn = RMSNorm(x) (moe_rmsnorm), the layer on xn, and the
+        gated residual (moe_combine_gated with residual x; moe_combine without a gate row).
+        Returns x_next."""
+        T = x.shape[0]
+        if T > self.T_max:
+            raise ValueError("T = %d exceeds T_max = %d" % (T, self.T_max))
+        out = self.out[:T] if out is None else out
+        moe_rmsnorm(self.norm, x, T, self.d, self.xn, self.z)
+        self._experts(self.xn[:T], T)
+        ys = self.y_shared if self.shared is not None else None
+        if self.norm.gate_w:
+            moe_combine_gated(self.y_pairs, self.pair_pos, self.weights, ys, self.z, x, T,
+                              self.k, self.d, out)
+        else:
+            moe_combine(self.y_pairs, self.pair_pos, self.weights, ys, x, T, self.k, self.d,
+                        out)
+        return out
+
+    def block_decode(self, x, out=None):
+        """block_forward's result, bit for bit, in three launches (moe_block_decode)."""
+        T = x.shape[0]
+        out = self.out[:T] if out is None else out
+        moe_block_decode(self.norm, self.router, self.routed, self.shared, x, T, self.k,
+                         self.ids, self.weights, out, self.ws_block)
+        return out
+
+    def _experts(self, x, T):
+        """route, permute and both expert FFNs of x (the combine's inputs)."""
+        k, E = self.k, self.E
         main = torch.cuda.current_stream()
         if self.shared is not None:
             # the shared expert does not depend on routing: run it on a side stream
@@ -130,9 +176,6 @@ class MoeLayer:
             main.wait_stream(self.side2)
         if self.shared is not None:
             main.wait_stream(self.side)
-        moe_combine(self.y_pairs, self.pair_pos, self.weights,
-                    self.y_shared if self.shared is not None else None, residual, T, k, d, out)
-        return out
 
     def route_logits(self, x, ids, weights):
         """moe_route with the logits requested (the fixed-order path) into self.logits; ids

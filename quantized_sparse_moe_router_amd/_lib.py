@@ -19,10 +19,11 @@ MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ER
 MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32 = 0, 1, 2, 3
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE, MOE_OP_EXPERTS_DECODE = \
     0, 1, 2, 3, 4
+MOE_OP_BLOCK_DECODE = 5
 
 EXPORTED = ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
             "moe_layer_decode", "moe_layer_decode_noalloc", "moe_experts_decode",
-            "moe_dequant_probe",
+            "moe_dequant_probe", "moe_rmsnorm", "moe_combine_gated", "moe_block_decode",
             "moe_workspace_size", "moe_check_device_error", "moe_status_string",
             "moe_last_error", "moe_version")
 
@@ -37,6 +38,11 @@ class moe_router(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("d_model", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("w", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+class moe_norm(ctypes.Structure):
+    _fields_ = [("gamma", ctypes.c_void_p), ("gate_w", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("gate_b", ctypes.c_float)]
 
 
 class moe_experts(ctypes.Structure):
@@ -68,6 +74,9 @@ def lib():
             "moe_experts_decode": [P, P, P, I32, I32, P, P, P, P, P, SZ, P],
             "moe_layer_decode_noalloc": [P, P, P, P, I32, I32, P, P, P, P, P],
             "moe_dequant_probe": [I32, I32, P, P, ctypes.c_int64, P, P],
+            "moe_rmsnorm": [P, P, I32, I32, P, P, P],
+            "moe_combine_gated": [P, P, P, P, P, P, I32, I32, I32, P, P],
+            "moe_block_decode": [P, P, P, P, P, I32, I32, P, P, P, P, SZ, P],
             "moe_workspace_size": [I32, I32, I32, I32, I32, I32],
             "moe_check_device_error": [P],
             "moe_status_string": [I32],
@@ -110,6 +119,13 @@ def router_desc(fmt, w, scale=None, bias=None):
     d = moe_router(int(fmt), int(w.shape[0]), int(w.shape[1]), 0, _ptr(w), _ptr(scale),
                    _ptr(bias))
     d._keep = (w, scale, bias)
+    return d
+
+
+def norm_desc(gamma, eps, gate_w=None, gate_b=0.0):
+    """moe_norm for a norm / residual-gate tensor set; keep the returned object alive."""
+    d = moe_norm(_ptr(gamma), _ptr(gate_w), float(eps), float(gate_b))
+    d._keep = (gamma, gate_w)
     return d
 
 
@@ -188,6 +204,29 @@ def moe_dequant_probe(fmt, form, w, s, n_groups, out, stream=None):
     st = lib().moe_dequant_probe(int(fmt), int(form), _ptr(w), _ptr(s), int(n_groups),
                                  _ptr(out), _stream(stream))
     _check(st, "moe_dequant_probe")
+
+
+def moe_rmsnorm(norm, x, T, d, xn, z, stream=None):
+    st = lib().moe_rmsnorm(ctypes.byref(norm), _ptr(x), int(T), int(d), _ptr(xn), _ptr(z),
+                           _stream(stream))
+    _check(st, "moe_rmsnorm")
+
+
+def moe_combine_gated(y_pairs, pair_pos, weights, y_shared, z, residual, T, k, d, out,
+                      stream=None):
+    st = lib().moe_combine_gated(_ptr(y_pairs), _ptr(pair_pos), _ptr(weights), _ptr(y_shared),
+                                 _ptr(z), _ptr(residual), int(T), int(k), int(d), _ptr(out),
+                                 _stream(stream))
+    _check(st, "moe_combine_gated")
+
+
+def moe_block_decode(norm, router, routed, shared, x, T, k, ids, weights, out, ws,
+                     stream=None):
+    st = lib().moe_block_decode(ctypes.byref(norm), ctypes.byref(router), ctypes.byref(routed),
+                                ctypes.byref(shared) if shared is not None else None, _ptr(x),
+                                int(T), int(k), _ptr(ids), _ptr(weights), _ptr(out), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_block_decode")
 
 
 def moe_check_device_error(stream=None):

@@ -89,6 +89,28 @@ size_t decode_ws(int T, int k, int E, int d, int F) {
     return round_up(route_exact_ws(T, E)) + moe::decode_ws_layout(T, k, d, F).bytes;
 }
 
+// decode block workspace: the decode layer's, then xn [T][d] bf16 and z [T] fp32
+size_t block_ws(int T, int k, int E, int d, int F) {
+    return decode_ws(T, k, E, d, F) + round_up((size_t)T * d * 2) + round_up((size_t)T * 4);
+}
+
+bool finite_f32(float v) { return v == v && v - v == 0.0f; }
+
+// moe_norm checks shared by moe_rmsnorm and moe_block_decode
+moe_status check_norm(const moe_norm* n, int d, const char* who) {
+    if (!n) return fail(MOE_ERR_INVALID_ARG, "%s: norm descriptor is NULL", who);
+    if (!n->gamma || !aligned16(n->gamma))
+        return fail(MOE_ERR_INVALID_ARG, "%s: gamma NULL or not 16-byte aligned", who);
+    if (n->gate_w && !aligned16(n->gate_w))
+        return fail(MOE_ERR_INVALID_ARG, "%s: gate_w not 16-byte aligned", who);
+    if (!finite_f32(n->eps) || n->eps < 0.0f || !finite_f32(n->gate_b))
+        return fail(MOE_ERR_INVALID_ARG, "%s: eps must be finite and >= 0, gate_b finite", who);
+    if (d != 256 && d != 512 && d != 1024 && d != 2048 && d != 4096)
+        return fail(MOE_ERR_INVALID_ARG, "%s: d_model %d must be 256..4096, a power of two",
+                    who, d);
+    return MOE_OK;
+}
+
 // Router descriptor checks shared by moe_route and moe_layer_decode.
 moe_status check_router(const moe_router* r, const char* who) {
     if (!r) return fail(MOE_ERR_INVALID_ARG, "%s: router descriptor is NULL", who);
@@ -167,6 +189,10 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
         case MOE_OP_EXPERTS_DECODE:
             return (d > 0 && d_ff > 0 && moe::decode_fits(T, k, d_ff, false))
                        ? moe::decode_ws_layout(T, k, d, d_ff).bytes
+                       : 0;
+        case MOE_OP_BLOCK_DECODE:
+            return (d > 0 && d_ff > 0 && moe::decode_fits(T, k, d_ff, false))
+                       ? block_ws(T, k, E, d, d_ff)
                        : 0;
         default: return 0;
     }
@@ -282,7 +308,8 @@ moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const f
     if (!aligned16(y_pairs) || !aligned16(out) || (y_shared && !aligned16(y_shared)) ||
         (residual && !aligned16(residual)))
         return fail(MOE_ERR_INVALID_ARG, "moe_combine: bf16 rows must be 16-byte aligned");
-    return hip_status(moe::launch_combine(y_pairs, pair_pos, weights, y_shared, residual, T, k,
+    return hip_status(moe::launch_combine(y_pairs, pair_pos, weights, y_shared, residual,
+                                          nullptr, T, k,
                                           d, out, static_cast<hipStream_t>(stream)),
                       "moe_combine");
 }
@@ -344,7 +371,8 @@ moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shar
     // no logits: the kernels only read ids and weights
     return hip_status(moe::launch_decode_ffn(*routed, shared, x, T, k, nullptr,
                                              const_cast<int32_t*>(ids),
-                                             const_cast<float*>(weights), residual, out, ws,
+                                             const_cast<float*>(weights), residual, nullptr,
+                                             out, ws,
                                              static_cast<hipStream_t>(stream)),
                       "moe_experts_decode");
 }
@@ -388,15 +416,15 @@ moe_status run_layer_decode(const moe_router* r, const moe_experts* routed,
         // logits only; every gate/up block selects the token's experts itself
         e = moe::launch_route_logits(*r, x, T, lg, s);
         if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
-        e = moe::launch_decode_ffn(*routed, shared, x, T, k, lg, ids, weights, residual, out,
-                                   ffn_ws, s);
+        e = moe::launch_decode_ffn(*routed, shared, x, T, k, lg, ids, weights, residual,
+                                   nullptr, out, ffn_ws, s);
     } else {
         // several tokens: the route kernel selects once (its last block, one wave per
         // token) instead of every gate/up block repeating one token's selection
         e = moe::launch_route(*r, x, T, k, ids, weights, lg, counter, s);
         if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
         e = moe::launch_decode_ffn(*routed, shared, x, T, k, nullptr, ids, weights, residual,
-                                   out, ffn_ws, s);
+                                   nullptr, out, ffn_ws, s);
     }
     return hip_status(e, "moe_layer_decode");
 }
@@ -482,6 +510,81 @@ moe_status moe_layer_decode_noalloc(const moe_router* r, const moe_experts* rout
     const hipError_t e = scratch_base(s, &base);
     if (e != hipSuccess) return hip_status(e, "moe_layer_decode_noalloc: fixed workspace");
     return run_layer_decode(r, routed, shared, x, T, k, ids, weights, residual, out, base, s);
+}
+
+moe_status moe_rmsnorm(const moe_norm* n, const uint16_t* x, int32_t T, int32_t d,
+                       uint16_t* xn, float* z, void* stream) {
+    const moe_status st = check_norm(n, d, "moe_rmsnorm");
+    if (st != MOE_OK) return st;
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: T = %d < 0", T);
+    if (T == 0) return ok();
+    if (!x || !aligned16(x) || !xn || !aligned16(xn))
+        return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: x/xn NULL or not 16-byte aligned");
+    if (n->gate_w && !z)
+        return fail(MOE_ERR_INVALID_ARG, "moe_rmsnorm: a gate row needs z");
+    return hip_status(moe::launch_rmsnorm(x, T, d, n->gamma, n->eps, n->gate_w, n->gate_b, xn,
+                                          n->gate_w ? z : nullptr,
+                                          static_cast<hipStream_t>(stream)),
+                      "moe_rmsnorm");
+}
+
+moe_status moe_combine_gated(const uint16_t* y_pairs, const int32_t* pair_pos,
+                             const float* weights, const uint16_t* y_shared, const float* z,
+                             const uint16_t* residual, int32_t T, int32_t k, int32_t d,
+                             uint16_t* out, void* stream) {
+    if (T > 0 && !z) return fail(MOE_ERR_INVALID_ARG, "moe_combine_gated: z NULL");
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_combine_gated: T = %d < 0", T);
+    if (k < 1 || k > kMaxK) return fail(MOE_ERR_INVALID_ARG, "moe_combine_gated: k = %d", k);
+    if (d < 8 || d % 8 != 0) return fail(MOE_ERR_INVALID_ARG, "moe_combine_gated: d = %d", d);
+    if (T == 0) return ok();
+    if (!y_pairs || !pair_pos || !weights || !out)
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_combine_gated: y_pairs/pair_pos/weights/out NULL");
+    if (!aligned16(y_pairs) || !aligned16(out) || (y_shared && !aligned16(y_shared)) ||
+        (residual && !aligned16(residual)))
+        return fail(MOE_ERR_INVALID_ARG, "moe_combine_gated: bf16 rows must be 16-byte aligned");
+    return hip_status(moe::launch_combine(y_pairs, pair_pos, weights, y_shared, residual, z, T,
+                                          k, d, out, static_cast<hipStream_t>(stream)),
+                      "moe_combine_gated");
+}
+
+moe_status moe_block_decode(const moe_norm* n, const moe_router* r, const moe_experts* routed,
+                            const moe_experts* shared, const uint16_t* x, int32_t T, int32_t k,
+                            int32_t* ids, float* weights, uint16_t* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    moe_status st = check_layer_decode(r, routed, shared, x, T, k, ids, weights, nullptr, out,
+                                       "moe_block_decode", &need);
+    if (st != MOE_OK) return st;
+    st = check_norm(n, r->d_model, "moe_block_decode");
+    if (st != MOE_OK) return st;
+    if (T == 0) return ok();
+    if (T > moe::kRouteGemvMaxTokens)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_block_decode: T = %d above %d; use moe_rmsnorm and the four calls", T,
+                    moe::kRouteGemvMaxTokens);
+    const int E = r->n_experts, d = r->d_model, F = routed->d_ff;
+    need = block_ws(T, k, E, d, F);
+    if (!ws || ws_bytes < need || !aligned16(ws))
+        return fail(MOE_ERR_WORKSPACE, "moe_block_decode: needs %zu workspace bytes (got %zu)",
+                    need, ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    unsigned* counter = reinterpret_cast<unsigned*>(base);
+    float* lg = reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
+    uint8_t* ffn_ws = base + round_up(route_exact_ws(T, E));
+    uint16_t* xn = reinterpret_cast<uint16_t*>(base + decode_ws(T, k, E, d, F));
+    float* z = n->gate_w ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(xn) +
+                                                    round_up((size_t)T * d * 2))
+                         : nullptr;
+    // the router on xn = RMSNorm(x) (it writes xn and z); T == 1: logits only, every
+    // gate/up block selects; several tokens: the route kernel's last block selects
+    hipError_t e = moe::launch_route_norm(*r, x, T, k, n->gamma, n->eps, n->gate_w, n->gate_b,
+                                          xn, z, ids, weights, lg, counter, s);
+    if (e != hipSuccess) return hip_status(e, "moe_block_decode: route");
+    e = moe::launch_decode_ffn(*routed, shared, xn, T, k, T == 1 ? lg : nullptr, ids, weights,
+                               x, z, out, ffn_ws, s);
+    return hip_status(e, "moe_block_decode");
 }
 
 moe_status moe_dequant_probe(int32_t fmt, int32_t form, const uint8_t* w, const uint16_t* s,

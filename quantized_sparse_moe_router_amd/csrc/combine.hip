@@ -14,7 +14,8 @@ namespace {
 __global__ void __launch_bounds__(256) combine_kernel(
     const uint16_t* __restrict__ y_pairs, const int32_t* __restrict__ pair_pos,
     const float* __restrict__ w, const uint16_t* __restrict__ y_shared,
-    const uint16_t* residual, int T, int k, int d, uint16_t* out) {
+    const uint16_t* residual, const float* __restrict__ z, int T, int k, int d,
+    uint16_t* out) {
     const int per_row = d / 8;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)T * per_row) return;
@@ -22,19 +23,20 @@ __global__ void __launch_bounds__(256) combine_kernel(
     const int c8 = (int)(idx % per_row);
     const uint4 o = combine8(y_pairs, pair_pos + (size_t)t * k, w + (size_t)t * k, k, d,
                                     c8, y_shared ? y_shared + (size_t)t * d : nullptr,
-                                    residual ? residual + (size_t)t * d : nullptr);
+                                    residual ? residual + (size_t)t * d : nullptr,
+                                    z ? z + t : nullptr);
     *reinterpret_cast<uint4*>(out + (size_t)t * d + 8 * c8) = o;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const float* w,
-                          const uint16_t* y_shared, const uint16_t* residual, int T, int k,
-                          int d, uint16_t* out, hipStream_t s) {
+                          const uint16_t* y_shared, const uint16_t* residual, const float* z,
+                          int T, int k, int d, uint16_t* out, hipStream_t s) {
     const int64_t n = (int64_t)T * (d / 8);
     const int blocks = (int)((n + 255) / 256);
-    combine_kernel<<<blocks, 256, 0, s>>>(y_pairs, pair_pos, w, y_shared, residual, T, k, d,
-                                          out);
+    combine_kernel<<<blocks, 256, 0, s>>>(y_pairs, pair_pos, w, y_shared, residual, z, T, k,
+                                          d, out);
     return hipGetLastError();
 }
 

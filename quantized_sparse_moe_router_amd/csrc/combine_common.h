@@ -5,9 +5,11 @@
 // out = bf16( sum_{j<k} w_j * y[q_j]  + y_shared ), summed in fp32 in slot order; slots are
 // taken in chunks of 8 (all index/weight loads, then all row loads, then the fused
 // multiply-adds in slot order), and the padding slots of the last chunk, like dropped
-// pairs (q_j < 0), add 0 * row 0.  With a residual: bf16(residual + bf16(sum)).
+// pairs (q_j < 0), add 0 * row 0.  With a residual-gate logit z the sum is scaled once,
+// sum = fl(sigmoid(z) * sum), before rounding.  With a residual: bf16(residual + bf16(sum)).
 #pragma once
 #include "moe_common.h"
+#include "norm_common.h"
 
 #pragma clang fp contract(off)
 
@@ -15,11 +17,12 @@ namespace moe {
 namespace {
 
 // Columns 8 c8 .. 8 c8 + 7 of one token.  pos / w: the token's k sorted positions and gate
-// weights; y_shared_row / residual_row may be null.
+// weights; y_shared_row / residual_row / z (the token's residual-gate logit) may be null.
 __device__ __forceinline__ uint4 combine8(const uint16_t* y_pairs, const int32_t* pos,
                                           const float* w, int k, int d, int c8,
                                           const uint16_t* y_shared_row,
-                                          const uint16_t* residual_row) {
+                                          const uint16_t* residual_row,
+                                          const float* z = nullptr) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -59,6 +62,11 @@ __device__ __forceinline__ uint4 combine8(const uint16_t* y_pairs, const int32_t
             acc[2 * i] += bf16lo(vv[i]);
             acc[2 * i + 1] += bf16hi(vv[i]);
         }
+    }
+    if (z) {
+        const float g = gate_value(*z);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = g * acc[i];
     }
     uint32_t o[4];
     if (residual_row) {

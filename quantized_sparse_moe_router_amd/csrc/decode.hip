@@ -36,6 +36,7 @@ struct DecodeArgs {
     int32_t* ids;                       // [T][k]; written by the gate/up kernel when logits
     float* weights;                     //   are given, read-only otherwise
     const uint16_t* residual;
+    const float* z;                     // [T] residual-gate logits, or null
     uint16_t* out;
     uint16_t* h;                        // [S][F] bf16: pair rows, then shared-token rows
     int* err;
@@ -237,6 +238,7 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
             }
         }
         if (a.sg) acc += y[(P + t) * DS::ROWS];
+        if (a.z) acc = gate_value(a.z[t]) * acc;
         uint32_t o;
         if (a.residual) {
             const float r = bf16_to_f32(t == lane ? res_bits : a.residual[(size_t)t * D + row]);
@@ -414,7 +416,7 @@ bool decode_fits(int T, int k, int F, bool shared) {
 hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* shared,
                              const uint16_t* x, int T, int k, const float* logits,
                              int32_t* ids, float* weights, const uint16_t* residual,
-                             uint16_t* out, void* ws, hipStream_t s) {
+                             const float* z, uint16_t* out, void* ws, hipStream_t s) {
     const int d = routed.d_model, F = routed.d_ff;
     const DecodeWs L = decode_ws_layout(T, k, d, F);
     uint8_t* base = static_cast<uint8_t*>(ws);
@@ -429,7 +431,7 @@ hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* share
     a.ssu = shared ? shared->s_up : nullptr;
     a.ssd = shared ? shared->s_down : nullptr;
     a.x = x; a.T = T; a.k = k; a.logits = logits; a.ids = ids; a.weights = weights;
-    a.residual = residual; a.out = out;
+    a.residual = residual; a.z = z; a.out = out;
     a.h = reinterpret_cast<uint16_t*>(base + L.h);
     a.err = device_error_flag();
     if (routed.fmt == MOE_FMT_INT4_G32) return launch_fmt<MOE_FMT_INT4_G32>(a, d, F, s);

@@ -117,6 +117,18 @@ hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, in
 hipError_t launch_route_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
                                hipStream_t s);
 
+// The pre-layer norm fused into the router, for the decode block (T <= kRouteGemvMaxTokens):
+// the router runs on xn = RMSNorm(x) (gamma [d], eps), stores xn [T][d] and, if gw is not
+// null, the residual-gate logits z [T].  T == 1: logits only (the decode gate/up kernel
+// selects); T > 1: logits, ids and weights as launch_route.
+hipError_t launch_route_norm(const moe_router& r, const uint16_t* x, int T, int k,
+                             const float* gamma, float eps, const float* gw, float gb,
+                             uint16_t* xn, float* z, int32_t* ids, float* weights,
+                             float* logits, unsigned* counter, hipStream_t s);
+// The norm alone (and the gate logits when gw is not null), one wave per token.
+hipError_t launch_rmsnorm(const uint16_t* x, int T, int d, const float* gamma, float eps,
+                          const float* gw, float gb, uint16_t* xn, float* z, hipStream_t s);
+
 // Many tokens, logits not wanted: the bounded form.  launch_route_bounded_logits writes
 // every logit to within 2^-11 (|x_t| nw[e] + |b_e|) of the fixed-order value (MFMA; planes
 // is a workspace of route_bounded_planes_bytes, nw [E] the row norm bounds);
@@ -144,9 +156,10 @@ hipError_t launch_ffn_mfma(const moe_experts& ex, const uint16_t* x, int T, int 
                            void* ws, hipStream_t s);
 size_t ffn_mfma_ws_bytes(int64_t rows, int E, int F);
 
+// z: residual-gate logits [T] or null
 hipError_t launch_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const float* w,
-                          const uint16_t* y_shared, const uint16_t* residual, int T, int k,
-                          int d, uint16_t* out, hipStream_t s);
+                          const uint16_t* y_shared, const uint16_t* residual, const float* z,
+                          int T, int k, int d, uint16_t* out, hipStream_t s);
 
 // Expert side of a decode step (routed + shared FFN and combine) in two launches, at most
 // 64 pairs and S = T*k (+ T shared) slots whose h rows fit in kDecodeMaxLds bytes of LDS.
@@ -159,10 +172,11 @@ DecodeWs decode_ws_layout(int T, int k, int d_model, int d_ff);
 bool decode_fits(int T, int k, int d_ff, bool shared);
 // logits non-null: the selection runs inside (ids and weights are written); null: ids and
 // weights are inputs.
+// z: residual-gate logits [T] applied in the combine, or null.
 hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* shared,
                              const uint16_t* x, int T, int k, const float* logits,
                              int32_t* ids, float* weights, const uint16_t* residual,
-                             uint16_t* out, void* ws, hipStream_t s);
+                             const float* z, uint16_t* out, void* ws, hipStream_t s);
 
 // The two expert paths' weight decoders over n_groups consecutive 32-code groups (form 0:
 // fp32 out[n_groups][32], the GEMV arithmetic on one-hot activations; form 1: bf16

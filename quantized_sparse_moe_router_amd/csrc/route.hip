@@ -11,6 +11,7 @@
 // tokens, no logits wanted) recomputes in that order every expert its MFMA logits cannot
 // rule out, so all forms select alike.
 #include "moe_common.h"
+#include "norm_common.h"
 #include "topk_common.h"
 
 #pragma clang fp contract(off)
@@ -22,14 +23,42 @@ namespace {
 // One wave per expert row.  Lane l holds its vectors v = l + 64 j of the row in
 // registers and walks them for every token; the butterfly is a shuffle-xor tree.
 // PV = elements per 16-byte vector (4 fp32 or 16 int8); NV = vectors per lane.
-template <int FMT, int NV, bool DEVICE_SCOPE_STORE, int WPB = 4>
+//
+// NORM: the tokens are the layer's un-normalised input; every wave computes a token's
+// norm scale itself (norm_common.h) and uses xn = RMSNorm(x) in its dot products, the wave
+// of row 0 stores xn [T][d], and the wave of row E (one past the experts) computes the
+// residual-gate logit z [T] instead of an expert logit.
+struct RouteNorm {
+    const float* gamma;   // [d]
+    float eps;
+    const float* gw;      // [d] gate row, or null: no gate logit
+    float gb;
+    uint16_t* xn;         // [T][d]
+    float* z;             // [T]
+};
+
+template <int FMT, int NV, bool DEVICE_SCOPE_STORE, int WPB = 4, bool NORM = false>
 __device__ __forceinline__ void router_gemv_rows(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
-    float* logits) {
+    float* logits, const RouteNorm& nm = RouteNorm{}) {
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
+    constexpr int NC = NV * PV / 4;          // the norm's 4-element chunks per lane
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.x * WPB + (threadIdx.x >> 6);   // WPB rows (waves) per block
+    if constexpr (NORM) {
+        if (e == E && nm.gw) {               // the gate row
+            for (int t = 0; t < T; ++t) {
+                uint2 x4[NC];
+                const float ss = group_sum<64>(rms_lane_sumsq<NC>(x + (size_t)t * d, lane, x4));
+                const float r = rms_scale(ss, d, nm.eps);
+                const float zt = rms_row_and_gate<NC>(x4, lane, r, nm.gamma, nm.gw, nm.gb,
+                                                      nullptr);
+                if (lane == 0) nm.z[t] = zt;
+            }
+            return;
+        }
+    }
     if (e >= E) return;
 
     float w[NV][PV];
@@ -58,24 +87,51 @@ __device__ __forceinline__ void router_gemv_rows(
 
     for (int t = 0; t < T; ++t) {
         const uint16_t* xt = x + (size_t)t * d;
+        float r = 1.0f;
+        if constexpr (NORM) {
+            uint2 x4[NC];
+            r = rms_scale(group_sum<64>(rms_lane_sumsq<NC>(xt, lane, x4)), d, nm.eps);
+        }
+        // element c of the layer's input: x, or xn under NORM (stored by row 0's wave)
+        auto in = [&](uint32_t bits, int c) __attribute__((always_inline)) -> uint32_t {
+            if constexpr (NORM) return rms_apply(bf16_to_f32(bits), r, nm.gamma[c]);
+            return bits;
+        };
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int c0 = (lane + 64 * j) * PV;
             if constexpr (PV == 4) {
-                uint2 xv = *reinterpret_cast<const uint2*>(xt + c0);
-                acc = __builtin_fmaf(bf16lo(xv.x), w[j][0], acc);
-                acc = __builtin_fmaf(bf16hi(xv.x), w[j][1], acc);
-                acc = __builtin_fmaf(bf16lo(xv.y), w[j][2], acc);
-                acc = __builtin_fmaf(bf16hi(xv.y), w[j][3], acc);
+                const uint2 xv = *reinterpret_cast<const uint2*>(xt + c0);
+                const uint32_t q0 = in(xv.x & 0xffffu, c0), q1 = in(xv.x >> 16, c0 + 1);
+                const uint32_t q2 = in(xv.y & 0xffffu, c0 + 2), q3 = in(xv.y >> 16, c0 + 3);
+                if constexpr (NORM)
+                    if (e == 0)
+                        *reinterpret_cast<uint2*>(nm.xn + (size_t)t * d + c0) =
+                            make_uint2(q0 | (q1 << 16), q2 | (q3 << 16));
+                acc = __builtin_fmaf(bf16_to_f32(q0), w[j][0], acc);
+                acc = __builtin_fmaf(bf16_to_f32(q1), w[j][1], acc);
+                acc = __builtin_fmaf(bf16_to_f32(q2), w[j][2], acc);
+                acc = __builtin_fmaf(bf16_to_f32(q3), w[j][3], acc);
             } else {
                 const uint4* xp = reinterpret_cast<const uint4*>(xt + c0);
                 uint4 a = xp[0], bq = xp[1];
                 uint32_t xs[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+                uint32_t qs[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    qs[i] = in(xs[i] & 0xffffu, c0 + 2 * i) |
+                            (in(xs[i] >> 16, c0 + 2 * i + 1) << 16);
+                if constexpr (NORM)
+                    if (e == 0) {
+                        uint4* dst = reinterpret_cast<uint4*>(nm.xn + (size_t)t * d + c0);
+                        dst[0] = make_uint4(qs[0], qs[1], qs[2], qs[3]);
+                        dst[1] = make_uint4(qs[4], qs[5], qs[6], qs[7]);
+                    }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    acc = __builtin_fmaf(bf16lo(xs[i]), w[j][2 * i], acc);
-                    acc = __builtin_fmaf(bf16hi(xs[i]), w[j][2 * i + 1], acc);
+                    acc = __builtin_fmaf(bf16lo(qs[i]), w[j][2 * i], acc);
+                    acc = __builtin_fmaf(bf16hi(qs[i]), w[j][2 * i + 1], acc);
                 }
             }
         }
@@ -479,12 +535,13 @@ __global__ void __launch_bounds__(256) route_bounded_select_kernel(
 // found it.  A release fence at device scope would also write back the whole L2 of each
 // XCD (buffer_wbl2), measured at 3.7 us per call here; the completed device-scope
 // stores already give the last block every logit.
-template <int FMT, int NV, int NPL>
+template <int FMT, int NV, int NPL, bool NORM = false>
 __global__ void __launch_bounds__(256) router_gemv_topk_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d, int k,
-    float* logits, int32_t* __restrict__ ids, float* __restrict__ weights, unsigned* counter) {
-    router_gemv_rows<FMT, NV, true>(W, scale, bias, x, T, E, d, logits);
+    float* logits, int32_t* __restrict__ ids, float* __restrict__ weights, unsigned* counter,
+    RouteNorm nm) {
+    router_gemv_rows<FMT, NV, true, 4, NORM>(W, scale, bias, x, T, E, d, logits, nm);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's stores have completed
     __syncthreads();
     __shared__ int is_last;
@@ -510,12 +567,34 @@ __global__ void __launch_bounds__(256) router_gemv_topk_kernel(
 // Logits only, for a consumer that runs the selection itself (the decode layer).  One
 // wave (one expert row) per block: E blocks reach every CU, where blocks of 4 rows would
 // leave half of them idle at E = 512.
-template <int FMT, int NV>
+template <int FMT, int NV, bool NORM = false>
 __global__ void __launch_bounds__(64) router_gemv_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
-    float* __restrict__ logits) {
-    router_gemv_rows<FMT, NV, false, 1>(W, scale, bias, x, T, E, d, logits);
+    float* __restrict__ logits, RouteNorm nm) {
+    router_gemv_rows<FMT, NV, false, 1, NORM>(W, scale, bias, x, T, E, d, logits, nm);
+}
+
+// the selection kernels for T <= kRouteGemvMaxTokens; NORM: with the fused norm (one more
+// row for the gate logit when there is a gate)
+template <int FMT, int NV, bool NORM>
+hipError_t launch_gemv_topk(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
+                            float* weights, float* logits, unsigned* counter,
+                            const RouteNorm& nm, hipStream_t s) {
+    const int E = r.n_experts, d = r.d_model;
+    const int npl = (E + 63) / 64;
+    const int rows = E + ((NORM && nm.gw) ? 1 : 0);
+    const dim3 grid((rows + 3) / 4), block(256);
+#define MOE_GT(N)                                                                          \
+    router_gemv_topk_kernel<FMT, NV, N, NORM><<<grid, block, 0, s>>>(                      \
+        r.w, r.scale, r.bias, x, T, E, d, k, logits, ids, weights, counter, nm)
+    if (npl <= 1) MOE_GT(1);
+    else if (npl <= 2) MOE_GT(2);
+    else if (npl <= 4) MOE_GT(4);
+    else if (npl <= 8) MOE_GT(8);
+    else MOE_GT(16);
+#undef MOE_GT
+    return hipGetLastError();
 }
 
 template <int FMT, int NV>
@@ -523,20 +602,9 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
                      float* weights, float* logits, unsigned* counter, hipStream_t s) {
     const int E = r.n_experts, d = r.d_model;
     const int npl = (E + 63) / 64;
-    if (T <= kRouteGemvMaxTokens) {   // one wave per expert row, selection by the last block
-        const dim3 grid((E + 3) / 4), block(256);
-#define MOE_GT(N)                                                                         \
-    router_gemv_topk_kernel<FMT, NV, N><<<grid, block, 0, s>>>(r.w, r.scale, r.bias, x, T, \
-                                                               E, d, k, logits, ids, weights, \
-                                                               counter)
-        if (npl <= 1) MOE_GT(1);
-        else if (npl <= 2) MOE_GT(2);
-        else if (npl <= 4) MOE_GT(4);
-        else if (npl <= 8) MOE_GT(8);
-        else MOE_GT(16);
-#undef MOE_GT
-        return hipGetLastError();
-    }
+    if (T <= kRouteGemvMaxTokens)   // one wave per expert row, selection by the last block
+        return launch_gemv_topk<FMT, NV, false>(r, x, T, k, ids, weights, logits, counter,
+                                                RouteNorm{}, s);
     {
         using R = RgShape<FMT>;
         constexpr int kLds = 2 * R::STAGE;
@@ -593,16 +661,16 @@ hipError_t launch_fmt(const moe_router& r, const uint16_t* x, int T, int k, int3
     return hipErrorInvalidValue;
 }
 
-template <int FMT>
+template <int FMT, bool NORM>
 hipError_t launch_logits_fmt(const moe_router& r, const uint16_t* x, int T, float* logits,
-                             hipStream_t s) {
+                             const RouteNorm& nm, hipStream_t s) {
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
     const int nv = r.d_model / (64 * PV);
-    const dim3 grid(r.n_experts), block(64);
+    const dim3 grid(r.n_experts + ((NORM && nm.gw) ? 1 : 0)), block(64);
 #define MOE_NV(N)                                                                         \
     if (nv == N) {                                                                        \
-        router_gemv_kernel<FMT, N><<<grid, block, 0, s>>>(r.w, r.scale, r.bias, x, T,     \
-                                                          r.n_experts, r.d_model, logits);\
+        router_gemv_kernel<FMT, N, NORM><<<grid, block, 0, s>>>(                          \
+            r.w, r.scale, r.bias, x, T, r.n_experts, r.d_model, logits, nm);              \
         return hipGetLastError();                                                         \
     }
     MOE_NV(1)
@@ -666,8 +734,50 @@ hipError_t launch_route_bounded_select(const moe_router& r, const uint16_t* x, i
 
 hipError_t launch_route_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
                                hipStream_t s) {
-    if (r.fmt == MOE_FMT_INT8_ROW) return launch_logits_fmt<MOE_FMT_INT8_ROW>(r, x, T, logits, s);
-    return launch_logits_fmt<MOE_FMT_FP32>(r, x, T, logits, s);
+    if (r.fmt == MOE_FMT_INT8_ROW)
+        return launch_logits_fmt<MOE_FMT_INT8_ROW, false>(r, x, T, logits, RouteNorm{}, s);
+    return launch_logits_fmt<MOE_FMT_FP32, false>(r, x, T, logits, RouteNorm{}, s);
+}
+
+namespace {
+template <int FMT>
+hipError_t launch_topk_norm_fmt(const moe_router& r, const uint16_t* x, int T, int k,
+                                int32_t* ids, float* weights, float* logits, unsigned* counter,
+                                const RouteNorm& nm, hipStream_t s) {
+    constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
+    const int nv = r.d_model / (64 * PV);
+#define MOE_NV(N)                                                                         \
+    if (nv == N) {                                                                        \
+        if constexpr (N * PV <= 64)                                                       \
+            return launch_gemv_topk<FMT, N, true>(r, x, T, k, ids, weights, logits,       \
+                                                  counter, nm, s);                        \
+        else                                                                              \
+            return hipErrorInvalidValue;                                                  \
+    }
+    MOE_NV(1)
+    MOE_NV(2)
+    MOE_NV(4)
+    MOE_NV(8)
+    MOE_NV(16)
+#undef MOE_NV
+    return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_route_norm(const moe_router& r, const uint16_t* x, int T, int k,
+                             const float* gamma, float eps, const float* gw, float gb,
+                             uint16_t* xn, float* z, int32_t* ids, float* weights,
+                             float* logits, unsigned* counter, hipStream_t s) {
+    const RouteNorm nm{gamma, eps, gw, gb, xn, z};
+    if (T == 1) {   // logits only: the decode gate/up kernel selects
+        if (r.fmt == MOE_FMT_INT8_ROW)
+            return launch_logits_fmt<MOE_FMT_INT8_ROW, true>(r, x, T, logits, nm, s);
+        return launch_logits_fmt<MOE_FMT_FP32, true>(r, x, T, logits, nm, s);
+    }
+    if (r.fmt == MOE_FMT_INT8_ROW)
+        return launch_topk_norm_fmt<MOE_FMT_INT8_ROW>(r, x, T, k, ids, weights, logits, counter,
+                                                      nm, s);
+    return launch_topk_norm_fmt<MOE_FMT_FP32>(r, x, T, k, ids, weights, logits, counter, nm, s);
 }
 
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,

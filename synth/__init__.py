@@ -8,6 +8,6 @@ GPU library's tests and the CPU oracle's tests take their inputs from here.
 from .workloads import WORKLOADS, Workload  # noqa: F401
 from .inputs import (  # noqa: F401
     FMT_FP32, FMT_INT8_ROW, FMT_INT4_G32, FMT_INT6_G32,
-    Layer, make_layer, make_layer_all_codes, make_tokens, quantize_int4_g32, quantize_int6_g32,
+    Layer, Norm, make_layer, make_layer_all_codes, make_norm, make_tokens, quantize_int4_g32, quantize_int6_g32,
     quantize_int8_row, pack_int4, pack_int6, zipf_bias, bits16,
 )

@@ -213,6 +213,36 @@ def make_layer(w, seed=0, layer=0, device="cpu", bias=None, with_shared=True,
     return Layer(router, routed, shared)
 
 
+@dataclass
+class Norm:
+    gamma: torch.Tensor             # fp32 [d]
+    gate_w: Optional[torch.Tensor]  # fp32 [d] or None
+    eps: float
+    gate_b: float
+
+    def host(self):
+        return {"gamma": self.gamma.cpu().numpy(), "eps": self.eps,
+                "gate_w": None if self.gate_w is None else self.gate_w.cpu().numpy(),
+                "gate_b": self.gate_b}
+
+
+_T_NORM, _T_GATE_ROW = 20, 21
+
+
+def make_norm(w, seed=0, layer=0, device="cpu", gate=True):
+    """A block's pre-layer norm and residual gate: gamma = 1 + 0.1 N(0, 1), gate row
+    N(0, 0.02) like a router row (so z = <gate_w, xn> has a spread of about 0.9 and the gate
+    sigmoid(z) stays inside (0.2, 0.8) for most tokens), gate bias 0, eps 1e-6."""
+    dev = torch.device(device)
+    g = _gen(dev, w.wid, seed, layer, _T_NORM)
+    gamma = (1.0 + 0.1 * torch.randn((w.d,), generator=g, device=dev)).to(torch.float32)
+    gw = None
+    if gate:
+        g2 = _gen(dev, w.wid, seed, layer, _T_GATE_ROW)
+        gw = (0.02 * torch.randn((w.d,), generator=g2, device=dev)).to(torch.float32)
+    return Norm(gamma.contiguous(), None if gw is None else gw.contiguous(), 1e-6, 0.0)
+
+
 _QRANGE = {"int4_g32": (-8, 7), "int6_g32": (-32, 31)}
 _PACK = {"int4_g32": pack_int4, "int6_g32": pack_int6}
 

@@ -205,6 +205,52 @@ def test_layer_decode_rejects(L):
     assert L.moe_workspace_size(_lib.MOE_OP_LAYER_DECODE, 7, 10, 512, 2048, 512) == 0
 
 
+def test_norm_calls_reject(L):
+    from quantized_sparse_moe_router_amd import _lib
+    P = ctypes.c_void_p
+
+    def nd(gamma=16, gate_w=16, eps=1e-6, gate_b=0.0):
+        return _lib.moe_norm(gamma, gate_w, eps, gate_b)
+
+    def rms(n=nd(), x=16, T=2, d=2048, xn=16, z=16):
+        return L.moe_rmsnorm(ctypes.byref(n) if n is not None else None, P(x), T, d, P(xn),
+                             P(z), None)
+    assert rms(n=None) == -1
+    assert rms(n=nd(gamma=None)) == -1
+    assert rms(n=nd(gamma=8)) == -1                       # misaligned gamma
+    assert rms(n=nd(gate_w=8)) == -1
+    assert rms(n=nd(eps=-1.0)) == -1
+    assert rms(n=nd(eps=float("nan"))) == -1
+    assert rms(n=nd(gate_b=float("inf"))) == -1
+    assert rms(d=768) == -1
+    assert rms(T=-1) == -1
+    assert rms(z=0) == -1                                 # a gate row needs z
+    assert rms(x=8) == -1
+    assert rms(T=0, x=0, xn=0, z=0) == 0
+    # gated combine: z required
+    assert L.moe_combine_gated(P(16), P(16), P(16), None, None, None, 2, 10, 2048, P(16),
+                               None) == -1
+    assert L.moe_combine_gated(P(16), P(16), P(16), None, P(16), None, 2, 10, 12, P(16),
+                               None) == -1
+    # the decode block: the layer's checks, the norm's, and T <= 16
+    r, ex = _router(), _experts()
+    n = nd()
+
+    def blk(n=n, T=1, k=10, ws=16, wsb=1 << 30):
+        return L.moe_block_decode(ctypes.byref(n) if n is not None else None,
+                                  ctypes.byref(r), ctypes.byref(ex), None, P(16), T, k,
+                                  P(16), P(16), P(16), P(ws), wsb, None)
+    assert blk(n=None) == -1
+    assert blk(n=nd(gamma=None)) == -1
+    assert blk(T=7) == -2                                 # 70 pairs
+    assert blk(T=17, k=1) == -2 and "T = 17" in _err(L)
+    assert blk(wsb=100) == -3
+    need = L.moe_workspace_size(_lib.MOE_OP_BLOCK_DECODE, 4, 10, 512, 2048, 512)
+    assert need == L.moe_workspace_size(_lib.MOE_OP_LAYER_DECODE, 4, 10, 512, 2048, 512) + \
+        4 * 2048 * 2 + 256
+    assert blk(T=4, wsb=need - 1) == -3
+
+
 def test_dequant_probe_rejects(L):
     P = ctypes.c_void_p
     dummy = P(16)
