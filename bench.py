@@ -348,38 +348,49 @@ def main():
 
 
 def decode_sweep(moe, synth, np, torch, args):
-    """48 distinct layers chained through the residual, x_{l+1} = bf16(x_l + out_l), one
-    token and four tokens (one real + three drafts) per step; the whole 48-layer step is
-    one graph.  Weights: 48 x 0.91 GB resident, so no cache holds them between steps."""
+    """48 distinct blocks chained: each is the pre-layer RMS norm, the MoE layer and the
+    gated residual, x_{l+1} = bf16(x_l + bf16(sigmoid(z_l) * out_l)) (moe_block_decode: the
+    norm and the gate fused into the layer's three launches), one token and four tokens (one
+    real + three drafts) per step; the whole 48-block step is one graph.  Weights: 48 x 0.91
+    GB resident, so no cache holds them between steps.  (Without the norm the stream grows
+    like x + c x^2 through the quadratic SwiGLU and overflows bf16 within ~30 layers.)"""
     w = synth.WORKLOADS["decode_sweep_48_layers"]
     lays = [synth.make_layer(w, seed=0, layer=l, device="cuda") for l in range(w.layers)]
+    nrms = [synth.make_norm(w, seed=0, layer=l, device="cuda") for l in range(w.layers)]
     E_b = expert_bytes(lays[0].routed)
     r_b = lays[0].router.w.numel() * lays[0].router.w.element_size()
-    out = {"workload": "decode_sweep_48_layers", "layers": w.layers, "router_bias": "zipf"}
+    n_b = 2 * w.d * 4                                 # gamma and the gate row, fp32
+    out = {"workload": "decode_sweep_48_layers", "layers": w.layers, "router_bias": "zipf",
+           "block": "rmsnorm -> moe layer -> gated residual (moe_block_decode)"}
     for T in (1, 4):
-        mls = [moe.MoeLayer(L.router, L.routed, L.shared, w.k, T) for L in lays]
+        mls = [moe.MoeLayer(L.router, L.routed, L.shared, w.k, T, norm=N)
+               for L, N in zip(lays, nrms)]
         xs = [synth.make_tokens(w, T=T, seed=0, device="cuda")]
         xs += [torch.empty_like(xs[0]) for _ in range(w.layers)]
 
         def step():
             for l in range(w.layers):
-                mls[l].decode(xs[l], residual=xs[l], out=xs[l + 1])
+                mls[l].block_decode(xs[l], out=xs[l + 1])
 
         step()
         torch.cuda.synchronize()
         moe.moe_check_device_error()
+        rms_out = float(xs[-1].float().pow(2).mean().sqrt())
+        if not np.isfinite(rms_out):
+            raise SystemExit("bench.py: the 48-block stream is not finite")
         # distinct routed experts per layer (the bytes a step must stream)
         U = [int(np.unique(m.ids[:T].cpu().numpy()).size) for m in mls]
         ms, ms_min, _ = time_graph(step, max(20, args.reps), 2)
-        bytes_step = sum(r_b + (u + 1) * E_b + 2 * T * w.d * 2 for u in U)
+        bytes_step = sum(r_b + n_b + (u + 1) * E_b + 2 * T * w.d * 2 for u in U)
         out["T%d" % T] = {"tokens_per_s": round(T / (ms * 1e-3), 1),
                           "ms_per_step": round(ms, 4), "ms_per_step_min": round(ms_min, 4),
                           "us_per_layer": round(ms * 1e3 / w.layers, 3),
                           "distinct_experts_per_layer_mean": round(float(np.mean(U)), 2),
                           "alg_bytes_per_step": bytes_step,
-                          "weight_stream_GBps": round(bytes_step / (ms * 1e-3) / 1e9, 1)}
+                          "weight_stream_GBps": round(bytes_step / (ms * 1e-3) / 1e9, 1),
+                          "rms_x_after_48_blocks": round(rms_out, 3)}
         del mls, xs
-    del lays
+    del lays, nrms
     return out
 
 

@@ -13,6 +13,7 @@
 //   r    = fl(1 / fl(sqrt(fl(fl(ss / d) + eps)))), IEEE division and square root (the
 //          compiler's default single-precision sqrt and division are correctly rounded);
 //   xn_c = bf16(fl(fl(x_c * r) * gamma_c)).
+// (Inputs are finite; an all-zero row needs eps > 0.)
 // The gate logit z = <gate_w, xn> + gate_b takes the router's fp32 order, whose 16-byte
 // weight vectors are the same 4-element chunks.
 #pragma once
@@ -47,10 +48,11 @@ __device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
     return 1.0f / sqrtf(ms + eps);
 }
 
-// bf16 bits of xn for one element
+// bf16 bits of xn for one element, rounded to nearest even (finite values; no branch)
 __device__ __forceinline__ uint32_t rms_apply(float x, float r, float gamma) {
     const float a = x * r;
-    return f32_to_bf16(a * gamma);
+    const uint32_t u = __float_as_uint(a * gamma);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
 // One wave, one token: xn of the whole row in the chunk order (stored if xn_row is not
@@ -60,24 +62,33 @@ template <int NC>
 __device__ __forceinline__ float rms_row_and_gate(const uint2* x4, int lane, float r,
                                                   const float* gamma, const float* gw,
                                                   float gb, uint16_t* xn_row) {
+    // every gamma and gate chunk requested before the first is used (left alone, the
+    // compiler awaits each chunk before requesting the next)
+    float4 g4[NC], w4[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c0 = (lane + 64 * j) * 4;
+        g4[j] = *reinterpret_cast<const float4*>(gamma + c0);
+        w4[j] = gw ? *reinterpret_cast<const float4*>(gw + c0) : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+        asm volatile("" : "+v"(g4[j].x), "+v"(g4[j].y), "+v"(g4[j].z), "+v"(g4[j].w),
+                     "+v"(w4[j].x), "+v"(w4[j].y), "+v"(w4[j].z), "+v"(w4[j].w));
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
         const int c0 = (lane + 64 * j) * 4;
-        const float4 g4 = *reinterpret_cast<const float4*>(gamma + c0);
-        const uint32_t n0 = rms_apply(bf16lo(x4[j].x), r, g4.x);
-        const uint32_t n1 = rms_apply(bf16hi(x4[j].x), r, g4.y);
-        const uint32_t n2 = rms_apply(bf16lo(x4[j].y), r, g4.z);
-        const uint32_t n3 = rms_apply(bf16hi(x4[j].y), r, g4.w);
+        const uint32_t n0 = rms_apply(bf16lo(x4[j].x), r, g4[j].x);
+        const uint32_t n1 = rms_apply(bf16hi(x4[j].x), r, g4[j].y);
+        const uint32_t n2 = rms_apply(bf16lo(x4[j].y), r, g4[j].z);
+        const uint32_t n3 = rms_apply(bf16hi(x4[j].y), r, g4[j].w);
         if (xn_row)
             *reinterpret_cast<uint2*>(xn_row + c0) = make_uint2(n0 | (n1 << 16), n2 | (n3 << 16));
-        if (gw) {
-            const float4 w4 = *reinterpret_cast<const float4*>(gw + c0);
-            acc = __builtin_fmaf(bf16_to_f32(n0), w4.x, acc);
-            acc = __builtin_fmaf(bf16_to_f32(n1), w4.y, acc);
-            acc = __builtin_fmaf(bf16_to_f32(n2), w4.z, acc);
-            acc = __builtin_fmaf(bf16_to_f32(n3), w4.w, acc);
-        }
+        acc = __builtin_fmaf(bf16_to_f32(n0), w4[j].x, acc);
+        acc = __builtin_fmaf(bf16_to_f32(n1), w4[j].y, acc);
+        acc = __builtin_fmaf(bf16_to_f32(n2), w4[j].z, acc);
+        acc = __builtin_fmaf(bf16_to_f32(n3), w4[j].w, acc);
     }
     if (!gw) return 0.0f;
     return group_sum<64>(acc) + gb;

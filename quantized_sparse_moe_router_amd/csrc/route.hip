@@ -84,31 +84,80 @@ __device__ __forceinline__ void router_gemv_rows(
     }
     const float b = bias ? bias[e] : 0.0f;
     const float se = (FMT == MOE_FMT_INT8_ROW) ? f16_to_f32(scale[e]) : 1.0f;
+    // NORM: gamma of the lane's elements, in registers for every token
+    float gam[NORM ? NV : 1][NORM ? PV : 1];
+    if constexpr (NORM) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int q = 0; q < PV / 4; ++q) {
+                const float4 g4 =
+                    *reinterpret_cast<const float4*>(nm.gamma + (lane + 64 * j) * PV + 4 * q);
+                gam[j][4 * q] = g4.x; gam[j][4 * q + 1] = g4.y;
+                gam[j][4 * q + 2] = g4.z; gam[j][4 * q + 3] = g4.w;
+            }
+    }
+    // NORM: the norm's chunks of the next token, requested before the current token's work
+    uint2 x4n[NORM ? NC : 1];
+    if constexpr (NORM) {
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            x4n[j] = *reinterpret_cast<const uint2*>(x + (lane + 64 * j) * 4);
+        // the row, gamma and the first token's chunks stay in these registers for the whole
+        // token loop: all requested above, awaited here once (left alone, the compiler
+        // issues and awaits them piece by piece inside the loop)
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int i = 0; i < PV; ++i) asm volatile("" : "+v"(w[j][i]), "+v"(gam[j][i]));
+#pragma unroll
+        for (int j = 0; j < NC; ++j) asm volatile("" : "+v"(x4n[j].x), "+v"(x4n[j].y));
+    }
 
     for (int t = 0; t < T; ++t) {
         const uint16_t* xt = x + (size_t)t * d;
         float r = 1.0f;
+        uint2 x4[NORM ? NC : 1];
         if constexpr (NORM) {
-            uint2 x4[NC];
-            r = rms_scale(group_sum<64>(rms_lane_sumsq<NC>(xt, lane, x4)), d, nm.eps);
+#pragma unroll
+            for (int j = 0; j < NC; ++j) x4[j] = x4n[j];
+            if (t + 1 < T) {
+#pragma unroll
+                for (int j = 0; j < NC; ++j)
+                    x4n[j] = *reinterpret_cast<const uint2*>(xt + d + (lane + 64 * j) * 4);
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NC; ++j) {
+                const float a0 = bf16lo(x4[j].x), a1 = bf16hi(x4[j].x);
+                const float a2 = bf16lo(x4[j].y), a3 = bf16hi(x4[j].y);
+                ss = __builtin_fmaf(a0, a0, ss);
+                ss = __builtin_fmaf(a1, a1, ss);
+                ss = __builtin_fmaf(a2, a2, ss);
+                ss = __builtin_fmaf(a3, a3, ss);
+            }
+            r = rms_scale(group_sum<64>(ss), d, nm.eps);
         }
-        // element c of the layer's input: x, or xn under NORM (stored by row 0's wave)
-        auto in = [&](uint32_t bits, int c) __attribute__((always_inline)) -> uint32_t {
-            if constexpr (NORM) return rms_apply(bf16_to_f32(bits), r, nm.gamma[c]);
-            return bits;
-        };
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             const int c0 = (lane + 64 * j) * PV;
             if constexpr (PV == 4) {
-                const uint2 xv = *reinterpret_cast<const uint2*>(xt + c0);
-                const uint32_t q0 = in(xv.x & 0xffffu, c0), q1 = in(xv.x >> 16, c0 + 1);
-                const uint32_t q2 = in(xv.y & 0xffffu, c0 + 2), q3 = in(xv.y >> 16, c0 + 3);
-                if constexpr (NORM)
+                // under NORM the router's vectors are the norm's chunks: x4[j]
+                uint2 xv;
+                if constexpr (NORM) xv = x4[j];
+                else xv = *reinterpret_cast<const uint2*>(xt + c0);
+                uint32_t q0 = xv.x & 0xffffu, q1 = xv.x >> 16;
+                uint32_t q2 = xv.y & 0xffffu, q3 = xv.y >> 16;
+                if constexpr (NORM) {
+                    q0 = rms_apply(bf16_to_f32(q0), r, gam[j][0]);
+                    q1 = rms_apply(bf16_to_f32(q1), r, gam[j][1]);
+                    q2 = rms_apply(bf16_to_f32(q2), r, gam[j][2]);
+                    q3 = rms_apply(bf16_to_f32(q3), r, gam[j][3]);
                     if (e == 0)
                         *reinterpret_cast<uint2*>(nm.xn + (size_t)t * d + c0) =
                             make_uint2(q0 | (q1 << 16), q2 | (q3 << 16));
+                }
                 acc = __builtin_fmaf(bf16_to_f32(q0), w[j][0], acc);
                 acc = __builtin_fmaf(bf16_to_f32(q1), w[j][1], acc);
                 acc = __builtin_fmaf(bf16_to_f32(q2), w[j][2], acc);
@@ -116,18 +165,18 @@ __device__ __forceinline__ void router_gemv_rows(
             } else {
                 const uint4* xp = reinterpret_cast<const uint4*>(xt + c0);
                 uint4 a = xp[0], bq = xp[1];
-                uint32_t xs[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-                uint32_t qs[8];
+                uint32_t qs[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+                if constexpr (NORM) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    qs[i] = in(xs[i] & 0xffffu, c0 + 2 * i) |
-                            (in(xs[i] >> 16, c0 + 2 * i + 1) << 16);
-                if constexpr (NORM)
+                    for (int i = 0; i < 8; ++i)
+                        qs[i] = rms_apply(bf16lo(qs[i]), r, gam[j][2 * i]) |
+                                (rms_apply(bf16hi(qs[i]), r, gam[j][2 * i + 1]) << 16);
                     if (e == 0) {
                         uint4* dst = reinterpret_cast<uint4*>(nm.xn + (size_t)t * d + c0);
                         dst[0] = make_uint4(qs[0], qs[1], qs[2], qs[3]);
                         dst[1] = make_uint4(qs[4], qs[5], qs[6], qs[7]);
                     }
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     acc = __builtin_fmaf(bf16lo(qs[i]), w[j][2 * i], acc);
