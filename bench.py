@@ -80,6 +80,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-sweep", action="store_true", help="skip the 48-layer decode sweep")
+    p.add_argument("--no-batches", action="store_true",
+                   help="skip the decode batch sizes 1..64")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="no graph capture (for profilers)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -318,6 +320,12 @@ def main():
                      "min_launch_us": round(ms_exp_min / L * 1e3, 3)},
     }
 
+    # ---- decode batches: 1 .. 64 tokens per call through the layer (several decode slots
+    # or drafts verified together), on the same rotated copies
+    if not args.no_batches:
+        line["decode_batches"] = decode_batches(moe, synth, np, torch, copies, w, args)
+        torch.cuda.empty_cache()
+
     # ---- 48 chained layers, 1 and 4 tokens per step
     if not args.no_sweep:
         line["decode_sweep"] = decode_sweep(moe, synth, np, torch, args)
@@ -345,6 +353,48 @@ def main():
         line["cpu_baseline"] = cpu_baseline(base, toks, w, args.cpu_seconds)
 
     print(json.dumps(line), flush=True)
+
+
+def decode_batches(moe, synth, np, torch, copies, w, args):
+    """T tokens per call through the decode layer (d 2048, 512 experts, top-10 + shared),
+    T = 1 .. 64: the four calls (forward) and, while T*k <= 64, moe_layer_decode; each step
+    on the next of the rotated layer copies (more than the 256 MB cache holds for T >= 2).
+    Weight-stream bytes: router + (distinct routed experts + shared) x 1.77 MB."""
+    E_b = expert_bytes(copies[0].routed)
+    r_b = copies[0].router.w.numel() * copies[0].router.w.element_size()
+    n_cp = len(copies)
+    out = {"workload": "decode_d2048_e512_top10", "copies_rotated": n_cp}
+    for T in (1, 4, 6, 8, 16, 32, 64):
+        mls = [moe.MoeLayer(c.router, c.routed, c.shared, w.k, T) for c in copies]
+        xs = [synth.make_tokens(w, T=T, seed=100 + i, device="cuda") for i in range(n_cp)]
+        for i in range(n_cp):
+            mls[i].forward(xs[i])
+        torch.cuda.synchronize()
+        moe.moe_check_device_error()
+        U = [int(np.unique(m.ids[:T].cpu().numpy()).size) for m in mls]
+        bytes_step = float(np.mean([r_b + (u + 1) * E_b + 2 * T * w.d * 2 for u in U]))
+        row = {"distinct_experts_mean": round(float(np.mean(U)), 2),
+               "alg_bytes_per_step": int(bytes_step)}
+
+        def fwd():
+            for i in range(n_cp):
+                mls[i].forward(xs[i])
+        ms, _, _ = time_graph(fwd, max(20, args.reps), 2)
+        ms /= n_cp
+        row["four_calls_us"] = round(ms * 1e3, 2)
+        row["four_calls_GBps"] = round(bytes_step / (ms * 1e-3) / 1e9, 1)
+        row["four_calls_tokens_per_s"] = round(T / (ms * 1e-3), 1)
+        if T * w.k <= 64:
+            def dec():
+                for i in range(n_cp):
+                    mls[i].decode(xs[i])
+            ms, _, _ = time_graph(dec, max(20, args.reps), 2)
+            ms /= n_cp
+            row["layer_decode_us"] = round(ms * 1e3, 2)
+            row["layer_decode_GBps"] = round(bytes_step / (ms * 1e-3) / 1e9, 1)
+        out["T%d" % T] = row
+        del mls, xs
+    return out
 
 
 def decode_sweep(moe, synth, np, torch, args):

@@ -157,8 +157,10 @@ moe_status moe_rmsnorm(const moe_norm* n, const uint16_t* x, int32_t T, int32_t 
  * logits.  How they are reached:
  *   T <= 16: logits and selection in one launch (the last block to finish its rows
  *            selects);
- *   T > 16, logits requested: an LDS-tiled fp32 GEMM in the fixed order, then selection;
- *   T > 16, logits NULL (the bounded form): bf16 MFMA logits (FP32 rows split exactly
+ *   16 < T <= 64: the same one-wave-per-expert-row logits (tokens four at a time), then
+ *            a selection kernel (a wave per token);
+ *   T > 64, logits requested: an LDS-tiled fp32 GEMM in the fixed order, then selection;
+ *   T > 64, logits NULL (the bounded form): bf16 MFMA logits (FP32 rows split exactly
  *            into two bf16 parts plus a dropped remainder below 2^-17 of the weight)
  *            within 2^-11 (|x_t| |w_e| + |b_e|) of the fixed-order value; per token the
  *            experts that this bound cannot rule out of the top k are recomputed in the

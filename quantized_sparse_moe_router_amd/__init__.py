@@ -49,7 +49,7 @@ class MoeLayer:
     them.  Graph capture records the forks and joins.  Intermediate results stay readable
     as attributes (ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared, and
     logits when ``keep_logits``).  Without ``keep_logits``, moe_route gets no logits buffer
-    and, for more than 16 tokens, selects through MFMA logits with an error bound and exact
+    and, for more than 64 tokens, selects through MFMA logits with an error bound and exact
     recomputation of the experts near the cut (the same ids and weights, bit for bit).
 
     decode(x) computes the same output bit for bit with moe_layer_decode (three launches, no

@@ -53,7 +53,6 @@ bool supported_router_dim(int fmt, int d) {
 
 constexpr int kMaxExperts = 1024;   // the decode layer's selection holds <= 16 keys per lane
 constexpr int kMaxK = 64;
-constexpr int64_t kGemvMaxRows = 64;   // pair rows up to which the GEMV path runs
 constexpr int64_t kDecodeMaxPairs = 64; // pairs up to which moe_layer_decode runs
 
 // route workspace, exact form: [counter][logits]
@@ -63,7 +62,7 @@ size_t route_exact_ws(int64_t T, int E) {
 
 // the bounded form (many tokens, no logits wanted) runs when this holds
 bool route_bounded(int64_t T, const float* logits) {
-    return logits == nullptr && T > moe::kRouteGemvMaxTokens;
+    return logits == nullptr && T > moe::kRouteSplitMaxTokens;
 }
 
 // route workspace: [counter]; with no logits from the caller also [logits], and for the
@@ -76,9 +75,10 @@ size_t route_ws(int64_t T, int E, int d, bool need_logits) {
     return n;
 }
 
-// expert FFN workspace: [counters][h][tile list]
+// expert FFN workspace: GEMV [h] or [h][chunk list][count]; MFMA [h][tile list][count]
 size_t ffn_ws(int64_t rows, int E, int F) {
-    const size_t gemv = round_up((size_t)rows * (size_t)F * 2);
+    size_t gemv = round_up((size_t)rows * (size_t)F * 2);
+    if (rows > moe::kGemvMaxBallotRows) gemv = moe::gemv_sorted_ws_layout(rows, E, F).bytes;
     const size_t mfma = moe::ffn_mfma_ws_bytes(rows, E, F);
     return gemv > mfma ? gemv : mfma;
 }
@@ -282,8 +282,10 @@ moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, i
                     need, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (rows <= kGemvMaxRows && moe::ffn_gemv_has_shape(d, F)) {
-        e = moe::launch_ffn_gemv(*ex, x, T, grouped ? k : 1, ids, y, ws, s);
+    if (moe::ffn_gemv_has_shape(d, F) &&
+        (rows <= moe::kGemvMaxBallotRows || (grouped && rows <= moe::kGemvSortedMaxRows))) {
+        e = moe::launch_ffn_gemv(*ex, x, T, grouped ? k : 1, ids, offsets, sorted_pairs, y, ws,
+                                 s);
     } else {
         // the grouped GEMM addresses x and h rows with 32-bit byte offsets
         if ((uint64_t)T * (uint64_t)d * 2 >= (1ull << 32) ||

@@ -16,10 +16,69 @@
 // expert-sorted position (valid pairs with a smaller id, plus earlier pairs with the same
 // id), the same position moe_permute assigns.
 // Dense mode (shared expert): a slot is a chunk of MT tokens.
+// Sorted mode (more than 64 pairs, up to kGemvSortedMaxRows): the grouping from moe_permute
+// is read instead of a ballot; a small kernel lists, expert by expert, chunks of at most MT
+// consecutive sorted positions, and a slot is one chunk.  Each expert's rows are streamed
+// once per chunk; a pair's arithmetic is the same in every mode, so its output bits do not
+// depend on the mode (or on the other pairs of the call).
 #include "gemv_common.h"
 
 namespace moe {
 namespace {
+
+// Chunk list of sorted mode: for every expert e with n pairs, ceil(n / MT) entries
+// (e, first sorted position, end of e's segment); count = number of entries.  One block,
+// E <= 1024.
+__global__ void __launch_bounds__(1024) build_chunks_kernel(const int32_t* __restrict__ offsets,
+                                                            int E, int MT,
+                                                            int4* __restrict__ chunks,
+                                                            int* __restrict__ count) {
+    __shared__ int part[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int b = 0, n = 0, cnt = 0;
+    if (tid < E) {
+        b = offsets[tid];
+        n = offsets[tid + 1] - b;
+        cnt = (n + MT - 1) / MT;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) part[wv] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int i = 0; i < 16; ++i) {
+            const int v = part[i];
+            part[i] = run;
+            run += v;
+        }
+        *count = run;
+    }
+    __syncthreads();
+    const int start = incl - cnt + part[wv];
+    for (int i = 0; i < cnt; ++i) chunks[start + i] = make_int4(tid, b + i * MT, b + n, 0);
+}
+
+// Slot of sorted mode: chunk blockIdx.x of the list, or false past its end.
+template <int MT>
+__device__ __forceinline__ bool sorted_slot(const int4* chunks, const int* count,
+                                            const int32_t* sorted, Slot& sl) {
+    if ((int)blockIdx.x >= *count) return false;
+    const int4 c = chunks[blockIdx.x];
+    sl.e = c.x;
+    sl.members = 0;
+    sl.seg0 = 0;
+    sl.first = 0;
+    sl.dense0 = sl.dense_n = 0;
+    sl.sorted = sorted;
+    sl.q0 = c.y;
+    sl.q1 = min(c.y + MT, c.z);
+    return true;
+}
 
 // grid.x = slots, grid.y = row blocks
 template <int FMT, int D, int F, int MT>
@@ -45,6 +104,55 @@ __global__ void __launch_bounds__(256) ffn_down_kernel(
     if (!resolve_slot<MT>(blockIdx.x, T, k, ids, E, sl)) return;
     gemv_rows<FMT, kModeDown, DN::LPR, DN::GPL, DN::ITERS, MT>(wd, sd, nullptr, nullptr, h, k,
                                                               D, blockIdx.y, sl, y);
+}
+
+template <int FMT, int D, int F, int MT>
+__global__ void __launch_bounds__(256) ffn_gateup_sorted_kernel(
+    const uint8_t* __restrict__ wg, const uint16_t* __restrict__ sg,
+    const uint8_t* __restrict__ wu, const uint16_t* __restrict__ su,
+    const uint16_t* __restrict__ x, int k, const int32_t* __restrict__ sorted,
+    const int4* __restrict__ chunks, const int* __restrict__ count, uint16_t* __restrict__ h) {
+    using GU = Shape<D>;
+    Slot sl;
+    if (!sorted_slot<MT>(chunks, count, sorted, sl)) return;
+    gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, MT>(wg, sg, wu, su, x, k, F,
+                                                                blockIdx.y, sl, h);
+}
+
+template <int FMT, int D, int F, int MT>
+__global__ void __launch_bounds__(256) ffn_down_sorted_kernel(
+    const uint8_t* __restrict__ wd, const uint16_t* __restrict__ sd,
+    const uint16_t* __restrict__ h, int k, const int32_t* __restrict__ sorted,
+    const int4* __restrict__ chunks, const int* __restrict__ count, uint16_t* __restrict__ y) {
+    using DN = Shape<F>;
+    Slot sl;
+    if (!sorted_slot<MT>(chunks, count, sorted, sl)) return;
+    gemv_rows<FMT, kModeDown, DN::LPR, DN::GPL, DN::ITERS, MT>(wd, sd, nullptr, nullptr, h, k,
+                                                              D, blockIdx.y, sl, y);
+}
+
+template <int FMT, int D, int F, int MT>
+hipError_t launch_sorted_mt(const moe_experts& ex, const uint16_t* x, int T, int k,
+                            const int32_t* offsets, const int32_t* sorted, uint16_t* y,
+                            void* ws, hipStream_t s) {
+    const GemvSortedWs L = gemv_sorted_ws_layout((int64_t)T * k, ex.n_experts, F);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
+    int4* chunks = reinterpret_cast<int4*>(base + L.chunks);
+    int* count = reinterpret_cast<int*>(base + L.count);
+    build_chunks_kernel<<<1, 1024, 0, s>>>(offsets, ex.n_experts, MT, chunks, count);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int cap = (int)gemv_sorted_chunk_capacity((int64_t)T * k, ex.n_experts);
+    constexpr int n_gu = (F + Shape<D>::RPB - 1) / Shape<D>::RPB;
+    constexpr int n_dn = (D + Shape<F>::RPB - 1) / Shape<F>::RPB;
+    ffn_gateup_sorted_kernel<FMT, D, F, MT><<<dim3(cap, n_gu), 256, 0, s>>>(
+        ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, k, sorted, chunks, count, h);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    ffn_down_sorted_kernel<FMT, D, F, MT><<<dim3(cap, n_dn), 256, 0, s>>>(
+        ex.w_down, ex.s_down, h, k, sorted, chunks, count, y);
+    return hipGetLastError();
 }
 
 template <int FMT, int D, int F, int MT>
@@ -74,10 +182,15 @@ hipError_t launch_shape(const moe_experts& ex, const uint16_t* x, int T, int k,
 
 template <int FMT>
 hipError_t launch_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
-                      const int32_t* ids, uint16_t* y, void* ws, hipStream_t s) {
+                      const int32_t* ids, const int32_t* offsets, const int32_t* sorted,
+                      uint16_t* y, void* ws, hipStream_t s) {
 #define MOE_DEC(DV, FV)                                                                  \
-    if (ex.d_model == DV && ex.d_ff == FV)                                               \
-        return launch_shape<FMT, DV, FV>(ex, x, T, k, ids, y, ws, s);
+    if (ex.d_model == DV && ex.d_ff == FV) {                                             \
+        if (ids && (int64_t)T * k > kGemvMaxBallotRows)                                  \
+            return launch_sorted_mt<FMT, DV, FV, kGemvSortedMT>(ex, x, T, k, offsets,    \
+                                                                sorted, y, ws, s);       \
+        return launch_shape<FMT, DV, FV>(ex, x, T, k, ids, y, ws, s);                    \
+    }
     MOE_DEC(2048, 512)
     MOE_DEC(256, 128)
     MOE_DEC(2048, 1024)
@@ -95,11 +208,28 @@ bool ffn_gemv_has_shape(int d, int F) {
            (d == 4096 && F == 1024) || (d == 1024 && F == 512);
 }
 
+size_t gemv_sorted_chunk_capacity(int64_t rows, int E) {
+    const int64_t c = (rows + kGemvSortedMT - 1) / kGemvSortedMT + E;
+    return (size_t)(c < rows ? c : rows);
+}
+
+GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F) {
+    auto al = [](size_t n) { return (n + 255) & ~size_t(255); };
+    GemvSortedWs w;
+    size_t off = 0;
+    w.h = off; off += al((size_t)rows * F * 2);
+    w.chunks = off; off += al(gemv_sorted_chunk_capacity(rows, E) * sizeof(int4));
+    w.count = off; off += 256;
+    w.bytes = off;
+    return w;
+}
+
 hipError_t launch_ffn_gemv(const moe_experts& ex, const uint16_t* x, int T, int k,
-                           const int32_t* ids, uint16_t* y, void* ws, hipStream_t s) {
+                           const int32_t* ids, const int32_t* offsets, const int32_t* sorted,
+                           uint16_t* y, void* ws, hipStream_t s) {
     if (ex.fmt == MOE_FMT_INT4_G32)
-        return launch_fmt<MOE_FMT_INT4_G32>(ex, x, T, k, ids, y, ws, s);
-    return launch_fmt<MOE_FMT_INT6_G32>(ex, x, T, k, ids, y, ws, s);
+        return launch_fmt<MOE_FMT_INT4_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
+    return launch_fmt<MOE_FMT_INT6_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
 }
 
 }  // namespace moe

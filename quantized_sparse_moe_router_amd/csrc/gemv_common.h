@@ -155,6 +155,10 @@ struct Slot {
     int seg0;           // grouped: sorted position of e's first pair
     int first;          // grouped: rank (among e's pairs) of this chunk's first pair
     int dense0, dense_n;
+    // sorted mode (more pairs than a ballot covers): this chunk is sorted positions
+    // [q0, q1) of expert e, pair indices sorted[q0 ..]
+    const int32_t* sorted = nullptr;
+    int q0 = 0, q1 = 0;
 };
 
 // Resolve slot s; returns false if this block has nothing to do.
@@ -222,7 +226,15 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
     int arow[MT], orow[MT];
     int mcount = 0;
     uint32_t xv[MT][GPL][16];
-    if (grouped) {
+    if (sl.sorted) {
+        mcount = sl.q1 - sl.q0;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int pos = sl.q0 + min(m, mcount - 1);
+            arow[m] = (MODE == kModeGateUp) ? sl.sorted[pos] / k : pos;
+            orow[m] = pos;
+        }
+    } else if (grouped) {
         uint64_t rest = sl.members;
         for (int skip = 0; skip < sl.first; ++skip) rest &= rest - 1;
 #pragma unroll

@@ -110,6 +110,9 @@ hipError_t read_and_clear_device_error(int* flag);
 
 // Tokens up to which moe_route computes logits and selection in one launch (GEMV).
 constexpr int kRouteGemvMaxTokens = 16;
+// Tokens up to which it computes the logits by GEMV (one wave per expert row, token groups)
+// and selects in a second kernel; above, the tiled GEMM (or the bounded form).
+constexpr int kRouteSplitMaxTokens = 64;
 
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
                         float* weights, float* logits, unsigned* counter, hipStream_t s);
@@ -145,11 +148,22 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
                           int32_t* sorted_pairs, int32_t* pair_pos, void* ws, hipStream_t s);
 size_t permute_ws_bytes(int64_t P, int E);
 
-// Small calls: weight-streaming GEMV, gate/up then down; positions come from ids
-// (grouped) or the token index (dense, ids == nullptr).  ws = [h].
+// Small calls: weight-streaming GEMV, gate/up then down.  Up to kGemvMaxBallotRows pairs
+// the positions come from ids alone (a ballot; ws = [h]); above, up to kGemvSortedMaxRows,
+// from the grouping (offsets, sorted_pairs; ws = gemv_sorted_ws_layout).  Dense mode
+// (ids == nullptr): the token index, at most kGemvMaxBallotRows tokens.
+constexpr int64_t kGemvMaxBallotRows = 64;
+constexpr int64_t kGemvSortedMaxRows = 640;
+constexpr int kGemvSortedMT = 4;    // pairs of one expert per pass over its weights
+struct GemvSortedWs {
+    size_t h, chunks, count, bytes;
+};
+size_t gemv_sorted_chunk_capacity(int64_t rows, int E);
+GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F);
 bool ffn_gemv_has_shape(int d_model, int d_ff);
 hipError_t launch_ffn_gemv(const moe_experts& ex, const uint16_t* x, int T, int k,
-                           const int32_t* ids, uint16_t* y, void* ws, hipStream_t s);
+                           const int32_t* ids, const int32_t* offsets, const int32_t* sorted,
+                           uint16_t* y, void* ws, hipStream_t s);
 // Large calls: grouped MFMA GEMM.  ws = [h][tile list].
 hipError_t launch_ffn_mfma(const moe_experts& ex, const uint16_t* x, int T, int k,
                            const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,

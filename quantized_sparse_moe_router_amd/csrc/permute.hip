@@ -26,52 +26,6 @@ namespace {
 constexpr int kChunk = 1024;     // pairs per chunk
 constexpr int kMaxE = 1024;
 
-// rank of this lane's id among lower lanes of the wave holding the same id, and the
-// number of lanes in the wave holding it (valid lanes only)
-__device__ __forceinline__ void wave_rank(int id, bool valid, int lane, int& rank, int& cnt) {
-    rank = 0;
-    cnt = 0;
-    const int vflag = valid ? 1 : 0;
-    for (int src = 0; src < 64; ++src) {
-        const int oid = __builtin_amdgcn_readlane(id, src);
-        const int ov = __builtin_amdgcn_readlane(vflag, src);
-        const bool same = valid && ov && oid == id;
-        cnt += same ? 1 : 0;
-        rank += (same && src < lane) ? 1 : 0;
-    }
-}
-
-// Scatter one chunk's pairs [p0, p1) in pair order, given per-expert bases in LDS.
-// Must be run by exactly one wave (threads 0..63 of the block).
-__device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t p0, int64_t p1, int E,
-                              int* base, int32_t* __restrict__ sorted_pairs,
-                              int32_t* __restrict__ pair_pos) {
-    const int lane = threadIdx.x;
-    for (int64_t q = p0; q < p1; q += 64) {
-        const int64_t p = q + lane;
-        const bool inrange = p < p1;
-        int id = inrange ? ids[p] : -1;
-        const bool valid = inrange && id >= 0 && id < E;
-        if (inrange && !valid) {
-            pair_pos[p] = -1;
-            atomicOr(&g_bad_id_flag, 1);
-        }
-        int rank, cnt;
-        wave_rank(id, valid, lane, rank, cnt);
-        int pos = 0;
-        if (valid) pos = base[id] + rank;
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-            sorted_pairs[pos] = (int32_t)p;
-            pair_pos[p] = pos;
-            if (rank == cnt - 1) base[id] += cnt;     // last lane of this id updates
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __builtin_amdgcn_wave_barrier();
-    }
-}
-
 // Exclusive scan of cnt[0..E) into out[0..E], out[E] = total; blockDim.x = 1024.
 __device__ void block_exclusive_scan(const int* cnt, int* out, int E) {
     __shared__ int part[1024 / 64];
@@ -154,26 +108,6 @@ __global__ void __launch_bounds__(64) permute_wave_kernel(
         sorted_pairs[pos] = lane;
         pair_pos[lane] = pos;
     }
-}
-
-// All three steps in one block (P <= kChunk).  blockDim.x = 1024.
-__global__ void __launch_bounds__(1024) permute_small_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
-    __shared__ int hist[kMaxE];
-    __shared__ int base[kMaxE + 1];
-    const int tid = threadIdx.x;
-    if (tid < E) hist[tid] = 0;
-    __syncthreads();
-    for (int p = tid; p < P; p += blockDim.x) {
-        const int id = ids[p];
-        if (id >= 0 && id < E) atomicAdd(&hist[id], 1);
-    }
-    __syncthreads();
-    block_exclusive_scan(hist, base, E);
-    for (int e = tid; e <= E; e += blockDim.x) offsets[e] = base[e];
-    __syncthreads();
-    if (tid < 64) scatter_chunk(ids, 0, P, E, base, sorted_pairs, pair_pos);
 }
 
 // Step 1: chunk histograms -> hist[chunk][E].
@@ -270,6 +204,42 @@ __global__ void __launch_bounds__(1024) chunk_scatter_kernel(
     }
 }
 
+// All three steps in one block (P <= kChunk), one thread per pair: the histogram (LDS
+// atomics), the scan of the counts gives the offsets, and a pair's position is its
+// expert's offset + the pairs of that expert in earlier waves + its rank in its own wave
+// (ballot match on the id bits).  blockDim.x = 1024.
+__global__ void __launch_bounds__(1024) permute_small_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int nbits, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
+    __shared__ int hist[kMaxE];
+    __shared__ int base[kMaxE + 1];
+    __shared__ __attribute__((aligned(16))) uint8_t wcnt[16][kMaxE];   // pairs of wave w with id e (<= 64)
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid < E) hist[tid] = 0;
+    for (int i = tid; i < 16 * kMaxE / 4; i += 1024) reinterpret_cast<uint32_t*>(wcnt)[i] = 0;
+    const bool inrange = tid < P;
+    const int id = inrange ? ids[tid] : -1;
+    const bool valid = inrange && id >= 0 && id < E;
+    if (inrange && !valid) {
+        pair_pos[tid] = -1;
+        atomicOr(&g_bad_id_flag, 1);
+    }
+    __syncthreads();
+    if (valid) atomicAdd(&hist[id], 1);
+    const uint64_t m = match_id(id, valid, nbits);
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) wcnt[w][id] = (uint8_t)__popcll(m);
+    __syncthreads();
+    block_exclusive_scan(hist, base, E);     // ends with a barrier
+    for (int e = tid; e <= E; e += 1024) offsets[e] = base[e];
+    if (valid) {
+        int pos = base[id] + rank;
+        for (int i = 0; i < w; ++i) pos += wcnt[i][id];
+        sorted_pairs[pos] = tid;
+        pair_pos[tid] = pos;
+    }
+}
+
 }  // namespace
 
 // workspace: [chunk table nchunk x E][expert totals E]
@@ -286,16 +256,16 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
         permute_wave_kernel<<<1, 64, 0, s>>>(ids, (int)P, E, offsets, sorted_pairs, pair_pos);
         return hipGetLastError();
     }
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
     if (P <= kChunk) {
-        permute_small_kernel<<<1, 1024, 0, s>>>(ids, (int)P, E, offsets, sorted_pairs,
+        permute_small_kernel<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, offsets, sorted_pairs,
                                                 pair_pos);
         return hipGetLastError();
     }
     const int nchunk = (int)((P + kChunk - 1) / kChunk);
     int* hist = static_cast<int*>(ws);
     int* tot = hist + (size_t)nchunk * E;
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
     chunk_hist_kernel<<<nchunk, 256, 0, s>>>(ids, P, E, hist);
     chunk_scan_kernel<<<(E + 63) / 64, 1024, 0, s>>>(hist, nchunk, E, tot);
     chunk_scatter_kernel<<<nchunk, 1024, 0, s>>>(ids, P, E, nbits, hist, tot, offsets,

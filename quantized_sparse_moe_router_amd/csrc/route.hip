@@ -114,6 +114,63 @@ __device__ __forceinline__ void router_gemv_rows(
         for (int j = 0; j < NC; ++j) asm volatile("" : "+v"(x4n[j].x), "+v"(x4n[j].y));
     }
 
+    if constexpr (!NORM) {
+        // G tokens at a time: every activation load of the group is issued before the first
+        // fma, and the G chains (each in its own, unchanged order) run interleaved
+        constexpr int G = (NV * PV <= 32) ? 4 : (NV * PV <= 64) ? 2 : 1;
+        constexpr int XW = PV / 2;           // 32-bit words of activations per vector
+        for (int t0 = 0; t0 < T; t0 += G) {
+            uint32_t xq[G][NV][XW];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const uint16_t* xt = x + (size_t)min(t0 + g, T - 1) * d;
+#pragma unroll
+                for (int j = 0; j < NV; ++j) {
+                    const int c0 = (lane + 64 * j) * PV;
+                    if constexpr (PV == 4) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(xt + c0);
+                        xq[g][j][0] = v.x; xq[g][j][1] = v.y;
+                    } else {
+                        const uint4* xp = reinterpret_cast<const uint4*>(xt + c0);
+                        const uint4 a = xp[0], bq = xp[1];
+                        xq[g][j][0] = a.x; xq[g][j][1] = a.y; xq[g][j][2] = a.z;
+                        xq[g][j][3] = a.w; xq[g][j][4] = bq.x; xq[g][j][5] = bq.y;
+                        xq[g][j][6] = bq.z; xq[g][j][7] = bq.w;
+                    }
+                }
+            }
+            float acc[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int i = 0; i < XW; ++i)
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        acc[g] = __builtin_fmaf(bf16lo(xq[g][j][i]), w[j][2 * i], acc[g]);
+                        acc[g] = __builtin_fmaf(bf16hi(xq[g][j][i]), w[j][2 * i + 1], acc[g]);
+                    }
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = group_sum<64>(acc[g]);
+            if (lane == 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int t = t0 + g;
+                    if (t >= T) break;
+                    float l = acc[g];
+                    if constexpr (FMT == MOE_FMT_INT8_ROW) l = l * se;
+                    if (bias) l = l + b;
+                    if constexpr (DEVICE_SCOPE_STORE)
+                        __hip_atomic_store(logits + (size_t)t * E + e, l, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        logits[(size_t)t * E + e] = l;
+                }
+            }
+        }
+        return;
+    }
     for (int t = 0; t < T; ++t) {
         const uint16_t* xt = x + (size_t)t * d;
         float r = 1.0f;
@@ -654,7 +711,10 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
     if (T <= kRouteGemvMaxTokens)   // one wave per expert row, selection by the last block
         return launch_gemv_topk<FMT, NV, false>(r, x, T, k, ids, weights, logits, counter,
                                                 RouteNorm{}, s);
-    {
+    if (T <= kRouteSplitMaxTokens) {   // one wave per expert row, then the selection kernel
+        router_gemv_kernel<FMT, NV, false><<<dim3(E), dim3(64), 0, s>>>(
+            r.w, r.scale, r.bias, x, T, E, d, logits, RouteNorm{});
+    } else {
         using R = RgShape<FMT>;
         constexpr int kLds = 2 * R::STAGE;
         constexpr int kMaxDev = 64;

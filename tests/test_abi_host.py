@@ -66,11 +66,14 @@ def test_workspace_sizes(L):
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 1, 10, 512, 2048, 512) == 0
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 8192, 10, 512, 2048, 512) >= 80 * 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 1, 10, 512, 2048, 512) >= 10 * 512 * 2
-    # more than 16 tokens without a logits output: the bounded form also keeps bf16 plane
+    # more than 64 tokens without a logits output: the bounded form also keeps bf16 plane
     # rows of the router (two per fp32 row) and one norm bound per expert
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 8192, 10, 512, 2048, 0) == \
         256 + 8192 * 512 * 4 + 512 * 2 * 2048 * 2 + 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 16, 10, 512, 2048, 0) == 256 + 16 * 512 * 4
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 64, 10, 512, 2048, 0) == 256 + 64 * 512 * 4
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 65, 10, 512, 2048, 0) == \
+        256 + 65 * 512 * 4 + 512 * 2 * 2048 * 2 + 512 * 4
 
 
 def _router(fmt=0, E=512, d=2048, w=16, scale=None, reserved=0):
@@ -115,8 +118,8 @@ def test_route_null_descriptor_and_workspace(L):
     assert st == -3 and "workspace" in _err(L)
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, None, 16, 100, None)
     assert st == -3
-    # bounded form (17 tokens, no logits): counter + logits alone are not enough
-    st = L.moe_route(ctypes.byref(r), 16, 17, 10, 16, 16, None, 16, 256 + 17 * 512 * 4, None)
+    # bounded form (65 tokens, no logits): counter + logits alone are not enough
+    st = L.moe_route(ctypes.byref(r), 16, 65, 10, 16, 16, None, 16, 256 + 65 * 512 * 4, None)
     assert st == -3 and "workspace" in _err(L)
     # with a logits output the workspace still holds the arrival counter
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, 16, None, 0, None)

@@ -106,7 +106,7 @@ def _check_layer(name, T=None, sample=None, bias=None, seed=0, stream=0, tiles=F
     layer, out = _run(moe, lay, w, x)
     k, E = w.k, w.E
 
-    # routing: full size, bit-exact.  forward() selects without logits (for T > 16 the
+    # routing: full size, bit-exact.  forward() selects without logits (for T > 64 the
     # bounded MFMA form); route_logits() runs the fixed-order path that returns them.
     logits_ref = oracle.router_logits(r_h, x_h)
     ids2 = torch.empty_like(layer.ids)
@@ -177,6 +177,30 @@ def test_decode_single_token():
 def test_decode_small_batches_zipf(T):
     # 4 = one token plus three drafts verified together; Zipf bias makes experts shared
     _check_layer("decode_d2048_e512_top10_t1", T=T, bias="zipf", stream=T)
+
+
+@pytest.mark.parametrize("T,bias", [(8, None), (16, None), (32, "zipf"), (64, None),
+                                    (64, "zipf")])
+def test_decode_batches_sorted_gemv(T, bias):
+    # 65..640 pairs: the GEMV kernels in sorted mode (chunks of consecutive sorted positions
+    # of one expert, from moe_permute's grouping); under Zipf the hot experts span several
+    # chunks
+    _check_layer("decode_d2048_e512_top10_t1", T=T, bias=bias, stream=T)
+
+
+def test_batch_invariance_up_to_64_tokens():
+    # a token's ids, weights and output bits are the same alone and among 64 tokens (the
+    # ballot and sorted GEMV modes share the per-pair arithmetic)
+    moe = _gpu()
+    w, lay, _ = _setup("decode_d2048_e512_top10_t1", bias="zipf")
+    x = synth.make_tokens(w, T=64, device="cuda", stream=77)
+    big, out = _run(moe, lay, w, x)
+    out = out.clone()
+    for t in (0, 13, 63):
+        one, o1 = _run(moe, lay, w, x[t:t + 1].contiguous())
+        assert torch.equal(one.ids[:1], big.ids[t:t + 1])
+        assert torch.equal(one.weights[:1].view(torch.int32), big.weights[t:t + 1].view(torch.int32))
+        assert torch.equal(o1.view(torch.int16), out[t:t + 1].view(torch.int16)), "token %d" % t
 
 
 def test_decode_sweep_layer_batch4():
