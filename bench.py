@@ -355,7 +355,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def decode_batches(moe, synth, np, torch, copies, w, args):
+def decode_batches(moe, synth, np, torch, copies, w, args, Ts=(1, 4, 6, 8, 16, 32, 64)):
     """T tokens per call through the decode layer (d 2048, 512 experts, top-10 + shared),
     T = 1 .. 64: the four calls (forward) and, while T*k <= 64, moe_layer_decode; each step
     on the next of the rotated layer copies (more than the 256 MB cache holds for T >= 2).
@@ -364,7 +364,7 @@ def decode_batches(moe, synth, np, torch, copies, w, args):
     r_b = copies[0].router.w.numel() * copies[0].router.w.element_size()
     n_cp = len(copies)
     out = {"workload": "decode_d2048_e512_top10", "copies_rotated": n_cp}
-    for T in (1, 4, 6, 8, 16, 32, 64):
+    for T in Ts:
         mls = [moe.MoeLayer(c.router, c.routed, c.shared, w.k, T) for c in copies]
         xs = [synth.make_tokens(w, T=T, seed=100 + i, device="cuda") for i in range(n_cp)]
         for i in range(n_cp):

@@ -26,14 +26,16 @@
 namespace moe {
 namespace {
 
-// Chunk list of sorted mode: for every expert e with n pairs, ceil(n / MT) entries
-// (e, first sorted position, end of e's segment); count = number of entries.  One block,
-// E <= 1024.
+// Chunk list of sorted mode: for every expert e with n pairs, ceil(n / MT) entries of two
+// int4, (e, first sorted position q0, pairs in the chunk, 0) and the tokens of its pairs
+// (the last repeated); entries from the list's end up to cap hold e = -1, so a block
+// learns from its own entry alone whether it has work.  One block, E <= 1024.
 __global__ void __launch_bounds__(1024) build_chunks_kernel(const int32_t* __restrict__ offsets,
-                                                            int E, int MT,
-                                                            int4* __restrict__ chunks,
-                                                            int* __restrict__ count) {
+                                                            const int32_t* __restrict__ sorted,
+                                                            int E, int k, int MT, int cap,
+                                                            int4* __restrict__ chunks) {
     __shared__ int part[16];
+    __shared__ int total;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int b = 0, n = 0, cnt = 0;
     if (tid < E) {
@@ -56,27 +58,34 @@ __global__ void __launch_bounds__(1024) build_chunks_kernel(const int32_t* __res
             part[i] = run;
             run += v;
         }
-        *count = run;
+        total = run;
     }
     __syncthreads();
     const int start = incl - cnt + part[wv];
-    for (int i = 0; i < cnt; ++i) chunks[start + i] = make_int4(tid, b + i * MT, b + n, 0);
+    for (int i = 0; i < cnt; ++i) {
+        const int q0 = b + i * MT, sn = min(MT, n - i * MT);
+        int t[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) t[m] = sorted[q0 + min(m, sn - 1)] / k;
+        chunks[2 * (start + i)] = make_int4(tid, q0, sn, 0);
+        chunks[2 * (start + i) + 1] = make_int4(t[0], t[1], t[2], t[3]);
+    }
+    for (int i = total + tid; i < cap; i += 1024) chunks[2 * i] = make_int4(-1, 0, 0, 0);
 }
 
-// Slot of sorted mode: chunk blockIdx.x of the list, or false past its end.
-template <int MT>
-__device__ __forceinline__ bool sorted_slot(const int4* chunks, const int* count,
-                                            const int32_t* sorted, Slot& sl) {
-    if ((int)blockIdx.x >= *count) return false;
-    const int4 c = chunks[blockIdx.x];
+// Slot of sorted mode: entry blockIdx.x of the list, or false for an empty entry.
+__device__ __forceinline__ bool sorted_slot(const int4* chunks, Slot& sl) {
+    const int4 c = chunks[2 * blockIdx.x];
+    if (c.x < 0) return false;
+    const int4 t = chunks[2 * blockIdx.x + 1];
     sl.e = c.x;
     sl.members = 0;
     sl.seg0 = 0;
     sl.first = 0;
     sl.dense0 = sl.dense_n = 0;
-    sl.sorted = sorted;
     sl.q0 = c.y;
-    sl.q1 = min(c.y + MT, c.z);
+    sl.sn = c.z;
+    sl.tok[0] = t.x; sl.tok[1] = t.y; sl.tok[2] = t.z; sl.tok[3] = t.w;
     return true;
 }
 
@@ -110,11 +119,11 @@ template <int FMT, int D, int F, int MT>
 __global__ void __launch_bounds__(256) ffn_gateup_sorted_kernel(
     const uint8_t* __restrict__ wg, const uint16_t* __restrict__ sg,
     const uint8_t* __restrict__ wu, const uint16_t* __restrict__ su,
-    const uint16_t* __restrict__ x, int k, const int32_t* __restrict__ sorted,
-    const int4* __restrict__ chunks, const int* __restrict__ count, uint16_t* __restrict__ h) {
-    using GU = Shape<D>;
+    const uint16_t* __restrict__ x, int k, const int4* __restrict__ chunks,
+    uint16_t* __restrict__ h) {
+    using GU = SortedShape<D, FMT>;
     Slot sl;
-    if (!sorted_slot<MT>(chunks, count, sorted, sl)) return;
+    if (!sorted_slot(chunks, sl)) return;
     gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, MT>(wg, sg, wu, su, x, k, F,
                                                                 blockIdx.y, sl, h);
 }
@@ -122,11 +131,11 @@ __global__ void __launch_bounds__(256) ffn_gateup_sorted_kernel(
 template <int FMT, int D, int F, int MT>
 __global__ void __launch_bounds__(256) ffn_down_sorted_kernel(
     const uint8_t* __restrict__ wd, const uint16_t* __restrict__ sd,
-    const uint16_t* __restrict__ h, int k, const int32_t* __restrict__ sorted,
-    const int4* __restrict__ chunks, const int* __restrict__ count, uint16_t* __restrict__ y) {
-    using DN = Shape<F>;
+    const uint16_t* __restrict__ h, int k, const int4* __restrict__ chunks,
+    uint16_t* __restrict__ y) {
+    using DN = SortedShape<F, FMT>;
     Slot sl;
-    if (!sorted_slot<MT>(chunks, count, sorted, sl)) return;
+    if (!sorted_slot(chunks, sl)) return;
     gemv_rows<FMT, kModeDown, DN::LPR, DN::GPL, DN::ITERS, MT>(wd, sd, nullptr, nullptr, h, k,
                                                               D, blockIdx.y, sl, y);
 }
@@ -139,19 +148,18 @@ hipError_t launch_sorted_mt(const moe_experts& ex, const uint16_t* x, int T, int
     uint8_t* base = static_cast<uint8_t*>(ws);
     uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
     int4* chunks = reinterpret_cast<int4*>(base + L.chunks);
-    int* count = reinterpret_cast<int*>(base + L.count);
-    build_chunks_kernel<<<1, 1024, 0, s>>>(offsets, ex.n_experts, MT, chunks, count);
+    const int cap = (int)gemv_sorted_chunk_capacity((int64_t)T * k, ex.n_experts);
+    build_chunks_kernel<<<1, 1024, 0, s>>>(offsets, sorted, ex.n_experts, k, MT, cap, chunks);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int cap = (int)gemv_sorted_chunk_capacity((int64_t)T * k, ex.n_experts);
-    constexpr int n_gu = (F + Shape<D>::RPB - 1) / Shape<D>::RPB;
-    constexpr int n_dn = (D + Shape<F>::RPB - 1) / Shape<F>::RPB;
+    constexpr int n_gu = (F + SortedShape<D, FMT>::RPB - 1) / SortedShape<D, FMT>::RPB;
+    constexpr int n_dn = (D + SortedShape<F, FMT>::RPB - 1) / SortedShape<F, FMT>::RPB;
     ffn_gateup_sorted_kernel<FMT, D, F, MT><<<dim3(cap, n_gu), 256, 0, s>>>(
-        ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, k, sorted, chunks, count, h);
+        ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, k, chunks, h);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     ffn_down_sorted_kernel<FMT, D, F, MT><<<dim3(cap, n_dn), 256, 0, s>>>(
-        ex.w_down, ex.s_down, h, k, sorted, chunks, count, y);
+        ex.w_down, ex.s_down, h, k, chunks, y);
     return hipGetLastError();
 }
 
@@ -218,8 +226,7 @@ GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F) {
     GemvSortedWs w;
     size_t off = 0;
     w.h = off; off += al((size_t)rows * F * 2);
-    w.chunks = off; off += al(gemv_sorted_chunk_capacity(rows, E) * sizeof(int4));
-    w.count = off; off += 256;
+    w.chunks = off; off += al(gemv_sorted_chunk_capacity(rows, E) * 2 * sizeof(int4));
     w.bytes = off;
     return w;
 }

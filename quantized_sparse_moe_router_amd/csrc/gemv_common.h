@@ -155,10 +155,11 @@ struct Slot {
     int seg0;           // grouped: sorted position of e's first pair
     int first;          // grouped: rank (among e's pairs) of this chunk's first pair
     int dense0, dense_n;
-    // sorted mode (more pairs than a ballot covers): this chunk is sorted positions
-    // [q0, q1) of expert e, pair indices sorted[q0 ..]
-    const int32_t* sorted = nullptr;
-    int q0 = 0, q1 = 0;
+    // sorted mode (more pairs than a ballot covers): this chunk is the sorted positions
+    // q0 .. q0 + sn - 1 of expert e (sn > 0), and tok[m] the token of position q0 + m
+    // (for m >= sn, the token of the last position)
+    int sn = 0, q0 = 0;
+    int tok[4];
 };
 
 // Resolve slot s; returns false if this block has nothing to do.
@@ -226,13 +227,14 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
     int arow[MT], orow[MT];
     int mcount = 0;
     uint32_t xv[MT][GPL][16];
-    if (sl.sorted) {
-        mcount = sl.q1 - sl.q0;
+    if (sl.sn > 0) {
+        static_assert(MT <= 4, "a sorted-mode chunk holds at most 4 pairs");
+        mcount = sl.sn;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const int pos = sl.q0 + min(m, mcount - 1);
-            arow[m] = (MODE == kModeGateUp) ? sl.sorted[pos] / k : pos;
-            orow[m] = pos;
+            const int mm = min(m, mcount - 1);
+            arow[m] = (MODE == kModeGateUp) ? sl.tok[m] : sl.q0 + mm;   // tok repeats its last
+            orow[m] = sl.q0 + mm;
         }
     } else if (grouped) {
         uint64_t rest = sl.members;
@@ -363,6 +365,18 @@ struct Shape {
     static constexpr int LPR = K >= 2048 ? 64 : K / 32;
     static constexpr int GPL = K >= 2048 ? K / 2048 : 1;
     static constexpr int ITERS = K >= 4096 ? 2 : 1;
+    static constexpr int RPB = 4 * ITERS * (64 / LPR);
+};
+
+// Sorted mode: more rows per wave (a block streams 4x the bytes of a ballot-mode block, so
+// the slot lookup and the activation loads are paid over more weights); a row's
+// arithmetic does not depend on ITERS.
+template <int K, int FMT>
+struct SortedShape {
+    static constexpr int LPR = Shape<K>::LPR;
+    static constexpr int GPL = Shape<K>::GPL;
+    // int6 groups take 6 registers: half the rows keep the wave out of scratch
+    static constexpr int ITERS = (GPL >= 2 || FMT == MOE_FMT_INT6_G32) ? 2 : 4;
     static constexpr int RPB = 4 * ITERS * (64 / LPR);
 };
 

@@ -156,7 +156,7 @@ constexpr int64_t kGemvMaxBallotRows = 64;
 constexpr int64_t kGemvSortedMaxRows = 640;
 constexpr int kGemvSortedMT = 4;    // pairs of one expert per pass over its weights
 struct GemvSortedWs {
-    size_t h, chunks, count, bytes;
+    size_t h, chunks, bytes;
 };
 size_t gemv_sorted_chunk_capacity(int64_t rows, int E);
 GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F);
