@@ -355,11 +355,13 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def decode_batches(moe, synth, np, torch, copies, w, args, Ts=(1, 4, 6, 8, 16, 32, 64)):
+def decode_batches(moe, synth, np, torch, copies, w, args, Ts=(1, 4, 6, 8, 16, 32, 64, 96, 128)):
     """T tokens per call through the decode layer (d 2048, 512 experts, top-10 + shared),
-    T = 1 .. 64: the four calls (forward) and, while T*k <= 64, moe_layer_decode; each step
+    T = 1 .. 128: the four calls (forward) and, while T*k <= 64, moe_layer_decode; each step
     on the next of the rotated layer copies (more than the 256 MB cache holds for T >= 2).
-    Weight-stream bytes: router + (distinct routed experts + shared) x 1.77 MB."""
+    Up to 1024 pairs the routed experts run the weight-streaming GEMV (sorted mode past 64
+    pairs), above it the grouped MFMA GEMM.  Weight-stream bytes: router + (distinct routed
+    experts + shared) x 1.77 MB."""
     E_b = expert_bytes(copies[0].routed)
     r_b = copies[0].router.w.numel() * copies[0].router.w.element_size()
     n_cp = len(copies)

@@ -199,12 +199,17 @@ moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  *   k ignored; y is bf16 [T][d], row t for token t.
  * Arithmetic: fp32 accumulation of bf16 activations times dequantised weights; the
  * hidden activation h = silu(g) * u is rounded to bf16 before the down projection.
- * Small calls (at most 64 rows, and a (d_model, d_ff) pair with a GEMV kernel: (2048, 512),
+ * Decode-sized calls on a (d_model, d_ff) pair with a GEMV kernel ((2048, 512),
  * (2048, 1024), (2048, 2048), (4096, 1024), (1024, 512), (256, 128)) stream each selected
- * expert's weights once (two launches: gate/up + SwiGLU, then down); they derive each
- * pair's row from ids alone and do not read offsets or sorted_pairs, so moe_permute may
- * run concurrently with them.  Larger calls run a grouped MFMA GEMM that reads offsets
- * and sorted_pairs; it needs T*d_model and T*k*d_ff (dense: T*d_ff) below 2^31 elements
+ * expert's weights (two launches: gate/up + SwiGLU, then down):
+ *   at most 64 rows: each pair's row is derived from ids alone; offsets and sorted_pairs
+ *     are not read, so moe_permute may run concurrently with the call;
+ *   65 .. 1024 rows (grouped mode): a third, earlier launch lists each expert's sorted
+ *     positions in chunks of at most 4 from offsets and sorted_pairs (so moe_permute must
+ *     have completed), and each chunk streams its expert's weights once.
+ * A pair's output bits are the same in both (and the same in moe_layer_decode).  Larger
+ * calls, and shapes without a GEMV kernel, run a grouped MFMA GEMM that reads offsets and
+ * sorted_pairs; it needs T*d_model and T*k*d_ff (dense: T*d_ff) below 2^31 elements
  * (MOE_ERR_UNSUPPORTED otherwise: split the call).
  * ws: moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, d_ff) bytes (pass k = 1, E = 1
  * for dense mode).

@@ -153,7 +153,7 @@ size_t permute_ws_bytes(int64_t P, int E);
 // from the grouping (offsets, sorted_pairs; ws = gemv_sorted_ws_layout).  Dense mode
 // (ids == nullptr): the token index, at most kGemvMaxBallotRows tokens.
 constexpr int64_t kGemvMaxBallotRows = 64;
-constexpr int64_t kGemvSortedMaxRows = 640;
+constexpr int64_t kGemvSortedMaxRows = 1024;
 constexpr int kGemvSortedMT = 4;    // pairs of one expert per pass over its weights
 struct GemvSortedWs {
     size_t h, chunks, bytes;

@@ -180,27 +180,43 @@ def test_decode_small_batches_zipf(T):
 
 
 @pytest.mark.parametrize("T,bias", [(8, None), (16, None), (32, "zipf"), (64, None),
-                                    (64, "zipf")])
+                                    (64, "zipf"), (96, "zipf"), (102, None)])
 def test_decode_batches_sorted_gemv(T, bias):
-    # 65..640 pairs: the GEMV kernels in sorted mode (chunks of consecutive sorted positions
+    # 65..1024 pairs: the GEMV kernels in sorted mode (chunks of consecutive sorted positions
     # of one expert, from moe_permute's grouping); under Zipf the hot experts span several
-    # chunks
+    # chunks.  T = 96, 102: past 64 tokens the router takes its bounded form
     _check_layer("decode_d2048_e512_top10_t1", T=T, bias=bias, stream=T)
 
 
-def test_batch_invariance_up_to_64_tokens():
-    # a token's ids, weights and output bits are the same alone and among 64 tokens (the
-    # ballot and sorted GEMV modes share the per-pair arithmetic)
+def test_batch_invariance_of_the_gemv_paths():
+    """A token's ids, weights and routed-expert rows are bit-identical alone and among 64
+    or 102 tokens (the ballot and sorted GEMV modes share the per-pair arithmetic); its
+    output too at 64 tokens.  At 102 the shared expert is one dense call over more than 64
+    tokens and takes the MFMA GEMM (another accumulation order): its output is checked
+    against the oracle by the layer tests instead."""
     moe = _gpu()
     w, lay, _ = _setup("decode_d2048_e512_top10_t1", bias="zipf")
-    x = synth.make_tokens(w, T=64, device="cuda", stream=77)
-    big, out = _run(moe, lay, w, x)
-    out = out.clone()
-    for t in (0, 13, 63):
-        one, o1 = _run(moe, lay, w, x[t:t + 1].contiguous())
-        assert torch.equal(one.ids[:1], big.ids[t:t + 1])
-        assert torch.equal(one.weights[:1].view(torch.int32), big.weights[t:t + 1].view(torch.int32))
-        assert torch.equal(o1.view(torch.int16), out[t:t + 1].view(torch.int16)), "token %d" % t
+    k = w.k
+    xall = synth.make_tokens(w, T=102, device="cuda", stream=77)
+    for T in (64, 102):
+        x = xall[:T].contiguous()
+        big, out = _run(moe, lay, w, x)
+        out = out.clone()
+        pp = big.pair_pos[:T * k].cpu().numpy()
+        yb = big.y_pairs.clone()
+        for t in (0, 13, T - 1):
+            one, o1 = _run(moe, lay, w, x[t:t + 1].contiguous())
+            assert torch.equal(one.ids[:1], big.ids[t:t + 1])
+            assert torch.equal(one.weights[:1].view(torch.int32),
+                               big.weights[t:t + 1].view(torch.int32))
+            pp1 = one.pair_pos[:k].cpu().numpy()
+            for j in range(k):
+                assert torch.equal(yb[int(pp[t * k + j])].view(torch.int16),
+                                   one.y_pairs[int(pp1[j])].view(torch.int16)), \
+                    "T %d token %d slot %d" % (T, t, j)
+            if T <= 64:
+                assert torch.equal(o1.view(torch.int16), out[t:t + 1].view(torch.int16)), \
+                    "T %d token %d" % (T, t)
 
 
 def test_decode_sweep_layer_batch4():
