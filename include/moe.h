@@ -39,6 +39,12 @@
  *   MOE_FMT_INT6_G32  row = K*3/4 bytes; each group of 32 codes is a 24-byte
  *                     little-endian bit string, code i at bits [6i, 6i+6);
  *                     value = s * (code - 32).
+ *   MOE_FMT_INT3_G32  row = K*3/8 bytes; a group is a 12-byte little-endian bit string,
+ *                     code i at bits [3i, 3i+3); value = s * (code - 4).
+ *   MOE_FMT_INT2_G32  row = K/4 bytes; a group is 8 bytes, code i at bits [2i, 2i+2);
+ *                     value = s * (code - 2).
+ *   (int3 and int2 are this library's own plain codecs for the low-bit expert tiers of
+ *   [Strata 与 Qwen3.8-Flash-Next (telli.sh)]: not the GGUF formats those tiers use.)
  *   MOE_FMT_INT8_ROW  router only: int8 [E][d] with one fp16 scale per row.
  *   MOE_FMT_FP32      router only: fp32 [E][d].
  */
@@ -62,7 +68,14 @@ enum {
     MOE_ERR_DEVICE = -5         /* a kernel reported bad data (expert id out of range) */
 };
 
-enum { MOE_FMT_FP32 = 0, MOE_FMT_INT8_ROW = 1, MOE_FMT_INT4_G32 = 2, MOE_FMT_INT6_G32 = 3 };
+enum {
+    MOE_FMT_FP32 = 0,
+    MOE_FMT_INT8_ROW = 1,
+    MOE_FMT_INT4_G32 = 2,
+    MOE_FMT_INT6_G32 = 3,
+    MOE_FMT_INT3_G32 = 4,
+    MOE_FMT_INT2_G32 = 5
+};
 
 /* Operation ids for moe_workspace_size. */
 enum {
@@ -87,7 +100,7 @@ typedef struct moe_router {
     const float* bias;
 } moe_router;
 
-/* A set of E experts of one format (INT4_G32 or INT6_G32).  Expert e:
+/* A set of E experts of one format (INT4_G32, INT6_G32, INT3_G32 or INT2_G32).  Expert e:
  *   gate, up : [d_ff][d_model] -> w_gate/w_up bytes [E][d_ff][row bytes(d_model)],
  *              s_gate/s_up fp16 [E][d_ff][d_model/32]
  *   down     : [d_model][d_ff] -> w_down bytes [E][d_model][row bytes(d_ff)],
@@ -331,8 +344,9 @@ moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shar
  * every decoded weight can be compared bit for bit with its exact value s * q (expert
  * weights at 4 and 6 bit [本地部署Qwen3.8-Flash-Next模型的两条路线 (blog.cycleuser.org),
  * section 精度和内存占用]).
- *   fmt   MOE_FMT_INT4_G32 or MOE_FMT_INT6_G32
- *   w     packed codes of n_groups groups (16 or 24 bytes each), device, 16-byte aligned
+ *   fmt   MOE_FMT_INT4_G32, MOE_FMT_INT6_G32, MOE_FMT_INT3_G32 or MOE_FMT_INT2_G32
+ *   w     packed codes of n_groups groups (16, 24, 12 or 8 bytes each), device, 16-byte
+ *         aligned
  *   s     fp16 scales [n_groups], device
  *   form 0: out fp32 [n_groups][32]: the few-token (GEMV) kernels' group arithmetic
  *           (dot product on offset codes, zero-point removal, scale) evaluated on one-hot

@@ -17,7 +17,7 @@ import subprocess
 
 import numpy as np
 
-FMT_FP32, FMT_INT8_ROW, FMT_INT4_G32, FMT_INT6_G32 = 0, 1, 2, 3
+FMT_FP32, FMT_INT8_ROW, FMT_INT4_G32, FMT_INT6_G32, FMT_INT3_G32, FMT_INT2_G32 = 0, 1, 2, 3, 4, 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")

@@ -32,6 +32,9 @@
  *             [0,15], value = s[n][c/32] * (u - 8); s is IEEE fp16
  *   INT6_G32  each group of 32 codes is a 24-byte little-endian bit string, code i of a
  *             group at bits [6i, 6i+6); value = s * (u - 32)
+ *   INT3_G32  the same with 3-bit codes: 12 bytes per group, code i at bits [3i, 3i+3);
+ *             value = s * (u - 4)
+ *   INT2_G32  2-bit codes: 8 bytes per group, code i at bits [2i, 2i+2); value = s * (u - 2)
  *   INT8_ROW  int8 two's complement q, value = s[n] * q (s fp16, one per row)
  *   FP32      plain IEEE binary32
  * All arithmetic is plain IEEE double unless stated otherwise.  Build with
@@ -45,7 +48,8 @@
 #include <omp.h>
 #endif
 
-enum { OFMT_FP32 = 0, OFMT_INT8_ROW = 1, OFMT_INT4_G32 = 2, OFMT_INT6_G32 = 3 };
+enum { OFMT_FP32 = 0, OFMT_INT8_ROW = 1, OFMT_INT4_G32 = 2, OFMT_INT6_G32 = 3,
+       OFMT_INT3_G32 = 4, OFMT_INT2_G32 = 5 };
 
 typedef struct {
     int32_t fmt;        /* OFMT_FP32 or OFMT_INT8_ROW */
@@ -58,7 +62,7 @@ typedef struct {
 } oracle_router;
 
 typedef struct {
-    int32_t fmt;        /* OFMT_INT4_G32 or OFMT_INT6_G32 */
+    int32_t fmt;        /* OFMT_INT4_G32, OFMT_INT6_G32, OFMT_INT3_G32 or OFMT_INT2_G32 */
     int32_t n_experts;
     int32_t d_model;
     int32_t d_ff;
@@ -142,6 +146,17 @@ int oracle_code(int fmt, const uint8_t* row, int c)
         int u = (int)((v >> (bit % 8)) & 63u);
         return u - 32;
     }
+    if (fmt == OFMT_INT3_G32 || fmt == OFMT_INT2_G32) {
+        /* bit by bit from the group's little-endian bit string */
+        const int b = (fmt == OFMT_INT3_G32) ? 3 : 2;
+        const uint8_t* g = row + (size_t)(c / 32) * (size_t)(4 * b);
+        int u = 0;
+        for (int j = 0; j < b; ++j) {
+            int bit = b * (c % 32) + j;
+            u |= ((g[bit / 8] >> (bit % 8)) & 1) << j;
+        }
+        return u - (1 << (b - 1));
+    }
     if (fmt == OFMT_INT8_ROW)
         return (int)(int8_t)row[c];
     return 0;
@@ -152,6 +167,8 @@ static size_t row_bytes(int fmt, int K)
 {
     if (fmt == OFMT_INT4_G32) return (size_t)K / 2;
     if (fmt == OFMT_INT6_G32) return (size_t)K * 3 / 4;
+    if (fmt == OFMT_INT3_G32) return (size_t)K * 3 / 8;
+    if (fmt == OFMT_INT2_G32) return (size_t)K / 4;
     return (size_t)K;
 }
 

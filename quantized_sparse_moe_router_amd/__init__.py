@@ -10,8 +10,8 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32,
-    MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE,
+    MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32, MOE_FMT_INT3_G32,
+    MOE_FMT_INT2_G32, MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE,
     MOE_OP_EXPERTS_DECODE, MOE_OP_BLOCK_DECODE, MoeError,
     moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_layer_decode, moe_experts_decode,
     moe_layer_decode_noalloc,
@@ -21,7 +21,8 @@ from ._lib import (  # noqa: F401
 )
 
 _FMT = {"fp32": MOE_FMT_FP32, "int8_row": MOE_FMT_INT8_ROW, "int4_g32": MOE_FMT_INT4_G32,
-        "int6_g32": MOE_FMT_INT6_G32}
+        "int6_g32": MOE_FMT_INT6_G32, "int3_g32": MOE_FMT_INT3_G32,
+        "int2_g32": MOE_FMT_INT2_G32}
 
 
 def _fmt(f):

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 MOE_OK = 0
 MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DEVICE = \
     -1, -2, -3, -4, -5
-MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32 = 0, 1, 2, 3
+(MOE_FMT_FP32, MOE_FMT_INT8_ROW, MOE_FMT_INT4_G32, MOE_FMT_INT6_G32, MOE_FMT_INT3_G32,
+ MOE_FMT_INT2_G32) = range(6)
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_EXPERT_FFN, MOE_OP_LAYER_DECODE, MOE_OP_EXPERTS_DECODE = \
     0, 1, 2, 3, 4
 MOE_OP_BLOCK_DECODE = 5

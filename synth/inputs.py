@@ -16,6 +16,11 @@ Encodings (the layer's input formats; decoding them is the layer's job, not this
             byte = (q[2i] + 8) | (q[2i+1] + 8) << 4
   int6_g32  s = fp16(max|w_group| / 31); q in [-32, 31]; code u = q + 32; the 32 codes of
             a group form a 24-byte little-endian bit string, code i at bits [6i, 6i+6)
+  int3_g32  s = fp16(max|w_group| / 3); q in [-4, 3]; code u = q + 4; the 32 codes of a
+            group form a 12-byte little-endian bit string, code i at bits [3i, 3i+3)
+  int2_g32  s = fp16(max|w_group| / 1); q in [-2, 1]; code u = q + 2; 8 bytes per group,
+            code i at bits [2i, 2i+2).  A max-abs scale never needs q = -2: this encoder
+            uses {-1, 0, 1}; the all-codes layers below reach -2 too
   int8_row  s = fp16(max|w_row| / 127); q = clamp(round_half_even(w / s), -127, 127)
 An all-zero group gets s = 0 and every code q = 0.
 """
@@ -25,9 +30,9 @@ from typing import Optional
 import numpy as np
 import torch
 
-FMT_FP32, FMT_INT8_ROW, FMT_INT4_G32, FMT_INT6_G32 = 0, 1, 2, 3
+FMT_FP32, FMT_INT8_ROW, FMT_INT4_G32, FMT_INT6_G32, FMT_INT3_G32, FMT_INT2_G32 = range(6)
 FMT_BY_NAME = {"fp32": FMT_FP32, "int8_row": FMT_INT8_ROW, "int4_g32": FMT_INT4_G32,
-               "int6_g32": FMT_INT6_G32}
+               "int6_g32": FMT_INT6_G32, "int3_g32": FMT_INT3_G32, "int2_g32": FMT_INT2_G32}
 
 # tensor ids inside one layer's seed
 _T_ROUTER, _T_BIAS, _T_GATE, _T_UP, _T_DOWN, _T_SGATE, _T_SUP, _T_SDOWN, _T_X = range(9)
@@ -66,6 +71,25 @@ def pack_int6(q):
     return b.reshape(*lead, -1).to(torch.uint8).contiguous()
 
 
+def pack_int3(q):
+    """q int codes in [-4, 3], [..., K] (K % 32 == 0) -> uint8 [..., K*3/8]."""
+    u = (q + 4).to(torch.int32)
+    lead = u.shape[:-1]
+    u8 = u.reshape(*lead, -1, 8)              # 8 codes = 24 bits = 3 bytes
+    v = torch.zeros_like(u8[..., 0])
+    for j in range(8):
+        v = v | (u8[..., j] << (3 * j))
+    b = torch.stack([v & 255, (v >> 8) & 255, (v >> 16) & 255], dim=-1)
+    return b.reshape(*lead, -1).to(torch.uint8).contiguous()
+
+
+def pack_int2(q):
+    """q int codes in [-2, 1], [..., K] (K % 32 == 0) -> uint8 [..., K/4]."""
+    u = (q + 2).to(torch.int32)
+    b = u[..., 0::4] | (u[..., 1::4] << 2) | (u[..., 2::4] << 4) | (u[..., 3::4] << 6)
+    return b.to(torch.uint8).contiguous()
+
+
 def _group_quant(w, qmax, qmin):
     *lead, N, K = w.shape
     g = w.reshape(*lead, N, K // 32, 32)
@@ -89,6 +113,18 @@ def quantize_int6_g32(w):
     return pack_int6(q), s
 
 
+def quantize_int3_g32(w):
+    """fp32 [..., N, K] -> (packed uint8 [..., N, K*3/8], fp16 scales [..., N, K/32])."""
+    q, s = _group_quant(w, 3, -4)
+    return pack_int3(q), s
+
+
+def quantize_int2_g32(w):
+    """fp32 [..., N, K] -> (packed uint8 [..., N, K/4], fp16 scales [..., N, K/32])."""
+    q, s = _group_quant(w, 1, -2)
+    return pack_int2(q), s
+
+
 def quantize_int8_row(w):
     """fp32 [E, d] -> (int8 [E, d], fp16 scales [E])."""
     s16 = (w.abs().amax(dim=-1) / 127.0).to(torch.float16)
@@ -98,7 +134,8 @@ def quantize_int8_row(w):
     return q.clamp(-127, 127).to(torch.int8).contiguous(), s16.contiguous()
 
 
-_QUANT = {"int4_g32": quantize_int4_g32, "int6_g32": quantize_int6_g32}
+_QUANT = {"int4_g32": quantize_int4_g32, "int6_g32": quantize_int6_g32,
+          "int3_g32": quantize_int3_g32, "int2_g32": quantize_int2_g32}
 
 
 def zipf_bias(E, s, gen, device):
@@ -243,17 +280,20 @@ def make_norm(w, seed=0, layer=0, device="cpu", gate=True):
     return Norm(gamma.contiguous(), None if gw is None else gw.contiguous(), 1e-6, 0.0)
 
 
-_QRANGE = {"int4_g32": (-8, 7), "int6_g32": (-32, 31)}
-_PACK = {"int4_g32": pack_int4, "int6_g32": pack_int6}
+_QRANGE = {"int4_g32": (-8, 7), "int6_g32": (-32, 31), "int3_g32": (-4, 3),
+           "int2_g32": (-2, 1)}
+_PACK = {"int4_g32": pack_int4, "int6_g32": pack_int6, "int3_g32": pack_int3,
+         "int2_g32": pack_int2}
 
 
 def _all_codes_matrix(fmt, E, N, K, gen, device):
     """Packed codes and fp16 scales of E matrices [N][K] in which every code of the format,
-    the lowest included (int4 -8, int6 -32), sits at every position of a group: row n,
+    the lowest included (int4 -8, int6 -32, int3 -4, int2 -2), sits at every position of a
+    group: row n,
     element c of matrix e holds qmin + ((n + c + e) mod ncodes) for the first ncodes rows,
     uniform random codes elsewhere.  Scales are fp16 of U(0.5, 1.5) * 0.02 / sd, sd the
     standard deviation of a code drawn uniformly from the format's range (int4 4.61, int6
-    18.47), so the weights spread like the N(0, 0.02) draws of make_layer; every 7th group
+    18.47, int3 2.29, int2 1.12), so the weights spread like the N(0, 0.02) draws of make_layer; every 7th group
     of a matrix (in row-major group order, from a random start) has scale 0."""
     qmin, qmax = _QRANGE[fmt]
     nc = qmax - qmin + 1

@@ -83,6 +83,7 @@ def test_bf16_rounding_matches_torch_on_fp32_values():
 
 def test_code_golden():
     fmts = {"int4": oracle.FMT_INT4_G32, "int6": oracle.FMT_INT6_G32,
+            "int3": oracle.FMT_INT3_G32, "int2": oracle.FMT_INT2_G32,
             "int8": oracle.FMT_INT8_ROW}
     for ln in _lines("codes.txt"):
         kind, hexbytes, *codes = ln.split()
@@ -94,6 +95,8 @@ def test_code_golden():
 @pytest.mark.parametrize("fmt,qmin,qmax,packer", [
     (oracle.FMT_INT4_G32, -8, 7, si.pack_int4),
     (oracle.FMT_INT6_G32, -32, 31, si.pack_int6),
+    (oracle.FMT_INT3_G32, -4, 3, si.pack_int3),
+    (oracle.FMT_INT2_G32, -2, 1, si.pack_int2),
 ])
 def test_pack_unpack_bijection(fmt, qmin, qmax, packer):
     # every code value at every position of a group (positions cycle through the codes)
@@ -108,6 +111,8 @@ def test_pack_unpack_bijection(fmt, qmin, qmax, packer):
 @pytest.mark.parametrize("fmt,quant,qmax", [
     (oracle.FMT_INT4_G32, si.quantize_int4_g32, 7),
     (oracle.FMT_INT6_G32, si.quantize_int6_g32, 31),
+    (oracle.FMT_INT3_G32, si.quantize_int3_g32, 3),
+    (oracle.FMT_INT2_G32, si.quantize_int2_g32, 1),
 ])
 def test_dequant_within_half_step_of_weight(fmt, quant, qmax):
     # closed-form bound of round-to-nearest quantisation: |w - s*q| <= s/2 per element,
@@ -439,7 +444,8 @@ def test_permute_counts_out_of_range_ids():
 # ---------------------------------------------------------------- expert FFN
 
 def _unit_scale_experts(q_gate, q_up, q_down, fmt="int4_g32"):
-    pack = si.pack_int4 if fmt == "int4_g32" else si.pack_int6
+    pack = {"int4_g32": si.pack_int4, "int6_g32": si.pack_int6, "int3_g32": si.pack_int3,
+            "int2_g32": si.pack_int2}[fmt]
     one = lambda n, K: torch.full((1, n, K // 32), 1.0, dtype=torch.float16)  # noqa: E731
     F, d = q_gate.shape
     return {"fmt": si.FMT_BY_NAME[fmt], "E": 1, "d": d, "F": F,
@@ -448,7 +454,8 @@ def _unit_scale_experts(q_gate, q_up, q_down, fmt="int4_g32"):
             "s_up": si.bits16(one(F, d)), "s_down": si.bits16(one(d, F))}
 
 
-@pytest.mark.parametrize("fmt,lo,hi", [("int4_g32", -8, 7), ("int6_g32", -32, 31)])
+@pytest.mark.parametrize("fmt,lo,hi", [("int4_g32", -8, 7), ("int6_g32", -32, 31),
+                                      ("int3_g32", -4, 3), ("int2_g32", -2, 1)])
 def test_expert_ffn_is_textbook_swiglu(fmt, lo, hi):
     # unit scales make the weights the integer codes themselves; then the expert must be
     # the dense SwiGLU MLP  y = Wd (silu(Wg x) * (Wu x))  evaluated by torch in fp64.
