@@ -80,8 +80,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-sweep", action="store_true", help="skip the 48-layer decode sweep")
+    p.add_argument("--no-mall", action="store_true",
+                   help="skip the cache residency leg (stream reads, Zipf decode over copies)")
+    p.add_argument("--no-low-bit", action="store_true",
+                   help="skip the int3 / int2 expert decode leg")
     p.add_argument("--no-batches", action="store_true",
-                   help="skip the decode batch sizes 1..64")
+                   help="skip the decode batch sizes 1..128")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="no graph capture (for profilers)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -326,6 +330,16 @@ def main():
         line["decode_batches"] = decode_batches(moe, synth, np, torch, copies, w, args)
         torch.cuda.empty_cache()
 
+    # ---- lower-bit expert codecs: the same decode step with every expert at 3 or 2 bits
+    if not args.no_low_bit:
+        line["decode_low_bit"] = decode_low_bit(moe, synth, np, torch, copies, w, args)
+        torch.cuda.empty_cache()
+
+    # ---- what the 256 MB cache in front of HBM gives the decode step under Zipf routing
+    if not args.no_mall:
+        line["mall_residency"] = mall_residency(moe, synth, np, torch, args)
+        torch.cuda.empty_cache()
+
     # ---- 48 chained layers, 1 and 4 tokens per step
     if not args.no_sweep:
         line["decode_sweep"] = decode_sweep(moe, synth, np, torch, args)
@@ -353,6 +367,145 @@ def main():
         line["cpu_baseline"] = cpu_baseline(base, toks, w, args.cpu_seconds)
 
     print(json.dumps(line), flush=True)
+
+
+def decode_low_bit(moe, synth, np, torch, copies4, w4, args, Ts=(1, 16, 64)):
+    """The decode layer (d 2048, 512 experts, top-10 + shared) with every expert in the int4,
+    int3 or int2 group-32 codec, T = 1 (moe_layer_decode, two launches after the router)
+    and T = 16, 64 (the four calls: GEMV in sorted mode), each format on its own rotated
+    layer copies.  Weight-stream bytes: router + (distinct routed experts + shared) x the
+    expert bytes of the format + activations; layer_weight_bytes = what one layer holds."""
+    out = {"workload": "decode_d2048_e512_top10, experts int4 / int3 / int2 g32",
+           "copies_rotated": len(copies4)}
+    for name in ("decode_d2048_e512_top10_t1", "int3_d2048_e512_top10",
+                 "int2_d2048_e512_top10"):
+        w = synth.WORKLOADS[name]
+        if name == "decode_d2048_e512_top10_t1":
+            copies = copies4
+        else:
+            base = synth.make_layer(w, seed=0, device="cuda")
+            copies = [base] + [clone_layer(base) for _ in range(len(copies4) - 1)]
+        n_cp = len(copies)
+        c0 = copies[0]
+        E_b = expert_bytes(c0.routed)
+        r_b = c0.router.w.numel() * c0.router.w.element_size()
+        row = {"expert_bytes": int(E_b),
+               "layer_weight_bytes": int(c0.routed.nbytes() + c0.shared.nbytes() + r_b)}
+        for T in Ts:
+            mls = [moe.MoeLayer(c.router, c.routed, c.shared, w.k, T) for c in copies]
+            xs = [synth.make_tokens(w, T=T, seed=200 + i, device="cuda") for i in range(n_cp)]
+            dec = T * w.k <= 64
+            for i in range(n_cp):
+                ref = mls[i].forward(xs[i]).clone()
+                if dec and not torch.equal(mls[i].decode(xs[i]).view(torch.int16),
+                                           ref.view(torch.int16)):
+                    raise SystemExit("bench.py: %s decode differs from the four calls" % name)
+            torch.cuda.synchronize()
+            moe.moe_check_device_error()
+            U = [int(np.unique(m.ids[:T].cpu().numpy()).size) for m in mls]
+            bytes_step = float(np.mean([r_b + (u + 1) * E_b + 2 * T * w.d * 2 for u in U]))
+
+            def run():
+                for i in range(n_cp):
+                    if dec:
+                        mls[i].decode(xs[i])
+                    else:
+                        mls[i].forward(xs[i])
+            ms, _, _ = time_graph(run, max(20, args.reps), 2)
+            us = ms * 1e3 / n_cp
+            row["T%d" % T] = {"entry": "moe_layer_decode" if dec else "four calls",
+                              "us_per_step": round(us, 2),
+                              "alg_bytes_per_step": int(bytes_step),
+                              "weight_stream_GBps": round(bytes_step / (us * 1e-6) / 1e9, 1),
+                              "tokens_per_s": round(T / (us * 1e-6), 1)}
+            del mls, xs
+        out[w.routed_fmt] = row
+        del copies
+        torch.cuda.empty_cache()
+    return out
+
+
+def mall_residency(moe, synth, np, torch, args):
+    """What the 256 MB Infinity Cache (MALL) in front of HBM gives the decode step.
+
+    read: our stream-read kernel over a working set of S MB, cold (after 1 GiB of other
+    reads) and warm (the same S MB read again at once): the effective GB/s of data the cache
+    holds against data it does not.
+    decode_zipf: one token per step through moe_layer_decode (d 2048, 512 experts, top-10 +
+    shared, Zipf router bias), 64 distinct tokens per replay, cycling over n_copies distinct
+    copies of the layer: one copy's hot experts (most of the Zipf traffic) stay cached, 32
+    copies touch more than the cache holds between reuses.  touched_MB = router rows and
+    distinct experts the 64 steps read, summed over the copies."""
+    import ctypes
+    import statistics
+    out = {}
+    P = ctypes.CDLL(os.path.join(ROOT, "quantized_sparse_moe_router_amd", "libmoe_peaks.so"))
+    P.moe_peaks_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.empty(P.moe_peaks_stream_blocks(), dtype=torch.int32, device="cuda")
+    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda")
+    big = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
+
+    def read(t, n):
+        assert P.moe_peaks_stream_read(t.data_ptr(), n, sink.data_ptr(), stream) == 0
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+    rows = {}
+    for mb in (16, 64, 128, 192, 256, 384, 512):
+        n = mb << 20
+        cold, warm = [], []
+        for _ in range(7):
+            read(flush, flush.numel() * 4)
+            torch.cuda.synchronize()
+            cold.append(timed(lambda: read(big, n)))
+            warm.append(timed(lambda: read(big, n)))
+        rows["%dMB" % mb] = {"cold_GBps": round(n / (statistics.median(cold) * 1e6), 1),
+                             "warm_GBps": round(n / (statistics.median(warm) * 1e6), 1)}
+    out["read"] = rows
+    del flush, big, sink
+    torch.cuda.empty_cache()
+
+    w = synth.WORKLOADS["decode_d2048_e512_top10_t1"]
+    base = synth.make_layer(w, seed=0, device="cuda", bias="zipf")
+    copies = [base] + [clone_layer(base) for _ in range(31)]
+    E_b = expert_bytes(base.routed)
+    r_b = base.router.w.numel() * base.router.w.element_size()
+    n_steps = 64
+    toks = synth.make_tokens(w, T=n_steps, seed=7, device="cuda")
+    xs = [toks[i:i + 1] for i in range(n_steps)]
+    dz = {}
+    for n_cp in (1, 2, 4, 8, 16, 32):
+        mls = [moe.MoeLayer(c.router, c.routed, c.shared, w.k, 1) for c in copies[:n_cp]]
+        seen = [set() for _ in range(n_cp)]
+        for s_ in range(n_steps):
+            m = mls[s_ % n_cp]
+            m.decode(xs[s_])
+            seen[s_ % n_cp].update(m.ids[:1].cpu().numpy().ravel().tolist())
+        torch.cuda.synchronize()
+        moe.moe_check_device_error()
+        touched = sum(r_b + (len(z) + 1) * E_b for z in seen)
+
+        def run():
+            for s_ in range(n_steps):
+                mls[s_ % n_cp].decode(xs[s_])
+        ms, ms_min, _ = time_graph(run, max(20, args.reps), 2)
+        dz["copies%d" % n_cp] = {"us_per_step": round(ms * 1e3 / n_steps, 3),
+                                 "us_per_step_min": round(ms_min * 1e3 / n_steps, 3),
+                                 "touched_MB": round(touched / 2 ** 20, 1),
+                                 "distinct_experts_per_copy": round(
+                                     float(np.mean([len(z) for z in seen])), 1)}
+        del mls
+    out["decode_zipf"] = dz
+    del copies, base
+    torch.cuda.empty_cache()
+    return out
 
 
 def decode_batches(moe, synth, np, torch, copies, w, args, Ts=(1, 4, 6, 8, 16, 32, 64, 96, 128)):

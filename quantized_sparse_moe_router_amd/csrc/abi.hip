@@ -133,12 +133,17 @@ moe_status check_router(const moe_router* r, const char* who) {
     return MOE_OK;
 }
 
+bool expert_fmt(int fmt) {
+    return fmt == MOE_FMT_INT4_G32 || fmt == MOE_FMT_INT6_G32 || fmt == MOE_FMT_INT3_G32 ||
+           fmt == MOE_FMT_INT2_G32;
+}
+
 // Expert-set descriptor checks shared by moe_expert_ffn and moe_layer_decode.
 moe_status check_experts(const moe_experts* ex, const char* who) {
     if (!ex) return fail(MOE_ERR_INVALID_ARG, "%s: expert descriptor is NULL", who);
-    if (ex->fmt != MOE_FMT_INT4_G32 && ex->fmt != MOE_FMT_INT6_G32)
-        return fail(MOE_ERR_INVALID_ARG, "%s: format %d is not INT4_G32/INT6_G32", who,
-                    ex->fmt);
+    if (!expert_fmt(ex->fmt))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "%s: format %d is not INT4_G32/INT6_G32/INT3_G32/INT2_G32", who, ex->fmt);
     const int E = ex->n_experts, d = ex->d_model, F = ex->d_ff;
     if (E < 1 || E > kMaxExperts)
         return fail(MOE_ERR_INVALID_ARG, "%s: n_experts %d", who, E);
@@ -591,8 +596,9 @@ moe_status moe_block_decode(const moe_norm* n, const moe_router* r, const moe_ex
 
 moe_status moe_dequant_probe(int32_t fmt, int32_t form, const uint8_t* w, const uint16_t* s,
                              int64_t n_groups, void* out, void* stream) {
-    if (fmt != MOE_FMT_INT4_G32 && fmt != MOE_FMT_INT6_G32)
-        return fail(MOE_ERR_INVALID_ARG, "moe_dequant_probe: format %d is not INT4_G32/INT6_G32",
+    if (!expert_fmt(fmt))
+        return fail(MOE_ERR_INVALID_ARG,
+                    "moe_dequant_probe: format %d is not INT4_G32/INT6_G32/INT3_G32/INT2_G32",
                     fmt);
     if (form != 0 && form != 1)
         return fail(MOE_ERR_INVALID_ARG, "moe_dequant_probe: form %d is not 0 or 1", form);

@@ -55,7 +55,8 @@ struct GuShape {
     static constexpr int RPB = GU_WAVES * (64 / LPR);   // rows per block
 };
 
-// 8 activations (16 bytes) as group_dot_int4 / group_dot_int6 take them from LDS
+// 8 activations (16 bytes) as the group dot products take them from LDS (int4 pairs
+// elements p, p + 4; the other formats neighbours)
 template <int FMT>
 __device__ __forceinline__ uint4 paired(uint4 v) {
     if constexpr (FMT == MOE_FMT_INT4_G32) return nibble_pairs(v.x, v.y, v.z, v.w);
@@ -434,8 +435,13 @@ hipError_t launch_decode_ffn(const moe_experts& routed, const moe_experts* share
     a.residual = residual; a.z = z; a.out = out;
     a.h = reinterpret_cast<uint16_t*>(base + L.h);
     a.err = device_error_flag();
-    if (routed.fmt == MOE_FMT_INT4_G32) return launch_fmt<MOE_FMT_INT4_G32>(a, d, F, s);
-    return launch_fmt<MOE_FMT_INT6_G32>(a, d, F, s);
+    switch (routed.fmt) {
+        case MOE_FMT_INT4_G32: return launch_fmt<MOE_FMT_INT4_G32>(a, d, F, s);
+        case MOE_FMT_INT6_G32: return launch_fmt<MOE_FMT_INT6_G32>(a, d, F, s);
+        case MOE_FMT_INT3_G32: return launch_fmt<MOE_FMT_INT3_G32>(a, d, F, s);
+        case MOE_FMT_INT2_G32: return launch_fmt<MOE_FMT_INT2_G32>(a, d, F, s);
+        default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace moe

@@ -234,9 +234,18 @@ GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F) {
 hipError_t launch_ffn_gemv(const moe_experts& ex, const uint16_t* x, int T, int k,
                            const int32_t* ids, const int32_t* offsets, const int32_t* sorted,
                            uint16_t* y, void* ws, hipStream_t s) {
-    if (ex.fmt == MOE_FMT_INT4_G32)
-        return launch_fmt<MOE_FMT_INT4_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
-    return launch_fmt<MOE_FMT_INT6_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
+    switch (ex.fmt) {
+        case MOE_FMT_INT4_G32:
+            return launch_fmt<MOE_FMT_INT4_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
+        case MOE_FMT_INT6_G32:
+            return launch_fmt<MOE_FMT_INT6_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
+        case MOE_FMT_INT3_G32:
+            return launch_fmt<MOE_FMT_INT3_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
+        case MOE_FMT_INT2_G32:
+            return launch_fmt<MOE_FMT_INT2_G32>(ex, x, T, k, ids, offsets, sorted, y, ws, s);
+        default:
+            return hipErrorNotSupported;
+    }
 }
 
 }  // namespace moe

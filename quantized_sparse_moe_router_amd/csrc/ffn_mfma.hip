@@ -20,8 +20,8 @@
 //     trip), 256 rows x 128 bytes, XOR-swizzled 16-byte chunks so the MFMA operand reads
 //     are free of bank conflicts;
 //   - weight codes and fp16 scales: global -> LDS directly, into a region private to the
-//     wave that uses them; each lane later reads back exactly the 16 (int4) or 24 (int6)
-//     bytes of the one 32-code group it dequantises;
+//     wave that uses them; each lane later reads back exactly the 16 (int4), 24 (int6),
+//     12 (int3) or 8 (int2) bytes of the one 32-code group it dequantises;
 //   - dequantisation happens in registers straight into the MFMA B operand (no LDS
 //     round trip for bf16 weights);
 //   - the bf16 output tile is staged through LDS so global stores are full rows.  The MFMA k order inside a step is permuted so that
@@ -94,10 +94,14 @@ enum { kGateUp = 0, kDown = 1 };
 // LDS bytes of one pipeline stage
 template <int FMT>
 struct StageLayout {
-    static constexpr int GB = (FMT == MOE_FMT_INT4_G32) ? 16 : 24;   // bytes per group
-    static constexpr int DMA_B = (FMT == MOE_FMT_INT4_G32) ? 1 : 2;   // loads per group
+    // bytes per group; loads per group (int4 one dwordx4, int6 two dwordx3, int3 one
+    // dwordx3, int2 two dword) and the LDS bytes one load gives each lane
+    static constexpr int GB = FMT == MOE_FMT_INT4_G32 ? 16 : FMT == MOE_FMT_INT6_G32 ? 24
+                              : FMT == MOE_FMT_INT3_G32 ? 12 : 8;
+    static constexpr int DMA_B = (FMT == MOE_FMT_INT6_G32 || FMT == MOE_FMT_INT2_G32) ? 2 : 1;
+    static constexpr int DMA_STRIDE = FMT == MOE_FMT_INT2_G32 ? 4 : 16;
     static constexpr int A = BM * BK * 2;                             // activations
-    static constexpr int B_WJ = DMA_B * 64 * 16;                      // codes of (wave, j)
+    static constexpr int B_WJ = DMA_B * 64 * DMA_STRIDE;              // codes of (wave, j)
     static constexpr int B = NW * NI * B_WJ;
     static constexpr int S_WJ = 64 * 4;                               // scales of (wave, j)
     static constexpr int S = NW * NI * S_WJ;
@@ -199,7 +203,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
 
     // stage byte offsets (relative to smem / absolute LDS addresses)
     const uint32_t a_rd = (uint32_t)(lane & 31) * 128;   // + 4096 i + swizzled chunk
-    const uint32_t own_b = (uint32_t)(wave * NI) * L::B_WJ + lane * 16;
+    const uint32_t own_b = (uint32_t)(wave * NI) * L::B_WJ + lane * L::DMA_STRIDE;
     const uint32_t own_s = (uint32_t)(wave * NI) * L::S_WJ + lane * 4;
 
     // load number q (0..NG-1) of k-step `step` into stage st
@@ -212,10 +216,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
             const int j = (q - MB) / L::DMA_B, part = (q - MB) % L::DMA_B;
             const uint8_t* src = b_base[j] + kk * 2 * GB;
             const uint32_t dst = base + L::A + (wave * NI + j) * L::B_WJ;
-            if (L::DMA_B == 1)
+            if constexpr (FMT == MOE_FMT_INT4_G32)
                 dma16s(src, b_off, dst);
-            else
+            else if constexpr (FMT == MOE_FMT_INT6_G32)
                 dma12s(src, b_off + 12 * part, dst + 1024 * part);
+            else if constexpr (FMT == MOE_FMT_INT3_G32)
+                dma12s(src, b_off, dst);
+            else
+                dma4s(src, b_off + 4 * part, dst + 256 * part);
         } else {
             const int j = q - MB - NI * L::DMA_B;
             dma2s(s_base[j] + kk * 2, s_off, base + L::A + L::B + (wave * NI + j) * L::S_WJ);
@@ -228,11 +236,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
         const uint8_t* p = base + L::A + own_b + j * L::B_WJ;
         if constexpr (FMT == MOE_FMT_INT4_G32) {
             c.a = *reinterpret_cast<const u32x4_t*>(p);
-        } else {
+        } else if constexpr (FMT == MOE_FMT_INT6_G32) {
             const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(p);          // bytes 0..11
             const u32x4_t q1 = *reinterpret_cast<const u32x4_t*>(p + 1024);   // bytes 12..23
             c.a = u32x4_t{q0.x, q0.y, q0.z, q1.x};
             c.b = u32x2_t{q1.y, q1.z};
+        } else if constexpr (FMT == MOE_FMT_INT3_G32) {
+            const u32x4_t q0 = *reinterpret_cast<const u32x4_t*>(p);          // bytes 0..11
+            c.a = u32x4_t{q0.x, q0.y, q0.z, 0u};
+        } else {
+            c.a = u32x4_t{*reinterpret_cast<const uint32_t*>(p),               // bytes 0..3
+                          *reinterpret_cast<const uint32_t*>(p + 256), 0u, 0u};   // 4..7
         }
         s = f16_to_f32(*reinterpret_cast<const uint16_t*>(base + L::A + L::B + own_s +
                                                           j * L::S_WJ));
@@ -251,7 +265,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int e, int m0, int 
     bf16x8_t fa[2][MB], fb[2][NI];
     uint32_t lo = 0, hi = 0;
     float e0 = 0.0f, e1 = 0.0f;
-    constexpr float kZero = (FMT == MOE_FMT_INT4_G32) ? 8.0f : 32.0f;
+    constexpr float kZero = kZeroPoint<FMT>;
 
     // Half H of B operand pair b (codes 8 ss + 2b, +1) of column block j for sub-step ss,
     // into fb[F][j]: half 0 converts the two codes to float, half 1 scales and packs them.
@@ -507,9 +521,18 @@ size_t ffn_mfma_ws_bytes(int64_t rows, int E, int F) {
 hipError_t launch_ffn_mfma(const moe_experts& ex, const uint16_t* x, int T, int k,
                            const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
                            void* ws, hipStream_t s) {
-    if (ex.fmt == MOE_FMT_INT4_G32)
-        return launch_fmt<MOE_FMT_INT4_G32>(ex, x, T, k, offsets, sorted_pairs, y, ws, s);
-    return launch_fmt<MOE_FMT_INT6_G32>(ex, x, T, k, offsets, sorted_pairs, y, ws, s);
+    switch (ex.fmt) {
+        case MOE_FMT_INT4_G32:
+            return launch_fmt<MOE_FMT_INT4_G32>(ex, x, T, k, offsets, sorted_pairs, y, ws, s);
+        case MOE_FMT_INT6_G32:
+            return launch_fmt<MOE_FMT_INT6_G32>(ex, x, T, k, offsets, sorted_pairs, y, ws, s);
+        case MOE_FMT_INT3_G32:
+            return launch_fmt<MOE_FMT_INT3_G32>(ex, x, T, k, offsets, sorted_pairs, y, ws, s);
+        case MOE_FMT_INT2_G32:
+            return launch_fmt<MOE_FMT_INT2_G32>(ex, x, T, k, offsets, sorted_pairs, y, ws, s);
+        default:
+            return hipErrorNotSupported;
+    }
 }
 
 }  // namespace moe

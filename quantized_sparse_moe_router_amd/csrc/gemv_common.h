@@ -1,14 +1,14 @@
 // gemv_common.h -- building blocks of the weight-streaming GEMV for few tokens: group
-// dot products on packed int4 / int6 codes, slot resolution, and one projection over a
+// dot products on packed int4 / int6 / int3 / int2 codes, slot resolution, and one projection over a
 // block of rows.  Shared by the per-call GEMV kernels and the decode layer kernels, so
 // both compute every output with exactly the same operations in the same order.
 //
-// A row of K packed codes is read by LPR = min(64, K/32) lanes, one 32-code group (16
-// bytes int4, 24 bytes int6) per lane per step, so a wave covers 64/LPR rows per load
-// instruction with fully used 16-byte loads.  Codes become bf16 pairs (128 + u) with a
-// shift and one and-or (int4: the two nibbles 16 bits apart in a word of codes, i.e.
-// elements p and p + 4 of its 8, so the activations are paired the same way, see
-// nibble_pairs), are multiplied against bf16 activation pairs by v_dot2_f32_bf16, and the
+// A row of K packed codes is read by LPR = min(64, K/32) lanes, one whole 32-code group
+// (16 bytes int4, 24 int6, 12 int3, 8 int2) per lane per step, so a wave covers 64/LPR
+// rows per load instruction and every byte loaded is used.  Codes become bf16 pairs
+// (128 + u) with shifts and and-ors (int4: the two nibbles 16 bits apart in a word of
+// codes, i.e. elements p and p + 4 of its 8, so the activations are paired the same way,
+// see nibble_pairs; int6, int3, int2: neighbouring codes 2p, 2p + 1), are multiplied against bf16 activation pairs by v_dot2_f32_bf16, and the
 // offset (128 + zero point) times the group's activation sum is removed afterwards; the
 // fp16 group scale is applied once per group.
 //
@@ -99,6 +99,47 @@ __device__ __forceinline__ float group_dot_int6(const uint32_t* w6, const uint32
     return acc;
 }
 
+// 12 bytes of int3 codes (32 elements, little-endian bit string) against 32 bf16: pair p
+// is codes 2p, 2p + 1 = the 6 bits at 6p.
+__device__ __forceinline__ float group_dot_int3(const uint32_t* w3, const uint32_t* xp) {
+    const uint64_t lo64 = (uint64_t)w3[0] | ((uint64_t)w3[1] << 32);
+    const uint32_t hi32 = w3[2];
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        uint32_t u[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int bit = 3 * (2 * p + s);              // bit inside the 96 bits
+            uint32_t v;
+            if (bit + 3 <= 64)
+                v = (uint32_t)(lo64 >> bit);
+            else if (bit >= 64)
+                v = hi32 >> (bit - 64);
+            else
+                v = (uint32_t)(lo64 >> bit) | (hi32 << (64 - bit));
+            u[s] = v & 7u;
+        }
+        const uint32_t pair = (u[0] | (u[1] << 16)) | 0x43004300u;
+        acc = dot2(pair, xp[p], acc);
+    }
+    return acc;
+}
+
+// 8 bytes of int2 codes (32 elements, code i at bits [2i, 2i+2)) against 32 bf16: pair p
+// is the nibble at 4p of its word.
+__device__ __forceinline__ float group_dot_int2(const uint32_t* w2, const uint32_t* xp) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const uint32_t w = w2[p / 8];
+        const int o = 4 * (p % 8);
+        const uint32_t pair = ((w >> o) & 3u) | (((w >> (o + 2)) & 3u) << 16) | 0x43004300u;
+        acc = dot2(pair, xp[p], acc);
+    }
+    return acc;
+}
+
 __device__ __forceinline__ float group_sum_x(const uint32_t* xp) {
     float s = 0.0f;
 #pragma unroll
@@ -118,12 +159,22 @@ struct Fmt<MOE_FMT_INT6_G32> {
     static constexpr int kGroupBytes = 24;
     static constexpr float kBias = 160.0f;    // 128 + 32
 };
+template <>
+struct Fmt<MOE_FMT_INT3_G32> {
+    static constexpr int kGroupBytes = 12;
+    static constexpr float kBias = 132.0f;    // 128 + 4
+};
+template <>
+struct Fmt<MOE_FMT_INT2_G32> {
+    static constexpr int kGroupBytes = 8;
+    static constexpr float kBias = 130.0f;    // 128 + 2
+};
 
 enum { kModeGateUp = 0, kModeDown = 1 };
 
 template <int FMT>
 struct GroupBits {
-    uint4 a;
+    uint4 a;   // int4: the group; int3: bytes 0..11 in x, y, z; int2: bytes 0..7 in x, y
     uint2 b;   // int6: bytes 16..23 of the group
 };
 
@@ -131,11 +182,17 @@ template <int FMT>
 __device__ __forceinline__ void load_bits(const uint8_t* p, GroupBits<FMT>& g) {
     if constexpr (FMT == MOE_FMT_INT4_G32) {
         g.a = *reinterpret_cast<const uint4*>(p);
-    } else {
+    } else if constexpr (FMT == MOE_FMT_INT6_G32) {
         const uint2* q = reinterpret_cast<const uint2*>(p);
         const uint2 x0 = q[0], x1 = q[1], x2 = q[2];
         g.a = make_uint4(x0.x, x0.y, x1.x, x1.y);
         g.b = x2;
+    } else if constexpr (FMT == MOE_FMT_INT3_G32) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);   // 4-byte aligned
+        g.a = make_uint4(q[0], q[1], q[2], 0u);
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        g.a = make_uint4(v.x, v.y, 0u, 0u);
     }
 }
 
@@ -143,9 +200,15 @@ template <int FMT>
 __device__ __forceinline__ float dot_bits(const GroupBits<FMT>& g, const uint32_t* xp) {
     if constexpr (FMT == MOE_FMT_INT4_G32) {
         return group_dot_int4(g.a, xp);
-    } else {
+    } else if constexpr (FMT == MOE_FMT_INT6_G32) {
         const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
         return group_dot_int6(w6, xp);
+    } else if constexpr (FMT == MOE_FMT_INT3_G32) {
+        const uint32_t w3[3] = {g.a.x, g.a.y, g.a.z};
+        return group_dot_int3(w3, xp);
+    } else {
+        const uint32_t w2[2] = {g.a.x, g.a.y};
+        return group_dot_int2(w2, xp);
     }
 }
 

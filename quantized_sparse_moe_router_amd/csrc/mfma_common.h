@@ -21,14 +21,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 
 // Global -> LDS loads.  lds is the wave-uniform byte address of the destination, set in M0
 // (the instruction needs one wait state after M0 is written).  Lane l's data lands at
-// lds + 16 l for dwordx4 and dwordx3 (12 bytes used), and at lds + 4 l for ushort
-// (zero-extended to 32 bits).  The compiler does not track these writes: callers count
+// lds + 16 l for dwordx4 and dwordx3 (12 bytes used), and at lds + 4 l for dword and
+// ushort (zero-extended to 32 bits).  The compiler does not track these writes: callers count
 // them with MOE_WAIT_VMCNT.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void dma12(const void* g, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void dma2(const void* g, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "{m0}"(lds) : "memory");
@@ -42,6 +45,10 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
 }
 __device__ __forceinline__ void dma12s(const void* sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx3 %0, %1" ::"v"(voff), "s"(sbase),
+                 "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
                  "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void dma2s(const void* sbase, uint32_t voff, uint32_t lds) {
@@ -61,12 +68,20 @@ __device__ __forceinline__ P* uniform_ptr(P* p) {
 
 // ---- dequantisation of packed weight codes into bf16 MFMA operands (the grouped GEMM
 // and the dequantisation probe call these same functions)
-// The codes of one 32-code group: int4 = 16 bytes (a), int6 = 24 bytes (a, then b).
+// The codes of one 32-code group: int4 = 16 bytes (a), int6 = 24 bytes (a, then b),
+// int3 = 12 bytes (a[0..2]), int2 = 8 bytes (a[0..1]).
 template <int FMT>
 struct GroupCodes {
     u32x4_t a;
     u32x2_t b;
 };
+
+// zero point of a format's codes (value = s * (code - zero point))
+template <int FMT>
+constexpr float kZeroPoint = FMT == MOE_FMT_INT4_G32   ? 8.0f
+                             : FMT == MOE_FMT_INT6_G32 ? 32.0f
+                             : FMT == MOE_FMT_INT3_G32 ? 4.0f
+                                                       : 2.0f;
 
 // Chunk c (codes 8c..8c+7) of a group, split into byte-aligned code fields: lo holds
 // codes 8c, 8c+2, 8c+4, 8c+6 in bytes 0..3, hi codes 8c+1, 8c+3, 8c+5, 8c+7.
@@ -77,7 +92,7 @@ __device__ __forceinline__ void chunk_codes(const GroupCodes<FMT>& g, int c, uin
         const uint32_t w = g.a[c];      // byte i: code 8c+2i (low nibble), 8c+2i+1 (high)
         lo = w & 0x0f0f0f0fu;
         hi = (w >> 4) & 0x0f0f0f0fu;
-    } else {
+    } else if constexpr (FMT == MOE_FMT_INT6_G32) {
         // 8 six-bit codes = bits [48c, 48c + 48) of the 24-byte group
         const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
         const int bit = 48 * c, wi = bit / 32, sh = bit % 32;
@@ -90,6 +105,31 @@ __device__ __forceinline__ void chunk_codes(const GroupCodes<FMT>& g, int c, uin
         }
         lo = l;
         hi = h;
+    } else if constexpr (FMT == MOE_FMT_INT3_G32) {
+        // 8 three-bit codes = bits [24c, 24c + 24) of the 12-byte group
+        const uint32_t w3[3] = {g.a.x, g.a.y, g.a.z};
+        const int bit = 24 * c, wi = bit / 32, sh = bit % 32;
+        const uint32_t nxt = wi + 1 < 3 ? w3[wi + 1 < 3 ? wi + 1 : 2] : 0u;
+        const uint64_t v = ((uint64_t)w3[wi] | ((uint64_t)nxt << 32)) >> sh;
+        uint32_t l = 0, h = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            l |= (uint32_t)((v >> (6 * p)) & 7u) << (8 * p);
+            h |= (uint32_t)((v >> (6 * p + 3)) & 7u) << (8 * p);
+        }
+        lo = l;
+        hi = h;
+    } else {
+        // 8 two-bit codes = bits [16c, 16c + 16) of the 8-byte group
+        const uint32_t w = (c < 2 ? g.a.x : g.a.y) >> (16 * (c & 1));
+        uint32_t l = 0, h = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            l |= ((w >> (4 * p)) & 3u) << (8 * p);
+            h |= ((w >> (4 * p + 2)) & 3u) << (8 * p);
+        }
+        lo = l;
+        hi = h;
     }
     asm volatile("" : "+v"(lo), "+v"(hi));   // keep the byte fields for byte-to-float ops
 }
@@ -97,7 +137,7 @@ __device__ __forceinline__ void chunk_codes(const GroupCodes<FMT>& g, int c, uin
 // Codes 8c+2b and 8c+2b+1 -> packed bf16 pair s * (code - zero point).
 template <int FMT>
 __device__ __forceinline__ uint32_t chunk_pair(uint32_t lo, uint32_t hi, int b, float s) {
-    const float zc = (FMT == MOE_FMT_INT4_G32) ? -8.0f * s : -32.0f * s;
+    const float zc = -kZeroPoint<FMT> * s;
     const float e0 = (float)((lo >> (8 * b)) & 0xffu);
     const float e1 = (float)((hi >> (8 * b)) & 0xffu);
     return pack_bf16(__builtin_fmaf(e0, s, zc), __builtin_fmaf(e1, s, zc));

@@ -1,7 +1,8 @@
 // probe.hip -- the weight decoders of the two expert paths, run on their own over whole
 // matrices, so that a test can compare every decoded weight with its exact value bit for
 // bit.  Expert weights are 4-bit, some layers 6-bit [本地部署Qwen3.8-Flash-Next模型的两条路线
-// (blog.cycleuser.org), section 精度和内存占用]; the code layouts are those of moe.h.
+// (blog.cycleuser.org), section 精度和内存占用], low-bit tiers 2-3 bit [Strata 与
+// Qwen3.8-Flash-Next (telli.sh)]; the code layouts are those of moe.h.
 //
 //   form 0 (few-token GEMV path): the group dot product dot_bits, the zero-point removal and
 //     the scale, exactly as gemv_rows applies them, evaluated on one-hot activations (the
@@ -53,15 +54,21 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(const uint8_t* __restri
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (g >= n_groups) return;
     GroupCodes<FMT> codes;
-    const uint8_t* p = w + g * (FMT == MOE_FMT_INT4_G32 ? 16 : 24);
+    const uint8_t* p = w + g * Fmt<FMT>::kGroupBytes;
     if constexpr (FMT == MOE_FMT_INT4_G32) {
         const uint4 v = *reinterpret_cast<const uint4*>(p);
         codes.a = u32x4_t{v.x, v.y, v.z, v.w};
-    } else {
+    } else if constexpr (FMT == MOE_FMT_INT6_G32) {
         const uint2* q = reinterpret_cast<const uint2*>(p);
         const uint2 a0 = q[0], a1 = q[1], b = q[2];
         codes.a = u32x4_t{a0.x, a0.y, a1.x, a1.y};
         codes.b = u32x2_t{b.x, b.y};
+    } else if constexpr (FMT == MOE_FMT_INT3_G32) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+        codes.a = u32x4_t{q[0], q[1], q[2], 0u};
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        codes.a = u32x4_t{v.x, v.y, 0u, 0u};
     }
     const float sc = f16_to_f32(s[g]);
     for (int c = 0; c < 4; ++c) {
@@ -81,22 +88,22 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(const uint8_t* __restri
 hipError_t launch_dequant_probe(int fmt, int form, const uint8_t* w, const uint16_t* s,
                                 int64_t n_groups, void* out, hipStream_t st) {
     const unsigned blocks = (unsigned)((n_groups + 255) / 256);
-    if (form == 0) {
-        if (fmt == MOE_FMT_INT4_G32)
-            probe_gemv_kernel<MOE_FMT_INT4_G32><<<blocks, 256, 0, st>>>(
-                w, s, n_groups, static_cast<float*>(out));
-        else
-            probe_gemv_kernel<MOE_FMT_INT6_G32><<<blocks, 256, 0, st>>>(
-                w, s, n_groups, static_cast<float*>(out));
-    } else {
-        if (fmt == MOE_FMT_INT4_G32)
-            probe_mfma_kernel<MOE_FMT_INT4_G32><<<blocks, 256, 0, st>>>(
-                w, s, n_groups, static_cast<uint16_t*>(out));
-        else
-            probe_mfma_kernel<MOE_FMT_INT6_G32><<<blocks, 256, 0, st>>>(
-                w, s, n_groups, static_cast<uint16_t*>(out));
+#define MOE_PROBE(F)                                                                      \
+    if (fmt == F) {                                                                       \
+        if (form == 0)                                                                    \
+            probe_gemv_kernel<F><<<blocks, 256, 0, st>>>(w, s, n_groups,                  \
+                                                         static_cast<float*>(out));       \
+        else                                                                              \
+            probe_mfma_kernel<F><<<blocks, 256, 0, st>>>(w, s, n_groups,                  \
+                                                         static_cast<uint16_t*>(out));    \
+        return hipGetLastError();                                                         \
     }
-    return hipGetLastError();
+    MOE_PROBE(MOE_FMT_INT4_G32)
+    MOE_PROBE(MOE_FMT_INT6_G32)
+    MOE_PROBE(MOE_FMT_INT3_G32)
+    MOE_PROBE(MOE_FMT_INT2_G32)
+#undef MOE_PROBE
+    return hipErrorNotSupported;
 }
 
 }  // namespace moe

@@ -41,7 +41,8 @@ template <int FMT, int NV, bool DEVICE_SCOPE_STORE, int WPB = 4, bool NORM = fal
 __device__ __forceinline__ void router_gemv_rows(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
-    float* logits, const RouteNorm& nm = RouteNorm{}) {
+    float* logits, const RouteNorm& nm = RouteNorm{}, int t_lo = 0) {
+    // tokens t_lo .. T - 1 (t_lo > 0 only without the norm)
     constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
     constexpr int NC = NV * PV / 4;          // the norm's 4-element chunks per lane
     const int lane = threadIdx.x & 63;
@@ -119,7 +120,7 @@ __device__ __forceinline__ void router_gemv_rows(
         // fma, and the G chains (each in its own, unchanged order) run interleaved
         constexpr int G = (NV * PV <= 32) ? 4 : (NV * PV <= 64) ? 2 : 1;
         constexpr int XW = PV / 2;           // 32-bit words of activations per vector
-        for (int t0 = 0; t0 < T; t0 += G) {
+        for (int t0 = t_lo; t0 < T; t0 += G) {
             uint32_t xq[G][NV][XW];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -681,6 +682,21 @@ __global__ void __launch_bounds__(64) router_gemv_kernel(
     router_gemv_rows<FMT, NV, false, 1, NORM>(W, scale, bias, x, T, E, d, logits, nm);
 }
 
+// Logits of more tokens (the split form): block (e, b) computes row e for tokens
+// [kRouteTokensPerWave b, kRouteTokensPerWave (b + 1)), so the token loop is short and
+// E x ceil(T / kRouteTokensPerWave) waves share the work.
+constexpr int kRouteTokensPerWave = 8;
+template <int FMT, int NV>
+__global__ void __launch_bounds__(64) router_gemv_split_kernel(
+    const void* __restrict__ W, const uint16_t* __restrict__ scale,
+    const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
+    float* __restrict__ logits) {
+    const int t_lo = blockIdx.y * kRouteTokensPerWave;
+    router_gemv_rows<FMT, NV, false, 1, false>(W, scale, bias, x,
+                                               min(T, t_lo + kRouteTokensPerWave), E, d,
+                                               logits, RouteNorm{}, t_lo);
+}
+
 // the selection kernels for T <= kRouteGemvMaxTokens; NORM: with the fused norm (one more
 // row for the gate logit when there is a gate)
 template <int FMT, int NV, bool NORM>
@@ -712,8 +728,9 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
         return launch_gemv_topk<FMT, NV, false>(r, x, T, k, ids, weights, logits, counter,
                                                 RouteNorm{}, s);
     if (T <= kRouteSplitMaxTokens) {   // one wave per expert row, then the selection kernel
-        router_gemv_kernel<FMT, NV, false><<<dim3(E), dim3(64), 0, s>>>(
-            r.w, r.scale, r.bias, x, T, E, d, logits, RouteNorm{});
+        router_gemv_split_kernel<FMT, NV>
+            <<<dim3(E, (T + kRouteTokensPerWave - 1) / kRouteTokensPerWave), dim3(64), 0, s>>>(
+                r.w, r.scale, r.bias, x, T, E, d, logits);
     } else {
         using R = RgShape<FMT>;
         constexpr int kLds = 2 * R::STAGE;

@@ -149,6 +149,7 @@ def test_expert_ffn_rejects(L):
                                 off, sp, y, ws, wsb, None)
     assert call(None) == -1
     assert call(_experts(fmt=0)) == -1
+    assert call(_experts(fmt=6)) == -1
     assert call(_experts(d=300)) == -1
     assert call(_experts(F=96)) == -1
     assert call(_experts(p=None)) == -1
@@ -259,6 +260,7 @@ def test_dequant_probe_rejects(L):
     dummy = P(16)
     # bad format, bad form, negative count, NULL pointers: rejected before any launch
     assert L.moe_dequant_probe(0, 0, dummy, dummy, 1, dummy, None) == -1
+    assert L.moe_dequant_probe(6, 0, dummy, dummy, 1, dummy, None) == -1
     assert L.moe_dequant_probe(2, 2, dummy, dummy, 1, dummy, None) == -1
     assert L.moe_dequant_probe(2, 0, dummy, dummy, -1, dummy, None) == -1
     assert L.moe_dequant_probe(3, 1, None, dummy, 1, dummy, None) == -1

@@ -46,6 +46,12 @@ def _same(a, b):
     ("int6_tiny_d256_e16_top2", 4, None),
     ("int6_d2048_e64_top10", 1, None),
     ("int6_d2048_e64_top10", 4, None),
+    ("int3_tiny_d256_e16_top2", 4, None),
+    ("int3_d2048_e512_top10", 1, None),
+    ("int3_d2048_e512_top10", 6, "zipf"),
+    ("int2_tiny_d256_e16_top2", 4, None),
+    ("int2_d2048_e512_top10", 1, None),
+    ("int2_d2048_e512_top10", 6, "zipf"),
 ])
 def test_decode_equals_composition(name, T, bias):
     moe = _gpu()

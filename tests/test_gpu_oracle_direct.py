@@ -7,7 +7,8 @@
     that layer on it, so output differences within tolerance cannot cascade into routing
     differences at the next layer;
   - layers whose codes cover the whole code range at every group position (int4 -8 and
-    int6 -32 included) with some all-zero-scale groups, through the GEMV, decode-layer and
+    int6 -32, int3 -4, int2 -2 included) with some all-zero-scale groups, through the GEMV,
+    decode-layer and
     MFMA paths, and the two weight decoders bit for bit (moe_dequant_probe).
 
 The layer: 512 routed experts, 10 of them plus one shared expert per token, 48 layers
@@ -161,7 +162,12 @@ def _all_codes(name):
     return w, synth.make_layer_all_codes(w, seed=0, device="cuda")
 
 
+_QRANGE = {"int4_g32": (-8, 7), "int6_g32": (-32, 31), "int3_g32": (-4, 3),
+           "int2_g32": (-2, 1)}
+
+
 @pytest.mark.parametrize("name", ["tiny_d256_e16_top2", "int6_tiny_d256_e16_top2",
+                                  "int3_tiny_d256_e16_top2", "int2_tiny_d256_e16_top2",
                                   "decode_d2048_e512_top10_t1"])
 def test_dequant_probe_every_code(name):
     moe = _gpu()
@@ -183,7 +189,7 @@ def test_dequant_probe_every_code(name):
             # every code occurs, the lowest included, and so do zero-scale groups
             s64 = np.repeat(si.bits16(sc).reshape(-1).view(np.float16).astype(np.float64), 32)
             q = ref[s64 > 0] / s64[s64 > 0]
-            qmin, qmax = (-8, 7) if ex.fmt == "int4_g32" else (-32, 31)
+            qmin, qmax = _QRANGE[ex.fmt]
             assert q.min() == qmin and q.max() == qmax and (s64 == 0).any()
             # s * q is exact in fp32 (11-bit scale times a code of at most 6 bits)
             got32 = g32.cpu().numpy().reshape(-1)
@@ -202,11 +208,22 @@ def test_dequant_probe_every_code(name):
 
 @pytest.mark.parametrize("name,T", [
     ("tiny_d256_e16_top2", 4),          # GEMV path and the decode layer
-    ("tiny_d256_e16_top2", 100),        # grouped MFMA GEMM
+    ("tiny_d256_e16_top2", 100),        # GEMV in sorted mode (200 pairs)
+    ("tiny_d256_e16_top2", 600),        # grouped MFMA GEMM (1200 pairs; dense shared rows)
     ("int6_tiny_d256_e16_top2", 4),
-    ("int6_tiny_d256_e16_top2", 100),
+    ("int6_tiny_d256_e16_top2", 600),
+    ("int3_tiny_d256_e16_top2", 4),
+    ("int3_tiny_d256_e16_top2", 100),
+    ("int3_tiny_d256_e16_top2", 600),
+    ("int2_tiny_d256_e16_top2", 4),
+    ("int2_tiny_d256_e16_top2", 100),
+    ("int2_tiny_d256_e16_top2", 600),
     ("decode_d2048_e512_top10_t1", 1),
     ("decode_d2048_e512_top10_t1", 17),
+    ("int3_d2048_e512_top10", 1),
+    ("int3_d2048_e512_top10", 8),
+    ("int2_d2048_e512_top10", 1),
+    ("int2_d2048_e512_top10", 8),
 ])
 def test_every_code_through_the_layer(name, T):
     moe = _gpu()

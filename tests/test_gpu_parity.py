@@ -223,11 +223,20 @@ def test_decode_sweep_layer_batch4():
     _check_layer("decode_sweep_48_layers", T=4)
 
 
-@pytest.mark.parametrize("T", [1, 4, 17])
+@pytest.mark.parametrize("T", [1, 4, 17, 65])
 def test_int6_experts_int8_router_small_batches(T):
-    # int6 routed and shared experts through the GEMV kernels; T = 17 routes through the
-    # bounded MFMA router in its int8 form
+    # int6 routed and shared experts through the GEMV kernels (ballot, then sorted mode);
+    # the int8 router by its one-launch form, its split form (T = 17) and its bounded MFMA
+    # form (T = 65)
     _check_layer("int6_d2048_e64_top10", T=T, stream=T)
+
+
+@pytest.mark.parametrize("name", ["int3_d2048_e512_top10", "int2_d2048_e512_top10"])
+@pytest.mark.parametrize("T,bias", [(1, None), (8, "zipf"), (64, None), (200, "zipf")])
+def test_low_bit_experts(name, T, bias):
+    # every expert at 3 or 2 bits: the decode-layer shape through the ballot GEMV (T = 1),
+    # the sorted GEMV (T = 8, 64) and the grouped MFMA GEMM (T = 200, 2000 pairs)
+    _check_layer(name, T=T, bias=bias, stream=T, sample=min(T, 24), tiles=T > 100)
 
 
 def test_int6_tiny_layer_all_tokens():
