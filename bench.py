@@ -86,6 +86,8 @@ def parse():
                    help="skip the int3 / int2 expert decode leg")
     p.add_argument("--no-batches", action="store_true",
                    help="skip the decode batch sizes 1..128")
+    p.add_argument("--batch-sizes", default="1,4,6,8,16,32,64,96,128",
+                   help="tokens per call of the decode-batches leg (comma-separated)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="no graph capture (for profilers)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -327,7 +329,9 @@ def main():
     # ---- decode batches: 1 .. 64 tokens per call through the layer (several decode slots
     # or drafts verified together), on the same rotated copies
     if not args.no_batches:
-        line["decode_batches"] = decode_batches(moe, synth, np, torch, copies, w, args)
+        line["decode_batches"] = decode_batches(
+            moe, synth, np, torch, copies, w, args,
+            Ts=tuple(int(t) for t in args.batch_sizes.split(",") if t.strip()))
         torch.cuda.empty_cache()
 
     # ---- lower-bit expert codecs: the same decode step with every expert at 3 or 2 bits
