@@ -153,7 +153,11 @@ moe_status moe_rmsnorm(const moe_norm* n, const uint16_t* x, int32_t T, int32_t 
                        uint16_t* xn, float* z, void* stream);
 
 /*
- * moe_route -- router logits, top-k selection and gate weights for T tokens.
+ * moe_route -- router logits, top-k selection and gate weights for T tokens.  A router
+ * picks 10 of each layer's 512 routed experts for every token [Strata 与 Qwen3.8-Flash-Next
+ * (telli.sh), section 稀疏架构创造了机会] and stays on the GPU [本地部署Qwen3.8-Flash-Next
+ * 模型的两条路线 (blog.cycleuser.org), section 硬件形态决定了各自的走法]; the linear map, the
+ * summation order and the softmax over the selected logits are this library's readings.
  *   x       bf16 [T][d] (16-byte aligned)
  *   ids     int32 [T][k]: out; the k experts with the largest fp32 logits, slot 0 the
  *           largest; equal logits (+0 == -0) -> lower expert id first
@@ -188,7 +192,9 @@ moe_status moe_route(const moe_router* r, const uint16_t* x, int32_t T, int32_t 
                      void* stream);
 
 /*
- * moe_permute -- group the P = T*k (token, slot) pairs by expert, stably.
+ * moe_permute -- group the P = T*k (token, slot) pairs by expert, stably.  Prefill runs
+ * many tokens through each expert in one batch [Strata 与 Qwen3.8-Flash-Next (telli.sh),
+ * section GPU、RAM 和 SSD 各司其职], which needs each expert's pairs contiguous.
  *   ids           int32 [T][k] expert ids from moe_route
  *   offsets       int32 [E+1]: out; expert e's pairs are sorted_pairs[offsets[e] ..
  *                 offsets[e+1]); offsets[E] = number of valid pairs
@@ -204,7 +210,13 @@ moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_expert_ffn -- y = Wd (silu(Wg x) * (Wu x)) for every (token, expert) pair.
+ * moe_expert_ffn -- y = Wd (silu(Wg x) * (Wu x)) for every (token, expert) pair: the
+ * routed experts a token activates and the always-on shared expert [Strata 与
+ * Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会], their weights stored at 4 bit
+ * (6 bit in mixed layers) [本地部署Qwen3.8-Flash-Next模型的两条路线 (blog.cycleuser.org),
+ * section 精度和内存占用] or 2-3 bit in low-bit tiers [Strata 与 Qwen3.8-Flash-Next
+ * (telli.sh)]; decode reads the active experts' weights once per step [Halogen Flash
+ * Server配置與實測 (lcz.me), replies comparing decode with bandwidth].
  * Grouped mode (routed experts): ids, offsets, sorted_pairs from moe_route/moe_permute;
  *   y is bf16 [T*k][d] in sorted order: row i belongs to pair sorted_pairs[i] and its
  *   token sorted_pairs[i] / k.  Rows past offsets[E] are left untouched.
@@ -239,6 +251,9 @@ moe_status moe_expert_ffn(const moe_experts* ex, const uint16_t* x, int32_t T, i
  * nothing.  If residual (bf16 [T][d]) is not NULL the stored value is instead
  * bf16(residual + bf16(that sum)), the next layer's input in a stacked sweep.
  * out may alias residual.  Needs d % 8 == 0 and 16-byte aligned rows.
+ * A token's output is its selected experts weighted by the router plus the shared expert
+ * [Strata 与 Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会]; the slot order and
+ * the single rounding are this library's readings.
  */
 moe_status moe_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const float* weights,
                        const uint16_t* y_shared, const uint16_t* residual, int32_t T,
