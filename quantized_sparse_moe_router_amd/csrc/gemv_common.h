@@ -48,31 +48,27 @@ __device__ __forceinline__ void nibble_pairs16(uint32_t* xp) {
     }
 }
 
-// 16 bytes of int4 codes (32 elements, element i in bits 4i..4i+3 of the group) against 32
-// bf16 activations in nibble_pairs order.  Returns sum_i (128 + u_i) * x_i, accumulated
-// pair by pair: (0, 4), (1, 5), (2, 6), (3, 7), (8, 12), ...
-__device__ __forceinline__ float group_dot_int4(const uint4 w, const uint32_t* xp) {
+// A group's 32 codes as 16 bf16 pairs (128 + u_a, 128 + u_b), in the order dot_pairs takes
+// them against the activation pairs.  Decoded once per group and reused for every token of a
+// pass (the decode is independent of the token).
+//
+// int4: 16 bytes, element i in bits 4i..4i+3; pair 4q + p = elements (8q + p, 8q + p + 4)
+// (the nibbles 16 bits apart in word q), so the activations come in nibble_pairs order.
+__device__ __forceinline__ void pairs_int4(const uint4 w, uint32_t* pr) {
     // the two constants live in registers so that each pair is one v_and_or_b32 (after a
     // shift): a VOP3 instruction cannot take literal operands on gfx9
     uint32_t mask, bias;
     asm("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
     asm("v_mov_b32 %0, 0x43004300" : "=v"(bias));
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-    float acc = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t pair = ((wd[q] >> (4 * p)) & mask) | bias;
-            acc = dot2(pair, xp[4 * q + p], acc);
-        }
-    }
-    return acc;
+        for (int p = 0; p < 4; ++p) pr[4 * q + p] = ((wd[q] >> (4 * p)) & mask) | bias;
 }
 
-// 24 bytes of int6 codes (32 elements, little-endian bit string) against 32 bf16.
-__device__ __forceinline__ float group_dot_int6(const uint32_t* w6, const uint32_t* xp) {
-    float acc = 0.0f;
+// int6: 24 bytes, a little-endian bit string; pair p = codes 2p, 2p + 1.
+__device__ __forceinline__ void pairs_int6(const uint32_t* w6, uint32_t* pr) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const uint64_t lo64 = (uint64_t)w6[3 * half] | ((uint64_t)w6[3 * half + 1] << 32);
@@ -92,19 +88,15 @@ __device__ __forceinline__ float group_dot_int6(const uint32_t* w6, const uint32
                     v = (uint32_t)(lo64 >> bit) | (uint32_t)(hi32 << (64 - bit));
                 u[s] = v & 63u;
             }
-            const uint32_t pair = (u[0] | (u[1] << 16)) | 0x43004300u;
-            acc = dot2(pair, xp[8 * half + p], acc);
+            pr[8 * half + p] = (u[0] | (u[1] << 16)) | 0x43004300u;
         }
     }
-    return acc;
 }
 
-// 12 bytes of int3 codes (32 elements, little-endian bit string) against 32 bf16: pair p
-// is codes 2p, 2p + 1 = the 6 bits at 6p.
-__device__ __forceinline__ float group_dot_int3(const uint32_t* w3, const uint32_t* xp) {
+// int3: 12 bytes, a little-endian bit string; pair p = codes 2p, 2p + 1 = the 6 bits at 6p.
+__device__ __forceinline__ void pairs_int3(const uint32_t* w3, uint32_t* pr) {
     const uint64_t lo64 = (uint64_t)w3[0] | ((uint64_t)w3[1] << 32);
     const uint32_t hi32 = w3[2];
-    float acc = 0.0f;
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
         uint32_t u[2];
@@ -120,23 +112,26 @@ __device__ __forceinline__ float group_dot_int3(const uint32_t* w3, const uint32
                 v = (uint32_t)(lo64 >> bit) | (hi32 << (64 - bit));
             u[s] = v & 7u;
         }
-        const uint32_t pair = (u[0] | (u[1] << 16)) | 0x43004300u;
-        acc = dot2(pair, xp[p], acc);
+        pr[p] = (u[0] | (u[1] << 16)) | 0x43004300u;
     }
-    return acc;
 }
 
-// 8 bytes of int2 codes (32 elements, code i at bits [2i, 2i+2)) against 32 bf16: pair p
-// is the nibble at 4p of its word.
-__device__ __forceinline__ float group_dot_int2(const uint32_t* w2, const uint32_t* xp) {
-    float acc = 0.0f;
+// int2: 8 bytes, code i at bits [2i, 2i+2); pair p = codes 2p, 2p + 1 = the nibble at 4p of
+// its word.
+__device__ __forceinline__ void pairs_int2(const uint32_t* w2, uint32_t* pr) {
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
         const uint32_t w = w2[p / 8];
         const int o = 4 * (p % 8);
-        const uint32_t pair = ((w >> o) & 3u) | (((w >> (o + 2)) & 3u) << 16) | 0x43004300u;
-        acc = dot2(pair, xp[p], acc);
+        pr[p] = ((w >> o) & 3u) | (((w >> (o + 2)) & 3u) << 16) | 0x43004300u;
     }
+}
+
+// sum_i (128 + u_i) * x_i over a group: 16 v_dot2_f32_bf16, pair by pair in ascending order.
+__device__ __forceinline__ float dot_pairs(const uint32_t* pr, const uint32_t* xp) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc = dot2(pr[i], xp[i], acc);
     return acc;
 }
 
@@ -197,19 +192,27 @@ __device__ __forceinline__ void load_bits(const uint8_t* p, GroupBits<FMT>& g) {
 }
 
 template <int FMT>
-__device__ __forceinline__ float dot_bits(const GroupBits<FMT>& g, const uint32_t* xp) {
+__device__ __forceinline__ void decode_pairs(const GroupBits<FMT>& g, uint32_t* pr) {
     if constexpr (FMT == MOE_FMT_INT4_G32) {
-        return group_dot_int4(g.a, xp);
+        pairs_int4(g.a, pr);
     } else if constexpr (FMT == MOE_FMT_INT6_G32) {
         const uint32_t w6[6] = {g.a.x, g.a.y, g.a.z, g.a.w, g.b.x, g.b.y};
-        return group_dot_int6(w6, xp);
+        pairs_int6(w6, pr);
     } else if constexpr (FMT == MOE_FMT_INT3_G32) {
         const uint32_t w3[3] = {g.a.x, g.a.y, g.a.z};
-        return group_dot_int3(w3, xp);
+        pairs_int3(w3, pr);
     } else {
         const uint32_t w2[2] = {g.a.x, g.a.y};
-        return group_dot_int2(w2, xp);
+        pairs_int2(w2, pr);
     }
+}
+
+// one group against one token's activations: sum_i (128 + u_i) * x_i
+template <int FMT>
+__device__ __forceinline__ float dot_bits(const GroupBits<FMT>& g, const uint32_t* xp) {
+    uint32_t pr[16];
+    decode_pairs<FMT>(g, pr);
+    return dot_pairs(pr, xp);
 }
 
 struct Slot {
@@ -395,29 +398,52 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) {
                     const float s = f16_to_f32(sbits[it][mt][i]);
+                    // the group's pairs once for every token of the chunk (held in
+                    // registers: left to itself the compiler rebuilds them per token)
+                    uint32_t pr[16];
+                    decode_pairs<FMT>(wbits[it][mt][i], pr);
+                    if constexpr (MT > 1) {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(pr[j]));
+                    }
 #pragma unroll
                     for (int m = 0; m < MT; ++m)
                         if (m < mcount) {
-                            const float raw = dot_bits<FMT>(wbits[it][mt][i], xv[m][i]);
+                            const float raw = dot_pairs(pr, xv[m][i]);
                             const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx[m][i], raw);
                             acc[mt][m] = __builtin_fmaf(s, part, acc[mt][m]);
                         }
                 }
+            // every lane of a row's group holds the row's sums for all the chunk's tokens;
+            // lane gp of the group finishes token gp (SwiGLU, rounding, store), so the tokens'
+            // epilogues run side by side instead of one after another on every lane
+            static_assert(MT <= LPR, "one lane of the row's group per token");
+            float v0s[MT], us[MT];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
+                v0s[m] = 0.0f;
+                us[m] = 0.0f;
                 if (m < mcount) {
-                    const float v0 = group_sum<LPR>(acc[0][m]);
-                    float res;
-                    if constexpr (MODE == kModeGateUp) {
-                        const float u = group_sum<LPR>(acc[NMAT - 1][m]);
-                        res = v0 / (1.0f + expf(-v0)) * u;
-                    } else {
-                        res = v0;
-                    }
-                    if (row < rows && gp == 0) {
-                        out[(size_t)orow[m] * rows + row] = (uint16_t)f32_to_bf16(res);
-                    }
+                    v0s[m] = group_sum<LPR>(acc[0][m]);
+                    if constexpr (MODE == kModeGateUp) us[m] = group_sum<LPR>(acc[NMAT - 1][m]);
                 }
+            }
+            float v0 = v0s[0], u = us[0];
+            int orr = orow[0];
+#pragma unroll
+            for (int m = 1; m < MT; ++m)
+                if (gp == m) {
+                    v0 = v0s[m];
+                    u = us[m];
+                    orr = orow[m];
+                }
+            if (row < rows && gp < mcount) {
+                float res;
+                if constexpr (MODE == kModeGateUp)
+                    res = v0 / (1.0f + expf(-v0)) * u;
+                else
+                    res = v0;
+                out[(size_t)orr * rows + row] = (uint16_t)f32_to_bf16(res);
             }
         }
     }
