@@ -11,13 +11,19 @@ To keep the 256 MB Infinity Cache from serving the weights, steps rotate over
 ``--copies`` distinct copies of the layer (a different token per copy).
 
 Also reported in the same line:
-  roofline      the expert kernels of a decode step (moe_experts_decode: gate/up kernel then
-                down + combine kernel): algorithmic bytes (10 routed + 1 shared expert's
-                packed weights and scales, activations in and out) / their event-timed
-                average duration vs 8 TB/s
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload
-  prefill       8192-token prefill through one layer (Zipf routing): tokens/s and the
-                grouped GEMM's MFMA utilisation (useful flops / time / 2.5 PFLOP/s)
+  roofline        the expert kernels of a decode step (moe_experts_decode: gate/up kernel then
+                  down + combine kernel): algorithmic bytes (10 routed + 1 shared expert's
+                  packed weights and scales, activations in and out) / their event-timed
+                  average duration vs 8 TB/s
+  decode_batches  1..128 tokens per call (several decode slots, or drafts verified together)
+  decode_low_bit  the decode layer with int4 / int3 / int2 experts at 1, 16 and 64 tokens
+  mall_residency  what the 256 MB cache in front of HBM gives: stream reads cold and warm,
+                  a Zipf-routed decode cycling over 1..32 layer copies
+  decode_sweep    48 distinct normed, gated blocks chained, 1 and 4 tokens per step
+  prefill         8192-token prefill through one layer (Zipf routing), and 32768 tokens with
+                  mixed formats: tokens/s and the grouped GEMM's MFMA utilisation
+  achievable      measured ceilings of this GPU (stream read, MFMA loop, vendor GEMM)
+  cpu_baseline    the CPU oracle on a bounded sample of the same workload
 """
 import argparse
 import json
