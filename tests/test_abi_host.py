@@ -66,6 +66,10 @@ def test_workspace_sizes(L):
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 1, 10, 512, 2048, 512) == 0
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 8192, 10, 512, 2048, 512) >= 80 * 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 1, 10, 512, 2048, 512) >= 10 * 512 * 2
+    # 640 pairs (the GEMV's sorted mode): h rows and a chunk list of two int4 per entry, at
+    # most one entry per pair
+    assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 64, 10, 512, 2048, 512) >= \
+        640 * 512 * 2 + 640 * 32
     # more than 64 tokens without a logits output: the bounded form also keeps bf16 plane
     # rows of the router (two per fp32 row) and one norm bound per expert
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 8192, 10, 512, 2048, 0) == \
