@@ -1,7 +1,8 @@
 """GPU: moe_permute against the oracle's stable counting sort, on id tables built to
-exercise the chunked form (more than 1024 pairs): ragged last chunks, expert counts that
-are not powers of two, every pair on one expert, and ids outside [0, E) (dropped, flag
-raised, pair_pos = -1)."""
+exercise each form -- one wave (at most 64 pairs), one block with a thread per pair (at most
+1024) and the chunked form (more): ragged last chunks, expert counts that are not powers of
+two, every pair on one expert, and ids outside [0, E) (dropped, flag raised,
+pair_pos = -1)."""
 import numpy as np
 import pytest
 import torch
@@ -26,18 +27,24 @@ def _ids(kind, T, k, E, rng):
         return np.minimum(r, E - 1)
     if kind == "one_expert":
         return np.full((T, k), E // 2)
-    if kind == "bad_ids":       # 1 % of ids outside [0, E)
+    if kind == "bad_ids":       # 1 % of ids outside [0, E), the first and last always
         a = rng.integers(0, E, size=(T, k))
         bad = rng.random((T, k)) < 0.01
         a[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, E + 3)
+        a[0, 0] = -1
+        a[-1, -1] = E + 3
         return a
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("T,k,E", [(103, 10, 512), (500, 10, 512), (4001, 10, 512),
-                                   (2100, 2, 16), (900, 7, 1000), (12289, 8, 1024)])
+@pytest.mark.parametrize("T,k,E", [
+    (1, 10, 512), (6, 10, 512), (32, 2, 16),                       # one wave
+    (7, 10, 512), (64, 10, 512), (100, 10, 1000), (128, 8, 1024),  # one block
+    (33, 2, 16), (93, 11, 1000),
+    (103, 10, 512), (500, 10, 512), (4001, 10, 512),               # chunked
+    (2100, 2, 16), (900, 7, 1000), (12289, 8, 1024)])
 @pytest.mark.parametrize("kind", ["uniform", "skewed", "one_expert", "bad_ids"])
-def test_permute_chunked(T, k, E, kind):
+def test_permute_every_form(T, k, E, kind):
     moe = _gpu()
     rng = np.random.default_rng(T * 31 + E + len(kind))
     ids_h = _ids(kind, T, k, E, rng).astype(np.int32)
