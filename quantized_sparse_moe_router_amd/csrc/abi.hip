@@ -89,6 +89,13 @@ size_t decode_ws(int T, int k, int E, int d, int F) {
     return round_up(route_exact_ws(T, E)) + moe::decode_ws_layout(T, k, d, F).bytes;
 }
 
+// the decode operations run for these sizes: at most 64 pairs, the h rows of every slot
+// within LDS, and a (d_model, d_ff) pair with decode kernels
+bool decode_runs(int T, int k, int d, int F) {
+    return d > 0 && F > 0 && (int64_t)T * k <= kDecodeMaxPairs && moe::ffn_gemv_has_shape(d, F) &&
+           moe::decode_fits(T, k, F, false);
+}
+
 // decode block workspace: the decode layer's, then xn [T][d] bf16 and z [T] fp32
 size_t block_ws(int T, int k, int E, int d, int F) {
     return decode_ws(T, k, E, d, F) + round_up((size_t)T * d * 2) + round_up((size_t)T * 4);
@@ -187,18 +194,14 @@ size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d
         case MOE_OP_ROUTE: return route_ws(T, E, d, true);
         case MOE_OP_PERMUTE: return moe::permute_ws_bytes((int64_t)T * k, E);
         case MOE_OP_EXPERT_FFN: return d_ff > 0 ? ffn_ws((int64_t)T * k, E, d_ff) : 0;
+        // the decode operations: 0 also where they do not run (more than 64 pairs, h rows
+        // beyond LDS, a (d_model, d_ff) pair without decode kernels)
         case MOE_OP_LAYER_DECODE:
-            return (d > 0 && d_ff > 0 && moe::decode_fits(T, k, d_ff, false))
-                       ? decode_ws(T, k, E, d, d_ff)
-                       : 0;
+            return decode_runs(T, k, d, d_ff) ? decode_ws(T, k, E, d, d_ff) : 0;
         case MOE_OP_EXPERTS_DECODE:
-            return (d > 0 && d_ff > 0 && moe::decode_fits(T, k, d_ff, false))
-                       ? moe::decode_ws_layout(T, k, d, d_ff).bytes
-                       : 0;
+            return decode_runs(T, k, d, d_ff) ? moe::decode_ws_layout(T, k, d, d_ff).bytes : 0;
         case MOE_OP_BLOCK_DECODE:
-            return (d > 0 && d_ff > 0 && moe::decode_fits(T, k, d_ff, false))
-                       ? block_ws(T, k, E, d, d_ff)
-                       : 0;
+            return decode_runs(T, k, d, d_ff) ? block_ws(T, k, E, d, d_ff) : 0;
         default: return 0;
     }
 }

@@ -66,6 +66,13 @@ def test_workspace_sizes(L):
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 1, 10, 512, 2048, 512) == 0
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 8192, 10, 512, 2048, 512) >= 80 * 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 1, 10, 512, 2048, 512) >= 10 * 512 * 2
+    # the decode operations report 0 where they do not run: more than 64 pairs, or a
+    # (d_model, d_ff) pair without decode kernels
+    for op in (_lib.MOE_OP_LAYER_DECODE, _lib.MOE_OP_EXPERTS_DECODE, _lib.MOE_OP_BLOCK_DECODE):
+        assert L.moe_workspace_size(op, 6, 10, 512, 2048, 512) > 0
+        assert L.moe_workspace_size(op, 7, 10, 512, 2048, 512) == 0
+        assert L.moe_workspace_size(op, 1, 4, 16, 512, 256) == 0
+        assert L.moe_workspace_size(op, 1, 4, 16, 1024, 512) > 0
     # 640 pairs (the GEMV's sorted mode): h rows and a chunk list of two int4 per entry, at
     # most one entry per pair
     assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 64, 10, 512, 2048, 512) >= \
