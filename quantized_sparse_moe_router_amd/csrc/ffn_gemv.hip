@@ -6,8 +6,10 @@
 // only the selected experts are touched, which is what sparse routing saves
 // [Strata 与 Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会].
 //
-// The per-row arithmetic lives in gemv_common.h.  Two launches: gate/up + SwiGLU -> h (bf16), then down -> y.  In each, a block owns one
-// slot and a block of rows and issues all its weight loads before it reads activations.
+// The per-row arithmetic lives in gemv_common.h.  Two launches, gate/up + SwiGLU -> h (bf16)
+// then down -> y (sorted mode adds the chunk list's launch before them).  In each, a block
+// owns one slot and a block of rows and requests its activation rows and every weight load
+// before any arithmetic.
 //
 // Grouped mode (at most 64 pairs): a slot is a pair p.  A block reads the whole ids vector
 // with one load, so the expert e = ids[p] is known after one memory round trip and the
@@ -18,8 +20,9 @@
 // Dense mode (shared expert): a slot is a chunk of MT tokens.
 // Sorted mode (more than 64 pairs, up to kGemvSortedMaxRows): the grouping from moe_permute
 // is read instead of a ballot; a small kernel lists, expert by expert, chunks of at most MT
-// consecutive sorted positions, and a slot is one chunk.  Each expert's rows are streamed
-// once per chunk; a pair's arithmetic is the same in every mode, so its output bits do not
+// consecutive sorted positions with their tokens (sentinels fill the list to the grid's
+// size), and a slot is one chunk.  Each expert's rows are streamed once per chunk, four
+// rows per wave; a pair's arithmetic is the same in every mode, so its output bits do not
 // depend on the mode (or on the other pairs of the call).
 #include "gemv_common.h"
 

@@ -12,7 +12,8 @@
 //   3. per chunk (16 waves of 64 pairs): the scan of the totals over experts gives the
 //      offsets; each wave ranks its pairs among equal ids (ballot match on the id bits),
 //      waves before it in the chunk add their counts, and the pairs are scattered.
-// A call with at most kChunk pairs runs all three steps in one block.
+// A call with at most kChunk pairs runs all three steps in one block, one thread per pair
+// (the several-token decode GEMV reads this grouping too); at most 64 pairs, in one wave.
 #include "moe_common.h"
 
 namespace moe {

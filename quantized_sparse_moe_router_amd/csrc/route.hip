@@ -21,7 +21,8 @@ namespace {
 
 // ------------------------------------------------------------------ few tokens: GEMV
 // One wave per expert row.  Lane l holds its vectors v = l + 64 j of the row in
-// registers and walks them for every token; the butterfly is a shuffle-xor tree.
+// registers and walks them for every token, a few tokens at a time (their activation loads
+// issued together, one unchanged chain per token); the butterfly is a shuffle-xor tree.
 // PV = elements per 16-byte vector (4 fp32 or 16 int8); NV = vectors per lane.
 //
 // NORM: the tokens are the layer's un-normalised input; every wave computes a token's
