@@ -151,7 +151,7 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
             for (int i = 0; i < GPL; ++i) {
                 const int g = gp + LPR * i;
                 load_bits<FMT>(wb + (size_t)g * GB, wbits[q][i]);
-                sbits[q][i] = sb[g];
+                sbits[q][i] = load_scale(sb + g);
             }
         }
     };
