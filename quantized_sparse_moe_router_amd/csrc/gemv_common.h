@@ -180,6 +180,9 @@ struct GroupBits {
 // sweep; no change at 64 tokens.
 typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+// 12 bytes at a 4-byte aligned address: one dwordx3 load (three 4-byte loads would be merged
+// into one without the cache policy)
+typedef uint32_t nt_u32x3 __attribute__((ext_vector_type(3), aligned(4)));
 
 template <int FMT>
 __device__ __forceinline__ void load_bits(const uint8_t* p, GroupBits<FMT>& g) {
@@ -194,9 +197,8 @@ __device__ __forceinline__ void load_bits(const uint8_t* p, GroupBits<FMT>& g) {
         g.a = make_uint4(x0[0], x0[1], x1[0], x1[1]);
         g.b = make_uint2(x2[0], x2[1]);
     } else if constexpr (FMT == MOE_FMT_INT3_G32) {
-        const uint32_t* q = reinterpret_cast<const uint32_t*>(p);   // 4-byte aligned
-        g.a = make_uint4(__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
-                         __builtin_nontemporal_load(q + 2), 0u);
+        const nt_u32x3 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x3*>(p));
+        g.a = make_uint4(v[0], v[1], v[2], 0u);
     } else {
         const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
         g.a = make_uint4(v[0], v[1], 0u, 0u);
