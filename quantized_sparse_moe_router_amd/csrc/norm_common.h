@@ -48,11 +48,15 @@ __device__ __forceinline__ float rms_scale(float ss, int d, float eps) {
     return 1.0f / sqrtf(ms + eps);
 }
 
-// bf16 bits of xn for one element, rounded to nearest even (finite values; no branch)
-__device__ __forceinline__ uint32_t rms_apply(float x, float r, float gamma) {
-    const float a = x * r;
-    const uint32_t u = __float_as_uint(a * gamma);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 norm_bf16x2 __attribute__((ext_vector_type(2)));
+
+// xn of two elements, fl(fl(x * r) * gamma) each, rounded to bf16 (to nearest even) by one
+// v_cvt_pk_bf16_f32; returns the pair packed (first element in the low half)
+__device__ __forceinline__ uint32_t rms_apply_pair(float x0, float x1, float r, float g0,
+                                                   float g1) {
+    const float a0 = x0 * r, a1 = x1 * r;
+    const norm_bf16x2 p = {(__bf16)(a0 * g0), (__bf16)(a1 * g1)};
+    return __builtin_bit_cast(uint32_t, p);
 }
 
 // One wave, one token: xn of the whole row in the chunk order (stored if xn_row is not
@@ -79,16 +83,15 @@ __device__ __forceinline__ float rms_row_and_gate(const uint2* x4, int lane, flo
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
         const int c0 = (lane + 64 * j) * 4;
-        const uint32_t n0 = rms_apply(bf16lo(x4[j].x), r, g4[j].x);
-        const uint32_t n1 = rms_apply(bf16hi(x4[j].x), r, g4[j].y);
-        const uint32_t n2 = rms_apply(bf16lo(x4[j].y), r, g4[j].z);
-        const uint32_t n3 = rms_apply(bf16hi(x4[j].y), r, g4[j].w);
-        if (xn_row)
-            *reinterpret_cast<uint2*>(xn_row + c0) = make_uint2(n0 | (n1 << 16), n2 | (n3 << 16));
-        acc = __builtin_fmaf(bf16_to_f32(n0), w4[j].x, acc);
-        acc = __builtin_fmaf(bf16_to_f32(n1), w4[j].y, acc);
-        acc = __builtin_fmaf(bf16_to_f32(n2), w4[j].z, acc);
-        acc = __builtin_fmaf(bf16_to_f32(n3), w4[j].w, acc);
+        const uint32_t n01 = rms_apply_pair(bf16lo(x4[j].x), bf16hi(x4[j].x), r, g4[j].x,
+                                            g4[j].y);
+        const uint32_t n23 = rms_apply_pair(bf16lo(x4[j].y), bf16hi(x4[j].y), r, g4[j].z,
+                                            g4[j].w);
+        if (xn_row) *reinterpret_cast<uint2*>(xn_row + c0) = make_uint2(n01, n23);
+        acc = __builtin_fmaf(bf16lo(n01), w4[j].x, acc);
+        acc = __builtin_fmaf(bf16hi(n01), w4[j].y, acc);
+        acc = __builtin_fmaf(bf16lo(n23), w4[j].z, acc);
+        acc = __builtin_fmaf(bf16hi(n23), w4[j].w, acc);
     }
     if (!gw) return 0.0f;
     return group_sum<64>(acc) + gb;

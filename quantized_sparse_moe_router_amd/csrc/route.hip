@@ -206,21 +206,15 @@ __device__ __forceinline__ void router_gemv_rows(
                 uint2 xv;
                 if constexpr (NORM) xv = x4[j];
                 else xv = *reinterpret_cast<const uint2*>(xt + c0);
-                uint32_t q0 = xv.x & 0xffffu, q1 = xv.x >> 16;
-                uint32_t q2 = xv.y & 0xffffu, q3 = xv.y >> 16;
                 if constexpr (NORM) {
-                    q0 = rms_apply(bf16_to_f32(q0), r, gam[j][0]);
-                    q1 = rms_apply(bf16_to_f32(q1), r, gam[j][1]);
-                    q2 = rms_apply(bf16_to_f32(q2), r, gam[j][2]);
-                    q3 = rms_apply(bf16_to_f32(q3), r, gam[j][3]);
-                    if (e == 0)
-                        *reinterpret_cast<uint2*>(nm.xn + (size_t)t * d + c0) =
-                            make_uint2(q0 | (q1 << 16), q2 | (q3 << 16));
+                    xv.x = rms_apply_pair(bf16lo(xv.x), bf16hi(xv.x), r, gam[j][0], gam[j][1]);
+                    xv.y = rms_apply_pair(bf16lo(xv.y), bf16hi(xv.y), r, gam[j][2], gam[j][3]);
+                    if (e == 0) *reinterpret_cast<uint2*>(nm.xn + (size_t)t * d + c0) = xv;
                 }
-                acc = __builtin_fmaf(bf16_to_f32(q0), w[j][0], acc);
-                acc = __builtin_fmaf(bf16_to_f32(q1), w[j][1], acc);
-                acc = __builtin_fmaf(bf16_to_f32(q2), w[j][2], acc);
-                acc = __builtin_fmaf(bf16_to_f32(q3), w[j][3], acc);
+                acc = __builtin_fmaf(bf16lo(xv.x), w[j][0], acc);
+                acc = __builtin_fmaf(bf16hi(xv.x), w[j][1], acc);
+                acc = __builtin_fmaf(bf16lo(xv.y), w[j][2], acc);
+                acc = __builtin_fmaf(bf16hi(xv.y), w[j][3], acc);
             } else {
                 const uint4* xp = reinterpret_cast<const uint4*>(xt + c0);
                 uint4 a = xp[0], bq = xp[1];
@@ -228,8 +222,8 @@ __device__ __forceinline__ void router_gemv_rows(
                 if constexpr (NORM) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        qs[i] = rms_apply(bf16lo(qs[i]), r, gam[j][2 * i]) |
-                                (rms_apply(bf16hi(qs[i]), r, gam[j][2 * i + 1]) << 16);
+                        qs[i] = rms_apply_pair(bf16lo(qs[i]), bf16hi(qs[i]), r, gam[j][2 * i],
+                                               gam[j][2 * i + 1]);
                     if (e == 0) {
                         uint4* dst = reinterpret_cast<uint4*>(nm.xn + (size_t)t * d + c0);
                         dst[0] = make_uint4(qs[0], qs[1], qs[2], qs[3]);
