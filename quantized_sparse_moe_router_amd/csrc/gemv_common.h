@@ -404,14 +404,15 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) sx[m][i] = group_sum_x(xv[m][i]);
 
+        // acc[it * MT + m][mt]: this lane's part of row `it`'s sum for token m, matrix mt
+        constexpr int NR = ITERS * MT;
+        float acc[NR][NMAT];
 #pragma unroll
-        for (int it = 0; it < ITERS; ++it) {
-            const int row = row_base + it * RPW;
-            float acc[NMAT][MT];
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt)
+            for (int mt = 0; mt < NMAT; ++mt) acc[r][mt] = 0.0f;
 #pragma unroll
-                for (int m = 0; m < MT; ++m) acc[mt][m] = 0.0f;
+        for (int it = 0; it < ITERS; ++it)
 #pragma unroll
             for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
@@ -430,36 +431,29 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                         if (m < mcount) {
                             const float raw = dot_pairs(pr, xv[m][i]);
                             const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx[m][i], raw);
-                            acc[mt][m] = __builtin_fmaf(s, part, acc[mt][m]);
+                            acc[it * MT + m][mt] = __builtin_fmaf(s, part, acc[it * MT + m][mt]);
                         }
                 }
-            // every lane of a row's group holds the row's sums for all the chunk's tokens;
-            // lane gp of the group finishes token gp (SwiGLU, rounding, store), so the tokens'
-            // epilogues run side by side instead of one after another on every lane
-            static_assert(MT <= LPR, "one lane of the row's group per token");
-            float v0s[MT], us[MT];
+        // the row sums over the row's LPR lanes, all (row, token) pairs at once; each sum
+        // ends on one lane of the group (tr_writer), which finishes it (SwiGLU, rounding,
+        // store), so the epilogues of all rows and tokens run side by side
+        group_sum_many<LPR, NR, NMAT>(acc, lane);
+        constexpr int R = NR > LPR ? NR / LPR : 1;
+        const int idx0 = tr_index<LPR, NR>(lane) * R;
+        const bool writer = tr_writer<LPR, NR>(lane);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                v0s[m] = 0.0f;
-                us[m] = 0.0f;
-                if (m < mcount) {
-                    v0s[m] = group_sum<LPR>(acc[0][m]);
-                    if constexpr (MODE == kModeGateUp) us[m] = group_sum<LPR>(acc[NMAT - 1][m]);
-                }
-            }
-            float v0 = v0s[0], u = us[0];
+        for (int r = 0; r < R; ++r) {
+            const int idx = idx0 + r, it = idx / MT, m = idx % MT;
+            const int row = row_base + it * RPW;
             int orr = orow[0];
 #pragma unroll
-            for (int m = 1; m < MT; ++m)
-                if (gp == m) {
-                    v0 = v0s[m];
-                    u = us[m];
-                    orr = orow[m];
-                }
-            if (row < rows && gp < mcount) {
+            for (int mm = 1; mm < MT; ++mm)
+                if (m == mm) orr = orow[mm];
+            if (writer && row < rows && m < mcount) {
+                const float v0 = acc[r][0];
                 float res;
                 if constexpr (MODE == kModeGateUp)
-                    res = v0 / (1.0f + expf(-v0)) * u;
+                    res = v0 / (1.0f + expf(-v0)) * acc[r][NMAT - 1];
                 else
                     res = v0;
                 out[(size_t)orr * rows + row] = (uint16_t)f32_to_bf16(res);

@@ -92,6 +92,126 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// ---- group_sum of many values at once, transposed
+// group_sum spends one exchange and one add per level on every value, and leaves each sum on
+// every lane.  With N values per lane, level j of the transposed form instead splits the
+// values between the two partner lanes: each keeps one half and adds the partner's copy of
+// it, so the level costs N/2 adds and the sums end spread over the lanes.  The partners and
+// the order of the levels are group_sum's, so every sum is the same tree of the same
+// additions (fp addition is commutative): the bits equal group_sum's.
+//
+// Which half a lane keeps at level j is bit sel_j of its lane index l (l0 = bit 0, ...):
+//   sel_0 = l0 ^ l2, sel_1 = l1 ^ l2, sel_2 = l2 ^ l3, sel_j = lj for j >= 3.
+// A lane and its partner at level j (l ^ 1, l ^ 2, l ^ 7, l ^ 15, l ^ 16, l ^ 32) differ in
+// sel_j and agree in every earlier sel, so they hold the same values when they split them.
+template <int J>
+__device__ __forceinline__ bool tr_sel(int lane) {
+    if constexpr (J == 0) return ((lane ^ (lane >> 2)) & 1) != 0;
+    else if constexpr (J == 1) return (((lane >> 1) ^ (lane >> 2)) & 1) != 0;
+    else if constexpr (J == 2) return (((lane >> 2) ^ (lane >> 3)) & 1) != 0;
+    else return ((lane >> J) & 1) != 0;
+}
+
+// level j of group_sum on one value
+template <int J>
+__device__ __forceinline__ float bf_level(float v) {
+    if constexpr (J == 0) return v + dpp<kDppXor1>(v);
+    else if constexpr (J == 1) return v + dpp<kDppXor2>(v);
+    else if constexpr (J == 2) return v + dpp<kDppHalfMirror>(v);
+    else if constexpr (J == 3) return v + dpp<kDppMirror>(v);
+    else return add_swapped<(J == 4) ? 16 : 32>(v);
+}
+
+// level j, transposed: lo / hi are values i and i + C/2 of the lane's C; returns the
+// level's sum of the one this lane keeps (lo where sel_j = 0, hi where sel_j = 1).  The
+// cross-row levels take both halves in one v_permlane16/32_swap: with (lo, hi) as
+// (vdst, vsrc), the rows of lanes with bit j = 0 end with lo of both partners, the others
+// with hi of both.
+template <int J>
+__device__ __forceinline__ float tr_level(float lo, float hi, bool sel) {
+    if constexpr (J <= 3) {
+        const float keep = sel ? hi : lo, send = sel ? lo : hi;
+        constexpr int kCtrl = J == 0 ? kDppXor1 : J == 1 ? kDppXor2
+                            : J == 2 ? kDppHalfMirror : kDppMirror;
+        return keep + dpp<kCtrl>(send);
+    } else {
+        const uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+        uint32_t x, y;
+        if constexpr (J == 4) {
+            const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+            x = r[0]; y = r[1];
+        } else {
+            const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+            x = r[0]; y = r[1];
+        }
+        return __uint_as_float(x) + __uint_as_float(y);
+    }
+}
+
+// Levels J .. log2(G) - 1 on v[0 .. C-1] (tuples of NM values that travel together):
+// transposed while a lane holds more than one tuple, then group_sum's levels.
+template <int G, int J, int C, int N, int NM>
+__device__ __forceinline__ void tr_levels(float (&v)[N][NM], int lane) {
+    if constexpr ((1 << J) < G) {
+        if constexpr (C > 1) {
+            constexpr int H = C / 2;
+            const bool sel = tr_sel<J>(lane);
+#pragma unroll
+            for (int i = 0; i < H; ++i)
+#pragma unroll
+                for (int c = 0; c < NM; ++c) v[i][c] = tr_level<J>(v[i][c], v[i + H][c], sel);
+            tr_levels<G, J + 1, H, N, NM>(v, lane);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NM; ++c) v[0][c] = bf_level<J>(v[0][c]);
+            tr_levels<G, J + 1, 1, N, NM>(v, lane);
+        }
+    }
+}
+
+// Sums over aligned groups of G lanes (a power of two <= 64) of N tuples (N a power of two)
+// of NM values each, each sum bit-identical to group_sum<G>.  On return the lane holds
+// R = max(1, N / G) tuples in v[0 .. R-1]: v[r] is tuple tr_index(lane) * R + r.  When
+// N < G, G / N lanes of the group hold each tuple; tr_writer picks one of them.
+template <int G, int N, int NM>
+__device__ __forceinline__ void group_sum_many(float (&v)[N][NM], int lane) {
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "G: a power of two <= 64");
+    static_assert(N >= 1 && (N & (N - 1)) == 0, "N: a power of two");
+    tr_levels<G, 0, N, N, NM>(v, lane);
+}
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+
+// the index of the tuples a lane holds after group_sum_many<G, N, ...>, divided by R
+template <int G, int N>
+__device__ __forceinline__ int tr_index(int lane) {
+    constexpr int NT = ilog2(N < G ? N : G);           // transposed levels
+    int idx = 0;
+    if constexpr (NT > 0) idx = idx * 2 + (int)tr_sel<0>(lane);
+    if constexpr (NT > 1) idx = idx * 2 + (int)tr_sel<1>(lane);
+    if constexpr (NT > 2) idx = idx * 2 + (int)tr_sel<2>(lane);
+    if constexpr (NT > 3) idx = idx * 2 + (int)tr_sel<3>(lane);
+    if constexpr (NT > 4) idx = idx * 2 + (int)tr_sel<4>(lane);
+    if constexpr (NT > 5) idx = idx * 2 + (int)tr_sel<5>(lane);
+    return idx;
+}
+
+// one lane per distinct tuple: sel_j = 0 at every level that was not transposed
+template <int G, int N>
+__device__ __forceinline__ bool tr_writer(int lane) {
+    constexpr int NT = ilog2(N < G ? N : G), L = ilog2(G);
+    // no level transposed: every lane of the group holds the sums, the first one writes
+    if constexpr (NT == 0) return (lane & (G - 1)) == 0;
+    bool w = true;
+    if constexpr (NT <= 0 && L > 0) w = w && !tr_sel<0>(lane);
+    if constexpr (NT <= 1 && L > 1) w = w && !tr_sel<1>(lane);
+    if constexpr (NT <= 2 && L > 2) w = w && !tr_sel<2>(lane);
+    if constexpr (NT <= 3 && L > 3) w = w && !tr_sel<3>(lane);
+    if constexpr (NT <= 4 && L > 4) w = w && !tr_sel<4>(lane);
+    if constexpr (NT <= 5 && L > 5) w = w && !tr_sel<5>(lane);
+    return w;
+}
+
 }  // namespace moe
 
 // ---------------------------------------------------------------- launchers (host)
