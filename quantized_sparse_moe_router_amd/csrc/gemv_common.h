@@ -362,7 +362,6 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                         xv[m][i][4 * v + 2] = q.z;
                         xv[m][i][4 * v + 3] = q.w;
                     }
-                    if constexpr (FMT == MOE_FMT_INT4_G32 && !PAIRED) nibble_pairs16(xv[m][i]);
                 }
             }
         }
@@ -397,6 +396,15 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
 
     // ---- compute
     {
+        // int4: the activations into nibble_pairs order, only now: done where they are
+        // loaded, it makes the wave wait for them before it requests the weights
+        if constexpr (FMT == MOE_FMT_INT4_G32 && !PAIRED) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < mcount)
+#pragma unroll
+                    for (int i = 0; i < GPL; ++i) nibble_pairs16(xv[m][i]);
+        }
         float sx[MT][GPL];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -404,59 +412,70 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) sx[m][i] = group_sum_x(xv[m][i]);
 
-        // acc[it * MT + m][mt]: this lane's part of row `it`'s sum for token m, matrix mt
-        constexpr int NR = ITERS * MT;
-        float acc[NR][NMAT];
+        // rows are taken RB at a time: acc[b * MT + m][mt] is this lane's part of row
+        // it0 + b's sum for token m, matrix mt; at most 16 sums are live, which keeps the
+        // sorted gate/up wave within 128 registers (4 waves per SIMD instead of 3)
+        constexpr int RB = (MT * NMAT * ITERS <= 16) ? ITERS
+                         : (16 / (MT * NMAT) >= 1 ? 16 / (MT * NMAT) : 1);
+        static_assert(ITERS % RB == 0, "row batches divide the rows");
+        constexpr int NR = RB * MT;
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
+        for (int it0 = 0; it0 < ITERS; it0 += RB) {
+            float acc[NR][NMAT];
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt) acc[r][mt] = 0.0f;
+            for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int it = 0; it < ITERS; ++it)
+                for (int mt = 0; mt < NMAT; ++mt) acc[r][mt] = 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < NMAT; ++mt)
+            for (int b = 0; b < RB; ++b)
 #pragma unroll
-                for (int i = 0; i < GPL; ++i) {
-                    const float s = f16_to_f32(sbits[it][mt][i]);
-                    // the group's pairs once for every token of the chunk (held in
-                    // registers: left to itself the compiler rebuilds them per token)
-                    uint32_t pr[16];
-                    decode_pairs<FMT>(wbits[it][mt][i], pr);
-                    if constexpr (MT > 1) {
+                for (int mt = 0; mt < NMAT; ++mt)
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(pr[j]));
-                    }
+                    for (int i = 0; i < GPL; ++i) {
+                        const int it = it0 + b;
+                        const float s = f16_to_f32(sbits[it][mt][i]);
+                        // the group's pairs once for every token of the chunk (held in
+                        // registers: left to itself the compiler rebuilds them per token)
+                        uint32_t pr[16];
+                        decode_pairs<FMT>(wbits[it][mt][i], pr);
+                        if constexpr (MT > 1) {
 #pragma unroll
-                    for (int m = 0; m < MT; ++m)
-                        if (m < mcount) {
-                            const float raw = dot_pairs(pr, xv[m][i]);
-                            const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx[m][i], raw);
-                            acc[it * MT + m][mt] = __builtin_fmaf(s, part, acc[it * MT + m][mt]);
+                            for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(pr[j]));
                         }
+#pragma unroll
+                        for (int m = 0; m < MT; ++m)
+                            if (m < mcount) {
+                                const float raw = dot_pairs(pr, xv[m][i]);
+                                const float part =
+                                    __builtin_fmaf(-Fmt<FMT>::kBias, sx[m][i], raw);
+                                acc[b * MT + m][mt] =
+                                    __builtin_fmaf(s, part, acc[b * MT + m][mt]);
+                            }
+                    }
+            // the row sums over the row's LPR lanes, all (row, token) pairs of the batch at
+            // once; each sum ends on one lane of the group (tr_writer), which finishes it
+            // (SwiGLU, rounding, store), so the epilogues run side by side
+            group_sum_many<LPR, NR, NMAT>(acc, lane);
+            constexpr int R = NR > LPR ? NR / LPR : 1;
+            const int idx0 = tr_index<LPR, NR>(lane) * R;
+            const bool writer = tr_writer<LPR, NR>(lane);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int idx = idx0 + r, m = idx % MT;
+                const int row = row_base + (it0 + idx / MT) * RPW;
+                int orr = orow[0];
+#pragma unroll
+                for (int mm = 1; mm < MT; ++mm)
+                    if (m == mm) orr = orow[mm];
+                if (writer && row < rows && m < mcount) {
+                    const float v0 = acc[r][0];
+                    float res;
+                    if constexpr (MODE == kModeGateUp)
+                        res = v0 / (1.0f + expf(-v0)) * acc[r][NMAT - 1];
+                    else
+                        res = v0;
+                    out[(size_t)orr * rows + row] = (uint16_t)f32_to_bf16(res);
                 }
-        // the row sums over the row's LPR lanes, all (row, token) pairs at once; each sum
-        // ends on one lane of the group (tr_writer), which finishes it (SwiGLU, rounding,
-        // store), so the epilogues of all rows and tokens run side by side
-        group_sum_many<LPR, NR, NMAT>(acc, lane);
-        constexpr int R = NR > LPR ? NR / LPR : 1;
-        const int idx0 = tr_index<LPR, NR>(lane) * R;
-        const bool writer = tr_writer<LPR, NR>(lane);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int idx = idx0 + r, it = idx / MT, m = idx % MT;
-            const int row = row_base + it * RPW;
-            int orr = orow[0];
-#pragma unroll
-            for (int mm = 1; mm < MT; ++mm)
-                if (m == mm) orr = orow[mm];
-            if (writer && row < rows && m < mcount) {
-                const float v0 = acc[r][0];
-                float res;
-                if constexpr (MODE == kModeGateUp)
-                    res = v0 / (1.0f + expf(-v0)) * acc[r][NMAT - 1];
-                else
-                    res = v0;
-                out[(size_t)orr * rows + row] = (uint16_t)f32_to_bf16(res);
             }
         }
     }

@@ -38,32 +38,10 @@ struct RouteNorm {
     float* z;             // [T]
 };
 
-template <int FMT, int NV, bool DEVICE_SCOPE_STORE, int WPB = 4, bool NORM = false>
-__device__ __forceinline__ void router_gemv_rows(
-    const void* __restrict__ W, const uint16_t* __restrict__ scale,
-    const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
-    float* logits, const RouteNorm& nm = RouteNorm{}, int t_lo = 0) {
-    // tokens t_lo .. T - 1 (t_lo > 0 only without the norm)
-    constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
-    constexpr int NC = NV * PV / 4;          // the norm's 4-element chunks per lane
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * WPB + (threadIdx.x >> 6);   // WPB rows (waves) per block
-    if constexpr (NORM) {
-        if (e == E && nm.gw) {               // the gate row
-            for (int t = 0; t < T; ++t) {
-                uint2 x4[NC];
-                const float ss = group_sum<64>(rms_lane_sumsq<NC>(x + (size_t)t * d, lane, x4));
-                const float r = rms_scale(ss, d, nm.eps);
-                const float zt = rms_row_and_gate<NC>(x4, lane, r, nm.gamma, nm.gw, nm.gb,
-                                                      nullptr);
-                if (lane == 0) nm.z[t] = zt;
-            }
-            return;
-        }
-    }
-    if (e >= E) return;
-
-    float w[NV][PV];
+// Row e's vectors lane + 64 j, j < NV, of the lane into registers (int8 codes as floats).
+template <int FMT, int NV, int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4>
+__device__ __forceinline__ void router_row_regs(const void* __restrict__ W, int e, int d,
+                                                int lane, float (&w)[NV][PV]) {
     if constexpr (FMT == MOE_FMT_INT8_ROW) {
         const uint4* row = reinterpret_cast<const uint4*>(
             static_cast<const int8_t*>(W) + (size_t)e * d);
@@ -84,6 +62,34 @@ __device__ __forceinline__ void router_gemv_rows(
             w[j][0] = v.x; w[j][1] = v.y; w[j][2] = v.z; w[j][3] = v.w;
         }
     }
+}
+
+template <int FMT, int NV, bool DEVICE_SCOPE_STORE, int WPB = 4, bool NORM = false>
+__device__ __forceinline__ void router_gemv_rows(
+    const void* __restrict__ W, const uint16_t* __restrict__ scale,
+    const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
+    float* logits, const RouteNorm& nm = RouteNorm{}) {
+    constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
+    constexpr int NC = NV * PV / 4;          // the norm's 4-element chunks per lane
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * WPB + (threadIdx.x >> 6);   // WPB rows (waves) per block
+    if constexpr (NORM) {
+        if (e == E && nm.gw) {               // the gate row
+            for (int t = 0; t < T; ++t) {
+                uint2 x4[NC];
+                const float ss = group_sum<64>(rms_lane_sumsq<NC>(x + (size_t)t * d, lane, x4));
+                const float r = rms_scale(ss, d, nm.eps);
+                const float zt = rms_row_and_gate<NC>(x4, lane, r, nm.gamma, nm.gw, nm.gb,
+                                                      nullptr);
+                if (lane == 0) nm.z[t] = zt;
+            }
+            return;
+        }
+    }
+    if (e >= E) return;
+
+    float w[NV][PV];
+    router_row_regs<FMT, NV>(W, e, d, lane, w);
     const float b = bias ? bias[e] : 0.0f;
     const float se = (FMT == MOE_FMT_INT8_ROW) ? f16_to_f32(scale[e]) : 1.0f;
     // NORM: gamma of the lane's elements, in registers for every token
@@ -121,7 +127,7 @@ __device__ __forceinline__ void router_gemv_rows(
         // fma, and the G chains (each in its own, unchanged order) run interleaved
         constexpr int G = (NV * PV <= 32) ? 4 : (NV * PV <= 64) ? 2 : 1;
         constexpr int XW = PV / 2;           // 32-bit words of activations per vector
-        for (int t0 = t_lo; t0 < T; t0 += G) {
+        for (int t0 = 0; t0 < T; t0 += G) {
             uint32_t xq[G][NV][XW];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -677,19 +683,97 @@ __global__ void __launch_bounds__(64) router_gemv_kernel(
     router_gemv_rows<FMT, NV, false, 1, NORM>(W, scale, bias, x, T, E, d, logits, nm);
 }
 
-// Logits of more tokens (the split form): block (e, b) computes row e for tokens
-// [kRouteTokensPerWave b, kRouteTokensPerWave (b + 1)), so the token loop is short and
-// E x ceil(T / kRouteTokensPerWave) waves share the work.
+// Logits of more tokens (the split form): block (c, b) computes rows NE c .. NE c + NE - 1
+// for tokens [kRouteTokensPerWave b, kRouteTokensPerWave (b + 1)), so the token loop is
+// short and ceil(E / NE) x ceil(T / kRouteTokensPerWave) waves share the work.  Every
+// activation vector a wave loads serves its NE rows: the activations are the bulk of what
+// the waves read (E T d bf16 over all waves with one row each, d fp32 per row).  Each
+// (token, expert) chain and its butterfly are the GEMV's, so the logits are the same bits.
 constexpr int kRouteTokensPerWave = 8;
+template <int FMT, int NV>
+struct SplitShape {
+    static constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
+    static constexpr int NE = (NV * PV <= 32) ? 2 : 1;                     // rows per wave
+    static constexpr int G = (NV * PV <= 32) ? 4 : (NV * PV <= 64) ? 2 : 1;   // tokens per pass
+};
 template <int FMT, int NV>
 __global__ void __launch_bounds__(64) router_gemv_split_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
     float* __restrict__ logits) {
+    using SS = SplitShape<FMT, NV>;
+    constexpr int PV = SS::PV, NE = SS::NE, G = SS::G;
+    constexpr int XW = PV / 2;                  // 32-bit words of activations per vector
+    const int lane = threadIdx.x;
+    const int e0 = blockIdx.x * NE;
     const int t_lo = blockIdx.y * kRouteTokensPerWave;
-    router_gemv_rows<FMT, NV, false, 1, false>(W, scale, bias, x,
-                                               min(T, t_lo + kRouteTokensPerWave), E, d,
-                                               logits, RouteNorm{}, t_lo);
+    const int t_hi = min(T, t_lo + kRouteTokensPerWave);
+    float w[NE][NV][PV];
+    float b[NE], se[NE];
+#pragma unroll
+    for (int r = 0; r < NE; ++r) {
+        const int e = min(e0 + r, E - 1);       // a row past E repeats the last, unstored
+        router_row_regs<FMT, NV>(W, e, d, lane, w[r]);
+        b[r] = bias ? bias[e] : 0.0f;
+        se[r] = (FMT == MOE_FMT_INT8_ROW) ? f16_to_f32(scale[e]) : 1.0f;
+    }
+    for (int t0 = t_lo; t0 < t_hi; t0 += G) {
+        // every activation load of the pass before the first fma
+        uint32_t xq[G][NV][XW];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint16_t* xt = x + (size_t)min(t0 + g, T - 1) * d;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int c0 = (lane + 64 * j) * PV;
+                if constexpr (PV == 4) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(xt + c0);
+                    xq[g][j][0] = v.x; xq[g][j][1] = v.y;
+                } else {
+                    const uint4* xp = reinterpret_cast<const uint4*>(xt + c0);
+                    const uint4 a = xp[0], bq = xp[1];
+                    xq[g][j][0] = a.x; xq[g][j][1] = a.y; xq[g][j][2] = a.z;
+                    xq[g][j][3] = a.w; xq[g][j][4] = bq.x; xq[g][j][5] = bq.y;
+                    xq[g][j][6] = bq.z; xq[g][j][7] = bq.w;
+                }
+            }
+        }
+        // acc[r * G + g]: row e0 + r, token t0 + g; NE x G chains, each in the GEMV's order
+        float acc[NE * G][1];
+#pragma unroll
+        for (int q = 0; q < NE * G; ++q) acc[q][0] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int i = 0; i < XW; ++i)
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float lo = bf16lo(xq[g][j][i]), hi = bf16hi(xq[g][j][i]);
+#pragma unroll
+                    for (int r = 0; r < NE; ++r) {
+                        float& a = acc[r * G + g][0];
+                        a = __builtin_fmaf(lo, w[r][j][2 * i], a);
+                        a = __builtin_fmaf(hi, w[r][j][2 * i + 1], a);
+                    }
+                }
+        // the butterflies of all NE x G chains at once (same tree, same bits); one lane
+        // per (row, token) finishes it
+        group_sum_many<64, NE * G, 1>(acc, lane);
+        const int q = tr_index<64, NE * G>(lane);
+        const int r = q / G, t = t0 + q % G;
+        float l = acc[0][0], bb = b[0], ss = se[0];
+#pragma unroll
+        for (int rr = 1; rr < NE; ++rr)
+            if (r == rr) {
+                bb = b[rr];
+                ss = se[rr];
+            }
+        if (tr_writer<64, NE * G>(lane) && t < t_hi && e0 + r < E) {
+            if constexpr (FMT == MOE_FMT_INT8_ROW) l = l * ss;
+            if (bias) l = l + bb;
+            logits[(size_t)t * E + e0 + r] = l;
+        }
+    }
 }
 
 // the selection kernels for T <= kRouteGemvMaxTokens; NORM: with the fused norm (one more
@@ -723,9 +807,10 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
         return launch_gemv_topk<FMT, NV, false>(r, x, T, k, ids, weights, logits, counter,
                                                 RouteNorm{}, s);
     if (T <= kRouteSplitMaxTokens) {   // one wave per expert row, then the selection kernel
+        constexpr int NE = SplitShape<FMT, NV>::NE;
         router_gemv_split_kernel<FMT, NV>
-            <<<dim3(E, (T + kRouteTokensPerWave - 1) / kRouteTokensPerWave), dim3(64), 0, s>>>(
-                r.w, r.scale, r.bias, x, T, E, d, logits);
+            <<<dim3((E + NE - 1) / NE, (T + kRouteTokensPerWave - 1) / kRouteTokensPerWave),
+               dim3(64), 0, s>>>(r.w, r.scale, r.bias, x, T, E, d, logits);
     } else {
         using R = RgShape<FMT>;
         constexpr int kLds = 2 * R::STAGE;
