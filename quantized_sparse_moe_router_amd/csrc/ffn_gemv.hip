@@ -22,8 +22,11 @@
 // is read instead of a ballot; a small kernel lists, expert by expert, chunks of at most MT
 // consecutive sorted positions with their tokens (sentinels fill the list to the grid's
 // size), and a slot is one chunk.  Each expert's rows are streamed once per chunk, four
-// rows per wave; a pair's arithmetic is the same in every mode, so its output bits do not
-// depend on the mode (or on the other pairs of the call).
+// rows per wave.  MT = kGemvSortedMT: larger chunks re-stream a hot expert's weights less
+// often, smaller ones keep the wave's registers (each token's activations) low enough for
+// more waves per SIMD and spread a hot expert over more blocks.  A pair's arithmetic is the
+// same in every mode, so its output bits do not depend on the mode (or on the other pairs of
+// the call).
 #include "gemv_common.h"
 
 namespace moe {

@@ -412,13 +412,14 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) sx[m][i] = group_sum_x(xv[m][i]);
 
-        // rows are taken RB at a time: acc[b * MT + m][mt] is this lane's part of row
-        // it0 + b's sum for token m, matrix mt; at most 16 sums are live, which keeps the
-        // sorted gate/up wave within 128 registers (4 waves per SIMD instead of 3)
-        constexpr int RB = (MT * NMAT * ITERS <= 16) ? ITERS
-                         : (16 / (MT * NMAT) >= 1 ? 16 / (MT * NMAT) : 1);
+        // rows are taken RB at a time: acc[b * MTP + m][mt] is this lane's part of row
+        // it0 + b's sum for token m, matrix mt (MTP: MT rounded up to a power of two for the
+        // reduction; the padding sums stay 0 and are not stored); at most 16 sums are live
+        constexpr int MTP = MT <= 1 ? 1 : MT <= 2 ? 2 : MT <= 4 ? 4 : 8;
+        constexpr int RB = (MTP * NMAT * ITERS <= 16) ? ITERS
+                         : (16 / (MTP * NMAT) >= 1 ? 16 / (MTP * NMAT) : 1);
         static_assert(ITERS % RB == 0, "row batches divide the rows");
-        constexpr int NR = RB * MT;
+        constexpr int NR = RB * MTP;
 #pragma unroll
         for (int it0 = 0; it0 < ITERS; it0 += RB) {
             float acc[NR][NMAT];
@@ -448,8 +449,8 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
                                 const float raw = dot_pairs(pr, xv[m][i]);
                                 const float part =
                                     __builtin_fmaf(-Fmt<FMT>::kBias, sx[m][i], raw);
-                                acc[b * MT + m][mt] =
-                                    __builtin_fmaf(s, part, acc[b * MT + m][mt]);
+                                acc[b * MTP + m][mt] =
+                                    __builtin_fmaf(s, part, acc[b * MTP + m][mt]);
                             }
                     }
             // the row sums over the row's LPR lanes, all (row, token) pairs of the batch at
@@ -461,8 +462,8 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
             const bool writer = tr_writer<LPR, NR>(lane);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int idx = idx0 + r, m = idx % MT;
-                const int row = row_base + (it0 + idx / MT) * RPW;
+                const int idx = idx0 + r, m = idx % MTP;
+                const int row = row_base + (it0 + idx / MTP) * RPW;
                 int orr = orow[0];
 #pragma unroll
                 for (int mm = 1; mm < MT; ++mm)

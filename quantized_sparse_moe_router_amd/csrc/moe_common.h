@@ -274,7 +274,7 @@ size_t permute_ws_bytes(int64_t P, int E);
 // (ids == nullptr): the token index, at most kGemvMaxBallotRows tokens.
 constexpr int64_t kGemvMaxBallotRows = 64;
 constexpr int64_t kGemvSortedMaxRows = 1024;
-constexpr int kGemvSortedMT = 4;    // pairs of one expert per pass over its weights
+constexpr int kGemvSortedMT = 3;    // pairs of one expert per pass over its weights
 struct GemvSortedWs {
     size_t h, chunks, bytes;
 };
