@@ -112,7 +112,11 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
     const float gate_w = a.weights[min((int)threadIdx.x, P - 1)];
     const uint16_t* res_src = a.residual ? a.residual : a.x;   // x: same shape, unused
     const uint16_t res_bits = res_src[(size_t)min(lane, a.T - 1) * D + row];
-    constexpr int kHPass = 2;
+    // chunks per thread requested up front: every chunk of h for the one-load-per-wave
+    // shapes (at most 1 024 chunks), three for the larger ones (44 slots at d_ff 512 -- four
+    // tokens with 10 experts and the shared one -- are 2 816 chunks), so that the staging
+    // costs one round trip
+    constexpr int kHPass = (ITB == DnShape<F>::ITB_SMALL) ? 1 : 3;
     const int n16 = S * F / 8;                    // 16-byte chunks of h
     // native 4-vectors: an array of HIP's uint4 struct is not kept in registers
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
