@@ -422,8 +422,8 @@ moe_status run_layer_decode(const moe_router* r, const moe_experts* routed,
     float* lg = reinterpret_cast<float*>(base + moe::kRouteCounterBytes);
     uint8_t* ffn_ws = base + round_up(route_exact_ws(T, E));
     hipError_t e;
-    if (T == 1) {
-        // logits only; every gate/up block selects the token's experts itself
+    if (T <= moe::kDecodeSelectMaxTokens) {
+        // logits only; every gate/up block selects its token's experts itself
         e = moe::launch_route_logits(*r, x, T, lg, s);
         if (e != hipSuccess) return hip_status(e, "moe_layer_decode: route");
         e = moe::launch_decode_ffn(*routed, shared, x, T, k, lg, ids, weights, residual,
@@ -587,12 +587,14 @@ moe_status moe_block_decode(const moe_norm* n, const moe_router* r, const moe_ex
     float* z = n->gate_w ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(xn) +
                                                     round_up((size_t)T * d * 2))
                          : nullptr;
-    // the router on xn = RMSNorm(x) (it writes xn and z); T == 1: logits only, every
-    // gate/up block selects; several tokens: the route kernel's last block selects
+    // the router on xn = RMSNorm(x) (it writes xn and z); up to kDecodeSelectMaxTokens
+    // tokens logits only, every gate/up block selects; more: the route kernel's last block
+    // selects
     hipError_t e = moe::launch_route_norm(*r, x, T, k, n->gamma, n->eps, n->gate_w, n->gate_b,
                                           xn, z, ids, weights, lg, counter, s);
     if (e != hipSuccess) return hip_status(e, "moe_block_decode: route");
-    e = moe::launch_decode_ffn(*routed, shared, xn, T, k, T == 1 ? lg : nullptr, ids, weights,
+    e = moe::launch_decode_ffn(*routed, shared, xn, T, k,
+                               T <= moe::kDecodeSelectMaxTokens ? lg : nullptr, ids, weights,
                                x, z, out, ffn_ws, s);
     return hip_status(e, "moe_block_decode");
 }

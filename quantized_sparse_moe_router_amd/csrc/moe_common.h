@@ -233,6 +233,9 @@ constexpr int kRouteGemvMaxTokens = 16;
 // Tokens up to which it computes the logits by GEMV (one wave per expert row, token groups)
 // and selects in a second kernel; above, the tiled GEMM (or the bounded form).
 constexpr int kRouteSplitMaxTokens = 64;
+// decode layer / block: up to this many tokens the router writes logits only and every
+// gate/up block selects its token's experts itself; above, the router's last block selects
+constexpr int kDecodeSelectMaxTokens = 1;
 
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
                         float* weights, float* logits, unsigned* counter, hipStream_t s);

@@ -975,7 +975,7 @@ hipError_t launch_route_norm(const moe_router& r, const uint16_t* x, int T, int 
                              uint16_t* xn, float* z, int32_t* ids, float* weights,
                              float* logits, unsigned* counter, hipStream_t s) {
     const RouteNorm nm{gamma, eps, gw, gb, xn, z};
-    if (T == 1) {   // logits only: the decode gate/up kernel selects
+    if (T <= kDecodeSelectMaxTokens) {   // logits only: the decode gate/up kernel selects
         if (r.fmt == MOE_FMT_INT8_ROW)
             return launch_logits_fmt<MOE_FMT_INT8_ROW, true>(r, x, T, logits, nm, s);
         return launch_logits_fmt<MOE_FMT_FP32, true>(r, x, T, logits, nm, s);
