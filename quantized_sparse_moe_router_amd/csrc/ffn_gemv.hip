@@ -79,11 +79,11 @@ __global__ void __launch_bounds__(1024) build_chunks_kernel(const int32_t* __res
     for (int i = total + tid; i < cap; i += 1024) chunks[2 * i] = make_int4(-1, 0, 0, 0);
 }
 
-// Slot of sorted mode: entry blockIdx.x of the list, or false for an empty entry.
+// Slot of sorted mode: entry blockIdx.y of the list, or false for an empty entry.
 __device__ __forceinline__ bool sorted_slot(const int4* chunks, Slot& sl) {
-    const int4 c = chunks[2 * blockIdx.x];
+    const int4 c = chunks[2 * blockIdx.y];
     if (c.x < 0) return false;
-    const int4 t = chunks[2 * blockIdx.x + 1];
+    const int4 t = chunks[2 * blockIdx.y + 1];
     sl.e = c.x;
     sl.members = 0;
     sl.seg0 = 0;
@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256) ffn_gateup_sorted_kernel(
     Slot sl;
     if (!sorted_slot(chunks, sl)) return;
     gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, MT>(wg, sg, wu, su, x, k, F,
-                                                                blockIdx.y, sl, h);
+                                                                blockIdx.x, sl, h);
 }
 
 template <int FMT, int D, int F, int MT>
@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(256) ffn_down_sorted_kernel(
     Slot sl;
     if (!sorted_slot(chunks, sl)) return;
     gemv_rows<FMT, kModeDown, DN::LPR, DN::GPL, DN::ITERS, MT>(wd, sd, nullptr, nullptr, h, k,
-                                                              D, blockIdx.y, sl, y);
+                                                              D, blockIdx.x, sl, y);
 }
 
 template <int FMT, int D, int F, int MT>
@@ -160,11 +160,14 @@ hipError_t launch_sorted_mt(const moe_experts& ex, const uint16_t* x, int T, int
     if (err != hipSuccess) return err;
     constexpr int n_gu = (F + SortedShape<D, FMT>::RPB - 1) / SortedShape<D, FMT>::RPB;
     constexpr int n_dn = (D + SortedShape<F, FMT>::RPB - 1) / SortedShape<F, FMT>::RPB;
-    ffn_gateup_sorted_kernel<FMT, D, F, MT><<<dim3(cap, n_gu), 256, 0, s>>>(
+    // grid (row block, chunk): with the row block fastest and a multiple of 8 row blocks,
+    // row block r always runs on XCD r % 8, so each XCD's L2 keeps its share of the rows of
+    // an expert that several chunks stream
+    ffn_gateup_sorted_kernel<FMT, D, F, MT><<<dim3(n_gu, cap), 256, 0, s>>>(
         ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, k, chunks, h);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    ffn_down_sorted_kernel<FMT, D, F, MT><<<dim3(cap, n_dn), 256, 0, s>>>(
+    ffn_down_sorted_kernel<FMT, D, F, MT><<<dim3(n_dn, cap), 256, 0, s>>>(
         ex.w_down, ex.s_down, h, k, chunks, y);
     return hipGetLastError();
 }
