@@ -95,7 +95,7 @@ __device__ __forceinline__ bool sorted_slot(const int4* chunks, Slot& sl) {
     return true;
 }
 
-// grid.x = slots, grid.y = row blocks
+// grid.x = row blocks, grid.y = slots
 template <int FMT, int D, int F, int MT>
 __global__ void __launch_bounds__(256) ffn_gateup_kernel(
     const uint8_t* __restrict__ wg, const uint16_t* __restrict__ sg,
@@ -104,9 +104,9 @@ __global__ void __launch_bounds__(256) ffn_gateup_kernel(
     uint16_t* __restrict__ h) {
     using GU = Shape<D>;   // gate/up rows have K = d_model
     Slot sl;
-    if (!resolve_slot<MT>(blockIdx.x, T, k, ids, E, sl)) return;
+    if (!resolve_slot<MT>(blockIdx.y, T, k, ids, E, sl)) return;
     gemv_rows<FMT, kModeGateUp, GU::LPR, GU::GPL, GU::ITERS, MT>(wg, sg, wu, su, x, k, F,
-                                                                blockIdx.y, sl, h);
+                                                                blockIdx.x, sl, h);
 }
 
 template <int FMT, int D, int F, int MT>
@@ -116,9 +116,9 @@ __global__ void __launch_bounds__(256) ffn_down_kernel(
     uint16_t* __restrict__ y) {
     using DN = Shape<F>;   // down rows have K = d_ff
     Slot sl;
-    if (!resolve_slot<MT>(blockIdx.x, T, k, ids, E, sl)) return;
+    if (!resolve_slot<MT>(blockIdx.y, T, k, ids, E, sl)) return;
     gemv_rows<FMT, kModeDown, DN::LPR, DN::GPL, DN::ITERS, MT>(wd, sd, nullptr, nullptr, h, k,
-                                                              D, blockIdx.y, sl, y);
+                                                              D, blockIdx.x, sl, y);
 }
 
 template <int FMT, int D, int F, int MT>
@@ -178,11 +178,13 @@ hipError_t launch_mt(const moe_experts& ex, const uint16_t* x, int T, int k, con
     const int nslots = ids ? T * k : (T + MT - 1) / MT;
     constexpr int n_gu = (F + Shape<D>::RPB - 1) / Shape<D>::RPB;
     constexpr int n_dn = (D + Shape<F>::RPB - 1) / Shape<F>::RPB;
-    ffn_gateup_kernel<FMT, D, F, MT><<<dim3(nslots, n_gu), 256, 0, s>>>(
+    // grid (row block, slot), the row block fastest: row block r on XCD r % 8, so slots
+    // that stream the same expert (the dense mode's token chunks) find its rows in that L2
+    ffn_gateup_kernel<FMT, D, F, MT><<<dim3(n_gu, nslots), 256, 0, s>>>(
         ex.w_gate, ex.s_gate, ex.w_up, ex.s_up, x, T, k, ids, ex.n_experts, h);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    ffn_down_kernel<FMT, D, F, MT><<<dim3(nslots, n_dn), 256, 0, s>>>(
+    ffn_down_kernel<FMT, D, F, MT><<<dim3(n_dn, nslots), 256, 0, s>>>(
         ex.w_down, ex.s_down, h, T, k, ids, ex.n_experts, y);
     return hipGetLastError();
 }
