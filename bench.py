@@ -16,6 +16,7 @@ Also reported in the same line:
                   packed weights and scales, activations in and out) / their event-timed
                   average duration vs 8 TB/s
   decode_batches  1..128 tokens per call (several decode slots, or drafts verified together)
+  decode_batches_zipf  16..128 tokens per call with Zipf-skewed routing (hot experts)
   decode_low_bit  the decode layer with int4 / int3 / int2 experts at 1, 16 and 64 tokens
   mall_residency  what the 256 MB cache in front of HBM gives: stream reads cold and warm,
                   a Zipf-routed decode cycling over 1..32 layer copies
@@ -339,6 +340,15 @@ def main():
             moe, synth, np, torch, copies, w, args,
             Ts=tuple(int(t) for t in args.batch_sizes.split(",") if t.strip()))
         torch.cuda.empty_cache()
+        # the same with the router's bias skewing the routing (Zipf, s = 1.1): fewer distinct
+        # experts, some chosen by many of the call's tokens
+        zbase = synth.make_layer(w, seed=0, device="cuda", bias="zipf")
+        zcopies = [zbase] + [clone_layer(zbase) for _ in range(L - 1)]
+        line["decode_batches_zipf"] = decode_batches(
+            moe, synth, np, torch, zcopies, w, args, Ts=(16, 32, 64, 96, 128))
+        line["decode_batches_zipf"]["routing"] = "zipf s=1.1 (router bias)"
+        del zbase, zcopies
+        torch.cuda.empty_cache()
 
     # ---- lower-bit expert codecs: the same decode step with every expert at 3 or 2 bits
     if not args.no_low_bit:
@@ -522,9 +532,9 @@ def decode_batches(moe, synth, np, torch, copies, w, args, Ts=(1, 4, 6, 8, 16, 3
     """T tokens per call through the decode layer (d 2048, 512 experts, top-10 + shared),
     T = 1 .. 128: the four calls (forward) and, while T*k <= 64, moe_layer_decode; each step
     on the next of the rotated layer copies (more than the 256 MB cache holds for T >= 2).
-    Up to 1024 pairs the routed experts run the weight-streaming GEMV (sorted mode past 64
-    pairs), above it the grouped MFMA GEMM.  Weight-stream bytes: router + (distinct routed
-    experts + shared) x 1.77 MB."""
+    Up to 4096 pairs the routed experts run the weight-streaming GEMV (sorted mode past 64
+    pairs; from 640 pairs the experts with many pairs on the grouped MFMA GEMM), above it the
+    GEMM alone.  Weight-stream bytes: router + (distinct routed experts + shared) x 1.77 MB."""
     E_b = expert_bytes(copies[0].routed)
     r_b = copies[0].router.w.numel() * copies[0].router.w.element_size()
     n_cp = len(copies)

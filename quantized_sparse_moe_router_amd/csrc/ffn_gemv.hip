@@ -35,39 +35,54 @@ namespace {
 // Chunk list of sorted mode: for every expert e with n pairs, ceil(n / MT) entries of two
 // int4, (e, first sorted position q0, pairs in the chunk, 0) and the tokens of its pairs
 // (the last repeated); entries from the list's end up to cap hold e = -1, so a block
-// learns from its own entry alone whether it has work.  One block, E <= 1024.
+// learns from its own entry alone whether it has work.  Split call (hot > 0): an expert with
+// hot pairs or more gets no chunks but entries of the grouped GEMM's work list instead
+// (kMfmaTileRows pairs each: (e, first position, end of e's positions, 0)) and the list's
+// length goes to *tile_count.  One block, E <= 1024.
 __global__ void __launch_bounds__(1024) build_chunks_kernel(const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ sorted,
-                                                            int E, int k, int MT, int cap,
-                                                            int4* __restrict__ chunks) {
-    __shared__ int part[16];
+                                                            int E, int k, int MT, int hot,
+                                                            int cap, int4* __restrict__ chunks,
+                                                            int4* __restrict__ tiles,
+                                                            int* __restrict__ tile_count) {
+    __shared__ int part[2][16];
     __shared__ int total;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    int b = 0, n = 0, cnt = 0;
+    int b = 0, n = 0, cnt = 0, tcnt = 0;
     if (tid < E) {
         b = offsets[tid];
         n = offsets[tid + 1] - b;
-        cnt = (n + MT - 1) / MT;
+        if (hot > 0 && n >= hot)
+            tcnt = (n + kMfmaTileRows - 1) / kMfmaTileRows;
+        else
+            cnt = (n + MT - 1) / MT;
     }
-    int incl = cnt;
+    int incl = cnt, tincl = tcnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
+        const int o = __shfl_up(incl, off, 64), to = __shfl_up(tincl, off, 64);
+        if (lane >= off) {
+            incl += o;
+            tincl += to;
+        }
     }
-    if (lane == 63) part[wv] = incl;
+    if (lane == 63) {
+        part[0][wv] = incl;
+        part[1][wv] = tincl;
+    }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < 2) {
         int run = 0;
         for (int i = 0; i < 16; ++i) {
-            const int v = part[i];
-            part[i] = run;
+            const int v = part[tid][i];
+            part[tid][i] = run;
             run += v;
         }
-        total = run;
+        if (tid == 0) total = run;
+        else if (tile_count) *tile_count = run;
     }
     __syncthreads();
-    const int start = incl - cnt + part[wv];
+    const int start = incl - cnt + part[0][wv];
     for (int i = 0; i < cnt; ++i) {
         const int q0 = b + i * MT, sn = min(MT, n - i * MT);
         int t[4];
@@ -76,6 +91,9 @@ __global__ void __launch_bounds__(1024) build_chunks_kernel(const int32_t* __res
         chunks[2 * (start + i)] = make_int4(tid, q0, sn, 0);
         chunks[2 * (start + i) + 1] = make_int4(t[0], t[1], t[2], t[3]);
     }
+    const int tstart = tincl - tcnt + part[1][wv];
+    for (int i = 0; i < tcnt; ++i)
+        tiles[tstart + i] = make_int4(tid, b + i * kMfmaTileRows, b + n, 0);
     for (int i = total + tid; i < cap; i += 1024) chunks[2 * i] = make_int4(-1, 0, 0, 0);
 }
 
@@ -155,7 +173,12 @@ hipError_t launch_sorted_mt(const moe_experts& ex, const uint16_t* x, int T, int
     uint16_t* h = reinterpret_cast<uint16_t*>(base + L.h);
     int4* chunks = reinterpret_cast<int4*>(base + L.chunks);
     const int cap = (int)gemv_sorted_chunk_capacity((int64_t)T * k, ex.n_experts);
-    build_chunks_kernel<<<1, 1024, 0, s>>>(offsets, sorted, ex.n_experts, k, MT, cap, chunks);
+    const int hot = gemv_hot_rows((int64_t)T * k);
+    int4* tiles = reinterpret_cast<int4*>(base + L.tiles);
+    int* tile_count = reinterpret_cast<int*>(base + L.count);
+    build_chunks_kernel<<<1, 1024, 0, s>>>(offsets, sorted, ex.n_experts, k, MT, hot, cap,
+                                           chunks, hot > 0 ? tiles : nullptr,
+                                           hot > 0 ? tile_count : nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     constexpr int n_gu = (F + SortedShape<D, FMT>::RPB - 1) / SortedShape<D, FMT>::RPB;
@@ -169,7 +192,10 @@ hipError_t launch_sorted_mt(const moe_experts& ex, const uint16_t* x, int T, int
     if (err != hipSuccess) return err;
     ffn_down_sorted_kernel<FMT, D, F, MT><<<dim3(n_dn, cap), 256, 0, s>>>(
         ex.w_down, ex.s_down, h, k, chunks, y);
-    return hipGetLastError();
+    err = hipGetLastError();
+    if (err != hipSuccess || hot == 0) return err;
+    // the experts with `hot` pairs or more: the grouped GEMM, on the same h and y
+    return launch_ffn_mfma_hot(ex, x, T, k, sorted, y, h, tiles, tile_count, L.tile_cap, s);
 }
 
 template <int FMT, int D, int F, int MT>
@@ -227,9 +253,26 @@ bool ffn_gemv_has_shape(int d, int F) {
            (d == 4096 && F == 1024) || (d == 1024 && F == 512);
 }
 
+// Pairs from which an expert goes to the grouped GEMM (0: the whole call on the GEMV).  The
+// GEMM's fixed cost per tile (a few microseconds of prologue and epilogue, and a launch
+// after the GEMV's) pays off only when enough pairs share few experts: measured with spread
+// and Zipf routing at 16 to 192 tokens of top-10 over 512 experts.
+int gemv_hot_rows(int64_t rows) {
+    if (rows < kHybridMinRows) return 0;
+    return rows <= 1024 ? 8 : 4;
+}
+
+// chunks of the GEMV's experts: at most one per pair, one per kGemvSortedMT pairs plus one
+// per expert, and (split call) ceil((hot - 1) / kGemvSortedMT) per expert
 size_t gemv_sorted_chunk_capacity(int64_t rows, int E) {
-    const int64_t c = (rows + kGemvSortedMT - 1) / kGemvSortedMT + E;
-    return (size_t)(c < rows ? c : rows);
+    int64_t c = (rows + kGemvSortedMT - 1) / kGemvSortedMT + E;
+    c = c < rows ? c : rows;
+    const int hot = gemv_hot_rows(rows);
+    if (hot > 0) {
+        const int64_t per_e = (int64_t)E * ((hot - 1 + kGemvSortedMT - 1) / kGemvSortedMT);
+        c = c < per_e ? c : per_e;
+    }
+    return (size_t)c;
 }
 
 GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F) {
@@ -238,6 +281,10 @@ GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F) {
     size_t off = 0;
     w.h = off; off += al((size_t)rows * F * 2);
     w.chunks = off; off += al(gemv_sorted_chunk_capacity(rows, E) * 2 * sizeof(int4));
+    const int hot = gemv_hot_rows(rows);
+    w.tile_cap = hot > 0 ? ffn_mfma_hot_tile_capacity(rows, E, hot) : 0;
+    w.tiles = off; off += al(w.tile_cap * sizeof(int4));
+    w.count = off; off += al(sizeof(int));
     w.bytes = off;
     return w;
 }

@@ -32,12 +32,13 @@
 // compiler does not track LDS written by these loads.
 #include "mfma_common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
 namespace {
 
-constexpr int BM = 256;          // rows (pairs) per tile
+constexpr int BM = kMfmaTileRows;   // rows (pairs) per tile
 constexpr int BN = 256;          // output columns per tile (gate/up: 128 f x 2)
 constexpr int NW = 4;            // waves per block
 constexpr int NT = 64 * NW;      // threads per block
@@ -469,25 +470,20 @@ __global__ void __launch_bounds__(NT, 1) grouped_gemm_kernel(
     }
 }
 
+// grouped: tiles / count hold the work list (capacity tile_cap, a multiple of kXcds; built
+// here from offsets when offsets is given); dense: tiles == nullptr
 template <int FMT>
-hipError_t launch_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
-                      const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
-                      void* ws, hipStream_t s) {
+hipError_t launch_gemm_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
+                           const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
+                           uint16_t* h, const int4* tiles, const int* count, size_t tile_cap,
+                           hipStream_t s) {
     const int d = ex.d_model, F = ex.d_ff, E = ex.n_experts;
-    const bool grouped = offsets != nullptr;
-    const int64_t rows = grouped ? (int64_t)T * k : (int64_t)T;
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    uint16_t* h = reinterpret_cast<uint16_t*>(base);
-    size_t off = ((size_t)rows * F * 2 + 255) & ~size_t(255);
-    int4* tiles = nullptr;
-    int* count = nullptr;
     int gx;
-    if (grouped) {
-        tiles = reinterpret_cast<int4*>(base + off);
-        off += (tile_capacity(rows, E) * sizeof(int4) + 255) & ~size_t(255);
-        count = reinterpret_cast<int*>(base + off);
-        build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, tiles, count);
-        gx = (int)tile_capacity(rows, E);
+    if (tiles) {
+        if (offsets)
+            build_tiles_kernel<<<1, 1024, 0, s>>>(offsets, E, const_cast<int4*>(tiles),
+                                                  const_cast<int*>(count));
+        gx = (int)tile_cap;
     } else {
         gx = (T + BM - 1) / BM;
     }
@@ -519,7 +515,55 @@ hipError_t launch_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
     return hipGetLastError();
 }
 
+template <int FMT>
+hipError_t launch_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
+                      const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
+                      void* ws, hipStream_t s) {
+    const int E = ex.n_experts, F = ex.d_ff;
+    const bool grouped = offsets != nullptr;
+    const int64_t rows = grouped ? (int64_t)T * k : (int64_t)T;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base);
+    size_t off = ((size_t)rows * F * 2 + 255) & ~size_t(255);
+    int4* tiles = nullptr;
+    int* count = nullptr;
+    if (grouped) {
+        tiles = reinterpret_cast<int4*>(base + off);
+        off += (tile_capacity(rows, E) * sizeof(int4) + 255) & ~size_t(255);
+        count = reinterpret_cast<int*>(base + off);
+    }
+    return launch_gemm_fmt<FMT>(ex, x, T, k, offsets, sorted_pairs, y, h, tiles, count,
+                                grouped ? tile_capacity(rows, E) : 0, s);
+}
+
 }  // namespace
+
+// tiles of the experts with at least min_rows >= 1 of rows pairs: at most ceil(rows / BM)
+// plus one per such expert, rounded up to whole XCD groups
+size_t ffn_mfma_hot_tile_capacity(int64_t rows, int E, int min_rows) {
+    const int64_t experts = std::min<int64_t>(E, rows / std::max(min_rows, 1));
+    const size_t n = (size_t)((rows + BM - 1) / BM + experts);
+    return (n + kXcds - 1) / kXcds * kXcds;
+}
+
+hipError_t launch_ffn_mfma_hot(const moe_experts& ex, const uint16_t* x, int T, int k,
+                               const int32_t* sorted_pairs, uint16_t* y, uint16_t* h,
+                               const int4* tiles, const int* count, size_t tile_cap,
+                               hipStream_t s) {
+    switch (ex.fmt) {
+#define MOE_HOT(F)                                                                        \
+        case F:                                                                           \
+            return launch_gemm_fmt<F>(ex, x, T, k, nullptr, sorted_pairs, y, h, tiles,     \
+                                      count, tile_cap, s);
+        MOE_HOT(MOE_FMT_INT4_G32)
+        MOE_HOT(MOE_FMT_INT6_G32)
+        MOE_HOT(MOE_FMT_INT3_G32)
+        MOE_HOT(MOE_FMT_INT2_G32)
+#undef MOE_HOT
+        default:
+            return hipErrorNotSupported;
+    }
+}
 
 size_t ffn_mfma_ws_bytes(int64_t rows, int E, int F) {
     size_t n = ((size_t)rows * F * 2 + 255) & ~size_t(255);

@@ -273,13 +273,20 @@ size_t permute_ws_bytes(int64_t P, int E);
 
 // Small calls: weight-streaming GEMV, gate/up then down.  Up to kGemvMaxBallotRows pairs
 // the positions come from ids alone (a ballot; ws = [h]); above, up to kGemvSortedMaxRows,
-// from the grouping (offsets, sorted_pairs; ws = gemv_sorted_ws_layout).  Dense mode
+// from the grouping (offsets, sorted_pairs; ws = gemv_sorted_ws_layout).  From
+// kHybridMinRows pairs the call is split by expert: an expert with fewer than
+// gemv_hot_rows(rows) pairs runs the GEMV in sorted mode, one with more the grouped MFMA
+// GEMM (its weights streamed once per 256 pairs instead of once per chunk).  Dense mode
 // (ids == nullptr): the token index, at most kGemvMaxBallotRows tokens.
 constexpr int64_t kGemvMaxBallotRows = 64;
-constexpr int64_t kGemvSortedMaxRows = 1024;
+constexpr int64_t kGemvSortedMaxRows = 4096;
 constexpr int kGemvSortedMT = 3;    // pairs of one expert per pass over its weights
+constexpr int64_t kHybridMinRows = 640;
+constexpr int kMfmaTileRows = 256;  // pairs per entry of the grouped GEMM's work list
+int gemv_hot_rows(int64_t rows);    // 0: no split
 struct GemvSortedWs {
-    size_t h, chunks, bytes;
+    size_t h, chunks, tiles, count, bytes;
+    size_t tile_cap;       // entries of the MFMA work list (hot experts)
 };
 size_t gemv_sorted_chunk_capacity(int64_t rows, int E);
 GemvSortedWs gemv_sorted_ws_layout(int64_t rows, int E, int F);
@@ -292,6 +299,16 @@ hipError_t launch_ffn_mfma(const moe_experts& ex, const uint16_t* x, int T, int 
                            const int32_t* offsets, const int32_t* sorted_pairs, uint16_t* y,
                            void* ws, hipStream_t s);
 size_t ffn_mfma_ws_bytes(int64_t rows, int E, int F);
+// the grouped GEMM for the experts with at least min_rows pairs only, on caller-placed
+// buffers: h [rows][d_ff], a work list of tile_cap entries (ffn_mfma_hot_tile_capacity) and
+// its count
+// (the list already built: entries (e, first sorted position, end of e's positions, 0) of
+// at most kMfmaTileRows pairs, then the count)
+size_t ffn_mfma_hot_tile_capacity(int64_t rows, int E, int min_rows);
+hipError_t launch_ffn_mfma_hot(const moe_experts& ex, const uint16_t* x, int T, int k,
+                               const int32_t* sorted_pairs, uint16_t* y, uint16_t* h,
+                               const int4* tiles, const int* count, size_t tile_cap,
+                               hipStream_t s);
 
 // z: residual-gate logits [T] or null
 hipError_t launch_combine(const uint16_t* y_pairs, const int32_t* pair_pos, const float* w,
