@@ -75,7 +75,8 @@ size_t route_ws(int64_t T, int E, int d, bool need_logits) {
     return n;
 }
 
-// expert FFN workspace: GEMV [h], or in sorted mode [h][chunk list]; MFMA [h][tile list][count]
+// expert FFN workspace: GEMV [h], or in sorted mode [h][chunk list][GEMM work list][count];
+// MFMA [h][tile list][count]
 size_t ffn_ws(int64_t rows, int E, int F) {
     size_t gemv = round_up((size_t)rows * (size_t)F * 2);
     if (rows > moe::kGemvMaxBallotRows) gemv = moe::gemv_sorted_ws_layout(rows, E, F).bytes;
