@@ -172,10 +172,10 @@ moe_status moe_rmsnorm(const moe_norm* n, const uint16_t* x, int32_t T, int32_t 
  * butterfly with offsets 1, 2, 4, ..., 32; then + bias (FP32), or
  * fl(fl(sum * scale) + bias) (INT8_ROW).  ids and weights are always those of these
  * logits.  How they are reached:
- *   T <= 16: logits and selection in one launch (the last block to finish its rows
+ *   T <= 4: logits and selection in one launch (the last block to finish its rows
  *            selects);
- *   16 < T <= 64: the same one-wave-per-expert-row logits (tokens four at a time), then
- *            a selection kernel (a wave per token);
+ *   4 < T <= 64: the same one-wave-per-expert-row logits (eight tokens and up to two
+ *            rows per wave), then a selection kernel (a wave per token);
  *   T > 64, logits requested: an LDS-tiled fp32 GEMM in the fixed order, then selection;
  *   T > 64, logits NULL (the bounded form): bf16 MFMA logits (FP32 rows split exactly
  *            into two bf16 parts plus a dropped remainder below 2^-17 of the weight)

@@ -803,7 +803,7 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
                      float* weights, float* logits, unsigned* counter, hipStream_t s) {
     const int E = r.n_experts, d = r.d_model;
     const int npl = (E + 63) / 64;
-    if (T <= kRouteGemvMaxTokens)   // one wave per expert row, selection by the last block
+    if (T <= kRouteOneLaunchMaxTokens)   // one wave per expert row, the last block selects
         return launch_gemv_topk<FMT, NV, false>(r, x, T, k, ids, weights, logits, counter,
                                                 RouteNorm{}, s);
     if (T <= kRouteSplitMaxTokens) {   // one wave per expert row, then the selection kernel

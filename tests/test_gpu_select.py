@@ -6,7 +6,8 @@ construct routers whose logits tie a lot: rows drawn from a handful of distinct 
 (many exact ties; more candidates than the fast form's compaction holds), integer-valued
 weights and activations (exact sums with occasional ties), and an all-zero router (every
 logit equal: ids 0..k-1, weights 1/k).  Each case runs every place the selection runs:
-moe_route for few tokens (one launch), moe_route for many tokens with logits requested
+moe_route for up to 4 tokens (one launch) and for 6 or 40 (logits, then a selection
+kernel), moe_route for many tokens with logits requested
 (fixed-order GEMM) and without (MFMA logits with an error bound, exact recomputation of
 the experts the bound cannot rule out), and the gate/up kernel of moe_layer_decode; all
 must agree with the oracle and with each other, weights bit for bit.
