@@ -180,6 +180,7 @@ __device__ __forceinline__ void down_rows_combine(const DecodeArgs& a, int r0, i
                 }
                 const float sx = sx_lds[s * NGRP + g];
                 const float sc = f16_to_f32(sbits[q][i]);
+                if constexpr (kPairInRegisters<FMT>) pair_in_registers<FMT>(xv);
                 const float raw = dot_bits<FMT>(wbits[q][i], xv);
                 const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx, raw);
                 acc[q] = __builtin_fmaf(sc, part, acc[q]);

@@ -93,38 +93,77 @@ __device__ __forceinline__ void pairs_int6(const uint32_t* w6, uint32_t* pr) {
     }
 }
 
-// int3: 12 bytes, a little-endian bit string; pair p = codes 2p, 2p + 1 = the 6 bits at 6p.
+// int3: 12 bytes, a little-endian bit string, code i at bits 3i..3i+2; pair i = codes
+// (i, i + 16), i = 0..15.  With A = the string and B = the string from bit 48 on, code i is
+// bits 3i of A and code i + 16 bits 3i of B: a word holding 16 bits of A in its low half
+// and the same 16 bits of B in its high half (one v_perm_b32) gives five pairs, each with
+// one shift and one v_and_or_b32.  The activations come in int3_pairs16 order.
 __device__ __forceinline__ void pairs_int3(const uint32_t* w3, uint32_t* pr) {
-    const uint64_t lo64 = (uint64_t)w3[0] | ((uint64_t)w3[1] << 32);
-    const uint32_t hi32 = w3[2];
+    uint32_t mask, bias;
+    asm("s_mov_b32 %0, 0x00070007" : "=s"(mask));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(bias));
+    const uint32_t d0 = w3[0], d1 = w3[1], d2 = w3[2];
+    const uint32_t b_lo = __builtin_amdgcn_alignbit(d2, d1, 16);   // string bits 48..79
+    const uint32_t b_hi = d2 >> 16;                                 // string bits 80..95
+    // window k: bits 15k .. 15k + 15 of A and of B (codes 5k .. 5k + 4 and their partners)
+    const uint32_t a_w[4] = {d0, __builtin_amdgcn_alignbit(d1, d0, 15),
+                             __builtin_amdgcn_alignbit(d1, d0, 30), d1 >> 13};
+    const uint32_t b_w[4] = {b_lo, __builtin_amdgcn_alignbit(b_hi, b_lo, 15),
+                             __builtin_amdgcn_alignbit(b_hi, b_lo, 30), b_hi >> 13};
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        uint32_t u[2];
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t q = __builtin_amdgcn_perm(b_w[k], a_w[k], 0x05040100u);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int bit = 3 * (2 * p + s);              // bit inside the 96 bits
-            uint32_t v;
-            if (bit + 3 <= 64)
-                v = (uint32_t)(lo64 >> bit);
-            else if (bit >= 64)
-                v = hi32 >> (bit - 64);
-            else
-                v = (uint32_t)(lo64 >> bit) | (hi32 << (64 - bit));
-            u[s] = v & 7u;
-        }
-        pr[p] = (u[0] | (u[1] << 16)) | 0x43004300u;
+        for (int p = 0; p < 5 && 5 * k + p < 16; ++p) pr[5 * k + p] = ((q >> (3 * p)) & mask) | bias;
     }
 }
 
-// int2: 8 bytes, code i at bits [2i, 2i+2); pair p = codes 2p, 2p + 1 = the nibble at 4p of
-// its word.
+// int2: 8 bytes, code i at bits 2i..2i+1 (word i / 16); pair 8w + j = codes (16w + j,
+// 16w + j + 8), the 2-bit fields 16 bits apart in word w: one shift and one v_and_or_b32.
+// The activations come in int2_pairs16 order.
 __device__ __forceinline__ void pairs_int2(const uint32_t* w2, uint32_t* pr) {
+    uint32_t mask, bias;
+    asm("s_mov_b32 %0, 0x00030003" : "=s"(mask));
+    asm("v_mov_b32 %0, 0x43004300" : "=v"(bias));
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        const uint32_t w = w2[p / 8];
-        const int o = 4 * (p % 8);
-        pr[p] = ((w >> o) & 3u) | (((w >> (o + 2)) & 3u) << 16) | 0x43004300u;
-    }
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pr[8 * w + j] = ((w2[w] >> (2 * j)) & mask) | bias;
+}
+
+// Activation pairs in the order pairs_int3 takes the codes: pair i = (x_i, x_{i + 16}).
+// xp: the group's 16 pairs in natural order, (x0, x1) .. (x30, x31).
+__device__ __forceinline__ void int3_pairs16(uint32_t* xp) {
+    uint32_t o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        o[i] = __builtin_amdgcn_perm(xp[8 + i / 2], xp[i / 2], (i & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xp[i] = o[i];
+}
+
+// ... in the order pairs_int2 takes them: pair 8w + j = (x_{16w + j}, x_{16w + j + 8}).
+__device__ __forceinline__ void int2_pairs16(uint32_t* xp) {
+    uint32_t o[16];
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            o[8 * w + j] = __builtin_amdgcn_perm(xp[8 * w + 4 + j / 2], xp[8 * w + j / 2],
+                                                 (j & 1) ? 0x07060302u : 0x05040100u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xp[i] = o[i];
+}
+
+// int3 and int2 activations are put in pair order in registers, after the group's sum has
+// been taken in natural order (int4 ones are stored in pair order where they are staged, and
+// summed in that order; int6 pairs are neighbours)
+template <int FMT>
+constexpr bool kPairInRegisters = FMT == MOE_FMT_INT3_G32 || FMT == MOE_FMT_INT2_G32;
+template <int FMT>
+__device__ __forceinline__ void pair_in_registers(uint32_t* xp) {
+    if constexpr (FMT == MOE_FMT_INT3_G32) int3_pairs16(xp);
+    else if constexpr (FMT == MOE_FMT_INT2_G32) int2_pairs16(xp);
 }
 
 // sum_i (128 + u_i) * x_i over a group: 16 v_dot2_f32_bf16, pair by pair in ascending order.
@@ -411,6 +450,13 @@ __device__ __forceinline__ void gemv_rows(const uint8_t* __restrict__ wa,
             if (m < mcount)
 #pragma unroll
                 for (int i = 0; i < GPL; ++i) sx[m][i] = group_sum_x(xv[m][i]);
+        if constexpr (kPairInRegisters<FMT>) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (m < mcount)
+#pragma unroll
+                    for (int i = 0; i < GPL; ++i) pair_in_registers<FMT>(xv[m][i]);
+        }
 
         // rows are taken RB at a time: acc[b * MTP + m][mt] is this lane's part of row
         // it0 + b's sum for token m, matrix mt (MTP: MT rounded up to a power of two for the

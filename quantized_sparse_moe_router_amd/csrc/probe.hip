@@ -40,6 +40,11 @@ __global__ void __launch_bounds__(256) probe_gemv_kernel(const uint8_t* __restri
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xp[i]));
         const float sx = group_sum_x(xp);
+        if constexpr (kPairInRegisters<FMT>) {
+            pair_in_registers<FMT>(xp);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(xp[i]));
+        }
         const float raw = dot_bits<FMT>(bits, xp);
         const float part = __builtin_fmaf(-Fmt<FMT>::kBias, sx, raw);
         out[g * 32 + c] = __builtin_fmaf(sc, part, 0.0f);
