@@ -756,6 +756,20 @@ def cpu_baseline(base, toks, w, seconds, prefill_every=64):
     pw = synth.WORKLOADS["prefill_8192_zipf"]
     lay = synth.make_layer(pw, seed=0, device="cuda")
     xp = si.bits16(synth.make_tokens(pw, seed=0, device="cuda"))
+    # the router's fp32 audit: tokens whose top-k set another valid fp32 summation order
+    # could change (exact logits within twice / once the rigorous rounding bound across the
+    # cut), and tokens whose fixed-order selection differs from the exact one
+    t = time.perf_counter()
+    audit = {}
+    for name, rr, xx, kk in (("decode_tokens", r_h, x_h, w.k),
+                             ("prefill_8192_zipf", lay.router.host(), xp, pw.k)):
+        a2 = oracle.router_tie_audit(rr, xx, kk, factor=2.0)
+        a1 = oracle.router_tie_audit(rr, xx, kk, factor=1.0)
+        audit[name] = {"tokens": int(xx.shape[0]), "within_2x_bound": a2["count"],
+                       "within_1x_bound": a1["count"],
+                       "fp32_selection_differs_from_exact": a1["differs"]}
+    audit["seconds"] = round(time.perf_counter() - t, 1)
+    out["router_tie_audit"] = audit
     sel = np.arange(0, pw.T, prefill_every, dtype=np.int32)
     oracle.set_num_threads(1)
     try:

@@ -345,3 +345,74 @@ def num_threads():
 
 def set_num_threads(n):
     lib().oracle_set_num_threads(int(n))
+
+
+# ---------------------------------------------------------------- fp32 error audit of the router
+
+def _bf16_bits_to_f64(x_bits):
+    x = _c(x_bits, np.uint16).astype(np.uint32) << 16
+    return x.view(np.float32).astype(np.float64)
+
+
+def router_error_bound(router, x_bits):
+    """Rigorous bound [T][E] on |fp32 logit - exact logit| for any summation order whose
+    every product passes through at most m roundings.
+
+    The fixed fp32 order gives each product term one fma rounding per remaining step of its
+    lane's chain (d/64 of them at most), 6 butterfly additions and the bias addition; the
+    int8 form adds the rounding of the product with the row scale.  Error analysis of
+    summation (Higham, Accuracy and Stability of Numerical Algorithms, Lemma 3.1 and
+    section 3.1): |fl - exact| <= gamma_m * (sum_c |x_c w_c| * |s| + |b|), gamma_m =
+    m u / (1 - m u), u = 2^-24, with m = d/64 + 7 (fp32) or d/64 + 8 (int8).  The sum of
+    absolute terms is taken in double (products of a bf16 and an fp32 or int8 value are
+    exact there; the non-negative sum is inflated by its own fp64 bound)."""
+    x = _bf16_bits_to_f64(x_bits)
+    d = int(router["d"])
+    if int(router["fmt"]) == FMT_INT8_ROW:
+        w = np.abs(_c(router["w"], np.int8).astype(np.float64).reshape(-1, d))
+        s = np.array([half_to_double(h) for h in _c(router["scale"], np.uint16)])
+        m = d // 64 + 8
+    else:
+        w = np.abs(_c(router["w"], np.float32).astype(np.float64).reshape(-1, d))
+        s = np.ones(w.shape[0])
+        m = d // 64 + 7
+    a = (np.abs(x) @ w.T) * (1.0 + (d + 1) * 2.0 ** -52) * np.abs(s)[None, :]
+    b = router.get("bias")
+    if b is not None:
+        a = a + np.abs(_c(b, np.float32).astype(np.float64))[None, :]
+    u = 2.0 ** -24
+    return (m * u / (1.0 - m * u)) * a
+
+
+def router_tie_audit(router, x_bits, k, factor=2.0):
+    """Tokens whose top-k set another valid fp32 summation order could change.
+
+    With exact logits l (the fp64 audit copy) and bounds B (router_error_bound, scaled by
+    `factor`), a token is flagged when some expert inside the exact top-k and some expert
+    outside it have overlapping intervals: min over selected (l - B) <= max over the
+    others (l + B).  Exactly tied logits are always flagged.  The fixed-order fp32 logits
+    still decide one selection; the flag says where only that fixed order makes it unique.
+    Also compares the selection made on the fixed-order fp32 logits (select_topk) with the
+    exact top-k set: where they differ the two intervals must overlap at factor 1.
+    Returns {flags [T] bool, count, margin [T], fp32_set_differs [T] bool, differs} with
+    margin = min(l - B) - max(l + B)."""
+    l64 = router_logits_fp64(router, x_bits)
+    bnd = factor * router_error_bound(router, x_bits)
+    T, E = l64.shape
+    if k >= E:
+        z = np.zeros(T, bool)
+        return {"flags": z, "count": 0, "margin": np.full(T, np.inf),
+                "fp32_set_differs": z, "differs": 0}
+    order = np.argsort(-l64, axis=1, kind="stable")
+    sel = np.zeros((T, E), bool)
+    np.put_along_axis(sel, order[:, :k], True, axis=1)
+    lo = np.where(sel, l64 - bnd, np.inf).min(axis=1)
+    hi = np.where(sel, -np.inf, l64 + bnd).max(axis=1)
+    margin = lo - hi
+    flags = margin <= 0.0
+    sel32 = np.zeros((T, E), bool)
+    np.put_along_axis(sel32, select_topk(router_logits(router, x_bits), k).astype(np.int64),
+                      True, axis=1)
+    differs = (sel32 != sel).any(axis=1)
+    return {"flags": flags, "count": int(flags.sum()), "margin": margin,
+            "fp32_set_differs": differs, "differs": int(differs.sum())}

@@ -249,6 +249,124 @@ def test_router_fp32_within_rounding_bound_of_exact():
     assert np.all(np.abs(l32 - exact.numpy()) <= gamma * mag)
 
 
+def _exact_logits(x, w, scale=None, bias=None):
+    """Real-number logits in torch fp64, independent of the oracle: bf16 x fp32 (or int8)
+    products and their sums are exact to ~1e-16 relative in double."""
+    l = x.double() @ torch.as_tensor(w).double().T
+    if scale is not None:
+        l = l * torch.as_tensor(scale).double()[None, :]
+    if bias is not None:
+        l = l + torch.as_tensor(bias).double()[None, :]
+    return l.numpy()
+
+
+@pytest.mark.parametrize("fmt", ["fp32", "int8"])
+def test_router_error_bound_holds_and_is_not_vacuous(fmt):
+    # The fp32 logits in the fixed order lie within the rigorous summation bound of the
+    # exact value (a theorem of floating-point summation), and the bound is within a few
+    # orders of magnitude of the observed error (a bound missing the unit roundoff or the
+    # row scale would fail one side).
+    g = torch.Generator().manual_seed(11)
+    E, d, T = 64, 2048, 8
+    x = torch.randn((T, d), generator=g).to(torch.bfloat16)
+    bias = (torch.randn(E, generator=g) * 0.5).float().numpy()
+    if fmt == "fp32":
+        w = (torch.randn((E, d), generator=g) * 0.02).float().numpy()
+        r = {"fmt": oracle.FMT_FP32, "E": E, "d": d, "w": w, "bias": bias}
+        exact = _exact_logits(x, w, bias=bias)
+    else:
+        q = torch.randint(-127, 128, (E, d), generator=g).to(torch.int8).numpy()
+        s16 = (torch.rand(E, generator=g) * 1e-3 + 1e-4).half()
+        r = {"fmt": oracle.FMT_INT8_ROW, "E": E, "d": d, "w": q,
+             "scale": s16.view(torch.int16).numpy().view(np.uint16), "bias": bias}
+        exact = _exact_logits(x, q.astype(np.float64), scale=s16.double().numpy(), bias=bias)
+    xb = si.bits16(x)
+    l32 = oracle.router_logits(r, xb).astype(np.float64)
+    bnd = oracle.router_error_bound(r, xb)
+    err = np.abs(l32 - exact)
+    assert np.all(err <= bnd)
+    assert (err / bnd).max() > 1e-4
+    assert np.allclose(oracle.router_logits_fp64(r, xb), exact, rtol=0, atol=1e-12)
+
+
+def test_router_error_bound_on_one_sided_rounding():
+    # x = 1 and every weight 1 + 2^-21: once a lane's running sum passes 16 each fma adds
+    # less than half an ulp and rounds the same way, so the fixed-order result falls
+    # short of the exact 2048 (1 + 2^-21) by a sizeable share of the worst-case bound.
+    # The bound must hold here and not be inflated by more than a small factor.
+    E, d, eps = 2, 2048, 2.0 ** -21
+    w = np.full((E, d), np.float32(1 + eps))
+    w[1] = -w[1]
+    x = torch.ones((1, d)).to(torch.bfloat16)
+    r = {"fmt": oracle.FMT_FP32, "E": E, "d": d, "w": w, "bias": None}
+    l32 = oracle.router_logits(r, si.bits16(x)).astype(np.float64)[0]
+    exact = d * (1 + eps)
+    bnd = oracle.router_error_bound(r, si.bits16(x))[0]
+    err = np.abs(np.abs(l32) - exact)
+    assert l32[0] < exact and l32[1] == -l32[0]
+    assert np.all(err <= bnd) and np.all(err / bnd > 0.05)
+
+
+def _tiny_router(seed, E=16, d=256, T=5):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((T, d), generator=g).to(torch.bfloat16)
+    w = (torch.randn((E, d), generator=g) * 0.05).float().numpy()
+    return x, w
+
+
+def test_tie_audit_identical_rows_are_flagged():
+    # two identical router rows give exactly equal logits for every token; placing them
+    # at ranks k and k + 1 (bias) makes every token's cut a true tie
+    x, w = _tiny_router(3)
+    E, k = w.shape[0], 2
+    w[5] = w[9]
+    bias = np.full(E, -50.0, np.float32)
+    bias[[0, 5, 9]] = [50.0, 0.0, 0.0]
+    r = {"fmt": oracle.FMT_FP32, "E": E, "d": w.shape[1], "w": w, "bias": bias}
+    a = oracle.router_tie_audit(r, si.bits16(x), k, factor=1.0)
+    assert a["count"] == x.shape[0] and np.all(a["margin"] <= 0)
+    # a tie goes to the lower index in both selections, so the sets agree
+    assert a["differs"] == 0
+
+
+def test_tie_audit_separated_cut_is_clear():
+    x, w = _tiny_router(4)
+    E, k = w.shape[0], 3
+    bias = np.zeros(E, np.float32)
+    bias[[2, 7, 11]] = 10.0
+    r = {"fmt": oracle.FMT_FP32, "E": E, "d": w.shape[1], "w": w, "bias": bias}
+    a = oracle.router_tie_audit(r, si.bits16(x), k)
+    assert a["count"] == 0 and a["differs"] == 0 and np.all(a["margin"] > 0)
+    a0 = oracle.router_tie_audit({**r, "w": np.zeros_like(w), "bias": None}, si.bits16(x), k)
+    assert a0["count"] == x.shape[0]          # all logits exactly zero: every cut is a tie
+
+
+def test_tie_audit_sub_ulp_gap_changes_the_fp32_choice():
+    # expert 1 = expert 0 with one weight raised by one ulp where x > 0: exactly, expert 1
+    # is larger; where the fp32 chain absorbs the difference the fixed-order logits tie and
+    # the lower index (0) is chosen.  The audit must see the different choice and flag it.
+    x, w = _tiny_router(6, T=1)
+    E, d, k = w.shape[0], w.shape[1], 1
+    bias = np.full(E, -50.0, np.float32)
+    bias[:2] = 0.0
+    xb = si.bits16(x)
+    found = False
+    for c in np.nonzero(x[0].float().numpy() > 0)[0]:
+        w2 = w.copy()
+        w2[1] = w2[0]
+        w2[1, c] = np.nextafter(w2[0, c], np.float32(np.inf))
+        r = {"fmt": oracle.FMT_FP32, "E": E, "d": d, "w": w2, "bias": bias}
+        l32 = oracle.router_logits(r, xb)
+        if l32[0, 0] == l32[0, 1]:
+            found = True
+            break
+    assert found
+    assert _exact_logits(x, w2, bias=bias)[0, 1] > _exact_logits(x, w2, bias=bias)[0, 0]
+    a = oracle.router_tie_audit(r, xb, k, factor=1.0)
+    assert a["differs"] == 1 and a["count"] == 1
+    assert oracle.select_topk(l32, k)[0, 0] == 0
+
+
 # ---------------------------------------------------------------- pre-layer norm, gate
 
 def _bf16_bits(v):
