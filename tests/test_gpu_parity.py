@@ -272,6 +272,49 @@ def test_prefill_8192_zipf():
     _check_layer("prefill_8192_zipf", sample=24, tiles=True)
 
 
+def test_prefill_batch_ids_equal_smaller_calls():
+    """A token's ids and gate weights do not depend on the batch it is routed in: the same
+    16 tokens inside the 8192-token Zipf prefill (bounded MFMA router), alone (the decode
+    layer, and moe_route's one-launch form), four at a time (one launch), 16 together
+    (GEMV logits + selection kernel) and among 100 with logits requested (fixed-order LDS
+    GEMM) all get the same ids and weights, bit for bit."""
+    moe = _gpu()
+    w, lay, _ = _setup("prefill_8192_zipf")
+    x = synth.make_tokens(w, seed=0, device="cuda", stream=41)
+    big, _ = _run(moe, lay, w, x)
+    ids_big = big.ids[:w.T].clone()
+    wt_big = big.weights[:w.T].clone().view(torch.int32)
+    del big
+    rng = np.random.default_rng(8192)
+    toks = np.unique(np.concatenate([[0, 1, w.T // 2, w.T - 1],
+                                     rng.choice(w.T, 12, replace=False)]))[:16]
+    tt = torch.from_numpy(toks).long().cuda()
+
+    one = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, 1)
+    for t in toks:
+        xt = x[int(t):int(t) + 1].contiguous()
+        one.decode(xt)
+        torch.cuda.synchronize()
+        assert torch.equal(one.ids[:1], ids_big[int(t):int(t) + 1]), "token %d decode" % t
+        assert torch.equal(one.weights[:1].view(torch.int32), wt_big[int(t):int(t) + 1])
+        one.route_only(xt)
+        torch.cuda.synchronize()
+        assert torch.equal(one.ids[:1], ids_big[int(t):int(t) + 1]), "token %d route" % t
+        assert torch.equal(one.weights[:1].view(torch.int32), wt_big[int(t):int(t) + 1])
+    for T in (4, 16):
+        small, _ = _run(moe, lay, w, x[tt[:T]].contiguous())
+        assert torch.equal(small.ids[:T], ids_big[tt[:T]]), "T %d" % T
+        assert torch.equal(small.weights[:T].view(torch.int32), wt_big[tt[:T]]), "T %d" % T
+    others = torch.from_numpy(np.setdiff1d(np.arange(w.T), toks)[:100 - toks.size]).long().cuda()
+    idx = torch.cat([tt, others])
+    lg = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, 100, keep_logits=True)
+    lg.forward(x[idx].contiguous())
+    torch.cuda.synchronize()
+    moe.moe_check_device_error()
+    assert torch.equal(lg.ids[:100], ids_big[idx])
+    assert torch.equal(lg.weights[:100].view(torch.int32), wt_big[idx])
+
+
 def test_prefill_32768_mixed_zipf():
     _check_layer("prefill_32768_mixed", sample=16, tiles=True)
 
