@@ -174,10 +174,16 @@ __device__ __forceinline__ float dot_pairs(const uint32_t* pr, const uint32_t* x
     return acc;
 }
 
+// sum of a group's 32 activations, pair by pair in ascending order: one v_dot2_f32_bf16
+// per pair against (1.0, 1.0) (the products are exact), where unpacking both halves and
+// adding them takes four instructions.  The pair (1.0, 1.0) is kept in a register: as an
+// inline constant the instruction would read it as one fp32 value.
 __device__ __forceinline__ float group_sum_x(const uint32_t* xp) {
+    uint32_t ones;
+    asm("v_mov_b32 %0, 0x3f803f80" : "=v"(ones));
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += bf16lo(xp[i]) + bf16hi(xp[i]);
+    for (int i = 0; i < 16; ++i) s = dot2(xp[i], ones, s);
     return s;
 }
 
