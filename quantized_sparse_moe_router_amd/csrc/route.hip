@@ -689,25 +689,47 @@ __global__ void __launch_bounds__(64) router_gemv_kernel(
 // activation vector a wave loads serves its NE rows: the activations are the bulk of what
 // the waves read (E T d bf16 over all waves with one row each, d fp32 per row).  Each
 // (token, expert) chain and its butterfly are the GEMV's, so the logits are the same bits.
+// From kRouteSplitBlockMinTokens tokens (and d <= 2048) blocks of kRouteSplitWaves waves
+// take WB NE consecutive rows: the token group's activations go to LDS once per block and
+// each wave reads them there, which divides the activation traffic through the caches by
+// WB; below that a block of WB waves would leave CUs without work.
 constexpr int kRouteTokensPerWave = 8;
+constexpr int kRouteSplitWaves = 4;
+constexpr int kRouteSplitBlockMinTokens = 17;
 template <int FMT, int NV>
 struct SplitShape {
     static constexpr int PV = (FMT == MOE_FMT_INT8_ROW) ? 16 : 4;
     static constexpr int NE = (NV * PV <= 32) ? 2 : 1;                     // rows per wave
     static constexpr int G = (NV * PV <= 32) ? 4 : (NV * PV <= 64) ? 2 : 1;   // tokens per pass
 };
-template <int FMT, int NV>
-__global__ void __launch_bounds__(64) router_gemv_split_kernel(
+template <int FMT, int NV, int WB>
+__global__ void __launch_bounds__(64 * WB) router_gemv_split_kernel(
     const void* __restrict__ W, const uint16_t* __restrict__ scale,
     const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
     float* __restrict__ logits) {
     using SS = SplitShape<FMT, NV>;
     constexpr int PV = SS::PV, NE = SS::NE, G = SS::G;
     constexpr int XW = PV / 2;                  // 32-bit words of activations per vector
-    const int lane = threadIdx.x;
-    const int e0 = blockIdx.x * NE;
-    const int t_lo = blockIdx.y * kRouteTokensPerWave;
-    const int t_hi = min(T, t_lo + kRouteTokensPerWave);
+    constexpr int D = NV * 64 * PV;             // d of this instantiation
+    constexpr int TPW = kRouteTokensPerWave;
+    const int lane = threadIdx.x & 63;
+    const int e0 = (blockIdx.x * WB + (threadIdx.x >> 6)) * NE;
+    const int t_lo = blockIdx.y * TPW;
+    const int t_hi = min(T, t_lo + TPW);
+    // WB > 1: tokens t_lo .. t_lo + TPW - 1 (past T: the last token again, unused) in LDS
+    __shared__ __attribute__((aligned(16))) uint16_t xs[WB > 1 ? TPW * D : 8];
+    constexpr int XPT = WB > 1 ? TPW * D / 8 / (64 * WB) : 1;   // 16-byte pieces per thread
+    static_assert(WB == 1 || XPT * 64 * WB * 8 == TPW * D, "whole pieces per thread");
+    uint4 xv[XPT];
+    if constexpr (WB > 1) {
+        // requested before the rows, so that both round trips overlap
+#pragma unroll
+        for (int p = 0; p < XPT; ++p) {
+            const int idx = (int)threadIdx.x + 64 * WB * p, tok = idx / (D / 8);
+            xv[p] = reinterpret_cast<const uint4*>(x + (size_t)min(t_lo + tok, T - 1) * D)
+                [idx % (D / 8)];
+        }
+    }
     float w[NE][NV][PV];
     float b[NE], se[NE];
 #pragma unroll
@@ -717,12 +739,19 @@ __global__ void __launch_bounds__(64) router_gemv_split_kernel(
         b[r] = bias ? bias[e] : 0.0f;
         se[r] = (FMT == MOE_FMT_INT8_ROW) ? f16_to_f32(scale[e]) : 1.0f;
     }
+    if constexpr (WB > 1) {
+#pragma unroll
+        for (int p = 0; p < XPT; ++p)
+            reinterpret_cast<uint4*>(xs)[(int)threadIdx.x + 64 * WB * p] = xv[p];
+        __syncthreads();
+    }
     for (int t0 = t_lo; t0 < t_hi; t0 += G) {
         // every activation load of the pass before the first fma
         uint32_t xq[G][NV][XW];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const uint16_t* xt = x + (size_t)min(t0 + g, T - 1) * d;
+            const uint16_t* xt = WB > 1 ? xs + (size_t)min(t0 + g - t_lo, TPW - 1) * D
+                                        : x + (size_t)min(t0 + g, T - 1) * d;
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int c0 = (lane + 64 * j) * PV;
@@ -808,9 +837,22 @@ hipError_t launch_nv(const moe_router& r, const uint16_t* x, int T, int k, int32
                                                 RouteNorm{}, s);
     if (T <= kRouteSplitMaxTokens) {   // one wave per expert row, then the selection kernel
         constexpr int NE = SplitShape<FMT, NV>::NE;
-        router_gemv_split_kernel<FMT, NV>
-            <<<dim3((E + NE - 1) / NE, (T + kRouteTokensPerWave - 1) / kRouteTokensPerWave),
-               dim3(64), 0, s>>>(r.w, r.scale, r.bias, x, T, E, d, logits);
+        constexpr int PV = SplitShape<FMT, NV>::PV;
+        const int ty = (T + kRouteTokensPerWave - 1) / kRouteTokensPerWave;
+        bool block_form = false;
+        if constexpr (NV * 64 * PV <= 2048) {
+            if (T >= kRouteSplitBlockMinTokens) {
+                constexpr int RB = NE * kRouteSplitWaves;   // rows per block
+                router_gemv_split_kernel<FMT, NV, kRouteSplitWaves>
+                    <<<dim3((E + RB - 1) / RB, ty), dim3(64 * kRouteSplitWaves), 0, s>>>(
+                        r.w, r.scale, r.bias, x, T, E, d, logits);
+                block_form = true;
+            }
+        }
+        if (!block_form)
+            router_gemv_split_kernel<FMT, NV, 1>
+                <<<dim3((E + NE - 1) / NE, ty), dim3(64), 0, s>>>(r.w, r.scale, r.bias, x, T,
+                                                                   E, d, logits);
     } else {
         using R = RgShape<FMT>;
         constexpr int kLds = 2 * R::STAGE;
