@@ -43,11 +43,12 @@ def experts_desc_of(ex):
 class MoeLayer:
     """Buffers and calls of one MoE layer for up to ``T_max`` tokens.
 
-    forward(x) enqueues moe_route -> moe_permute -> moe_expert_ffn(routed) on the current
-    stream and moe_expert_ffn(shared, dense) on a side stream forked from it, joins, then
-    moe_combine; it returns ``out`` (bf16 [T][d]).  For small calls (T*k <= 64) the routed
-    experts do not read the grouping, so moe_permute runs on a second side stream beside
-    them.  Graph capture records the forks and joins.  Intermediate results stay readable
+    forward(x) enqueues moe_route -> moe_permute -> moe_expert_ffn(routed) ->
+    moe_expert_ffn(shared, dense) -> moe_combine on the current stream and returns ``out``
+    (bf16 [T][d]).  Above SHARED_SIDE_STREAM_ABOVE_TOKENS tokens the shared expert runs on a
+    side stream forked from it instead (joined before the combine), beside the router's
+    long MFMA form; graph capture records the fork and join.  Below that a fork and join
+    cost more than the overlap gives.  Intermediate results stay readable
     as attributes (ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared, and
     logits when ``keep_logits``).  Without ``keep_logits``, moe_route gets no logits buffer
     and, for more than 64 tokens, selects through MFMA logits with an error bound and exact
@@ -57,6 +58,12 @@ class MoeLayer:
     side streams) when T*k <= 64 and the shapes allow it (``can_decode``); it fills ids,
     weights and out only.
     """
+
+    # forward() runs the shared expert on a side stream above this many tokens: there the
+    # router takes its MFMA form and the overlap pays (128 tokens: 187 -> 167 us per layer
+    # call); at 64 and below the fork and join cost more than they hide (one token 42 ->
+    # 29 us, 64 tokens 173 -> 169 us without them).
+    SHARED_SIDE_STREAM_ABOVE_TOKENS = 64
 
     def __init__(self, router, routed, shared, k, T_max, device="cuda", keep_logits=False,
                  norm=None):
@@ -110,7 +117,6 @@ class MoeLayer:
                 if self.can_decode else 0
             self.ws_block = torch.zeros((max(ws_blk, 256),), dtype=u8, device=dev)
         self.side = torch.cuda.Stream(device=dev)     # default priority
-        self.side2 = torch.cuda.Stream(device=dev)
 
     def forward(self, x, residual=None, out=None):
         T = x.shape[0]
@@ -154,29 +160,23 @@ class MoeLayer:
         """route, permute and both expert FFNs of x (the combine's inputs)."""
         k, E = self.k, self.E
         main = torch.cuda.current_stream()
-        if self.shared is not None:
-            # the shared expert does not depend on routing: run it on a side stream
+        side = self.shared is not None and T > self.SHARED_SIDE_STREAM_ABOVE_TOKENS
+        if side:
+            # the shared expert does not depend on routing: beside the router
             self.side.wait_stream(main)
             moe_expert_ffn(self.shared, x, T, 1, None, None, None, self.y_shared,
                            self.ws_shared, stream=self.side)
         moe_route(self.router, x, T, k, self.ids, self.weights,
                   self.logits if self.keep_logits else None, self.ws_route)
-        small = T * k <= 64
-        if small:
-            # small calls of moe_expert_ffn read only ids, so the grouping (needed by the
-            # combine) can run beside the routed experts
-            self.side2.wait_stream(main)
-            moe_permute(self.ids, T, k, E, self.offsets, self.sorted_pairs, self.pair_pos,
-                        self.ws_perm, stream=self.side2)
-        else:
-            moe_permute(self.ids, T, k, E, self.offsets, self.sorted_pairs, self.pair_pos,
-                        self.ws_perm)
+        moe_permute(self.ids, T, k, E, self.offsets, self.sorted_pairs, self.pair_pos,
+                    self.ws_perm)
         moe_expert_ffn(self.routed, x, T, k, self.ids, self.offsets, self.sorted_pairs,
                        self.y_pairs, self.ws_ffn)
-        if small:
-            main.wait_stream(self.side2)
-        if self.shared is not None:
+        if side:
             main.wait_stream(self.side)
+        elif self.shared is not None:
+            moe_expert_ffn(self.shared, x, T, 1, None, None, None, self.y_shared,
+                           self.ws_shared)
 
     def route_logits(self, x, ids, weights):
         """moe_route with the logits requested (the fixed-order path) into self.logits; ids
