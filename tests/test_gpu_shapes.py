@@ -127,3 +127,19 @@ def test_degenerate_routing(E, k, bias):
         if k == E:
             assert np.array_equal(np.sort(ids, axis=1), np.tile(np.arange(E), (T, 1)))
             assert np.all(np.abs(wts.astype(np.float64).sum(axis=1) - 1.0) <= k * 2.0 ** -23)
+
+
+@pytest.mark.parametrize("E,k", [(1000, 10), (1024, 10), (1024, 64)])
+def test_most_experts(E, k):
+    """The largest expert counts the library takes (E up to 1024: 16 router keys per lane in
+    every selection form), at d 256 / F 128, Zipf routing, T = 1 and 4 (one-launch router,
+    the decode layer selecting in its gate/up blocks), 20 (logits then the selection
+    kernel) and 300 (the bounded MFMA router), against the oracle."""
+    moe = _gpu()
+    w = synth.Workload("most_experts_e%d_k%d" % (E, k), 70 + k, d=256, E=E, k=k, F=128, T=1)
+    lay = synth.make_layer(w, seed=0, device="cuda", bias="zipf")
+    for T in (1, 4, 20, 300):
+        print("case E=%d k=%d T=%d" % (E, k, T), flush=True)
+        ids, wts = _check_layer(moe, w, lay, T, 9, T * k <= 64)
+        assert np.all((ids >= 0) & (ids < E))
+        assert all(len(set(r)) == k for r in ids.tolist())
