@@ -8,7 +8,9 @@ is checked bit for bit against the four-call composition before timing (whose ti
 step is reported too).  Inputs are resident in HBM before timing; the step sequence is
 captured in a HIP graph and replayed.
 To keep the 256 MB Infinity Cache from serving the weights, steps rotate over
-``--copies`` distinct copies of the layer (a different token per copy).
+``--copies`` distinct copies of the layer (a different token per copy).  Before the warm-up
+a graph of the timed region's shape is replayed once on other copies (the process's first
+replay of such a graph costs ~24 us more, once), then every copy is read again.
 
 Also reported in the same line:
   roofline        the expert kernels of a decode step (moe_experts_decode: gate/up kernel then
