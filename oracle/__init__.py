@@ -387,6 +387,10 @@ def router_error_bound(router, x_bits):
 def router_tie_audit(router, x_bits, k, factor=2.0):
     """Tokens whose top-k set another valid fp32 summation order could change.
 
+    The router sends each token to 10 of a layer's 512 routed experts [Strata 与
+    Qwen3.8-Flash-Next (telli.sh), section 稀疏架构创造了机会]; the pages fix no summation
+    order, so this audit reports where the choice rests on the fixed order alone.
+
     With exact logits l (the fp64 audit copy) and bounds B (router_error_bound, scaled by
     `factor`), a token is flagged when some expert inside the exact top-k and some expert
     outside it have overlapping intervals: min over selected (l - B) <= max over the
