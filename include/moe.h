@@ -376,10 +376,13 @@ moe_status moe_experts_decode(const moe_experts* routed, const moe_experts* shar
 moe_status moe_dequant_probe(int32_t fmt, int32_t form, const uint8_t* w, const uint16_t* s,
                              int64_t n_groups, void* out, void* stream);
 
-/* Workspace bytes an operation needs for these sizes (0 = none).  For the decode operations
- * (MOE_OP_LAYER_DECODE, MOE_OP_EXPERTS_DECODE, MOE_OP_BLOCK_DECODE) 0 also means that they do
- * not run for these sizes (more than 64 pairs, or a (d_model, d_ff) pair without decode
- * kernels): the call returns MOE_ERR_UNSUPPORTED.  Pure host function. */
+/* Workspace bytes an operation needs for these sizes (0 = none).  0 also for sizes that
+ * every call of the operation rejects: T, k or n_experts not positive, more than 1024
+ * experts, more than 2^31 - 1 (token, expert) pairs, or (MOE_OP_ROUTE above 64 tokens) a
+ * d_model that is not positive.  For the decode operations (MOE_OP_LAYER_DECODE,
+ * MOE_OP_EXPERTS_DECODE, MOE_OP_BLOCK_DECODE) 0 also means that they do not run for these
+ * sizes (more than 64 pairs, or a (d_model, d_ff) pair without decode kernels): the call
+ * returns MOE_ERR_UNSUPPORTED.  Pure host function. */
 size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d,
                           int32_t d_ff);
 

@@ -189,12 +189,18 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_workspace_size(int32_t op, int32_t T, int32_t k, int32_t E, int32_t d,
                           int32_t d_ff) {
-    (void)d;
-    if (T <= 0 || k <= 0 || E <= 0) return 0;
+    // 0 for sizes every call of these operations rejects; within these limits no product
+    // below exceeds 2^63
+    if (T <= 0 || k <= 0 || E <= 0 || E > kMaxExperts) return 0;
+    const int64_t pairs = (int64_t)T * k;
+    if (pairs > INT32_MAX) return 0;
     switch (op) {
-        case MOE_OP_ROUTE: return route_ws(T, E, d, true);
-        case MOE_OP_PERMUTE: return moe::permute_ws_bytes((int64_t)T * k, E);
-        case MOE_OP_EXPERT_FFN: return d_ff > 0 ? ffn_ws((int64_t)T * k, E, d_ff) : 0;
+        case MOE_OP_ROUTE:
+            // the bounded form keeps bf16 copies of the router rows: d must be a size
+            if (route_bounded(T, nullptr) && d <= 0) return 0;
+            return route_ws(T, E, d, true);
+        case MOE_OP_PERMUTE: return moe::permute_ws_bytes(pairs, E);
+        case MOE_OP_EXPERT_FFN: return d_ff > 0 ? ffn_ws(pairs, E, d_ff) : 0;
         // the decode operations: 0 also where they do not run (more than 64 pairs, h rows
         // beyond LDS, a (d_model, d_ff) pair without decode kernels)
         case MOE_OP_LAYER_DECODE:

@@ -288,3 +288,42 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+# ---------------------------------------------------------------- workspace sizes, fuzzed
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_I32 = st.one_of(st.integers(-2 ** 31, 2 ** 31 - 1),
+                 st.sampled_from([0, 1, 2, 4, 10, 16, 64, 65, 127, 128, 256, 512, 640, 1023,
+                                  1024, 1025, 2048, 4096, 8192, 32768, 2 ** 31 - 1]))
+
+
+@settings(max_examples=3000, deadline=None)
+@given(op=st.integers(-1, 7), T=_I32, k=_I32, E=_I32, d=_I32, F=_I32)
+def test_workspace_size_never_wraps(L, op, T, k, E, d, F):
+    """Over the whole int32 range of every argument: 0 for the sizes every call rejects, and
+    otherwise at least the buffers the operation's calls place in the workspace (so a
+    wrapped product, which would come out small, fails), never near 2^64."""
+    n = L.moe_workspace_size(op, T, k, E, d, F)
+    assert 0 <= n < 2 ** 63
+    pairs = T * k
+    if T <= 0 or k <= 0 or E <= 0 or E > 1024 or pairs > 2 ** 31 - 1:
+        assert n == 0
+        return
+    if op == 0:                                   # route: counter + logits [T][E] fp32
+        if T > 64 and d <= 0:
+            assert n == 0
+        else:
+            assert n >= 256 + T * E * 4
+            if T > 64:                            # + bf16 router planes and row norms
+                assert n >= 256 + T * E * 4 + E * 2 * d * 2 + E * 4
+    elif op == 2:                                 # expert FFN: h rows [pairs][d_ff] bf16
+        assert n == 0 if F <= 0 else n >= pairs * F * 2
+    elif op in (3, 4, 5):                         # decode operations: at most 64 pairs
+        if pairs > 64 or F <= 0 or d <= 0:
+            assert n == 0
+        elif n:
+            assert n >= pairs * F * 2
+    elif op not in (1,):
+        assert n == 0
