@@ -670,6 +670,9 @@ def prefill_bench(moe, synth, np, torch, name, bias):
     return {"workload": name, "router_bias": bias or w.bias, "tokens": w.T,
             "tokens_per_s": round(w.T / (ms_layer * 1e-3), 1),
             "ms_layer": round(ms_layer, 4), "ms_layer_min": round(ms_layer_min, 4),
+            # the routed moe_expert_ffn call: the grouped GEMM for experts with 4 or more
+            # pairs, the GEMV for the others
+            "routed_call": "moe_expert_ffn (grouped MFMA GEMM; GEMV for experts with < 4 pairs)",
             "ms_routed_grouped_gemm": round(ms_gemm, 4),
             "ms_routed_grouped_gemm_min": round(ms_gemm_min, 4),
             "routed_gemm_tflops": round(flops / (ms_gemm * 1e-3) / 1e12, 1),

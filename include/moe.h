@@ -229,16 +229,16 @@ moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  * expert's weights (two launches: gate/up + SwiGLU, then down):
  *   at most 64 rows: each pair's row is derived from ids alone; offsets and sorted_pairs
  *     are not read, so moe_permute may run concurrently with the call;
- *   65 .. 4096 rows (grouped mode): a third, earlier launch lists each expert's sorted
+ *   more than 64 rows (grouped mode): a third, earlier launch lists each expert's sorted
  *     positions in chunks of at most 3 from offsets and sorted_pairs (so moe_permute must
  *     have completed), and each chunk streams its expert's weights once; from 640 rows an
  *     expert with 8 or more pairs (4 or more above 1024 rows) runs the grouped MFMA GEMM
  *     below instead, in two more launches on the same h and y.
  * A pair's output bits are the same whenever it runs on the GEMV (and the same in
- * moe_layer_decode); on the GEMM they differ by rounding.  Larger calls, and shapes without
- * a GEMV kernel, run the grouped MFMA GEMM alone, reading offsets and sorted_pairs; it
- * needs T*d_model and T*k*d_ff (dense: T*d_ff) below 2^31 elements (MOE_ERR_UNSUPPORTED
- * otherwise: split the call).
+ * moe_layer_decode); on the GEMM they differ by rounding.  Dense calls above 64 tokens, and
+ * shapes without a GEMV kernel, run the grouped MFMA GEMM alone, reading offsets and
+ * sorted_pairs.  Wherever the GEMM may run it needs T*d_model and T*k*d_ff (dense: T*d_ff)
+ * below 2^31 elements (MOE_ERR_UNSUPPORTED otherwise: split the call).
  * ws: moe_workspace_size(MOE_OP_EXPERT_FFN, T, k, E, d, d_ff) bytes (pass k = 1, E = 1
  * for dense mode).
  */

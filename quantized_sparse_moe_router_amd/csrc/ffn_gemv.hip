@@ -18,7 +18,7 @@
 // expert-sorted position (valid pairs with a smaller id, plus earlier pairs with the same
 // id), the same position moe_permute assigns.
 // Dense mode (shared expert): a slot is a chunk of MT tokens.
-// Sorted mode (more than 64 pairs, up to kGemvSortedMaxRows): the grouping from moe_permute
+// Sorted mode (more than 64 pairs): the grouping from moe_permute
 // is read instead of a ballot; a small kernel lists, expert by expert, chunks of at most MT
 // consecutive sorted positions with their tokens (sentinels fill the list to the grid's
 // size), and a slot is one chunk.  Each expert's rows are streamed once per chunk, four

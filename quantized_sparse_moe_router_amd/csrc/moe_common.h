@@ -275,15 +275,14 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
                           int32_t* sorted_pairs, int32_t* pair_pos, void* ws, hipStream_t s);
 size_t permute_ws_bytes(int64_t P, int E);
 
-// Small calls: weight-streaming GEMV, gate/up then down.  Up to kGemvMaxBallotRows pairs
-// the positions come from ids alone (a ballot; ws = [h]); above, up to kGemvSortedMaxRows,
-// from the grouping (offsets, sorted_pairs; ws = gemv_sorted_ws_layout).  From
-// kHybridMinRows pairs the call is split by expert: an expert with fewer than
-// gemv_hot_rows(rows) pairs runs the GEMV in sorted mode, one with more the grouped MFMA
-// GEMM (its weights streamed once per 256 pairs instead of once per chunk).  Dense mode
+// Weight-streaming GEMV, gate/up then down.  Up to kGemvMaxBallotRows pairs the positions
+// come from ids alone (a ballot; ws = [h]); above, from the grouping (offsets, sorted_pairs;
+// ws = gemv_sorted_ws_layout).  From kHybridMinRows pairs the call is split by expert: an
+// expert with fewer than gemv_hot_rows(rows) pairs runs the GEMV in sorted mode, one with
+// more the grouped MFMA GEMM (its weights streamed once per 256 pairs instead of once per
+// chunk); at prefill sizes that leaves the GEMM only the experts worth a tile.  Dense mode
 // (ids == nullptr): the token index, at most kGemvMaxBallotRows tokens.
 constexpr int64_t kGemvMaxBallotRows = 64;
-constexpr int64_t kGemvSortedMaxRows = 4096;
 constexpr int kGemvSortedMT = 3;    // pairs of one expert per pass over its weights
 constexpr int64_t kHybridMinRows = 640;
 constexpr int kMfmaTileRows = 256;  // pairs per entry of the grouped GEMM's work list
