@@ -174,10 +174,10 @@ moe_status moe_rmsnorm(const moe_norm* n, const uint16_t* x, int32_t T, int32_t 
  * logits.  How they are reached:
  *   T <= 4: logits and selection in one launch (the last block to finish its rows
  *            selects);
- *   4 < T <= 64: the same one-wave-per-expert-row logits (eight tokens and up to two
+ *   4 < T <= 512: the same one-wave-per-expert-row logits (eight tokens and up to two
  *            rows per wave), then a selection kernel (a wave per token);
- *   T > 64, logits requested: an LDS-tiled fp32 GEMM in the fixed order, then selection;
- *   T > 64, logits NULL (the bounded form): bf16 MFMA logits (FP32 rows split exactly
+ *   T > 512, logits requested: an LDS-tiled fp32 GEMM in the fixed order, then selection;
+ *   T > 512, logits NULL (the bounded form): bf16 MFMA logits (FP32 rows split exactly
  *            into two bf16 parts plus a dropped remainder below 2^-17 of the weight)
  *            within 2^-11 (|x_t| |w_e| + |b_e|) of the fixed-order value; per token the
  *            experts that this bound cannot rule out of the top k are recomputed in the
@@ -378,7 +378,7 @@ moe_status moe_dequant_probe(int32_t fmt, int32_t form, const uint8_t* w, const 
 
 /* Workspace bytes an operation needs for these sizes (0 = none).  0 also for sizes that
  * every call of the operation rejects: T, k or n_experts not positive, more than 1024
- * experts, more than 2^31 - 1 (token, expert) pairs, or (MOE_OP_ROUTE above 64 tokens) a
+ * experts, more than 2^31 - 1 (token, expert) pairs, or (MOE_OP_ROUTE above 512 tokens) a
  * d_model that is not positive.  For the decode operations (MOE_OP_LAYER_DECODE,
  * MOE_OP_EXPERTS_DECODE, MOE_OP_BLOCK_DECODE) 0 also means that they do not run for these
  * sizes (more than 64 pairs, or a (d_model, d_ff) pair without decode kernels): the call

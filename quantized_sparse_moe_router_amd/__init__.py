@@ -46,12 +46,12 @@ class MoeLayer:
     forward(x) enqueues moe_route -> moe_permute -> moe_expert_ffn(routed) ->
     moe_expert_ffn(shared, dense) -> moe_combine on the current stream and returns ``out``
     (bf16 [T][d]).  Above SHARED_SIDE_STREAM_ABOVE_TOKENS tokens the shared expert runs on a
-    side stream forked from it instead (joined before the combine), beside the router's
-    long MFMA form; graph capture records the fork and join.  Below that a fork and join
+    side stream forked from it instead (joined before the combine), beside the router and
+    the routed experts; graph capture records the fork and join.  Below that a fork and join
     cost more than the overlap gives.  Intermediate results stay readable
     as attributes (ids, weights, offsets, sorted_pairs, pair_pos, y_pairs, y_shared, and
     logits when ``keep_logits``).  Without ``keep_logits``, moe_route gets no logits buffer
-    and, for more than 64 tokens, selects through MFMA logits with an error bound and exact
+    and, for more than 512 tokens, selects through MFMA logits with an error bound and exact
     recomputation of the experts near the cut (the same ids and weights, bit for bit).
 
     decode(x) computes the same output bit for bit with moe_layer_decode (three launches, no
@@ -59,10 +59,10 @@ class MoeLayer:
     weights and out only.
     """
 
-    # forward() runs the shared expert on a side stream above this many tokens: there the
-    # router takes its MFMA form and the overlap pays (128 tokens: 187 -> 167 us per layer
-    # call); at 64 and below the fork and join cost more than they hide (one token 42 ->
-    # 29 us, 64 tokens 173 -> 169 us without them).
+    # forward() runs the shared expert on a side stream above this many tokens, where the
+    # overlap pays (per layer call 220 -> 202 us at 96 tokens, 276 -> 250 us at 128, 457 ->
+    # 415 us at 512); at 64 and below the fork and join cost more than they hide (one token
+    # 42 -> 29 us, 64 tokens 173 -> 169 us without them).
     SHARED_SIDE_STREAM_ABOVE_TOKENS = 64
 
     def __init__(self, router, routed, shared, k, T_max, device="cuda", keep_logits=False,

@@ -235,15 +235,19 @@ constexpr int kRouteGemvMaxTokens = 16;
 // parallel): 88.8 -> 82.3 us per 16-token layer step when this went from 16 to 4
 constexpr int kRouteOneLaunchMaxTokens = 4;
 // Tokens up to which it computes the logits by GEMV (one wave per expert row, token groups)
-// and selects in a second kernel; above, the tiled GEMM (or the bounded form).
-constexpr int kRouteSplitMaxTokens = 64;
+// and selects in a second kernel; above, the tiled GEMM (or the bounded form).  The bounded
+// form's three launches cost more than the GEMV's repeated router reads (which the L2 and
+// the cache below it serve) up to about 512 tokens: a layer call at 128 tokens 284 -> 250 us,
+// at 512 tokens 430 -> 415 us when this went from 64 to 512.
+constexpr int kRouteSplitMaxTokens = 512;
 // decode layer / block: up to this many tokens the router writes logits only and every
 // gate/up block selects its token's experts itself; above, the router's last block selects
 constexpr int kDecodeSelectMaxTokens = 1;
 
 hipError_t launch_route(const moe_router& r, const uint16_t* x, int T, int k, int32_t* ids,
                         float* weights, float* logits, unsigned* counter, hipStream_t s);
-// Router logits only (fp32 [T][E], the same values launch_route computes), for T <= 64.
+// Router logits only (fp32 [T][E], the same values launch_route computes), for
+// T <= kRouteSplitMaxTokens.
 hipError_t launch_route_logits(const moe_router& r, const uint16_t* x, int T, float* logits,
                                hipStream_t s);
 

@@ -77,14 +77,16 @@ def test_workspace_sizes(L):
     # most one entry per pair
     assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 64, 10, 512, 2048, 512) >= \
         640 * 512 * 2 + 640 * 32
-    # more than 64 tokens without a logits output: the bounded form also keeps bf16 plane
+    # more than 512 tokens without a logits output: the bounded form also keeps bf16 plane
     # rows of the router (two per fp32 row) and one norm bound per expert
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 8192, 10, 512, 2048, 0) == \
         256 + 8192 * 512 * 4 + 512 * 2 * 2048 * 2 + 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 16, 10, 512, 2048, 0) == 256 + 16 * 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 64, 10, 512, 2048, 0) == 256 + 64 * 512 * 4
-    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 65, 10, 512, 2048, 0) == \
-        256 + 65 * 512 * 4 + 512 * 2 * 2048 * 2 + 512 * 4
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 512, 10, 512, 2048, 0) == \
+        256 + 512 * 512 * 4
+    assert L.moe_workspace_size(_lib.MOE_OP_ROUTE, 513, 10, 512, 2048, 0) == \
+        256 + 513 * 512 * 4 + 512 * 2 * 2048 * 2 + 512 * 4
 
 
 def _router(fmt=0, E=512, d=2048, w=16, scale=None, reserved=0):
@@ -129,8 +131,8 @@ def test_route_null_descriptor_and_workspace(L):
     assert st == -3 and "workspace" in _err(L)
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, None, 16, 100, None)
     assert st == -3
-    # bounded form (65 tokens, no logits): counter + logits alone are not enough
-    st = L.moe_route(ctypes.byref(r), 16, 65, 10, 16, 16, None, 16, 256 + 65 * 512 * 4, None)
+    # bounded form (513 tokens, no logits): counter + logits alone are not enough
+    st = L.moe_route(ctypes.byref(r), 16, 513, 10, 16, 16, None, 16, 256 + 513 * 512 * 4, None)
     assert st == -3 and "workspace" in _err(L)
     # with a logits output the workspace still holds the arrival counter
     st = L.moe_route(ctypes.byref(r), 16, 1, 10, 16, 16, 16, None, 0, None)
@@ -295,7 +297,7 @@ def test_bench_refuses_more_than_one_gpu():
 from hypothesis import given, settings, strategies as st  # noqa: E402
 
 _I32 = st.one_of(st.integers(-2 ** 31, 2 ** 31 - 1),
-                 st.sampled_from([0, 1, 2, 4, 10, 16, 64, 65, 127, 128, 256, 512, 640, 1023,
+                 st.sampled_from([0, 1, 2, 4, 10, 16, 64, 65, 127, 128, 256, 512, 513, 640, 1023,
                                   1024, 1025, 2048, 4096, 8192, 32768, 2 ** 31 - 1]))
 
 
@@ -312,11 +314,11 @@ def test_workspace_size_never_wraps(L, op, T, k, E, d, F):
         assert n == 0
         return
     if op == 0:                                   # route: counter + logits [T][E] fp32
-        if T > 64 and d <= 0:
+        if T > 512 and d <= 0:
             assert n == 0
         else:
             assert n >= 256 + T * E * 4
-            if T > 64:                            # + bf16 router planes and row norms
+            if T > 512:                            # + bf16 router planes and row norms
                 assert n >= 256 + T * E * 4 + E * 2 * d * 2 + E * 4
     elif op == 2:                                 # expert FFN: h rows [pairs][d_ff] bf16
         assert n == 0 if F <= 0 else n >= pairs * F * 2

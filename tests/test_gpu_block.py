@@ -142,7 +142,8 @@ def test_block_decode_against_composition_and_oracle(name, bias, T, gate):
 
 
 @pytest.mark.parametrize("name,bias,T", [
-    ("tiny_d256_e16_top2", None, 300),             # bounded router, grouped GEMM
+    ("tiny_d256_e16_top2", None, 300),             # split router, grouped GEMM
+    ("tiny_d256_e16_top2", None, 600),             # bounded router, grouped GEMM
     ("decode_d2048_e512_top10_t1", "zipf", 96),
 ])
 def test_block_forward_many_tokens_against_oracle(name, bias, T):

@@ -49,15 +49,17 @@ def test_graph_replays_match_eager():
     moe.moe_check_device_error()
 
 
-def test_graph_replays_match_eager_prefill_path():
-    # 300 tokens x top-10: the bounded router (planes, MFMA logits, selection), the chunked
-    # grouping (3000 pairs), the grouped MFMA GEMM and the combine, all inside one graph
+@pytest.mark.parametrize("T", [300, 600])
+def test_graph_replays_match_eager_prefill_path(T):
+    # 300 tokens x top-10: the split router, the chunked grouping (3000 pairs), the GEMV for
+    # the experts with few pairs and the grouped MFMA GEMM for the rest, and the combine;
+    # 600 tokens: the bounded router (planes, MFMA logits, selection) and the GEMM alone
+    # (6000 pairs); each inside one graph
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import quantized_sparse_moe_router_amd as moe
     w = synth.WORKLOADS["decode_d2048_e512_top10_t1"]
     lay = synth.make_layer(w, seed=5, device="cuda", bias="zipf")
-    T = 300
     x = synth.make_tokens(w, T=T, seed=5, device="cuda")
     layer = moe.MoeLayer(lay.router, lay.routed, lay.shared, w.k, T)
     print("case graph prefill T=%d" % T, flush=True)

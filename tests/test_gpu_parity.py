@@ -106,7 +106,7 @@ def _check_layer(name, T=None, sample=None, bias=None, seed=0, stream=0, tiles=F
     layer, out = _run(moe, lay, w, x)
     k, E = w.k, w.E
 
-    # routing: full size, bit-exact.  forward() selects without logits (for T > 64 the
+    # routing: full size, bit-exact.  forward() selects without logits (for T > 512 the
     # bounded MFMA form); route_logits() runs the fixed-order path that returns them.
     logits_ref = oracle.router_logits(r_h, x_h)
     ids2 = torch.empty_like(layer.ids)
@@ -186,7 +186,7 @@ def test_decode_batches_sorted_gemv(T, bias):
     # 65..4096 pairs: the GEMV kernels in sorted mode (chunks of consecutive sorted positions
     # of one expert, from moe_permute's grouping); under Zipf the hot experts span several
     # chunks, and from 640 pairs the experts with many pairs take the grouped GEMM in the
-    # same call.  Past 64 tokens the router takes its bounded form.
+    # same call.  Up to 512 tokens the router computes its logits by GEMV.
     _check_layer("decode_d2048_e512_top10_t1", T=T, bias=bias, stream=T,
                  sample=None if T <= 102 else 40, tiles=T > 102)
 
@@ -241,12 +241,15 @@ def test_decode_sweep_layer_batch4():
     _check_layer("decode_sweep_48_layers", T=4)
 
 
-@pytest.mark.parametrize("T", [1, 4, 17, 65])
+@pytest.mark.parametrize("T", [1, 4, 17, 65, 513])
 def test_int6_experts_int8_router_small_batches(T):
-    # int6 routed and shared experts through the GEMV kernels (ballot, then sorted mode);
-    # the int8 router by its one-launch form, its split form (T = 17) and its bounded MFMA
-    # form (T = 65)
-    _check_layer("int6_d2048_e64_top10", T=T, stream=T)
+    # int6 routed and shared experts through the GEMV kernels (ballot, then sorted mode) and
+    # at 5130 pairs the grouped GEMM; the int8 router by its one-launch form, its split form
+    # (T = 17, 65) and its bounded MFMA form (T = 513)
+    if T > 512:
+        _check_layer("int6_d2048_e64_top10", T=T, stream=T, sample=40, tiles=True)
+    else:
+        _check_layer("int6_d2048_e64_top10", T=T, stream=T)
 
 
 @pytest.mark.parametrize("name", ["int3_d2048_e512_top10", "int2_d2048_e512_top10"])

@@ -75,7 +75,7 @@ def test_selection_with_ties(name, kind):
     r_h = router.host()
     k = w.k
     T_dec = min(6, 64 // k)
-    for T in (T_dec, 4, 40, 300):
+    for T in (T_dec, 4, 40, 300, 600):
         print("case %s %s T=%d" % (name, kind, T), flush=True)
         x = _tokens(kind, T, w.d, gen).cuda()
         x_h = si.bits16(x)
@@ -112,7 +112,7 @@ def test_selection_with_ties_int8_router(kind):
     router = si.Router("int8_row", w.E, w.d, q.cuda(), sc.cuda(),
                        None if bias is None else bias.cuda())
     r_h = router.host()
-    for T in (40, 300):
+    for T in (40, 300, 600):
         print("case int8 %s T=%d" % (kind, T), flush=True)
         x = _tokens(kind, T, w.d, gen).cuda()
         logits_ref = oracle.router_logits(r_h, si.bits16(x))

@@ -2,8 +2,8 @@
 workloads' own ((256, 128) and (2048, 512)), and at one that only the grouped GEMM serves,
 against the oracle.  16 experts, top-4 plus the shared expert; T = 1 and 4 (GEMV by ballot,
 and the decode layer, which must equal the four calls bit for bit), 20 (80 pairs: the GEMV in
-sorted mode) and 300 (1200 pairs: the grouped MFMA GEMM, the shared expert dense on it too).
-int8 routers where the router has an int8 kernel (d >= 1024), int3 / int6 experts on two of
+sorted mode), 300 (1200 pairs: the grouped MFMA GEMM, the shared expert dense on it too) and
+600 (the router's bounded MFMA form).  int8 routers where the router has an int8 kernel (d >= 1024), int3 / int6 experts on two of
 the shapes.  Bar as everywhere: ids bit-exact, weights |dw| <= 1e-6, rows and outputs within
 2e-2 + 1e-2 |r| and rel-Frobenius 1e-2."""
 import numpy as np
@@ -98,7 +98,7 @@ def test_layer_shapes_against_oracle(i):
     d, F, routed, shared, router = SHAPES[i]
     w = _workload(i, d, F, routed, shared, router)
     lay = synth.make_layer(w, seed=0, device="cuda", bias="zipf")
-    for T in (1, 4, 20, 300):
+    for T in (1, 4, 20, 300, 600):
         print("case d=%d F=%d %s/%s/%s T=%d" % (d, F, routed, shared, router, T), flush=True)
         # the decode layer runs for at most 64 pairs on the shapes with GEMV kernels
         _check_layer(moe, w, lay, T, 5, T * w.k <= 64 and (d, F) != (512, 256))
@@ -134,11 +134,12 @@ def test_most_experts(E, k):
     """The largest expert counts the library takes (E up to 1024: 16 router keys per lane in
     every selection form), at d 256 / F 128, Zipf routing, T = 1 and 4 (one-launch router,
     the decode layer selecting in its gate/up blocks), 20 (logits then the selection
-    kernel) and 300 (the bounded MFMA router), against the oracle."""
+    kernel), 300 (the split router past 64 tokens) and 600 (the bounded MFMA router),
+    against the oracle."""
     moe = _gpu()
     w = synth.Workload("most_experts_e%d_k%d" % (E, k), 70 + k, d=256, E=E, k=k, F=128, T=1)
     lay = synth.make_layer(w, seed=0, device="cuda", bias="zipf")
-    for T in (1, 4, 20, 300):
+    for T in (1, 4, 20, 300, 600):
         print("case E=%d k=%d T=%d" % (E, k, T), flush=True)
         ids, wts = _check_layer(moe, w, lay, T, 9, T * k <= 64)
         assert np.all((ids >= 0) & (ids < E))
