@@ -12,8 +12,9 @@
 //   3. per chunk (16 waves of 64 pairs): the scan of the totals over experts gives the
 //      offsets; each wave ranks its pairs among equal ids (ballot match on the id bits),
 //      waves before it in the chunk add their counts, and the pairs are scattered.
-// A call with at most kChunk pairs runs all three steps in one block, one thread per pair
-// (the several-token decode GEMV reads this grouping too); at most 64 pairs, in one wave.
+// A call with at most 2 kChunk pairs runs all three steps in one block, one or two pairs per
+// thread (the several-token decode GEMV reads this grouping too); at most 64 pairs, in one
+// wave.
 #include "moe_common.h"
 
 namespace moe {
@@ -205,47 +206,66 @@ __global__ void __launch_bounds__(1024) chunk_scatter_kernel(
     }
 }
 
-// All three steps in one block (P <= kChunk), one thread per pair: the histogram (LDS
-// atomics), the scan of the counts gives the offsets, and a pair's position is its
-// expert's offset + the pairs of that expert in earlier waves + its rank in its own wave
-// (ballot match on the id bits).  blockDim.x = 1024.
+// All three steps in one block (P <= R * kChunk), R pairs per thread: pair p = r * kChunk +
+// tid is handled in round r by wave 16 r + (tid >> 6) of R * 16 virtual waves, so virtual
+// waves come in pair order.  The histogram (LDS atomics), the scan of the counts gives the
+// offsets, and a pair's position is its expert's offset + the pairs of that expert in
+// earlier virtual waves + its rank in its own (ballot match on the id bits).
+// blockDim.x = 1024.  R = 2 replaces the three chunked launches from 1025 to 2048 pairs
+// (128 tokens x top-10: 14.4 -> one launch).
+template <int R>
 __global__ void __launch_bounds__(1024) permute_small_kernel(
     const int32_t* __restrict__ ids, int P, int E, int nbits, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
     __shared__ int hist[kMaxE];
     __shared__ int base[kMaxE + 1];
-    __shared__ __attribute__((aligned(16))) uint8_t wcnt[16][kMaxE];   // pairs of wave w with id e (<= 64)
+    // pairs of virtual wave v with id e (<= 64)
+    __shared__ __attribute__((aligned(16))) uint8_t wcnt[16 * R][kMaxE];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (tid < E) hist[tid] = 0;
-    for (int i = tid; i < 16 * kMaxE / 4; i += 1024) reinterpret_cast<uint32_t*>(wcnt)[i] = 0;
-    const bool inrange = tid < P;
-    const int id = inrange ? ids[tid] : -1;
-    const bool valid = inrange && id >= 0 && id < E;
-    if (inrange && !valid) {
-        pair_pos[tid] = -1;
-        atomicOr(&g_bad_id_flag, 1);
+    for (int i = tid; i < 16 * R * kMaxE / 4; i += 1024)
+        reinterpret_cast<uint32_t*>(wcnt)[i] = 0;
+    int id[R], rank[R];
+    bool valid[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int p = r * kChunk + tid;
+        const bool inrange = p < P;
+        id[r] = inrange ? ids[p] : -1;
+        valid[r] = inrange && id[r] >= 0 && id[r] < E;
+        if (inrange && !valid[r]) {
+            pair_pos[p] = -1;
+            atomicOr(&g_bad_id_flag, 1);
+        }
     }
     __syncthreads();
-    if (valid) atomicAdd(&hist[id], 1);
-    const uint64_t m = match_id(id, valid, nbits);
-    const int rank = __popcll(m & ((1ull << lane) - 1ull));
-    if (valid && rank == 0) wcnt[w][id] = (uint8_t)__popcll(m);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (valid[r]) atomicAdd(&hist[id[r]], 1);
+        const uint64_t m = match_id(id[r], valid[r], nbits);
+        rank[r] = __popcll(m & ((1ull << lane) - 1ull));
+        if (valid[r] && rank[r] == 0) wcnt[r * 16 + w][id[r]] = (uint8_t)__popcll(m);
+    }
     __syncthreads();
     block_exclusive_scan(hist, base, E);     // ends with a barrier
     for (int e = tid; e <= E; e += 1024) offsets[e] = base[e];
-    if (valid) {
-        int pos = base[id] + rank;
-        for (int i = 0; i < w; ++i) pos += wcnt[i][id];
-        sorted_pairs[pos] = tid;
-        pair_pos[tid] = pos;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (valid[r]) {
+            const int p = r * kChunk + tid;
+            int pos = base[id[r]] + rank[r];
+            for (int i = 0; i < r * 16 + w; ++i) pos += wcnt[i][id[r]];
+            sorted_pairs[pos] = p;
+            pair_pos[p] = pos;
+        }
     }
 }
 
 }  // namespace
 
-// workspace: [chunk table nchunk x E][expert totals E]
+// workspace: [chunk table nchunk x E][expert totals E]; none for the one-block form
 size_t permute_ws_bytes(int64_t P, int E) {
-    if (P <= kChunk) return 0;
+    if (P <= 2 * kChunk) return 0;
     const int64_t nchunk = (P + kChunk - 1) / kChunk;
     return (size_t)(nchunk + 1) * (size_t)E * sizeof(int);
 }
@@ -260,8 +280,13 @@ hipError_t launch_permute(const int32_t* ids, int T, int k, int E, int32_t* offs
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     if (P <= kChunk) {
-        permute_small_kernel<<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, offsets, sorted_pairs,
-                                                pair_pos);
+        permute_small_kernel<1><<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, offsets,
+                                                   sorted_pairs, pair_pos);
+        return hipGetLastError();
+    }
+    if (P <= 2 * kChunk) {
+        permute_small_kernel<2><<<1, 1024, 0, s>>>(ids, (int)P, E, nbits, offsets,
+                                                   sorted_pairs, pair_pos);
         return hipGetLastError();
     }
     const int nchunk = (int)((P + kChunk - 1) / kChunk);

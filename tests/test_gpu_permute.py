@@ -41,7 +41,8 @@ def _ids(kind, T, k, E, rng):
     (1, 10, 512), (6, 10, 512), (32, 2, 16),                       # one wave
     (7, 10, 512), (64, 10, 512), (100, 10, 1000), (128, 8, 1024),  # one block
     (33, 2, 16), (93, 11, 1000),
-    (103, 10, 512), (500, 10, 512), (4001, 10, 512),               # chunked
+    (103, 10, 512), (204, 10, 512), (128, 16, 1024), (1000, 2, 16),  # one block, 2 per thread
+    (205, 10, 512), (500, 10, 512), (4001, 10, 512),               # chunked
     (2100, 2, 16), (900, 7, 1000), (12289, 8, 1024)])
 @pytest.mark.parametrize("kind", ["uniform", "skewed", "one_expert", "bad_ids"])
 def test_permute_every_form(T, k, E, kind):
