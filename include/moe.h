@@ -227,9 +227,10 @@ moe_status moe_permute(const int32_t* ids, int32_t T, int32_t k, int32_t E,
  * Decode-sized calls on a (d_model, d_ff) pair with a GEMV kernel ((2048, 512),
  * (2048, 1024), (2048, 2048), (4096, 1024), (1024, 512), (256, 128)) stream each selected
  * expert's weights (two launches: gate/up + SwiGLU, then down):
- *   at most 64 rows: each pair's row is derived from ids alone; offsets and sorted_pairs
+ *   at most 24 pairs (grouped), or at most 64 rows (dense): each pair's row is derived
+ *     from ids alone (dense: the token index); offsets and sorted_pairs
  *     are not read, so moe_permute may run concurrently with the call;
- *   more than 64 rows (grouped mode): a third, earlier launch lists each expert's sorted
+ *   more than 24 pairs (grouped mode): a third, earlier launch lists each expert's sorted
  *     positions in chunks of at most 3 from offsets and sorted_pairs (so moe_permute must
  *     have completed), and each chunk streams its expert's weights once; from 640 rows an
  *     expert with 8 or more pairs (4 or more above 1024 rows) runs the grouped MFMA GEMM

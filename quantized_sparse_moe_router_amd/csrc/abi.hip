@@ -79,7 +79,7 @@ size_t route_ws(int64_t T, int E, int d, bool need_logits) {
 // MFMA [h][tile list][count]
 size_t ffn_ws(int64_t rows, int E, int F) {
     size_t gemv = round_up((size_t)rows * (size_t)F * 2);
-    if (rows > moe::kGemvMaxBallotRows) gemv = moe::gemv_sorted_ws_layout(rows, E, F).bytes;
+    if (rows > moe::kGemvMaxBallotPairs) gemv = moe::gemv_sorted_ws_layout(rows, E, F).bytes;
     const size_t mfma = moe::ffn_mfma_ws_bytes(rows, E, F);
     return gemv > mfma ? gemv : mfma;
 }

@@ -11,14 +11,14 @@
 // owns one slot and a block of rows and requests its activation rows and every weight load
 // before any arithmetic.
 //
-// Grouped mode (at most 64 pairs): a slot is a pair p.  A block reads the whole ids vector
+// Grouped mode (at most kGemvMaxBallotPairs = 24 pairs): a slot is a pair p.  A block reads the whole ids vector
 // with one load, so the expert e = ids[p] is known after one memory round trip and the
 // weight loads start at once; the pairs routed to e form a ballot mask, every MT-th of
 // them leads a chunk of MT pairs and the others return.  A pair's row is its
 // expert-sorted position (valid pairs with a smaller id, plus earlier pairs with the same
 // id), the same position moe_permute assigns.
 // Dense mode (shared expert): a slot is a chunk of MT tokens.
-// Sorted mode (more than 64 pairs): the grouping from moe_permute
+// Sorted mode (more than 24 pairs): the grouping from moe_permute
 // is read instead of a ballot; a small kernel lists, expert by expert, chunks of at most MT
 // consecutive sorted positions with their tokens (sentinels fill the list to the grid's
 // size), and a slot is one chunk.  Each expert's rows are streamed once per chunk, four
@@ -231,7 +231,7 @@ hipError_t launch_fmt(const moe_experts& ex, const uint16_t* x, int T, int k,
                       uint16_t* y, void* ws, hipStream_t s) {
 #define MOE_DEC(DV, FV)                                                                  \
     if (ex.d_model == DV && ex.d_ff == FV) {                                             \
-        if (ids && (int64_t)T * k > kGemvMaxBallotRows)                                  \
+        if (ids && (int64_t)T * k > kGemvMaxBallotPairs)                                 \
             return launch_sorted_mt<FMT, DV, FV, kGemvSortedMT>(ex, x, T, k, offsets,    \
                                                                 sorted, y, ws, s);       \
         return launch_shape<FMT, DV, FV>(ex, x, T, k, ids, y, ws, s);                    \

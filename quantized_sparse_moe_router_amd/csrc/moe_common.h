@@ -287,6 +287,11 @@ size_t permute_ws_bytes(int64_t P, int E);
 // chunk); at prefill sizes that leaves the GEMM only the experts worth a tile.  Dense mode
 // (ids == nullptr): the token index, at most kGemvMaxBallotRows tokens.
 constexpr int64_t kGemvMaxBallotRows = 64;
+// Grouped calls leave the ballot for sorted mode above this many pairs: the ballot's slots
+// stream the experts' weights at a lower rate than the sorted chunks once a call holds a few
+// dozen pairs (four-call layer, top-10 of 512: 3 tokens 44.8 -> 39.6 us, 4 51.8 -> 43.2,
+// 6 65.3 -> 50.7 in sorted mode; 2 tokens 35.6 -> 36.0).
+constexpr int64_t kGemvMaxBallotPairs = 24;
 constexpr int kGemvSortedMT = 3;    // pairs of one expert per pass over its weights
 constexpr int64_t kHybridMinRows = 640;
 constexpr int kMfmaTileRows = 256;  // pairs per entry of the grouped GEMM's work list

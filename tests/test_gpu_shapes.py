@@ -111,7 +111,8 @@ def test_degenerate_routing(E, k, bias):
     decides nothing: every id 0, every weight exactly 1), every expert selected (k = E: the
     ids are a permutation of all experts in descending logit order, the weights a softmax
     over all of them, summing to 1), and top-1 (a single pair per token, weight exactly 1).
-    k = E = 64 at one token fills the 64 pairs of the ballot GEMV and the decode layer;
+    k = E = 64 at one token fills the 64 pairs of the decode layer (the four calls take the
+    sorted GEMV from 25 pairs);
     T = 4, 20 and 300 take the sorted GEMV, the GEMV / grouped GEMM split and the grouped
     GEMM."""
     moe = _gpu()
