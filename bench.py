@@ -350,7 +350,7 @@ def main():
                      "min_launch_us": round(ms_exp_min / L * 1e3, 3)},
     }
 
-    # ---- decode batches: 1 .. 64 tokens per call through the layer (several decode slots
+    # ---- decode batches: 1 .. 128 tokens per call through the layer (several decode slots
     # or drafts verified together), on the same rotated copies
     if not args.no_batches:
         line["decode_batches"] = decode_batches(
@@ -549,9 +549,9 @@ def decode_batches(moe, synth, np, torch, copies, w, args, Ts=(1, 4, 6, 8, 16, 3
     """T tokens per call through the decode layer (d 2048, 512 experts, top-10 + shared),
     T = 1 .. 128: the four calls (forward) and, while T*k <= 64, moe_layer_decode; each step
     on the next of the rotated layer copies (more than the 256 MB cache holds for T >= 2).
-    Up to 4096 pairs the routed experts run the weight-streaming GEMV (sorted mode past 64
-    pairs; from 640 pairs the experts with many pairs on the grouped MFMA GEMM), above it the
-    GEMM alone.  Weight-stream bytes: router + (distinct routed experts + shared) x 1.77 MB."""
+    The routed experts run the weight-streaming GEMV (sorted mode past 24 pairs; from 640
+    pairs the experts with many pairs on the grouped MFMA GEMM); the router computes its
+    logits by GEMV up to 512 tokens.  Weight-stream bytes: router + (distinct routed experts + shared) x 1.77 MB."""
     E_b = expert_bytes(copies[0].routed)
     r_b = copies[0].router.w.numel() * copies[0].router.w.element_size()
     n_cp = len(copies)
