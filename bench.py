@@ -97,6 +97,9 @@ def parse():
                    help="skip the decode batch sizes 1..128")
     p.add_argument("--batch-sizes", default="1,4,6,8,16,32,64,96,128",
                    help="tokens per call of the decode-batches leg (comma-separated)")
+    p.add_argument("--zipf-batch-sizes", default="16,32,64,96,128",
+                   help="tokens per call of the Zipf-routed decode-batches leg "
+                        "(comma-separated; empty skips the leg)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="no graph capture (for profilers)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -359,13 +362,15 @@ def main():
         torch.cuda.empty_cache()
         # the same with the router's bias skewing the routing (Zipf, s = 1.1): fewer distinct
         # experts, some chosen by many of the call's tokens
-        zbase = synth.make_layer(w, seed=0, device="cuda", bias="zipf")
-        zcopies = [zbase] + [clone_layer(zbase) for _ in range(L - 1)]
-        line["decode_batches_zipf"] = decode_batches(
-            moe, synth, np, torch, zcopies, w, args, Ts=(16, 32, 64, 96, 128))
-        line["decode_batches_zipf"]["routing"] = "zipf s=1.1 (router bias)"
-        del zbase, zcopies
-        torch.cuda.empty_cache()
+        zts = tuple(int(t) for t in args.zipf_batch_sizes.split(",") if t.strip())
+        if zts:
+            zbase = synth.make_layer(w, seed=0, device="cuda", bias="zipf")
+            zcopies = [zbase] + [clone_layer(zbase) for _ in range(L - 1)]
+            line["decode_batches_zipf"] = decode_batches(
+                moe, synth, np, torch, zcopies, w, args, Ts=zts)
+            line["decode_batches_zipf"]["routing"] = "zipf s=1.1 (router bias)"
+            del zbase, zcopies
+            torch.cuda.empty_cache()
 
     # ---- lower-bit expert codecs: the same decode step with every expert at 3 or 2 bits
     if not args.no_low_bit:
