@@ -65,6 +65,11 @@ def test_workspace_sizes(L):
     # small permutes run in one block without workspace
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 1, 10, 512, 2048, 512) == 0
     assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 8192, 10, 512, 2048, 512) >= 80 * 512 * 4
+    # the one-block grouping (up to 2048 pairs, two per thread) needs none; above, a chunk
+    # table of 1024-pair chunks plus the expert totals
+    assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 204, 10, 512, 0, 0) == 0
+    assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 128, 16, 1024, 0, 0) == 0
+    assert L.moe_workspace_size(_lib.MOE_OP_PERMUTE, 205, 10, 512, 0, 0) == (3 + 1) * 512 * 4
     assert L.moe_workspace_size(_lib.MOE_OP_EXPERT_FFN, 1, 10, 512, 2048, 512) >= 10 * 512 * 2
     # the decode operations report 0 where they do not run: more than 64 pairs, or a
     # (d_model, d_ff) pair without decode kernels
